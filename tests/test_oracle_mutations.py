@@ -1,0 +1,167 @@
+"""Plant plausible mistakes into the oracle (CPU only) and check that the
+pins catch every one of them."""
+
+import numpy as np
+import pytest
+
+import oracle.convrot_oracle as O
+from tests import oracle_pins as P
+
+_h4 = O.h4
+_sylvester = O.sylvester
+_rotate64 = O.rotate64
+_quantize_rows = O.quantize_rows
+_epilogue64 = O.epilogue64
+_int_gemm = O.int_gemm
+_bf16_round = O.bf16_round
+_randomized_block = O.randomized_block
+
+
+def _h4_sign_flip():
+    m = _h4().copy()
+    m[0, 3] = -m[0, 3]
+    return m
+
+
+def _h4_unnormalised():
+    return _h4() * 2.0
+
+
+def _h4_wrong_row_order():
+    return _h4()[::-1].copy()
+
+
+def _rotate_strided_groups(X, G, kind=O.REGULAR, signs=None):
+    # groups taken as columns {b, b + nb, ...} instead of contiguous blocks
+    X = np.asarray(X, np.float64)
+    rows, K = X.shape
+    nb = K // G
+    Xt = X.reshape(rows, G, nb).transpose(0, 2, 1).reshape(rows, K)
+    out = _rotate64(Xt, G, kind, signs)
+    return out.reshape(rows, nb, G).transpose(0, 2, 1).reshape(rows, K)
+
+
+def _rotate_signs_after(X, G, kind=O.REGULAR, signs=None):
+    if kind != O.RANDOMIZED:
+        return _rotate64(X, G, kind, signs)
+    X = np.asarray(X, np.float64)
+    rows, K = X.shape
+    nb = K // G
+    d = np.asarray(signs, np.float64).reshape(nb, G)
+    out = (X.reshape(rows, nb, G) @ O.sylvester(G)) * d[None] / np.sqrt(G)
+    return out.reshape(rows, K)
+
+
+def _rotate_no_normalise(X, G, kind=O.REGULAR, signs=None):
+    out = _rotate64(X, G, kind, signs)
+    return out * np.sqrt(G) if kind == O.RANDOMIZED else out
+
+
+def _quant_128(x):
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(128)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    q[nz] = np.clip(np.rint(x[nz] / s[nz][:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def _quant_half_away(x):
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(127)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    v = (x[nz] / s[nz][:, None]).astype(np.float32)
+    q[nz] = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -127, 127).astype(np.int8)
+    return q, s
+
+
+def _quant_truncate(x):
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(127)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    q[nz] = np.clip(np.trunc(x[nz] / s[nz][:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def _quant_first_group_scale(x):
+    # scale from the first 4 columns only instead of the whole row
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x[:, :4]), axis=1)
+    s = (amax / np.float32(127)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    q[nz] = np.clip(np.rint(x[nz] / s[nz][:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def _epi_no_bias(A, sx, sw, bias=None):
+    return _epilogue64(A, sx, sw, None)
+
+
+def _epi_no_sw(A, sx, sw, bias=None):
+    return _epilogue64(A, sx, np.ones_like(np.asarray(sw)), bias)
+
+
+def _epi_swapped(A, sx, sw, bias=None):
+    A = np.asarray(A, np.float64)
+    Y = A * np.resize(np.asarray(sw, np.float64), A.shape[0])[:, None]
+    Y = Y * np.resize(np.asarray(sx, np.float64), A.shape[1])[None, :]
+    return Y + (0 if bias is None else np.asarray(bias, np.float64)[None, :])
+
+
+def _gemm_untransposed(Qx, Qw):
+    return (Qx.astype(np.float64) @ Qw.astype(np.float64).T[::-1]).astype(np.int64) \
+        if Qx.shape[1] == Qw.shape[1] else None
+
+
+def _gemm_float32(Qx, Qw):
+    return (Qx.astype(np.float32) @ Qw.astype(np.float32).T).astype(np.int64)
+
+
+def _bf16_truncate(x):
+    u = np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint32)
+    return (u & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def _sylvester_wrong_sign(G):
+    h = _sylvester(G).copy()
+    h[-1, -1] = -h[-1, -1]
+    return h
+
+
+MUTATIONS = {
+    "h4_sign_flip": ("h4", _h4_sign_flip),
+    "h4_unnormalised": ("h4", _h4_unnormalised),
+    "h4_row_order": ("h4", _h4_wrong_row_order),
+    "rotate_strided_groups": ("rotate64", _rotate_strided_groups),
+    "randomized_signs_after_wht": ("rotate64", _rotate_signs_after),
+    "randomized_no_normalise": ("rotate64", _rotate_no_normalise),
+    "sylvester_wrong_sign": ("sylvester", _sylvester_wrong_sign),
+    "quant_divides_by_128": ("quantize_rows", _quant_128),
+    "quant_half_away": ("quantize_rows", _quant_half_away),
+    "quant_truncates": ("quantize_rows", _quant_truncate),
+    "quant_partial_row_scale": ("quantize_rows", _quant_first_group_scale),
+    "epilogue_drops_bias": ("epilogue64", _epi_no_bias),
+    "epilogue_drops_weight_scale": ("epilogue64", _epi_no_sw),
+    "epilogue_swaps_scales": ("epilogue64", _epi_swapped),
+    "gemm_wrong_operand_order": ("int_gemm", _gemm_untransposed),
+    "gemm_float32_accumulation": ("int_gemm", _gemm_float32),
+    "bf16_truncates": ("bf16_round", _bf16_truncate),
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert P.run_all() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = P.run_all()
+    assert failed, f"planted mistake {name!r} passed every pin"
