@@ -1,0 +1,179 @@
+/*
+ * convrot.h -- C ABI of the MI355X (gfx950) INT8 ConvRot W8A8 linear layer.
+ *
+ * The method (stable-diffusion.cpp documentation page "INT8 Convrot
+ * Safetensors", sections "How INT8 convrot works", "Weight quantization" and
+ * "Runtime activation quantization"):
+ *
+ *   R        block-diagonal rotation; every contiguous group of G input
+ *            features is multiplied by the normalised Kronecker power of the
+ *            4x4 regular Hadamard matrix H4 (G = 4^n).  R is orthogonal and
+ *            symmetric.
+ *   W_rot  = W R          (offline)      X_rot = X R          (run time)
+ *   s[r]   = max_i |rot[r, i]| / 127     one scale per row (weights: per
+ *                                        output row; activations: per row,
+ *                                        computed at run time)
+ *   Q[r,i] = clamp(round(rot[r, i] / s[r]), -127, 127)
+ *   A[r,o] = sum_i Qx[r, i] * Qw[o, i]   exact signed 32-bit accumulation
+ *   Y[r,o] = A[r, o] * s_x[r] * s_w[o] + b[o]
+ *
+ * One packed activation (Qx, s_x) serves every linear layer that shares the
+ * same input and the same rotation (same page, "Runtime activation
+ * quantization", last paragraph).
+ *
+ * A second rotation kind follows the gemma.cpp issue "Add experimental W8A8
+ * MatMul with optional QuaRot-style rotation", section "Rotation method":
+ * each block of G features is multiplied elementwise by fixed +-1 signs,
+ * then by the natural-order (Sylvester) Walsh-Hadamard matrix, then by
+ * 1/sqrt(G); the same transform is applied to activation rows and to weight
+ * rows.
+ *
+ * Layers whose input width K is not a multiple of G stay unquantised (sglang
+ * PR 34581 summary page, implementation section on kitchen_int8 routing);
+ * convrot_linear_bf16 is that path.  The library never falls back silently:
+ * routing is the caller's decision.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device,
+ *   row-major, with explicit leading dimensions counted in ELEMENTS of the
+ *   tensor's own type.  Every input matrix (X, W, packed codes) and every
+ *   output of the pack and rotate entry points must have a 16-byte aligned
+ *   base and a leading dimension whose size in bytes is a multiple of 16.
+ *   The Y output of the linear entry points only needs element alignment.
+ * - The caller owns every buffer.  The library allocates no device memory
+ *   and keeps no mutable global state beyond a thread-local error string.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the
+ *   default stream).  Inputs must stay alive, and outputs untouched, until
+ *   the stream has passed the call.  Outputs must not alias inputs.
+ * - Validation happens on the host before anything is enqueued.  On any
+ *   error the call enqueues nothing, leaves outputs untouched and returns a
+ *   non-zero status; convrot_last_error() then describes it.  A launch that
+ *   the HIP runtime rejects returns CONVROT_ERR_HIP.
+ * - Empty problems (M == 0 or N == 0) return CONVROT_OK and launch nothing.
+ * - K must be a positive multiple of 16 (the kernels move 16-byte chunks).
+ * - Non-finite inputs are outside the method's domain; results are then
+ *   unspecified (no fault, no error).
+ * - No exception crosses this boundary.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVROT_ABI_VERSION 1
+
+typedef enum {
+  CONVROT_OK = 0,
+  CONVROT_ERR_INVALID_ARG = 1, /* null pointer, negative size, K % 16 != 0, bad leading dimension */
+  CONVROT_ERR_GROUP = 2,       /* G not allowed for the rotation kind, or K % G != 0 */
+  CONVROT_ERR_DTYPE = 3,       /* element type not accepted by this entry point */
+  CONVROT_ERR_ALIGN = 4,       /* base pointer not 16-byte aligned, or ld * elt % 16 != 0 */
+  CONVROT_ERR_MISMATCH = 5,    /* activation and weight packed with different K or rotation */
+  CONVROT_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} convrot_status;
+
+typedef enum {
+  CONVROT_F32 = 0,
+  CONVROT_BF16 = 1,
+  CONVROT_I32 = 2 /* raw accumulator A (convrot_linear output only; for checking) */
+} convrot_dtype;
+
+typedef enum {
+  /* "INT8 Convrot Safetensors": R_G = normalised H4^{(x)n}, G = 4^n in {4, 16, 64, 256, 1024}. */
+  CONVROT_ROT_REGULAR = 0,
+  /* gemma.cpp issue, "Rotation method": (1/sqrt G) H_sylvester D, G = 2^m in {16, 32, ..., 1024}. */
+  CONVROT_ROT_RANDOMIZED = 1
+} convrot_rot_kind;
+
+/* Rotation descriptor.  `signs` is a device vector of K int8 values, each +1
+ * or -1 (one sign per input feature, block b using signs[b*G .. b*G+G-1]);
+ * it is required for CONVROT_ROT_RANDOMIZED and must be NULL otherwise. */
+typedef struct {
+  int32_t group;        /* G */
+  int32_t kind;         /* convrot_rot_kind */
+  const int8_t* signs;  /* [K] +-1, randomized kind only */
+} convrot_rot;
+
+/* A packed operand: int8 rows and one fp32 scale per row, both caller-owned
+ * device buffers, plus the rotation that produced them.
+ *   q      [rows, ld] int8, row-major, ld >= K, ld % 16 == 0
+ *   scale  [rows] fp32
+ * The same struct describes a packed activation (rows = M) and a packed
+ * weight (rows = N; the canonical checkpoint layout, one int8 row per output
+ * feature, "INT8 Convrot Safetensors", "Checkpoint format"). */
+typedef struct {
+  int8_t* q;
+  float* scale;
+  int64_t rows;
+  int64_t K;
+  int64_t ld;
+  convrot_rot rot;
+} convrot_packed;
+
+/* Rotate and quantise activation rows ("Runtime activation quantization").
+ *   X     [out->rows, ldx] of `xdt` (CONVROT_F32 or CONVROT_BF16), K = out->K
+ *   out   descriptor of the caller-owned destination; out->q and out->scale
+ *         are written, the struct itself is not modified.
+ * One fused kernel: group-wise Hadamard rotation, whole-row absmax, rounding
+ * to nearest even and clamping to [-127, 127].  An all-zero row gets scale 0
+ * and zero codes.  Deterministic: the same input gives the same bits. */
+convrot_status convrot_pack_act(const void* X, convrot_dtype xdt, int64_t ldx,
+                                const convrot_packed* out, void* stream);
+
+/* Rotate and quantise weight rows ("Weight quantization"): the same
+ * transform and rule as convrot_pack_act, one scale per output row.  Runs
+ * once, offline, on W [out->rows = N, K]. */
+convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw,
+                                   const convrot_packed* out, void* stream);
+
+/* The quantised linear ("Runtime activation quantization"):
+ *   Y[r, o] = A[r, o] * act->scale[r] * w->scale[o] + bias[o]
+ * with A the exact int32 product of act->q and w->q^T.
+ *   act   packed activation [M = act->rows, K]
+ *   w     packed weight [N = w->rows, K]; act->K == w->K and the two
+ *         rotation descriptors must be equal (same G, kind and signs
+ *         pointer), otherwise CONVROT_ERR_MISMATCH
+ *   bias  [N] fp32 or NULL
+ *   Y     [M, ldy] of `ydt`: CONVROT_F32, CONVROT_BF16 (round to nearest
+ *         even) or CONVROT_I32 (the raw accumulator A; scales and bias are
+ *         then not applied)
+ * Small M uses a weight-streaming kernel, larger M a tiled matrix-core
+ * kernel; both produce bit-identical A. */
+convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w,
+                              const float* bias, void* Y, convrot_dtype ydt, int64_t ldy,
+                              void* stream);
+
+/* The unquantised path for layers the rotation cannot cover (K % G != 0):
+ *   Y[r, o] = sum_i X[r, i] W[o, i] + bias[o]
+ * bf16 operands, fp32 accumulation, output CONVROT_BF16 or CONVROT_F32.
+ *   X [M, ldx] bf16, W [N, ldw] bf16, bias [N] fp32 or NULL, Y [M, ldy]. */
+convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                   const float* bias, int64_t M, int64_t N, int64_t K,
+                                   void* Y, convrot_dtype ydt, int64_t ldy, void* stream);
+
+/* The rotation alone, for checking: the same kernel as convrot_pack_act with
+ * quantisation switched off, writing the fp32 rotated rows X R.
+ *   X [M, ldx] of `xdt`, Xrot [M, ldr] fp32. */
+convrot_status convrot_rotate(const void* X, convrot_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                              convrot_rot rot, float* Xrot, int64_t ldr, void* stream);
+
+/* Static description of a status code. */
+const char* convrot_status_string(convrot_status status);
+
+/* Description of the last error returned on the calling thread ("" if the
+ * last call succeeded). */
+const char* convrot_last_error(void);
+
+/* CONVROT_ABI_VERSION of the built library. */
+int convrot_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -1,0 +1,194 @@
+"""The C ABI library on the host: it loads, exports every entry point that
+include/convrot.h declares, and rejects bad arguments before launching
+anything (CPU only: no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from w8a8_int8_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+# Fake, 16-byte aligned "device" addresses: validation never dereferences them.
+A16 = 0x10000
+A16B = 0x20000
+A16C = 0x30000
+MIS = 0x10008
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header(lib):
+    src = open(HEADER).read()
+    v = int(re.search(r"#define CONVROT_ABI_VERSION (\d+)", src).group(1))
+    assert lib.convrot_abi_version() == v == _lib.ABI_VERSION
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["CONVROT_OK", "CONVROT_ERR_INVALID_ARG", "CONVROT_ERR_GROUP", "CONVROT_ERR_DTYPE",
+                                 "CONVROT_ERR_ALIGN", "CONVROT_ERR_MISMATCH", "CONVROT_ERR_HIP"]):
+        assert lib.convrot_status_string(code).decode() == name
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(_lib.Rot) == 16
+    assert ctypes.sizeof(_lib.Packed) == 56
+    assert _lib.Packed.rot.offset == 40
+
+
+def packed(rows=4, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=A16, scale=A16B):
+    return _lib.Packed(q, scale, rows, K, ld if ld is not None else K, _lib.Rot(G, kind, signs))
+
+
+def pack_status(lib, X=A16C, xdt=_lib.BF16, ldx=None, out=None):
+    out = out if out is not None else packed()
+    return lib.convrot_pack_act(X, xdt, ldx if ldx is not None else out.K, ctypes.byref(out), None)
+
+
+@pytest.mark.parametrize("G", [2, 8, 32, 128, 512, 2048, 0, -4])
+def test_pack_rejects_regular_group(lib, G):
+    assert pack_status(lib, out=packed(K=4096, G=G)) == _lib.ERR_GROUP
+
+
+def test_pack_rejects_k_not_multiple_of_g(lib):
+    assert pack_status(lib, out=packed(K=2688, G=256)) == _lib.ERR_GROUP
+    assert b"2688" in lib.convrot_last_error()
+
+
+def test_pack_rejects_k_not_multiple_of_16(lib):
+    assert pack_status(lib, out=packed(K=1028, G=4)) == _lib.ERR_INVALID_ARG
+
+
+def test_pack_rejects_k_too_large(lib):
+    assert pack_status(lib, out=packed(K=65536 + 1024, G=1024)) == _lib.ERR_INVALID_ARG
+
+
+def test_pack_rejects_dtype(lib):
+    assert pack_status(lib, xdt=_lib.I32) == _lib.ERR_DTYPE
+    assert pack_status(lib, xdt=7) == _lib.ERR_DTYPE
+
+
+def test_pack_rejects_null_and_misaligned(lib):
+    assert pack_status(lib, X=None) == _lib.ERR_INVALID_ARG
+    assert pack_status(lib, out=packed(q=None)) == _lib.ERR_INVALID_ARG
+    assert pack_status(lib, out=packed(scale=None)) == _lib.ERR_INVALID_ARG
+    assert pack_status(lib, X=MIS) == _lib.ERR_ALIGN
+    assert pack_status(lib, out=packed(q=MIS)) == _lib.ERR_ALIGN
+    assert pack_status(lib, out=packed(scale=A16B + 2)) == _lib.ERR_ALIGN
+    assert lib.convrot_pack_act(A16C, _lib.BF16, 256, None, None) == _lib.ERR_INVALID_ARG
+
+
+def test_pack_rejects_bad_leading_dimensions(lib):
+    assert pack_status(lib, ldx=128) == _lib.ERR_INVALID_ARG        # ld < K
+    assert pack_status(lib, ldx=260) == _lib.ERR_ALIGN               # 520 bytes
+    assert pack_status(lib, out=packed(ld=264)) == _lib.ERR_ALIGN    # int8 ld % 16
+    assert pack_status(lib, out=packed(ld=200)) == _lib.ERR_INVALID_ARG
+
+
+def test_pack_rotation_kind_and_signs(lib):
+    assert pack_status(lib, out=packed(G=128, kind=_lib.ROT_RANDOMIZED, K=1152)) == _lib.ERR_INVALID_ARG
+    assert pack_status(lib, out=packed(G=256, signs=A16)) == _lib.ERR_INVALID_ARG
+    assert pack_status(lib, out=packed(G=128, kind=_lib.ROT_RANDOMIZED, K=1152, signs=MIS)) == _lib.ERR_ALIGN
+    assert pack_status(lib, out=packed(G=8, kind=_lib.ROT_RANDOMIZED, K=1152, signs=A16)) == _lib.ERR_GROUP
+    assert pack_status(lib, out=packed(G=2048, kind=_lib.ROT_RANDOMIZED, K=4096, signs=A16)) == _lib.ERR_GROUP
+    assert pack_status(lib, out=packed(kind=5)) == _lib.ERR_INVALID_ARG
+
+
+def test_pack_zero_rows_is_a_no_op(lib):
+    assert pack_status(lib, out=packed(rows=0)) == _lib.OK
+    assert lib.convrot_last_error() == b""
+    assert pack_status(lib, out=packed(rows=-1)) == _lib.ERR_INVALID_ARG
+
+
+def linear_status(lib, act=None, w=None, bias=None, Y=A16C, ydt=_lib.BF16, ldy=None):
+    act = act if act is not None else packed(rows=32)
+    w = w if w is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    return lib.convrot_linear(ctypes.byref(act), ctypes.byref(w), bias, Y, ydt,
+                              ldy if ldy is not None else w.rows, None)
+
+
+def test_linear_mismatch(lib):
+    assert linear_status(lib, w=packed(rows=64, K=512, q=0x40000)) == _lib.ERR_MISMATCH
+    assert linear_status(lib, w=packed(rows=64, G=64, q=0x40000)) == _lib.ERR_MISMATCH
+    a = packed(rows=32, G=128, kind=_lib.ROT_RANDOMIZED, K=1152, signs=0x60000)
+    w = packed(rows=64, G=128, kind=_lib.ROT_RANDOMIZED, K=1152, signs=0x70000, q=0x40000)
+    assert linear_status(lib, act=a, w=w) == _lib.ERR_MISMATCH
+    a2 = packed(rows=32, G=16, K=1152)
+    assert linear_status(lib, act=a2, w=packed(rows=64, G=16, kind=_lib.ROT_RANDOMIZED, K=1152,
+                                                 signs=0x60000, q=0x40000)) == _lib.ERR_MISMATCH
+
+
+def test_linear_output_checks(lib):
+    assert linear_status(lib, ydt=9) == _lib.ERR_DTYPE
+    assert linear_status(lib, Y=None) == _lib.ERR_INVALID_ARG
+    assert linear_status(lib, Y=A16C + 1) == _lib.ERR_ALIGN        # not element aligned
+    assert linear_status(lib, Y=A16C + 2, ydt=_lib.F32) == _lib.ERR_ALIGN
+    assert linear_status(lib, ldy=32) == _lib.ERR_INVALID_ARG     # ldy < N
+    assert linear_status(lib, bias=A16 + 2) == _lib.ERR_ALIGN
+    assert lib.convrot_linear(None, None, None, A16C, _lib.BF16, 64, None) == _lib.ERR_INVALID_ARG
+
+
+def test_linear_empty_is_a_no_op(lib):
+    assert linear_status(lib, act=packed(rows=0)) == _lib.OK
+    assert linear_status(lib, w=packed(rows=0, q=0x40000), ldy=0) == _lib.OK
+
+
+def test_linear_k_overflow_guard(lib):
+    K = 1024 * 1024
+    assert linear_status(lib, act=packed(rows=4, K=K, G=1024),
+                         w=packed(rows=4, K=K, G=1024, q=0x40000)) == _lib.ERR_INVALID_ARG
+
+
+def test_linear_bf16_checks(lib):
+    f = lib.convrot_linear_bf16
+    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2690, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.I32, 16, None) == _lib.ERR_DTYPE
+    assert f(None, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2684, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2688, A16B, 2688, None, 0, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.OK
+
+
+def test_rotate_checks(lib):
+    f = lib.convrot_rotate
+    rot = _lib.Rot(256, _lib.ROT_REGULAR, None)
+    assert f(A16, _lib.BF16, 4, 2688, 2688, rot, A16B, 2688, None) == _lib.ERR_GROUP
+    assert f(A16, _lib.BF16, 4, 1024, 1024, rot, MIS, 1024, None) == _lib.ERR_ALIGN
+    assert f(A16, _lib.BF16, 0, 1024, 1024, rot, A16B, 1024, None) == _lib.OK
+
+
+def test_error_string_is_cleared_by_success(lib):
+    assert pack_status(lib, out=packed(K=2688)) == _lib.ERR_GROUP
+    assert lib.convrot_last_error() != b""
+    assert pack_status(lib, out=packed(rows=0)) == _lib.OK
+    assert lib.convrot_last_error() == b""
+
+
+def test_python_layer_raises_on_error():
+    with pytest.raises(_lib.ConvrotError) as e:
+        _lib.check(_lib.ERR_GROUP)
+    assert e.value.status == _lib.ERR_GROUP
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "nope.so"))

@@ -1,0 +1,135 @@
+"""Parity of the quantised linear (tiled MFMA GEMM and small-M kernel) with
+the CPU oracle: the int32 accumulator bit-exact, Y within tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.convrot_oracle as O
+import w8a8_int8_linear_amd as cr
+from tests import parity as R
+from tests.gpu_util import to_dev, to_np
+from workloads import config1, random_codes, random_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed_from_codes(q, s, G, cuda):
+    return cr.Packed(to_dev(q, torch.int8), to_dev(s, torch.float32), G)
+
+
+GEMM_SHAPES = [
+    # (M, N, K, G): several 256x256 tiles with ragged M/N tails, K tails
+    (300, 520, 1024, 256), (256, 256, 128, 64), (513, 260, 3072, 256), (17, 33, 64, 64),
+    (700, 1000, 1040, 16), (64, 1024, 1024, 256), (1000, 300, 12288, 256), (257, 4, 256, 256),
+    (40, 8, 1152, 64),
+    # small M: the weight-streaming kernel
+    (1, 6912, 1152, 64), (4, 1152, 6912, 64), (16, 520, 1024, 256), (3, 17, 80, 16), (16, 16, 64, 4),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+def test_accumulator_bit_exact(cuda, M, N, K, G):
+    qx = random_codes((M, K), seed=M + 3 * K)
+    qw = random_codes((N, K), seed=N + 5 * K)
+    sx = np.ones(M, np.float32)
+    sw = np.ones(N, np.float32)
+    A_gpu = to_np(cr.linear(_packed_from_codes(qx, sx, G, cuda), _packed_from_codes(qw, sw, G, cuda),
+                            out_dtype=torch.int32))
+    A_ref = O.int_gemm(qx, qw)
+    assert np.array_equal(A_gpu.astype(np.int64), A_ref)
+
+
+def test_accumulator_extremes(cuda):
+    K = 12288
+    qx = np.full((20, K), 127, np.int8)
+    qx[1::2] = -127
+    qw = np.full((40, K), -127, np.int8)
+    qw[::3] = 127
+    sx, sw = np.ones(20, np.float32), np.ones(40, np.float32)
+    A = to_np(cr.linear(_packed_from_codes(qx, sx, 256, cuda), _packed_from_codes(qw, sw, 256, cuda),
+                        out_dtype=torch.int32))
+    assert np.array_equal(A.astype(np.int64), O.int_gemm(qx, qw))
+    assert np.max(np.abs(A)) == K * 127 * 127
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (16, 520, 1024), (1, 64, 256)])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_epilogue_from_oracle_codes(cuda, M, N, K, with_bias):
+    G = 256
+    g = np.random.default_rng(M + N)
+    qx, qw = random_codes((M, K), 1), random_codes((N, K), 2)
+    sx = g.uniform(1e-3, 0.1, M).astype(np.float32)
+    sw = g.uniform(1e-5, 1e-3, N).astype(np.float32)
+    b = (g.standard_normal(N) * 0.01).astype(np.float32) if with_bias else None
+    y64 = O.epilogue64(O.int_gemm(qx, qw), sx, sw, b)
+    a, w = _packed_from_codes(qx, sx, G, cuda), _packed_from_codes(qw, sw, G, cuda)
+    bd = to_dev(b, torch.float32) if with_bias else None
+    y32 = to_np(cr.linear(a, w, bd, out_dtype=torch.float32))
+    assert R.rel_fro(y32, y64.astype(np.float32)) <= 1e-6
+    ybf = to_np(cr.linear(a, w, bd, out_dtype=torch.bfloat16))
+    ref_bf = O.bf16_round(y64.astype(np.float32))
+    assert R.rel_fro(ybf, ref_bf) <= 1e-3
+    # bf16 outputs are the RNE rounding of the kernel's own fp32 outputs
+    assert np.array_equal(ybf, O.bf16_round(y32))
+
+
+def test_unit_layer_end_to_end(cuda):
+    """Unit layer (fp32 X [64, 1024] with 0.5% outliers x50, W [1024, 1024],
+    G=256): GPU pack of X and W, GPU linear, against the oracle."""
+    wl = config1()
+    lin = wl.linears[0]
+    x, W, b = wl.X, lin.W, lin.b
+    qw_ref, sw_ref, xrw = O.pack(W, 256)
+    ref = O.linear(x, qw_ref, sw_ref, b, 256)
+    pw = cr.pack_weight(to_dev(W, torch.float32), 256)
+    rep_w = R.compare_codes(to_np(pw.q), qw_ref, O.code_values(xrw, sw_ref))
+    assert rep_w.ok(), rep_w
+    pa = cr.pack_act(to_dev(x, torch.float32), 256)
+    rep_x = R.compare_codes(to_np(pa.q), ref["qx"], O.code_values(ref["xrot"], ref["sx"]))
+    assert rep_x.ok(), rep_x
+    y = to_np(cr.linear(pa, pw, to_dev(b, torch.float32), out_dtype=torch.float32))
+    err = R.rel_fro(y, ref["y32"])
+    print(f"unit layer: rel Frobenius {err:.3e}; {rep_x}; {rep_w}")
+    assert err <= R.Y_RTOL
+
+
+def test_small_m_kernel_matches_tiled_kernel(cuda):
+    K, N = 3072, 1000
+    qx, qw = random_codes((48, K), 7), random_codes((N, K), 8)
+    s48, sw = np.ones(48, np.float32), np.ones(N, np.float32)
+    w = _packed_from_codes(qw, sw, 256, cuda)
+    full = cr.linear(_packed_from_codes(qx, s48, 256, cuda), w, out_dtype=torch.int32)
+    for m in (1, 5, 16):
+        small = cr.linear(_packed_from_codes(qx[:m], s48[:m], 256, cuda), w, out_dtype=torch.int32)
+        assert torch.equal(small, full[:m])
+
+
+def test_row_split_bit_exact(cuda):
+    """Rows are independent: 8192-row style chunking (here 256) gives the same bits."""
+    x = to_dev(random_rows((700, 1024), 9, dtype="bf16"), torch.bfloat16)
+    w = cr.pack_weight(to_dev(random_rows((300, 1024), 10, sigma=0.02, dtype="bf16"), torch.bfloat16), 256)
+    b = torch.randn(300, device=cuda) * 0.01
+    pa = cr.pack_act(x, 256)
+    full = cr.linear(pa, w, b)
+    parts = [cr.linear(cr.pack_act(x[s:e], 256), w, b) for s, e in ((0, 256), (256, 512), (512, 700))]
+    assert torch.equal(torch.cat(parts), full)
+    again = cr.linear(pa, w, b)
+    assert torch.equal(again, full)
+
+
+def test_strided_output(cuda):
+    qx, qw = random_codes((100, 512), 11), random_codes((200, 512), 12)
+    a = _packed_from_codes(qx, np.ones(100, np.float32), 256, cuda)
+    w = _packed_from_codes(qw, np.ones(200, np.float32), 256, cuda)
+    buf = torch.full((100, 264), -7, dtype=torch.int32, device=cuda)
+    cr.linear(a, w, out_dtype=torch.int32, out=buf[:, 8:208])
+    assert np.array_equal(to_np(buf[:, 8:208]).astype(np.int64), O.int_gemm(qx, qw))
+    assert torch.all(buf[:, :8] == -7) and torch.all(buf[:, 208:] == -7)
+
+
+def test_mismatch_is_an_error(cuda):
+    x = to_dev(random_rows((8, 1024), 13, dtype="bf16"), torch.bfloat16)
+    w = cr.pack_weight(to_dev(random_rows((16, 1024), 14, dtype="bf16"), torch.bfloat16), 256)
+    with pytest.raises(cr.ConvrotError):
+        cr.linear(cr.pack_act(x, 64), w)

@@ -1,0 +1,108 @@
+"""ctypes view of libconvrot.so (the C ABI declared in include/convrot.h).
+
+Loading fails loudly when the library is missing: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
+
+ABI_VERSION = 1
+
+# convrot_status
+OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
+# convrot_dtype
+F32, BF16, I32 = 0, 1, 2
+# convrot_rot_kind
+ROT_REGULAR, ROT_RANDOMIZED = 0, 1
+
+EXPORTED = (
+    "convrot_pack_act",
+    "convrot_pack_weight",
+    "convrot_linear",
+    "convrot_linear_bf16",
+    "convrot_rotate",
+    "convrot_status_string",
+    "convrot_last_error",
+    "convrot_abi_version",
+)
+
+
+class Rot(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("kind", ctypes.c_int32), ("signs", ctypes.c_void_p)]
+
+
+class Packed(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("ld", ctypes.c_int64),
+        ("rot", Rot),
+    ]
+
+
+class ConvrotError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    c_int, c_i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    P = ctypes.POINTER(Packed)
+    lib.convrot_pack_act.argtypes = [vp, c_int, c_i64, P, vp]
+    lib.convrot_pack_act.restype = c_int
+    lib.convrot_pack_weight.argtypes = [vp, c_int, c_i64, P, vp]
+    lib.convrot_pack_weight.restype = c_int
+    lib.convrot_linear.argtypes = [P, P, vp, vp, c_int, c_i64, vp]
+    lib.convrot_linear.restype = c_int
+    lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp]
+    lib.convrot_linear_bf16.restype = c_int
+    lib.convrot_rotate.argtypes = [vp, c_int, c_i64, c_i64, c_i64, Rot, vp, c_i64, vp]
+    lib.convrot_rotate.restype = c_int
+    lib.convrot_status_string.argtypes = [c_int]
+    lib.convrot_status_string.restype = ctypes.c_char_p
+    lib.convrot_last_error.argtypes = []
+    lib.convrot_last_error.restype = ctypes.c_char_p
+    lib.convrot_abi_version.argtypes = []
+    lib.convrot_abi_version.restype = c_int
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libconvrot.so once; raise if it is missing or incompatible."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise ImportError(
+                f"{p} is missing: build it with `python -m w8a8_int8_linear_amd.build` "
+                "(the library has no fallback path)")
+        lib = ctypes.CDLL(p)
+        _declare(lib)
+        v = lib.convrot_abi_version()
+        if v != ABI_VERSION:
+            raise ImportError(f"libconvrot ABI {v}, binding expects {ABI_VERSION}")
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def check(status: int) -> None:
+    if status != OK:
+        lib = load()
+        name = lib.convrot_status_string(status).decode()
+        msg = lib.convrot_last_error().decode()
+        raise ConvrotError(status, f"{name}: {msg}")

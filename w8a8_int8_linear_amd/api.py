@@ -1,0 +1,159 @@
+"""Python binding of the ConvRot W8A8 linear C ABI.
+
+Every function marshals torch CUDA tensors (device memory) and the current
+torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
+kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
+``linear``, ``linear_bf16``, ``rotate``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+REGULAR = "regular"
+RANDOMIZED = "randomized"
+_KIND = {REGULAR: _lib.ROT_REGULAR, RANDOMIZED: _lib.ROT_RANDOMIZED}
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.int32: _lib.I32}
+
+
+@dataclass
+class Packed:
+    """int8 rows + one fp32 scale per row + the rotation that produced them.
+
+    Used both for a packed activation (rows = tokens) and for a packed weight
+    (rows = output features).  ``signs`` (int8 +-1, length K) is kept alive
+    with the codes because the rotation descriptor points at it.
+    """
+    q: torch.Tensor          # [rows, K] int8 (row stride may exceed K)
+    scale: torch.Tensor      # [rows] fp32
+    group: int
+    kind: str = REGULAR
+    signs: torch.Tensor | None = None
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.q.shape[1]
+
+    def descriptor(self) -> _lib.Packed:
+        return _lib.Packed(self.q.data_ptr(), self.scale.data_ptr(), self.q.shape[0], self.q.shape[1],
+                           _ld(self.q), _rot(self.group, self.kind, self.signs))
+
+
+def _rot(group: int, kind: str, signs: torch.Tensor | None) -> _lib.Rot:
+    if kind not in _KIND:
+        raise ValueError(f"unknown rotation kind {kind!r}")
+    return _lib.Rot(int(group), _KIND[kind], signs.data_ptr() if signs is not None else None)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_cuda(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or (t.shape[0] > 1 and t.stride(1) != 1) or (t.shape[0] <= 1 and t.numel() and t.stride(-1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit stride along K")
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _check_signs(signs, K, kind):
+    if kind == RANDOMIZED:
+        if signs is None:
+            raise ValueError("the randomized rotation needs a sign vector")
+        if signs.dtype != torch.int8 or signs.numel() != K or not signs.is_cuda or not signs.is_contiguous():
+            raise ValueError("signs must be a contiguous int8 device vector of length K")
+    elif signs is not None:
+        raise ValueError("signs are only used by the randomized rotation")
+
+
+def _pack(fn, x: torch.Tensor, group: int, kind: str, signs, out: Packed | None) -> Packed:
+    _need_cuda(x, "input")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("input must be float32 or bfloat16")
+    rows, K = x.shape
+    _check_signs(signs, K, kind)
+    if out is None:
+        out = Packed(torch.empty((rows, K), dtype=torch.int8, device=x.device),
+                     torch.empty((rows,), dtype=torch.float32, device=x.device), group, kind, signs)
+    desc = out.descriptor()
+    _lib.check(fn(x.data_ptr(), _DT[x.dtype], _ld(x), ctypes.byref(desc), _stream(x.device)))
+    return out
+
+
+def pack_act(x: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
+             out: Packed | None = None) -> Packed:
+    """Rotate + quantise activation rows (convrot_pack_act)."""
+    return _pack(_lib.load().convrot_pack_act, x, group, kind, signs, out)
+
+
+def pack_weight(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
+                out: Packed | None = None) -> Packed:
+    """Rotate + quantise weight rows offline (convrot_pack_weight)."""
+    return _pack(_lib.load().convrot_pack_weight, w, group, kind, signs, out)
+
+
+def linear(act: Packed, w: Packed, bias: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = A * s_x * s_w + b from a packed activation and a packed weight
+    (convrot_linear).  ``out_dtype=torch.int32`` returns the raw accumulator."""
+    M, N = act.rows, w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=act.q.device)
+    if out.dtype not in _DT:
+        raise ValueError("output must be float32, bfloat16 or int32")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 vector of length N")
+    a, b = act.descriptor(), w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
+                                  out.data_ptr(), _DT[out.dtype], _ld(out), _stream(out.device)))
+    return out
+
+
+def linear_bf16(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Unquantised bf16 linear Y = X W^T + b for routed layers (convrot_linear_bf16)."""
+    _need_cuda(x, "x")
+    _need_cuda(w, "w")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bfloat16")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 vector of length N")
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_bf16(x.data_ptr(), _ld(x), w.data_ptr(), _ld(w),
+                                       bias.data_ptr() if bias is not None else None, M, N, K,
+                                       out.data_ptr(), _DT[out.dtype], _ld(out), _stream(x.device)))
+    return out
+
+
+def rotate(x: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 rotated rows X R from the pack kernel with quantisation off (convrot_rotate)."""
+    _need_cuda(x, "x")
+    M, K = x.shape
+    _check_signs(signs, K, kind)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    lib = _lib.load()
+    _lib.check(lib.convrot_rotate(x.data_ptr(), _DT[x.dtype], M, K, _ld(x), _rot(group, kind, signs),
+                                  out.data_ptr(), _ld(out), _stream(x.device)))
+    return out

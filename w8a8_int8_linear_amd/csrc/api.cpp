@@ -1,0 +1,252 @@
+// C ABI of the ConvRot W8A8 linear library: host-side validation, dispatch
+// to the gfx950 kernels, status codes and the thread-local error string.
+// The declarations and the contract of every entry point are in convrot.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "convrot.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+convrot_status fail(convrot_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+convrot_status ok() {
+  g_last_error[0] = '\0';
+  return CONVROT_OK;
+}
+
+convrot_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CONVROT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_size(convrot_dtype d) { return d == CONVROT_BF16 ? 2 : 4; }
+
+int log2_exact(int64_t g) {
+  if (g <= 0 || (g & (g - 1)) != 0) return -1;
+  int l = 0;
+  while ((int64_t{1} << l) < g) ++l;
+  return l;
+}
+
+// |A| <= K * 127^2 must fit in int32.
+constexpr int64_t kMaxK = (int64_t{1} << 31) / (127 * 127) - 1;
+// The pack kernel keeps a row in at most 1024 threads x 4 chunks x 16 features.
+constexpr int64_t kMaxPackK = 1024 * 4 * 16;
+// Grid dimensions.
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+// The tiled kernels address a 256-row tile with 32-bit byte offsets.
+constexpr int64_t kMaxLdBytes = (int64_t{1} << 31) / 256;
+
+convrot_status check_rot(const convrot_rot& rot, int64_t K, int* log2G) {
+  const int lg = log2_exact(rot.group);
+  if (rot.kind == CONVROT_ROT_REGULAR) {
+    if (lg < 2 || lg > 10 || (lg & 1))
+      return fail(CONVROT_ERR_GROUP, "regular rotation needs G in {4, 16, 64, 256, 1024}, got %d", rot.group);
+    if (rot.signs != nullptr) return fail(CONVROT_ERR_INVALID_ARG, "regular rotation takes no sign vector");
+  } else if (rot.kind == CONVROT_ROT_RANDOMIZED) {
+    if (lg < 4 || lg > 10)
+      return fail(CONVROT_ERR_GROUP, "randomized rotation needs G = 2^m in [16, 1024], got %d", rot.group);
+    if (rot.signs == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "randomized rotation needs a sign vector");
+    if (!aligned16(rot.signs)) return fail(CONVROT_ERR_ALIGN, "sign vector must be 16-byte aligned");
+  } else {
+    return fail(CONVROT_ERR_INVALID_ARG, "unknown rotation kind %d", rot.kind);
+  }
+  if (K % rot.group != 0)
+    return fail(CONVROT_ERR_GROUP, "K = %lld is not a multiple of G = %d", static_cast<long long>(K), rot.group);
+  *log2G = lg;
+  return CONVROT_OK;
+}
+
+convrot_status check_k(int64_t K, int64_t limit) {
+  if (K <= 0 || K % 16 != 0)
+    return fail(CONVROT_ERR_INVALID_ARG, "K = %lld must be a positive multiple of 16", static_cast<long long>(K));
+  if (K > limit)
+    return fail(CONVROT_ERR_INVALID_ARG, "K = %lld exceeds the supported maximum %lld", static_cast<long long>(K),
+                static_cast<long long>(limit));
+  return CONVROT_OK;
+}
+
+// Inputs are read in 16-byte chunks: base and row pitch must be 16-byte
+// multiples.  Outputs of the linear entry points only need element
+// alignment (the kernels fall back to narrower stores where needed).
+convrot_status check_matrix(const char* name, const void* p, int64_t rows, int64_t cols, int64_t ld, int elt,
+                            bool chunked = true) {
+  if (rows > 0 && p == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s is NULL", name);
+  if (rows < 0 || rows > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad row count", name);
+  if (ld < cols)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: leading dimension %lld < %lld", name, static_cast<long long>(ld),
+                static_cast<long long>(cols));
+  if (!chunked) {
+    if ((reinterpret_cast<uintptr_t>(p) % elt) != 0)
+      return fail(CONVROT_ERR_ALIGN, "%s must be aligned to its element size", name);
+    return CONVROT_OK;
+  }
+  if (!aligned16(p)) return fail(CONVROT_ERR_ALIGN, "%s must be 16-byte aligned", name);
+  if ((ld * elt) % 16 != 0)
+    return fail(CONVROT_ERR_ALIGN, "%s: leading dimension x element size must be a multiple of 16 bytes", name);
+  return CONVROT_OK;
+}
+
+convrot_status check_packed(const char* name, const convrot_packed* p, int* log2G) {
+  if (p == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+  convrot_status st = check_k(p->K, kMaxK);
+  if (st != CONVROT_OK) return st;
+  st = check_rot(p->rot, p->K, log2G);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix(name, p->q, p->rows, p->K, p->ld, 1);
+  if (st != CONVROT_OK) return st;
+  if (p->rows > 0 && p->scale == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s scale is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(p->scale) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "%s scale must be 4-byte aligned", name);
+  return CONVROT_OK;
+}
+
+convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int64_t ldx,
+                         const convrot_packed* out, void* stream) {
+  int log2G = 0;
+  if (out == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: output descriptor is NULL", what);
+  convrot_status st = check_k(out->K, kMaxPackK);
+  if (st != CONVROT_OK) return st;
+  st = check_packed("packed output", out, &log2G);
+  if (st != CONVROT_OK) return st;
+  if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
+  st = check_matrix("input", X, out->rows, out->K, ldx, elt_size(xdt));
+  if (st != CONVROT_OK) return st;
+  if (out->rows == 0) return ok();
+  const hipError_t e = convrot::launch_pack_rows(
+      X, static_cast<convrot::Elt>(xdt), out->rows, out->K, ldx, log2G,
+      static_cast<convrot::RotKind>(out->rot.kind), out->rot.signs, out->q, out->ld, out->scale, nullptr, 0,
+      static_cast<hipStream_t>(stream));
+  return from_hip(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+convrot_status convrot_pack_act(const void* X, convrot_dtype xdt, int64_t ldx, const convrot_packed* out,
+                                void* stream) {
+  return pack_impl("convrot_pack_act", X, xdt, ldx, out, stream);
+}
+
+convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw, const convrot_packed* out,
+                                   void* stream) {
+  return pack_impl("convrot_pack_weight", W, wdt, ldw, out, stream);
+}
+
+convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
+                              convrot_dtype ydt, int64_t ldy, void* stream) {
+  int lga = 0, lgw = 0;
+  convrot_status st = check_packed("activation", act, &lga);
+  if (st != CONVROT_OK) return st;
+  st = check_packed("weight", w, &lgw);
+  if (st != CONVROT_OK) return st;
+  if (act->K != w->K)
+    return fail(CONVROT_ERR_MISMATCH, "activation K = %lld but weight K = %lld", static_cast<long long>(act->K),
+                static_cast<long long>(w->K));
+  if (act->rot.group != w->rot.group || act->rot.kind != w->rot.kind || act->rot.signs != w->rot.signs)
+    return fail(CONVROT_ERR_MISMATCH,
+                "activation and weight were packed with different rotations (G %d/%d, kind %d/%d, signs %p/%p)",
+                act->rot.group, w->rot.group, act->rot.kind, w->rot.kind, static_cast<const void*>(act->rot.signs),
+                static_cast<const void*>(w->rot.signs));
+  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16 && ydt != CONVROT_I32)
+    return fail(CONVROT_ERR_DTYPE, "convrot_linear: output must be CONVROT_F32, CONVROT_BF16 or CONVROT_I32");
+  const int64_t M = act->rows, N = w->rows, K = act->K;
+  st = check_matrix("Y", Y, M, N, ldy, elt_size(ydt), false);
+  if (st != CONVROT_OK) return st;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (act->ld > kMaxLdBytes || w->ld > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of a packed operand exceeds %lld bytes",
+                static_cast<long long>(kMaxLdBytes));
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (M <= convrot::kGemvMaxRows) {
+    e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
+  } else {
+    e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
+  }
+  return from_hip(e, "convrot_linear");
+}
+
+convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw, const float* bias,
+                                   int64_t M, int64_t N, int64_t K, void* Y, convrot_dtype ydt, int64_t ldy,
+                                   void* stream) {
+  convrot_status st = check_k(K, int64_t{1} << 30);
+  if (st != CONVROT_OK) return st;
+  if (N < 0 || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "bad N");
+  st = check_matrix("X", X, M, K, ldx, 2);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("W", W, N, K, ldw, 2);
+  if (st != CONVROT_OK) return st;
+  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "convrot_linear_bf16: output must be CONVROT_F32 or CONVROT_BF16");
+  st = check_matrix("Y", Y, M, N, ldy, elt_size(ydt), false);
+  if (st != CONVROT_OK) return st;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (2 * ldx > kMaxLdBytes || 2 * ldw > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of X or W exceeds %lld bytes",
+                static_cast<long long>(kMaxLdBytes));
+  if (M == 0 || N == 0) return ok();
+  const hipError_t e = convrot::launch_gemm_bf16(X, ldx, W, ldw, bias, M, N, K, Y, static_cast<convrot::Elt>(ydt),
+                                                 ldy, static_cast<hipStream_t>(stream));
+  return from_hip(e, "convrot_linear_bf16");
+}
+
+convrot_status convrot_rotate(const void* X, convrot_dtype xdt, int64_t M, int64_t K, int64_t ldx, convrot_rot rot,
+                              float* Xrot, int64_t ldr, void* stream) {
+  int log2G = 0;
+  convrot_status st = check_k(K, kMaxPackK);
+  if (st != CONVROT_OK) return st;
+  st = check_rot(rot, K, &log2G);
+  if (st != CONVROT_OK) return st;
+  if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "convrot_rotate: input must be CONVROT_F32 or CONVROT_BF16");
+  st = check_matrix("X", X, M, K, ldx, elt_size(xdt));
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("Xrot", Xrot, M, K, ldr, 4);
+  if (st != CONVROT_OK) return st;
+  if (M == 0) return ok();
+  const hipError_t e = convrot::launch_pack_rows(X, static_cast<convrot::Elt>(xdt), M, K, ldx, log2G,
+                                                 static_cast<convrot::RotKind>(rot.kind), rot.signs, nullptr, 0,
+                                                 nullptr, Xrot, ldr, static_cast<hipStream_t>(stream));
+  return from_hip(e, "convrot_rotate");
+}
+
+const char* convrot_status_string(convrot_status status) {
+  switch (status) {
+    case CONVROT_OK: return "CONVROT_OK";
+    case CONVROT_ERR_INVALID_ARG: return "CONVROT_ERR_INVALID_ARG";
+    case CONVROT_ERR_GROUP: return "CONVROT_ERR_GROUP";
+    case CONVROT_ERR_DTYPE: return "CONVROT_ERR_DTYPE";
+    case CONVROT_ERR_ALIGN: return "CONVROT_ERR_ALIGN";
+    case CONVROT_ERR_MISMATCH: return "CONVROT_ERR_MISMATCH";
+    case CONVROT_ERR_HIP: return "CONVROT_ERR_HIP";
+  }
+  return "unknown convrot_status";
+}
+
+const char* convrot_last_error(void) { return g_last_error; }
+
+int convrot_abi_version(void) { return CONVROT_ABI_VERSION; }
+
+}  // extern "C"

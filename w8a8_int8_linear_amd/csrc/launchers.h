@@ -1,0 +1,45 @@
+// Internal launcher declarations shared by the C-ABI layer (api.cpp) and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+enum class Elt : int { F32 = 0, BF16 = 1, I32 = 2 };
+enum class RotKind : int { Regular = 0, Randomized = 1 };
+
+// Fused group rotation + whole-row absmax + int8 quantisation of `rows` rows
+// of X.  When `q` is null the kernel writes the fp32 rotated rows to `xrot`
+// instead (checking mode).  Shapes were validated by the caller.
+hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx,
+                            int log2G, RotKind kind, const int8_t* signs,
+                            int8_t* q, int64_t ldq, float* scale,
+                            float* xrot, int64_t ldr, hipStream_t stream);
+
+// Tiled matrix-core GEMM, C = A B^T with both operands K-contiguous.
+//   int8 mode : A = Qx [M, K] int8, B = Qw [N, K] int8, exact int32
+//               accumulation, epilogue acc * sa[m] * sb[n] + bias[n]
+//               (or the raw accumulator when out == I32).
+//   bf16 mode : A = X [M, K] bf16, B = W [N, K] bf16, fp32 accumulation,
+//               epilogue acc + bias[n].
+// lda/ldb/ldc in elements.
+hipError_t launch_gemm_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                          const float* sa, const float* sb, const float* bias,
+                          int64_t M, int64_t N, int64_t K,
+                          void* C, Elt out, int64_t ldc, hipStream_t stream);
+
+hipError_t launch_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* C, Elt out, int64_t ldc, hipStream_t stream);
+
+// Weight-streaming kernel for small M (M <= kGemvMaxRows); same result bits
+// as launch_gemm_i8.
+constexpr int64_t kGemvMaxRows = 16;
+hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                          const float* sa, const float* sb, const float* bias,
+                          int64_t M, int64_t N, int64_t K,
+                          void* C, Elt out, int64_t ldc, hipStream_t stream);
+
+}  // namespace convrot

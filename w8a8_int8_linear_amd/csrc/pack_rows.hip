@@ -1,0 +1,431 @@
+// Fused group rotation + row absmax + int8 quantisation ("pack") for gfx950.
+//
+// What it computes ("INT8 Convrot Safetensors", sections "How INT8 convrot
+// works", "Weight quantization", "Runtime activation quantization"): every
+// contiguous group of G features of a row is multiplied by R_G, the
+// normalised Kronecker power of the 4x4 regular Hadamard matrix H4; the
+// row's scale is its largest rotated magnitude over 127; codes are the
+// rotated values divided by the scale, rounded to nearest (ties to even) and
+// clamped to [-127, 127].  The randomized kind ("Add experimental W8A8 MatMul
+// with optional QuaRot-style rotation", section "Rotation method") multiplies
+// each block by fixed +-1 signs, applies the natural-order Walsh-Hadamard
+// transform and scales by 1/sqrt(G).
+//
+// Design (one workgroup per row, the whole row held in VGPRs):
+//  * Each thread owns chunks of 16 contiguous features (two 16-byte loads for
+//    bf16, four for fp32), so one chunk is exactly one 16-byte store of
+//    codes.  A G-group spans G/16 lanes of one wavefront.
+//  * H4 = J/2 - (anti-diagonal), so a radix-4 butterfly on (a0..a3) is
+//    s = a0+a1+a2+a3, y_j = s - 2 a_{3-j} (3 adds + 4 FMAs).  The factor 1/2
+//    of every stage is left out and the total power of two is folded into
+//    the scale at the end, which is bit-identical (binary scaling commutes
+//    with fp32 rounding).
+//  * The two low base-4 digits of a group index live inside a chunk
+//    (in-register butterflies).  Higher digits live in lane bits and are
+//    exchanged with DPP (quad_perm within 4 lanes, row_ror within 16 lanes)
+//    and, for G = 1024, ds_swizzle / ds_bpermute across 64 lanes.  The digit
+//    held in lane bits 2-3 (and 4-5) is Gray-coded across lanes, so that the
+//    partner holding digit 3-j is always lane ^ 8 (or lane ^ 32) and the
+//    butterfly needs only rotations that DPP provides.
+//  * Absmax: per-thread max, DPP/swizzle wavefront reduction, LDS reduction
+//    across waves.  Quantisation multiplies by 127/amax and rounds with the
+//    1.5*2^23 trick (one FMA rounds to nearest even and leaves the int8 code
+//    in the low byte); three v_perm_b32 pack four codes per dword.
+#include <hip/hip_runtime.h>
+
+#include "launchers.h"
+
+namespace convrot {
+namespace {
+
+constexpr int kChunk = 16;
+constexpr int kMaxThreads = 1024;
+
+// DPP control words.
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kQuadXor3 = 0x1B;  // quad_perm [3,2,1,0]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;  // lane ^ 8 within a row of 16
+// ds_swizzle bit-mask mode: lane' = lane ^ xor_mask within 32 lanes.
+constexpr int kSwzXor4 = 0x1F | (4 << 10);
+constexpr int kSwzXor16 = 0x1F | (16 << 10);
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int PATTERN>
+__device__ __forceinline__ float swz(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), PATTERN));
+}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Value held by lane ^ MASK (MASK a power of two below 64).
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float x) {
+  if constexpr (MASK == 1) return dpp<kQuadXor1>(x);
+  else if constexpr (MASK == 2) return dpp<kQuadXor2>(x);
+  else if constexpr (MASK == 4) return swz<kSwzXor4>(x);
+  else if constexpr (MASK == 8) return dpp<kRowRor8>(x);
+  else if constexpr (MASK == 16) return swz<kSwzXor16>(x);
+  else return xor32(x);
+}
+
+// Unnormalised radix-4 butterfly (2 H4) on four registers.
+__device__ __forceinline__ void bfly4(float& a0, float& a1, float& a2, float& a3) {
+  const float s = (a0 + a1) + (a2 + a3);
+  const float b0 = fmaf(-2.f, a3, s);
+  const float b1 = fmaf(-2.f, a2, s);
+  const float b2 = fmaf(-2.f, a1, s);
+  const float b3 = fmaf(-2.f, a0, s);
+  a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+}
+
+// Radix-4 butterfly whose digit lives in lane bits (2k, 2k+1).
+// k = 0: identity digit order within a quad, partner at lane ^ 3.
+// k = 1: Gray-coded digit in lane bits 2-3, partner at lane ^ 8.
+// k = 2: Gray-coded digit in lane bits 4-5, partner at lane ^ 32.
+template <int K>
+__device__ __forceinline__ float bfly4_lanes(float x) {
+  if constexpr (K == 0) {
+    const float t = x + dpp<kQuadXor1>(x);
+    const float s = t + dpp<kQuadXor2>(t);
+    return fmaf(-2.f, dpp<kQuadXor3>(x), s);
+  } else if constexpr (K == 1) {
+    const float p = dpp<kRowRor8>(x);
+    const float t = x + p;
+    const float s = t + dpp<kRowRor4>(t);
+    return fmaf(-2.f, p, s);
+  } else {
+    const float p = xor32(x);
+    const float t = x + p;
+    const float s = t + swz<kSwzXor16>(t);
+    return fmaf(-2.f, p, s);
+  }
+}
+
+// Radix-2 (Sylvester) butterfly across lane bit b: the lane with the bit
+// clear keeps a + c, the other keeps a - c (a = low lane's value).
+template <int MASK>
+__device__ __forceinline__ float bfly2_lanes(float x, int lane) {
+  const float p = lane_xor<MASK>(x);
+  return (lane & MASK) ? (p - x) : (x + p);
+}
+
+__device__ __forceinline__ int gray2(int m) { return m ^ (m >> 1); }
+
+// Position of a lane's chunk inside its group.  Regular kind: base-4 digit
+// 0 of the lane position as is, digits 1 and 2 Gray-coded.  Randomized kind:
+// identity (radix-2 exchanges need no reordering).
+template <bool RAND>
+__device__ __forceinline__ int chunk_in_group(int pos) {
+  if constexpr (RAND) {
+    return pos;
+  } else {
+    return (pos & 3) + 4 * gray2((pos >> 2) & 3) + 16 * gray2((pos >> 4) & 3);
+  }
+}
+
+template <typename InT>
+__device__ __forceinline__ void load_chunk(const InT* p, float v[kChunk]);
+
+template <>
+__device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float v[kChunk]) {
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
+  const u32x4 a = __builtin_nontemporal_load(p4);
+  const u32x4 b = __builtin_nontemporal_load(p4 + 1);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = as_f(w[i] << 16);
+    v[2 * i + 1] = as_f(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_chunk<float>(const float* p, float v[kChunk]) {
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 a = __builtin_nontemporal_load(p4 + i);
+    v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+  }
+}
+
+// Round-to-nearest-even int8 codes of a*inv..d*inv (|.| <= 127 + tiny),
+// packed little-endian into one dword.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: ulp 1, low byte = two's complement code
+  const uint32_t qa = as_u(fmaf(a, inv, kMagic));
+  const uint32_t qb = as_u(fmaf(b, inv, kMagic));
+  const uint32_t qc = as_u(fmaf(c, inv, kMagic));
+  const uint32_t qd = as_u(fmaf(d, inv, kMagic));
+  const uint32_t ab = __builtin_amdgcn_perm(qb, qa, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(qd, qc, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+  m = fmaxf(m, dpp<kQuadXor1>(m));
+  m = fmaxf(m, dpp<kQuadXor2>(m));
+  m = fmaxf(m, dpp<kRowRor4>(m));
+  m = fmaxf(m, dpp<kRowRor8>(m));
+  m = fmaxf(m, swz<kSwzXor16>(m));
+  m = fmaxf(m, xor32(m));
+  return m;
+}
+
+template <typename InT, int LOG2G, bool RAND, bool QUANT, int CPT>
+__global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
+    const InT* __restrict__ X, int64_t ldx, int K, const int8_t* __restrict__ signs,
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+    float* __restrict__ xrot, int64_t ldr) {
+  constexpr int G = 1 << LOG2G;
+  constexpr int L = G >= kChunk ? G / kChunk : 1;  // lanes per group
+  static_assert(L <= 64, "a group must fit in one wavefront");
+  static_assert(RAND ? (LOG2G >= 4 && LOG2G <= 10) : (LOG2G % 2 == 0 && LOG2G >= 2 && LOG2G <= 10),
+                "unsupported group size");
+  __shared__ float wave_amax[kMaxThreads / 64];
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int T = blockDim.x;
+  const int lane = tid & 63;
+  const InT* xrow = X + static_cast<int64_t>(row) * ldx;
+
+  float v[CPT][kChunk];
+  int off[CPT];
+  bool ok[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int vt = tid + c * T;
+    const int grp = vt / L;
+    const int pos = vt % L;
+    off[c] = (grp * L + chunk_in_group<RAND>(pos)) * kChunk;
+    ok[c] = off[c] < K;
+    if (ok[c]) {
+      load_chunk<InT>(xrow + off[c], v[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) v[c][e] = 0.f;
+    }
+  }
+
+  if constexpr (RAND) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (ok[c]) {
+        const uint4 sv = *reinterpret_cast<const uint4*>(signs + off[c]);
+        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          const int8_t sgn = static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
+          v[c][e] = sgn < 0 ? -v[c][e] : v[c][e];
+        }
+      }
+    }
+    // In-register radix-2 stages over element bits 0..3.
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          if ((e >> b) & 1) continue;
+          const float a = v[c][e], d = v[c][e | (1 << b)];
+          v[c][e] = a + d;
+          v[c][e | (1 << b)] = a - d;
+        }
+      }
+    }
+    // Lane bits 0..LOG2G-5.
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        float x = v[c][e];
+        if constexpr (LOG2G >= 5) x = bfly2_lanes<1>(x, lane);
+        if constexpr (LOG2G >= 6) x = bfly2_lanes<2>(x, lane);
+        if constexpr (LOG2G >= 7) x = bfly2_lanes<4>(x, lane);
+        if constexpr (LOG2G >= 8) x = bfly2_lanes<8>(x, lane);
+        if constexpr (LOG2G >= 9) x = bfly2_lanes<16>(x, lane);
+        if constexpr (LOG2G >= 10) x = bfly2_lanes<32>(x, lane);
+        v[c][e] = x;
+      }
+    }
+  } else {
+    // Base-4 digit 0 (element bits 0-1), in registers.
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) bfly4(v[c][4 * a], v[c][4 * a + 1], v[c][4 * a + 2], v[c][4 * a + 3]);
+    }
+    // Digit 1 (element bits 2-3), in registers.
+    if constexpr (LOG2G >= 4) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bfly4(v[c][b], v[c][4 + b], v[c][8 + b], v[c][12 + b]);
+      }
+    }
+    // Digits 2.. across lanes.
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        float x = v[c][e];
+        if constexpr (LOG2G >= 6) x = bfly4_lanes<0>(x);
+        if constexpr (LOG2G >= 8) x = bfly4_lanes<1>(x);
+        if constexpr (LOG2G >= 10) x = bfly4_lanes<2>(x);
+        v[c][e] = x;
+      }
+    }
+  }
+
+  // Scale that turns the unnormalised transform into the orthonormal one:
+  // 2^-(LOG2G/2) for the regular kind (one factor 1/2 per radix-4 stage),
+  // 1/sqrt(G) for the randomized kind.
+  const float norm = RAND ? (1.0f / __builtin_sqrtf(static_cast<float>(G)))
+                          : __builtin_ldexpf(1.0f, -(LOG2G / 2));
+
+  if constexpr (!QUANT) {
+    float* rrow = xrot + static_cast<int64_t>(row) * ldr;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (!ok[c]) continue;
+      float4* o4 = reinterpret_cast<float4*>(rrow + off[c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o4[i] = make_float4(v[c][4 * i] * norm, v[c][4 * i + 1] * norm, v[c][4 * i + 2] * norm,
+                            v[c][4 * i + 3] * norm);
+      }
+    }
+    return;
+  } else {
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+    }
+    m = wave_max(m);
+    const int nwaves = T >> 6;
+    if (lane == 0) wave_amax[tid >> 6] = m;
+    __syncthreads();
+    float amax_u = wave_amax[0];
+    for (int w = 1; w < nwaves; ++w) amax_u = fmaxf(amax_u, wave_amax[w]);
+
+    // Unnormalised codes: y_u * (127 / amax_u) == y / s exactly up to the
+    // rounding of the reciprocal; all-zero rows give inv = 0 and codes 0.
+    const float inv = amax_u > 0.f ? 127.0f / amax_u : 0.f;
+    if (tid == 0) scale[row] = (amax_u * norm) / 127.0f;
+
+    int8_t* qrow = q + static_cast<int64_t>(row) * ldq;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (!ok[c]) continue;
+      u32x4 o;
+      o.x = quant4(v[c][0], v[c][1], v[c][2], v[c][3], inv);
+      o.y = quant4(v[c][4], v[c][5], v[c][6], v[c][7], inv);
+      o.z = quant4(v[c][8], v[c][9], v[c][10], v[c][11], inv);
+      o.w = quant4(v[c][12], v[c][13], v[c][14], v[c][15], inv);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qrow + off[c]));
+    }
+  }
+}
+
+template <typename InT, int LOG2G, bool RAND, bool QUANT>
+hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, const int8_t* signs,
+                        int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
+                        hipStream_t stream) {
+  const int64_t nvt = K / kChunk;  // chunks in a row
+  int cpt = 1;
+  while ((nvt + cpt - 1) / cpt > kMaxThreads) cpt *= 2;
+  const int64_t threads = ((nvt + cpt - 1) / cpt + 63) / 64 * 64;
+  const dim3 grid(static_cast<unsigned>(rows));
+  const dim3 block(static_cast<unsigned>(threads));
+  const InT* x = static_cast<const InT*>(X);
+  switch (cpt) {
+    case 1:
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 1>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      break;
+    case 2:
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 2>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      break;
+    case 4:
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 4>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      break;
+    default:
+      return hipErrorInvalidValue;  // K above 64 * 1024 is rejected by the caller
+  }
+  return hipGetLastError();
+}
+
+template <typename InT, bool RAND, bool QUANT>
+hipError_t dispatch_group(int log2G, const void* X, int64_t rows, int64_t K, int64_t ldx,
+                          const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot,
+                          int64_t ldr, hipStream_t stream) {
+#define CONVROT_PACK_CASE(LG)                                                                   \
+  case LG:                                                                                      \
+    return dispatch_cpt<InT, LG, RAND, QUANT>(X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, \
+                                              stream);
+  if constexpr (RAND) {
+    switch (log2G) {
+      CONVROT_PACK_CASE(4)
+      CONVROT_PACK_CASE(5)
+      CONVROT_PACK_CASE(6)
+      CONVROT_PACK_CASE(7)
+      CONVROT_PACK_CASE(8)
+      CONVROT_PACK_CASE(9)
+      CONVROT_PACK_CASE(10)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (log2G) {
+      CONVROT_PACK_CASE(2)
+      CONVROT_PACK_CASE(4)
+      CONVROT_PACK_CASE(6)
+      CONVROT_PACK_CASE(8)
+      CONVROT_PACK_CASE(10)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef CONVROT_PACK_CASE
+}
+
+template <typename InT>
+hipError_t dispatch_kind(int log2G, RotKind kind, bool quant, const void* X, int64_t rows, int64_t K,
+                         int64_t ldx, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
+                         float* xrot, int64_t ldr, hipStream_t stream) {
+  if (kind == RotKind::Randomized) {
+    return quant ? dispatch_group<InT, true, true>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream)
+                 : dispatch_group<InT, true, false>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+  }
+  return quant ? dispatch_group<InT, false, true>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream)
+               : dispatch_group<InT, false, false>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+}
+
+}  // namespace
+
+hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
+                            RotKind kind, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
+                            float* xrot, int64_t ldr, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const bool quant = q != nullptr;
+  if (xdt == Elt::BF16) {
+    return dispatch_kind<uint16_t>(log2G, kind, quant, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+  }
+  return dispatch_kind<float>(log2G, kind, quant, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+}
+
+}  // namespace convrot
