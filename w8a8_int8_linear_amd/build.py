@@ -59,6 +59,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # Every kernel must have its host launch stub: a kernel body the host pass
+    # cannot type-check is silently left without one.
+    r = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l for l in r.stdout.splitlines() if "convrot" in l]
+    if r.returncode != 0 or missing:
+        raise RuntimeError("libconvrot.so has undefined symbols:\n" + "\n".join(missing[:20]))
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

@@ -34,6 +34,8 @@
 //  * Integer accumulation is exact, so every tiling gives the same bits.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "launchers.h"
 
 namespace convrot {
@@ -51,40 +53,105 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kBM = 256;
-constexpr int kBN = 256;
 constexpr int kBK = 128;  // bytes of K per LDS slice
 constexpr int kWM = 128;
-constexpr int kWN = 128;
 constexpr int kTM = kWM / 16;
-constexpr int kTN = kWN / 16;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
-constexpr int kTileBytes = kBM * kBK;            // one operand slice
-constexpr int kStageBytes = 2 * kTileBytes;      // A + B slices
-constexpr int kSmemBytes = 2 * kStageBytes;      // double buffer
-constexpr int kChunksPerThread = kTileBytes / 16 / kThreads;  // per operand
+constexpr int kATileBytes = kBM * kBK;  // one A slice
 
+// The MFMAs are issued through inline asm so that the accumulator is pinned
+// to AGPRs and tied in/out ("+a"): with the builtins the register allocator
+// spreads the 256 accumulators over both register files once two fragment
+// sets are live and copies them every iteration.  The compiler does not see
+// these as MFMAs, so the kernel pads the MFMA hazards itself (see s_nop uses
+// below): a VALU write feeding an MFMA needs 2 wait states, and an MFMA
+// result read by non-MFMA instructions needs up to 11 (8-pass) / 19 (16-pass).
 template <bool I8>
 struct Mfma;
 
+//
+// Statements that only make sense for the GPU target (AMDGPU register
+// constraints, s_waitcnt) sit under __HIP_DEVICE_COMPILE__: the host pass of
+// the same source must still see a well-formed kernel to emit its launch
+// stub.
 template <>
 struct Mfma<true> {
   typedef i32x4 acc_t;
-  static __device__ __forceinline__ i32x4 run(i32x4 a, i32x4 b, i32x4 c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ void run(i32x4& c, const i32x4& a, const i32x4& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+#endif
   }
 };
 
 template <>
 struct Mfma<false> {
   typedef f32x4 acc_t;
-  static __device__ __forceinline__ f32x4 run(i32x4 a, i32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
+  static __device__ __forceinline__ void run(f32x4& c, const i32x4& a, const i32x4& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+#endif
   }
 };
 
-__device__ __forceinline__ int swizzled(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+// s_waitcnt immediates (GFX9 layout: vmcnt [3:0] + [15:14], expcnt [6:4],
+// lgkmcnt [11:8]): lgkmcnt(0) only, and vmcnt(0) lgkmcnt(0).
+__device__ __forceinline__ void wait_lds() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+#endif
+}
+__device__ __forceinline__ void wait_lds_and_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0x0070);
+#endif
+}
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane
+// l's 16 bytes land at lds + 16 l.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+#endif
+}
+// Keeps the compiler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+// Hazard padding (wait states) as an ordered statement.
+template <int N>
+__device__ __forceinline__ void pad() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(N == 5 || N == 24, "add the padding length needed");
+  if constexpr (N == 5) {
+    asm volatile("s_nop 4" ::);
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+// Zero the B fragments of chunks past the end of K, then pad the VALU ->
+// MFMA hazard; the asm operands keep the selects ahead of the padding.
+template <int TN>
+__device__ __forceinline__ void mask_tail(i32x4* fb, bool dead) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[j] = dead ? i32x4{0, 0, 0, 0} : fb[j];
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(TN == 4 || TN == 6 || TN == 8, "unsupported tile width");
+  if constexpr (TN == 4) {
+    asm volatile("s_nop 4" : "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]));
+  } else if constexpr (TN == 6) {
+    asm volatile("s_nop 4" : "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]), "+v"(fb[4]), "+v"(fb[5]));
+  } else {
+    asm volatile("s_nop 4" : "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]), "+v"(fb[4]), "+v"(fb[5]),
+                 "+v"(fb[6]), "+v"(fb[7]));
+  }
+#endif
+}
 
 // Tile coordinates for this workgroup: XCD-contiguous ranges, then grouped
 // row-major order inside each range.
@@ -102,12 +169,23 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
+template <int TN>
+constexpr int smem_bytes() {
+  return 2 * (kBM + 32 * TN) * kBK;
+}
+
 // OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator.
-template <bool I8, int OUT, bool KTAIL>
+// TN: 16-wide output tiles per wave along N; the workgroup tile is
+// 256 x (32 TN), 4 waves in a 2 x 2 grid, each wave 128 x (16 TN).
+template <bool I8, int OUT, bool KTAIL, int TN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     const float* __restrict__ sa, const float* __restrict__ sb, const float* __restrict__ bias, int M, int N,
     int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n) {
+  constexpr int kBN = 32 * TN;
+  constexpr int kWN = 16 * TN;
+  constexpr int kBTileBytes = kBN * kBK;
+  constexpr int kStageBytes = kATileBytes + kBTileBytes;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using Op = Mfma<I8>;
   using acc_t = typename Op::acc_t;
@@ -125,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 
   // Global -> LDS without registers (global_load_lds_dwordx4): one
   // instruction fills a contiguous 1 KiB LDS block, i.e. 8 swizzled rows of
-  // the slice, lane l writing physical chunk l % 8 of row l / 8.  Wave w
+  // a slice, lane l writing physical chunk l % 8 of row l / 8.  Wave w
   // fills blocks w, w + 4, ..., so each lane fetches logical chunk
   // (l % 8) ^ (l / 8) of rows 8 (w + 4 i) + l / 8.  Rows past the matrix edge
   // re-read the last row (their results are never stored).  Offsets are
@@ -133,43 +211,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   const uint8_t* a_tile = A + static_cast<int64_t>(m_blk) * lda;
   const uint8_t* b_tile = B + static_cast<int64_t>(n_blk) * ldb;
   const int dma_ch = (lane & 7) ^ (lane >> 3);
-  int a_off[kChunksPerThread], b_off[kChunksPerThread];
+  int a_off[kBM / 32], b_off[kBN / 32];
 #pragma unroll
-  for (int i = 0; i < kChunksPerThread; ++i) {
+  for (int i = 0; i < kBM / 32; ++i) {
     const int row = 8 * (wid + 4 * i) + (lane >> 3);
     a_off[i] = (min(m_blk + row, M - 1) - m_blk) * static_cast<int>(lda) + dma_ch * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kBN / 32; ++i) {
+    const int row = 8 * (wid + 4 * i) + (lane >> 3);
     b_off[i] = (min(n_blk + row, N - 1) - n_blk) * static_cast<int>(ldb) + dma_ch * 16;
   }
   auto issue_slice = [&](int buf, int k0) {
     uint8_t* sA = smem + buf * kStageBytes;
-    uint8_t* sB = sA + kTileBytes;
+    uint8_t* sB = sA + kATileBytes;
     // A chunk past the end of K fetches the row's first chunk instead (a
-    // valid address); the tail slice is zero-filled after it lands.
+    // valid address); fragments of such chunks are zeroed when read.
     const int kk = (KTAIL && k0 + dma_ch * 16 >= Kb) ? -dma_ch * 16 : k0;
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      __builtin_amdgcn_global_load_lds(a_tile + a_off[i] + kk, (lds_ptr_t)(sA + (wid + 4 * i) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(b_tile + b_off[i] + kk, (lds_ptr_t)(sB + (wid + 4 * i) * 1024), 16, 0, 0);
-    }
-  };
-  auto zero_tail = [&](int buf, int k0) {
-    uint8_t* sA = smem + buf * kStageBytes;
+    for (int i = 0; i < kBM / 32; ++i)
+      dma16(a_tile + a_off[i] + kk, sA + (wid + 4 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 3, ch = idx & 7;
-      if (k0 + ch * 16 >= Kb) {
-        *reinterpret_cast<i32x4*>(sA + swizzled(row, ch)) = i32x4{0, 0, 0, 0};
-        *reinterpret_cast<i32x4*>(sA + kTileBytes + swizzled(row, ch)) = i32x4{0, 0, 0, 0};
-      }
-    }
+    for (int i = 0; i < kBN / 32; ++i)
+      dma16(b_tile + b_off[i] + kk, sB + (wid + 4 * i) * 1024);
   };
 
-  acc_t acc[kTM][kTN];
+  acc_t acc[kTM][TN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+    for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+  // The zeroing above is VALU work read by the first MFMAs.
+  pad<5>();
 
   // Fragment addresses: row (l & 15) of each 16-row tile, chunk (l >> 4) of
   // each 64-byte K step; the swizzle term depends on the lane only.
@@ -179,37 +252,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) frag_off[ks] = frag_row * kBK + (((4 * ks + frag_ch) ^ (frag_row & 7)) << 4);
 
+  // Two register sets of fragments: one feeds the MFMAs while the other is
+  // being loaded from LDS.
+  i32x4 fa0[kTM], fb0[TN], fa1[kTM], fb1[TN];
+  auto load_frags = [&](int buf, int ks, int k0, i32x4* fa, i32x4* fb) {
+    const uint8_t* sA = smem + buf * kStageBytes;
+    const uint8_t* sB = sA + kATileBytes;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) fa[i] = *reinterpret_cast<const i32x4*>(sA + (wm + 16 * i) * kBK + frag_off[ks]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const i32x4*>(sB + (wn + 16 * j) * kBK + frag_off[ks]);
+    if constexpr (KTAIL) mask_tail<TN>(fb, k0 + (4 * ks + frag_ch) * 16 >= Kb);
+  };
+  auto mfmas = [&](const i32x4* fa, const i32x4* fb) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Op::run(acc[i][j], fb[j], fa[i]);
+  };
+
+  // Pipeline per 128-byte slice kt (two 64-byte MFMA steps):
+  //   load step-1 fragments of kt | MFMAs of step 0
+  //   wait for own LDS reads and for the DMA of slice kt+1; barrier
+  //   DMA slice kt+2 into kt's buffer | load step-0 fragments of kt+1 | MFMAs of step 1
+  // so the MFMAs never wait on an LDS read issued just before them, and
+  // one barrier per slice both publishes slice kt+1 and frees kt's buffer.
   const int nk = (Kb + kBK - 1) / kBK;
   issue_slice(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_lds_and_vmem();
   __syncthreads();
+  if (nk > 1) issue_slice(1, kBK);
+  load_frags(0, 0, 0, fa0, fb0);
 
-  for (int kt = 0; kt < nk; ++kt) {
+  const int last = (nk - 1) * kBK;
+  for (int kt = 0; kt < nk - 1; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) issue_slice(cur ^ 1, (kt + 1) * kBK);
-    if (KTAIL && kt == nk - 1) {
-      zero_tail(cur, kt * kBK);
-      __syncthreads();
-    }
-    const uint8_t* sA = smem + cur * kStageBytes;
-    const uint8_t* sB = sA + kTileBytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x4 fa[kTM], fb[kTN];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        fa[i] = *reinterpret_cast<const i32x4*>(sA + (wm + 16 * i) * kBK + frag_off[ks]);
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        fb[j] = *reinterpret_cast<const i32x4*>(sB + (wn + 16 * j) * kBK + frag_off[ks]);
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) acc[i][j] = Op::run(fb[j], fa[i], acc[i][j]);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int k0 = kt * kBK;
+    // The step-0 fragments were requested a whole MFMA block ago; retire
+    // them before the 16+ new requests, which the 4-bit LDS counter could
+    // not tell apart from them afterwards.
+    wait_lds();
+    load_frags(cur, 1, k0, fa1, fb1);
+    sched_fence();
+    mfmas(fa0, fb0);
+    sched_fence();
+    wait_lds_and_vmem();
     __syncthreads();
+    if (kt + 2 < nk) issue_slice(cur, k0 + 2 * kBK);
+    load_frags(cur ^ 1, 0, k0 + kBK, fa0, fb0);
+    sched_fence();
+    mfmas(fa1, fb1);
+    sched_fence();
   }
+  {
+    const int cur = (nk - 1) & 1;
+    wait_lds();
+    load_frags(cur, 1, last, fa1, fb1);
+    mfmas(fa0, fb0);
+    mfmas(fa1, fb1);
+  }
+  // MFMA results are read below by ordinary instructions: wait out the
+  // longest MFMA write latency first.
+  pad<24>();
 
   // Epilogue.  Lane holds, for tile (i, j), output row m = m0 + 16 i + (l & 15)
   // and the four consecutive output features n = n0 + 16 j + 4 (l >> 4) + r.
@@ -221,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     s_row[i] = (I8 && OUT != 2) ? sa[m] : 1.f;
   }
 #pragma unroll
-  for (int j = 0; j < kTN; ++j) {
+  for (int j = 0; j < TN; ++j) {
     const int n = n_blk + wn + 16 * j + n_lane;
     if (n >= N) continue;
     float s_col[4], b_col[4];
@@ -276,32 +380,85 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   }
 }
 
-template <bool I8, int OUT, bool KTAIL>
+int num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        prop.multiProcessorCount > 0)
+      cus = prop.multiProcessorCount;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Output-tile width: the candidate minimising (rounds of one tile per CU) x
+// (work per tile), i.e. the fewest idle CU-slots in the last round; ties go
+// to the wider tile (less LDS traffic per MFMA).
+int choose_tn(int64_t M, int64_t N) {
+  // CONVROT_GEMM_TN=4|6|8 pins the width (tuning and checking only).
+  static const int forced = [] {
+    const char* e = std::getenv("CONVROT_GEMM_TN");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 4 || v == 6 || v == 8) ? v : 0;
+  }();
+  if (forced) return forced;
+  const int cands[] = {8, 6, 4};
+  const int64_t cus = num_cus();
+  int best = 8;
+  int64_t best_cost = -1;
+  for (int tn : cands) {
+    const int64_t bn = 32 * tn;
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
+    const int64_t cost = ((tiles + cus - 1) / cus) * bn;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = tn;
+    }
+  }
+  return best;
+}
+
+template <bool I8, int OUT, bool KTAIL, int TN>
 hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                         const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C,
                         int64_t ldc, hipStream_t stream) {
-  auto kern = gemm_nt_kernel<I8, OUT, KTAIL>;
+  auto kern = gemm_nt_kernel<I8, OUT, KTAIL, TN>;
+  constexpr int kSmem = smem_bytes<TN>();
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-  const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+  const int tiles_n = static_cast<int>((N + 32 * TN - 1) / (32 * TN));
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kSmemBytes, stream, A, lda, B, ldb, sa, sb, bias,
-                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m, tiles_n);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kSmem, stream, A, lda, B, ldb, sa, sb, bias, static_cast<int>(M),
+                     static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <bool I8, int OUT, bool KTAIL>
+hipError_t launch_tn(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
+                     const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc,
+                     hipStream_t stream) {
+  switch (choose_tn(M, N)) {
+    case 6: return launch_typed<I8, OUT, KTAIL, 6>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+    case 4: return launch_typed<I8, OUT, KTAIL, 4>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+    default: return launch_typed<I8, OUT, KTAIL, 8>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+  }
 }
 
 template <bool I8, int OUT>
 hipError_t launch_ktail(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                         const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C,
                         int64_t ldc, hipStream_t stream) {
-  if (Kb % kBK == 0) return launch_typed<I8, OUT, false>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
-  return launch_typed<I8, OUT, true>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+  if (Kb % kBK == 0) return launch_tn<I8, OUT, false>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+  return launch_tn<I8, OUT, true>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
 }
 
 }  // namespace
