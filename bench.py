@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_attn_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is data parallel over rows "
@@ -177,6 +179,13 @@ def main():
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle")
     torch.cuda.synchronize()
 
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         sets[i % len(sets)].step()
     torch.cuda.synchronize()

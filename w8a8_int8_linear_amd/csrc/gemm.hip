@@ -34,7 +34,9 @@
 //  * Integer accumulation is exact, so every tiling gives the same bits.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "launchers.h"
 
@@ -114,6 +116,24 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
 #endif
 }
+// 16-byte LDS read into a fragment register, issued in program order (the
+// caller retires it with wait_lds()).
+template <int OFF>
+__device__ __forceinline__ void lds_read16(i32x4& r, uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+#endif
+}
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(p)));
+}
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 // Keeps the compiler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -181,7 +201,7 @@ template <bool I8, int OUT, bool KTAIL, int TN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     const float* __restrict__ sa, const float* __restrict__ sb, const float* __restrict__ bias, int M, int N,
-    int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n) {
+    int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool staged) {
   constexpr int kBN = 32 * TN;
   constexpr int kWN = 16 * TN;
   constexpr int kBTileBytes = kBN * kBK;
@@ -251,65 +271,123 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   int frag_off[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) frag_off[ks] = frag_row * kBK + (((4 * ks + frag_ch) ^ (frag_row & 7)) << 4);
+  const uint32_t lds0 = lds_address(smem);
+  auto addr_a = [&](int buf, int ks) -> uint32_t { return lds0 + buf * kStageBytes + wm * kBK + frag_off[ks]; };
+  auto addr_b = [&](int buf, int ks) -> uint32_t {
+    return lds0 + buf * kStageBytes + kATileBytes + wn * kBK + frag_off[ks];
+  };
 
   // Two register sets of fragments: one feeds the MFMAs while the other is
-  // being loaded from LDS.
+  // being read from LDS.
   i32x4 fa0[kTM], fb0[TN], fa1[kTM], fb1[TN];
-  auto load_frags = [&](int buf, int ks, int k0, i32x4* fa, i32x4* fb) {
-    const uint8_t* sA = smem + buf * kStageBytes;
-    const uint8_t* sB = sA + kATileBytes;
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) fa[i] = *reinterpret_cast<const i32x4*>(sA + (wm + 16 * i) * kBK + frag_off[ks]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const i32x4*>(sB + (wn + 16 * j) * kBK + frag_off[ks]);
+  constexpr int kReads = kTM + TN;              // fragment reads per step
+  constexpr int kDmas = kBM / 32 + kBN / 32;    // DMA instructions per slice and wave
+  // Fragment read number s of a step into (fa, fb).
+  auto read_frag = [&](auto s_c, i32x4* fa, i32x4* fb, uint32_t aa, uint32_t ab) {
+    constexpr int s = decltype(s_c)::value;
+    if constexpr (s < kTM) {
+      lds_read16<2048 * s>(fa[s], aa);
+    } else {
+      lds_read16<2048 * (s - kTM)>(fb[s - kTM], ab);
+    }
+  };
+  // DMA instruction number s of a slice.
+  auto dma_block = [&](auto s_c, int buf, int k0) {
+    constexpr int s = decltype(s_c)::value;
+    uint8_t* sA = smem + buf * kStageBytes;
+    const int kk = (KTAIL && k0 + dma_ch * 16 >= Kb) ? -dma_ch * 16 : k0;
+    if constexpr (s < kBM / 32) {
+      dma16(a_tile + a_off[s] + kk, sA + (wid + 4 * s) * 1024);
+    } else {
+      dma16(b_tile + b_off[s - kBM / 32] + kk, sA + kATileBytes + (wid + 4 * (s - kBM / 32)) * 1024);
+    }
+  };
+  // One 64-byte K step: the TM x TN MFMAs on (fa, fb), with op(0..NOPS-1)
+  // spread evenly over all but the last 8 MFMAs, so that LDS and DMA
+  // traffic trickles out while the matrix cores are busy instead of
+  // queueing in front of them, and the last read has landed by the end.
+  auto mfma_step = [&](const i32x4* fa, const i32x4* fb, auto nops_c, auto&& op) {
+    constexpr int kOps = decltype(nops_c)::value;
+    constexpr int kM = kTM * TN;
+    constexpr int kSpread = kM - 8;
+    static_assert(kOps <= kSpread, "more side operations than MFMA slots");
+    static_for<kM>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
+      // Ops s with floor(s * kSpread / kOps) == m go right before MFMA m.
+      constexpr int first = (m * kOps + kSpread - 1) / kSpread;
+      constexpr int next = ((m + 1) * kOps + kSpread - 1) / kSpread;
+      constexpr int count = (first < kOps ? (next < kOps ? next : kOps) - first : 0);
+      static_for<count>([&](auto c_c) { op(std::integral_constant<int, first + decltype(c_c)::value>{}); });
+      Op::run(acc[m / TN][m % TN], fb[m % TN], fa[m / TN]);
+    });
+  };
+  auto tail_mask = [&](i32x4* fb, int k0, int ks) {
     if constexpr (KTAIL) mask_tail<TN>(fb, k0 + (4 * ks + frag_ch) * 16 >= Kb);
   };
-  auto mfmas = [&](const i32x4* fa, const i32x4* fb) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) Op::run(acc[i][j], fb[j], fa[i]);
-  };
+  using no_ops = std::integral_constant<int, 0>;
+  using read_ops = std::integral_constant<int, kReads>;
+  using dma_read_ops = std::integral_constant<int, kDmas + kReads>;
 
-  // Pipeline per 128-byte slice kt (two 64-byte MFMA steps):
-  //   load step-1 fragments of kt | MFMAs of step 0
+  // Pipeline per 128-byte slice kt (two 64-byte steps), buffers kt & 1:
+  //   step 0: MFMAs on set 0 | reads of set 1 (slice kt, step 1)
   //   wait for own LDS reads and for the DMA of slice kt+1; barrier
-  //   DMA slice kt+2 into kt's buffer | load step-0 fragments of kt+1 | MFMAs of step 1
-  // so the MFMAs never wait on an LDS read issued just before them, and
-  // one barrier per slice both publishes slice kt+1 and frees kt's buffer.
+  //   step 1: MFMAs on set 1 | DMA of slice kt+2 into kt's buffer, then reads
+  //           of set 0 (slice kt+1, step 0)
+  // The MFMAs never wait on a read issued in the same step, and one barrier
+  // per slice both publishes slice kt+1 and frees kt's buffer.
   const int nk = (Kb + kBK - 1) / kBK;
   issue_slice(0, 0);
   wait_lds_and_vmem();
   __syncthreads();
   if (nk > 1) issue_slice(1, kBK);
-  load_frags(0, 0, 0, fa0, fb0);
+  static_for<kReads>([&](auto s_c) { read_frag(s_c, fa0, fb0, addr_a(0, 0), addr_b(0, 0)); });
 
-  const int last = (nk - 1) * kBK;
-  for (int kt = 0; kt < nk - 1; ++kt) {
+  auto slice = [&](int kt, auto with_dma_c) {
+    constexpr bool kWithDma = decltype(with_dma_c)::value;
     const int cur = kt & 1;
     const int k0 = kt * kBK;
-    // The step-0 fragments were requested a whole MFMA block ago; retire
-    // them before the 16+ new requests, which the 4-bit LDS counter could
-    // not tell apart from them afterwards.
     wait_lds();
-    load_frags(cur, 1, k0, fa1, fb1);
-    sched_fence();
-    mfmas(fa0, fb0);
-    sched_fence();
+    tail_mask(fb0, k0, 0);
+    {
+      const uint32_t aa = addr_a(cur, 1), ab = addr_b(cur, 1);
+      mfma_step(fa0, fb0, read_ops{}, [&](auto s_c) { read_frag(s_c, fa1, fb1, aa, ab); });
+    }
     wait_lds_and_vmem();
     __syncthreads();
-    if (kt + 2 < nk) issue_slice(cur, k0 + 2 * kBK);
-    load_frags(cur ^ 1, 0, k0 + kBK, fa0, fb0);
-    sched_fence();
-    mfmas(fa1, fb1);
-    sched_fence();
+    tail_mask(fb1, k0, 1);
+    {
+      const uint32_t aa = addr_a(cur ^ 1, 0), ab = addr_b(cur ^ 1, 0);
+      if constexpr (kWithDma) {
+        mfma_step(fa1, fb1, dma_read_ops{}, [&](auto s_c) {
+          constexpr int s = decltype(s_c)::value;
+          if constexpr (s < kDmas) {
+            dma_block(s_c, cur, k0 + 2 * kBK);
+          } else {
+            read_frag(std::integral_constant<int, s - kDmas>{}, fa0, fb0, aa, ab);
+          }
+        });
+      } else {
+        mfma_step(fa1, fb1, read_ops{}, [&](auto s_c) { read_frag(s_c, fa0, fb0, aa, ab); });
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
+  if (kt + 1 < nk) {
+    slice(kt, std::false_type{});
+    ++kt;
   }
   {
-    const int cur = (nk - 1) & 1;
+    // Last slice: no DMA, no next slice.
+    const int cur = kt & 1;
+    const int k0 = kt * kBK;
     wait_lds();
-    load_frags(cur, 1, last, fa1, fb1);
-    mfmas(fa0, fb0);
-    mfmas(fa1, fb1);
+    tail_mask(fb0, k0, 0);
+    const uint32_t aa = addr_a(cur, 1), ab = addr_b(cur, 1);
+    mfma_step(fa0, fb0, read_ops{}, [&](auto s_c) { read_frag(s_c, fa1, fb1, aa, ab); });
+    wait_lds();
+    tail_mask(fb1, k0, 1);
+    mfma_step(fa1, fb1, no_ops{}, [&](auto) {});
   }
   // MFMA results are read below by ordinary instructions: wait out the
   // longest MFMA write latency first.
@@ -317,24 +395,99 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 
   // Epilogue.  Lane holds, for tile (i, j), output row m = m0 + 16 i + (l & 15)
   // and the four consecutive output features n = n0 + 16 j + 4 (l >> 4) + r.
+  // Every scale and bias it needs is requested first, in one batch (16-byte
+  // loads where the columns allow), so the tile pays one memory round trip.
   const int n_lane = 4 * (lane >> 4);
   float s_row[kTM];
+  f32x4 s_col[TN], b_col[TN];
+  if constexpr (OUT != 2) {
+    if (vec_cols && n_blk + kBN <= N) {  // uniform: the whole tile is inside N
 #pragma unroll
-  for (int i = 0; i < kTM; ++i) {
-    const int m = min(m_blk + wm + 16 * i + frag_row, M - 1);
-    s_row[i] = (I8 && OUT != 2) ? sa[m] : 1.f;
+      for (int j = 0; j < TN; ++j) {
+        const int n = n_blk + wn + 16 * j + n_lane;
+        s_col[j] = I8 ? *reinterpret_cast<const f32x4*>(sb + n) : f32x4{1.f, 1.f, 1.f, 1.f};
+        b_col[j] = bias ? *reinterpret_cast<const f32x4*>(bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n_blk + wn + 16 * j + n_lane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int nn = min(n + r, N - 1);
+          s_col[j][r] = I8 ? sb[nn] : 1.f;
+          b_col[j][r] = bias ? bias[nn] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) s_row[i] = I8 ? sa[min(m_blk + wm + 16 * i + frag_row, M - 1)] : 1.f;
+  }
+  // fp32 / bf16 outputs leave through LDS when the destination allows
+  // 16-byte stores: each wave writes one 16-row block of its results into a
+  // private, padded LDS area and reads it back as 16-byte chunks, so that
+  // consecutive lanes store consecutive bytes of an output row (whole cache
+  // lines) instead of 32-byte pieces of 16 different rows.
+  if constexpr (OUT != 2) {
+    if (staged) {
+      using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
+      constexpr int kElt = sizeof(out_t);
+      constexpr int kRowBytes = 16 * TN * kElt;    // one row of the wave's block
+      constexpr int kPitch = kRowBytes + 32;       // padding spreads rows over banks
+      constexpr int kSegs = kRowBytes / 16;        // 16-byte chunks per row
+      constexpr int kChunks = 16 * kSegs;          // per 16-row block
+      __syncthreads();  // every wave is done reading the slice buffers
+      uint8_t* stage = smem + wid * 16 * kPitch;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const acc_t a = acc[i][j];
+          float y[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (I8) {
+              y[r] = fmaf(static_cast<float>(a[r]), s_row[i] * s_col[j][r], b_col[j][r]);
+            } else {
+              y[r] = a[r] + b_col[j][r];
+            }
+          }
+          uint8_t* dst = stage + frag_row * kPitch + (16 * j + n_lane) * kElt;
+          if constexpr (OUT == 0) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4*>(dst) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
+                                                     static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+          }
+        }
+#pragma unroll
+        for (int c0 = 0; c0 < kChunks; c0 += 64) {
+          const int c = c0 + lane;
+          if (kChunks % 64 == 0 || c < kChunks) {
+            const int row = c / kSegs, seg = c % kSegs;
+            const i32x4 v = *reinterpret_cast<const i32x4*>(stage + row * kPitch + seg * 16);
+            const int m = m_blk + wm + 16 * i + row;
+            const int n = n_blk + wn + seg * (16 / kElt);
+            if (m < M) {
+              out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+              if (n + 16 / kElt <= N) {
+                *reinterpret_cast<i32x4*>(out) = v;
+              } else {
+                const out_t* e = reinterpret_cast<const out_t*>(&v);
+                for (int r = 0; r < 16 / kElt && n + r < N; ++r) out[r] = e[r];
+              }
+            }
+          }
+        }
+      }
+      return;
+    }
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n_blk + wn + 16 * j + n_lane;
     if (n >= N) continue;
-    float s_col[4], b_col[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nn = min(n + r, N - 1);
-      s_col[r] = (I8 && OUT != 2) ? sb[nn] : 1.f;
-      b_col[r] = (bias && OUT != 2) ? bias[nn] : 0.f;
-    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int m = m_blk + wm + 16 * i + frag_row;
@@ -352,9 +505,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (I8) {
-            y[r] = fmaf(static_cast<float>(a[r]), s_row[i] * s_col[r], b_col[r]);
+            y[r] = fmaf(static_cast<float>(a[r]), s_row[i] * s_col[j][r], b_col[j][r]);
           } else {
-            y[r] = a[r] + b_col[r];
+            y[r] = a[r] + b_col[j][r];
           }
         }
         if constexpr (OUT == 0) {
@@ -437,8 +590,13 @@ hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + 32 * TN - 1) / (32 * TN));
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
+  // 16-byte scale/bias loads need 16-byte aligned vectors.
+  const bool vec_cols = (reinterpret_cast<uintptr_t>(sb) & 15) == 0 && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+  // Staged stores need 16-byte aligned output rows.
+  const int out_elt = OUT == 1 ? 2 : 4;
+  const bool staged = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc * out_elt) % 16 == 0;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), kSmem, stream, A, lda, B, ldb, sa, sb, bias, static_cast<int>(M),
-                     static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m, tiles_n);
+                     static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m, tiles_n, vec_cols, staged);
   return hipGetLastError();
 }
 
