@@ -38,6 +38,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant GEMM from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is none for this
+    workload or the GEMM source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_i8_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256") != digest:
+        return None
+    return int(fields["traffic_bytes"])
+
+
 def make_workload(name: str):
     import workloads as W
 
@@ -240,7 +261,8 @@ def main():
                 "unit": "GB/s", "frac": round(kb["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         roof = {"kernel": f"linear_{big.name}", "bound": "mfma", "achieved": round(kb["TOPS"], 2),
-                "peak": PEAK_I8_TOPS, "unit": "TFLOP/s", "frac": round(kb["TOPS"] / PEAK_I8_TOPS, 4), "traffic": None}
+                "peak": PEAK_I8_TOPS, "unit": "TFLOP/s", "frac": round(kb["TOPS"] / PEAK_I8_TOPS, 4),
+                "traffic": measured_traffic(args.workload)}
 
     value = total_ops / (ms_step * 1e-3) / 1e12
     result = {
