@@ -1,11 +1,25 @@
 """Benchmark of the ConvRot W8A8 linear hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: pack the activation
-rows once (rotate + absmax + int8), then run every linear that shares the
-packed activation.  The default workload is the DiT attention projection:
-X bf16 [4096, 3072] with 8 outlier channels, a fused QKV weight
-[9216, 3072] and a second weight [3072, 3072], G = 256, bf16 output.  Weights
-are packed once before timing (offline, as in a checkpoint).
+rows once (rotate + absmax + int8), then run every linear that consumes the
+packed activation; where a workload chains layers (the MLP pair, the gated
+FFN) the intermediate activation is packed again.  Weights are packed once
+before timing (offline, as in a checkpoint).  Layers whose input width is not
+a multiple of G run on the routed bf16 linear.
+
+Workloads (``--workload``):
+  dit_attn_proj  (default) X bf16 [4096, 3072], 8 outlier channels; fused QKV
+                 W [9216, 3072] and a second W [3072, 3072] share one pack.
+  dit_mlp        X bf16 [8192, 3072]; W_up [12288, 3072], GELU, W_down
+                 [3072, 12288].
+  large_m_qkv    X bf16 [32700, 6144]; W [18432, 6144]; plus the routed layer
+                 X' [32700, 2688] -> W' [6144, 2688] on the bf16 linear.
+  decode_m{M}_g{G}[r]  gated FFN at M in {1, 4, 16}, K = 1152: W_gate, W_up
+                 [6912, 1152] share one pack, h = gelu_tanh(gate) * up feeds
+                 W_down [1152, 6912]; G in {16, 64, 1024}, "r" = randomized
+                 block rotation (G = 128).  G = 1024 divides neither width,
+                 so every linear routes to bf16.
+  unit_layer     X fp32 [64, 1024], W [1024, 1024], fp32 output.
 
 Inputs live in HBM before timing starts.  To keep the 256 MB Infinity Cache
 from serving them, each step uses the next of several independent buffer sets
@@ -17,8 +31,10 @@ Prints one JSON line on stdout; per-kernel details go to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,29 +48,30 @@ PEAK_I8_TOPS = 5000.0    # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0    # 8 TB/s HBM3E
 COLD_BYTES = 512 << 20
+SMALL_M = 16             # up to this many rows a linear runs on the weight-streaming kernel
+METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
+KERNEL_SOURCE = {"gemm_i8": "gemm.hip", "gemv_i8": "gemv.hip", "gemm_bf16": "gemm.hip", "pack_rows": "pack_rows.hip"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the dominant GEMM from the committed rocprofv3
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary, or None when there is none for this
-    workload or the GEMM source has changed since the counters were taken."""
-    import hashlib
-
-    path = os.path.join(ROOT, "profiles", f"traffic_gemm_i8_{workload}.txt")
-    if not os.path.exists(path):
+    workload or the kernel's source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCE:
         return None
     fields = {}
     for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", "gemm.hip")
+    src = os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", KERNEL_SOURCE[kernel])
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("gemm_source_sha256") != digest:
+    if fields.get("source_sha256") != digest:
         return None
     return int(fields["traffic_bytes"])
 
@@ -67,104 +84,272 @@ def make_workload(name: str):
     if name == "dit_mlp":
         return W.config3()
     if name == "large_m_qkv":
-        return W.config4(with_routed=False)
-    if name.startswith("decode_m"):
-        m = int(name[len("decode_m"):])
-        return W.config5(M=m, G=64)
+        return W.config4(with_routed=True)
+    m = re.fullmatch(r"decode_m(\d+)_g(\d+)(r?)", name)
+    if m:
+        return W.config5(M=int(m.group(1)), G=int(m.group(2)), kind="randomized" if m.group(3) else "regular")
     if name == "unit_layer":
         return W.config1()
     raise SystemExit(f"unknown workload {name}")
 
 
-class Kernels:
-    """Device state for one buffer set plus the step itself."""
+class Op:
+    """One timed launch of the step and what it moves or computes."""
+
+    def __init__(self, name, fn, kind, M=0, N=0, K=0, in_b=0, out_b=0):
+        self.name, self.fn, self.kind = name, fn, kind
+        self.M, self.N, self.K, self.in_b, self.out_b = M, N, K, in_b, out_b
+
+    @property
+    def kernel(self):
+        if self.kind == "pack":
+            return "pack_rows"
+        if self.kind == "int8":
+            return "gemv_i8" if self.M <= SMALL_M else "gemm_i8"
+        if self.kind == "bf16":
+            return "gemm_bf16"
+        return "torch"
+
+    def ops(self):
+        return 2.0 * self.M * self.N * self.K if self.kind in ("int8", "bf16") else 0.0
+
+    def bytes(self):
+        M, N, K = self.M, self.N, self.K
+        if self.kind == "pack":
+            return M * K * (self.in_b + 1) + 4 * M
+        if self.kind == "int8":
+            return M * K + 4 * M + N * K + 8 * N + M * N * self.out_b
+        if self.kind == "bf16":
+            return 2 * M * K + 2 * N * K + 4 * N + M * N * self.out_b
+        return 0
+
+
+class StepSet:
+    """Device state of one buffer set and the ordered launches of one step."""
 
     def __init__(self, wl, dev, torch, cr, template=None):
-        self.torch, self.cr = torch, cr
-        xdt = torch.bfloat16 if wl.xdtype == "bf16" else torch.float32
-        self.odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-        self.G = wl.G
+        self.torch, self.cr, self.wl = torch, cr, wl
+        bf16, f32 = torch.bfloat16, torch.float32
+        self.xdt = bf16 if wl.xdtype == "bf16" else f32
+        self.odt = bf16 if wl.out_dtype == "bf16" else f32
+        G, kind = wl.G, wl.kind
+        K0 = wl.X.shape[1]
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
         if template is None:
-            self.X = torch.from_numpy(wl.X).to(xdt).to(dev)
-            self.pw = []
-            self.bias = []
-            for lin in wl.linears:
-                wd = torch.from_numpy(lin.W).to(torch.bfloat16 if lin.wdtype == "bf16" else torch.float32).to(dev)
-                self.pw.append(cr.pack_weight(wd, wl.G))
-                del wd
-                self.bias.append(torch.from_numpy(lin.b).to(dev) if lin.b is not None else None)
+            self.signs = {}
+            if wl.signs is not None:
+                self.signs[K0] = up(wl.signs, torch.int8)
+            if wl.extra.get("signs_down") is not None:
+                sd = wl.extra["signs_down"]
+                self.signs[sd.shape[0]] = up(sd, torch.int8)
+            self.X = up(wl.X, self.xdt)
+            self.W, self.b = {}, {}
+            routed = wl.extra.get("routed")
+            for lin in list(wl.linears) + ([routed] if routed is not None else []):
+                K = lin.W.shape[1]
+                wd = up(lin.W, bf16 if lin.wdtype == "bf16" else f32)
+                if lin is routed or K % G != 0:
+                    self.W[lin.name] = wd.to(bf16)
+                else:
+                    self.W[lin.name] = cr.pack_weight(wd, G, kind, self.signs.get(K))
+                    del wd
+                self.b[lin.name] = up(lin.b, f32) if lin.b is not None else None
+            self.X2 = up(wl.extra["X_routed"], bf16) if "X_routed" in wl.extra else None
         else:
+            self.signs = template.signs
             self.X = template.X.clone()
-            self.pw = [cr.Packed(p.q.clone(), p.scale.clone(), p.group) for p in template.pw]
-            self.bias = template.bias
-        M, K = self.X.shape
-        self.mlp = wl.extra.get("activation") == "gelu_erf"
-        self.pa = cr.Packed(torch.empty((M, K), dtype=torch.int8, device=dev),
-                            torch.empty(M, dtype=torch.float32, device=dev), wl.G)
-        self.Y = [torch.empty((M, p.rows), dtype=self.odt, device=dev) for p in self.pw]
-        if self.mlp:
-            Kd = self.pw[0].rows
-            self.pa2 = cr.Packed(torch.empty((M, Kd), dtype=torch.int8, device=dev),
-                                 torch.empty(M, dtype=torch.float32, device=dev), wl.G)
+            self.W = {k: (cr.Packed(v.q.clone(), v.scale.clone(), v.group, v.kind, v.signs)
+                          if isinstance(v, cr.Packed) else v.clone()) for k, v in template.W.items()}
+            self.b = template.b
+            self.X2 = template.X2.clone() if template.X2 is not None else None
+        self.bufs = []
+        self.ops = self._plan(dev)
+
+    # -- buffers -----------------------------------------------------------
+    def _packed(self, rows, K, dev):
+        t = self.torch
+        p = self.cr.Packed(t.empty((rows, K), dtype=t.int8, device=dev), t.empty(rows, dtype=t.float32, device=dev),
+                           self.wl.G, self.wl.kind, self.signs.get(K))
+        self.bufs.append(p.q)
+        return p
+
+    def _out(self, name, rows, dev):
+        w = self.W[name]
+        N = w.rows if isinstance(w, self.cr.Packed) else w.shape[0]
+        y = self.torch.empty((rows, N), dtype=self.odt, device=dev)
+        self.bufs.append(y)
+        return y
 
     def nbytes(self):
-        t = [self.X, self.pa.q, *[p.q for p in self.pw], *self.Y]
-        if self.mlp:
-            t.append(self.pa2.q)
+        t = [self.X, *self.bufs] + ([self.X2] if self.X2 is not None else [])
+        for v in self.W.values():
+            t.append(v.q if isinstance(v, self.cr.Packed) else v)
         return sum(x.numel() * x.element_size() for x in t)
 
-    def step(self, ev=None):
+    # -- launches ----------------------------------------------------------
+    def _pack_op(self, name, src, dst):
         cr = self.cr
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        rec(0)
-        cr.pack_act(self.X, self.G, out=self.pa)
-        rec(1)
-        if not self.mlp:
-            for j, (p, b, y) in enumerate(zip(self.pw, self.bias, self.Y)):
-                cr.linear(self.pa, p, b, out=y)
-                rec(2 + j)
+        M, K = src.shape
+        return Op(name, lambda: cr.pack_act(src, dst.group, dst.kind, dst.signs, out=dst), "pack", M=M, K=K,
+                  in_b=src.element_size())
+
+    def _linear_op(self, name, src, y):
+        """src is a packed activation (int8 path) or a bf16 tensor (routed layer)."""
+        cr, w, b = self.cr, self.W[name], self.b[name]
+        ob = y.element_size()
+        if isinstance(w, cr.Packed):
+            return Op(f"linear_{name}", lambda: cr.linear(src, w, b, out=y), "int8", M=src.rows, N=w.rows, K=w.K,
+                      out_b=ob)
+        return Op(f"linear_{name}", lambda: cr.linear_bf16(src, w, b, out=y), "bf16", M=src.shape[0],
+                  N=w.shape[0], K=w.shape[1], out_b=ob)
+
+    def _plan(self, dev):
+        wl, torch = self.wl, self.torch
+        gelu = torch._C._nn.gelu
+        M, K = self.X.shape
+        ops = []
+        names = [l.name for l in wl.linears]
+        if isinstance(self.W[names[0]], self.cr.Packed):
+            src0 = self._packed(M, K, dev)
+            ops.append(self._pack_op("pack_act", self.X, src0))
         else:
-            cr.linear(self.pa, self.pw[0], self.bias[0], out=self.Y[0])
-            rec(2)
-            h = self.torch.nn.functional.gelu(self.Y[0])
-            rec(3)
-            cr.pack_act(h, self.G, out=self.pa2)
-            rec(4)
-            cr.linear(self.pa2, self.pw[1], self.bias[1], out=self.Y[1])
-            rec(5)
+            src0 = self.X
+        if wl.cfg in (1, 2):
+            for n in names:
+                ops.append(self._linear_op(n, src0, self._out(n, M, dev)))
+        elif wl.cfg == 3:
+            y_up = self._out("up", M, dev)
+            ops.append(self._linear_op("up", src0, y_up))
+            h = torch.empty_like(y_up)
+            self.bufs.append(h)
+            ops.append(Op("gelu_torch", lambda: gelu(y_up, out=h), "torch"))
+            pa2 = self._packed(M, h.shape[1], dev)
+            ops.append(self._pack_op("pack_act2", h, pa2))
+            ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
+        elif wl.cfg == 4:
+            ops.append(self._linear_op("qkv", src0, self._out("qkv", M, dev)))
+            r = wl.extra["routed"].name
+            ops.append(self._linear_op(r, self.X2, self._out(r, M, dev)))
+        elif wl.cfg == 5:
+            g = self._out("gate", M, dev)
+            u = self._out("up", M, dev)
+            ops.append(self._linear_op("gate", src0, g))
+            ops.append(self._linear_op("up", src0, u))
+            t, h = torch.empty_like(u), torch.empty_like(u)
+            self.bufs += [t, h]
+            ops.append(Op("gelu_tanh_mul_torch", lambda: torch.mul(gelu(g, approximate="tanh", out=t), u, out=h),
+                          "torch"))
+            if isinstance(self.W["down"], self.cr.Packed):
+                pa2 = self._packed(M, h.shape[1], dev)
+                ops.append(self._pack_op("pack_act2", h, pa2))
+                ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
+            else:
+                ops.append(self._linear_op("down", h, self._out("down", M, dev)))
+        else:
+            raise SystemExit(f"no step plan for config {wl.cfg}")
+        return ops
+
+    def step(self, ev=None):
+        if ev is None:
+            for op in self.ops:
+                op.fn()
+            return
+        ev[0].record()
+        for i, op in enumerate(self.ops):
+            op.fn()
+            ev[i + 1].record()
 
 
-def cpu_baseline(wl, budget_s: float = 15.0):
-    """Time the oracle on a bounded row sample of the same step."""
+def _gelu_erf(y):
+    from scipy.special import erf
+
+    return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+
+
+def _gelu_tanh(y):
+    return 0.5 * y * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (y + 0.044715 * y ** 3)))
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """Time the oracle on a bounded row sample of the same step.
+
+    Weights are packed beforehand (untimed).  The harness activations between
+    chained layers (GELU) are computed with numpy inside the timed region.
+    """
     import threadpoolctl
 
     import oracle.convrot_oracle as O
 
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    packed = []
-    for lin in wl.linears:
-        qw, sw, _ = O.pack(lin.W, wl.G)
-        packed.append((qw, sw, lin.b))
-    M, K = wl.X.shape
-    ops_per_row = sum(2.0 * K * qw.shape[0] for qw, _, _ in packed) if not wl.extra.get("activation") == "gelu_erf" \
-        else 2.0 * K * packed[0][0].shape[0] * 2
+    G, kind = wl.G, wl.kind
+    signs = {wl.X.shape[1]: wl.signs}
+    if wl.extra.get("signs_down") is not None:
+        signs[wl.extra["signs_down"].shape[0]] = wl.extra["signs_down"]
+    routed = wl.extra.get("routed")
+    lin = {l.name: l for l in wl.linears}
+    if routed is not None:
+        lin[routed.name] = routed
+
+    def sg(K):
+        return signs.get(K) if kind == "randomized" else None
+
+    packed = {}
+    for n, l in lin.items():
+        K = l.W.shape[1]
+        if l is not routed and K % G == 0:
+            q, s, _ = O.pack(l.W, G, kind, sg(K))
+            packed[n] = (q, s)
+
+    def gemm(name, qx, sx):
+        return O.epilogue64(O.int_gemm(qx, packed[name][0]), sx, packed[name][1], lin[name].b).astype(np.float32)
+
+    def layer(name, x):
+        if name in packed:
+            qx, sx, _ = O.pack(x, G, kind, sg(x.shape[1]))
+            return gemm(name, qx, sx)
+        return O.linear_unquantized64(x, lin[name].W, lin[name].b).astype(np.float32)
+
+    def shared(names, x):
+        if all(n in packed for n in names):
+            qx, sx, _ = O.pack(x, G, kind, sg(x.shape[1]))
+            return [gemm(n, qx, sx) for n in names]
+        return [layer(n, x) for n in names]
 
     def run(m):
         t0 = time.perf_counter()
-        qx, sx, _ = O.pack(wl.X[:m], wl.G)
-        for qw, sw, b in packed[:1] if wl.extra.get("activation") == "gelu_erf" else packed:
-            O.epilogue64(O.int_gemm(qx, qw), sx, sw, b).astype(np.float32)
+        x = wl.X[:m]
+        if wl.cfg in (1, 2):
+            shared(list(l.name for l in wl.linears), x)
+        elif wl.cfg == 3:
+            layer("down", _gelu_erf(layer("up", x)).astype(np.float32))
+        elif wl.cfg == 4:
+            layer("qkv", x)
+            layer(routed.name, wl.extra["X_routed"][:m])
+        elif wl.cfg == 5:
+            g, u = shared(["gate", "up"], x)
+            layer("down", (_gelu_tanh(g) * u).astype(np.float32))
         return time.perf_counter() - t0
 
+    ops_per_row = sum(2.0 * l.W.shape[0] * l.W.shape[1] for l in lin.values())
+    M = wl.X.shape[0]
     m = min(M, 64)
     t = run(m)
     while m < M and t < budget_s / 4:
         m = min(M, m * 4)
         t = run(m)
-    return {"value": round(ops_per_row * m / t / 1e12, 6), "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {m} of {M} activation rows of the same step (pack + every linear's exact int GEMM "
-                      f"and epilogue; weights packed beforehand, untimed); {t:.2f} s"}
+    reps, total = 1, t
+    while total < budget_s and m == M:
+        total += run(m)
+        reps += 1
+    return {"value": round(ops_per_row * m * reps / total / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {m} of {M} activation rows of the same step, {reps} run(s) (pack + every linear's "
+                      f"exact int GEMM and epilogue, routed layers in fp64, GELU in numpy; weights packed "
+                      f"beforehand, untimed); {total:.2f} s"}
 
 
 def main():
@@ -192,16 +377,18 @@ def main():
     t0 = time.time()
     wl = make_workload(args.workload)
     log(f"[bench] workload {wl.name}: X {wl.X.shape} {wl.xdtype}, linears "
-        f"{[(l.name, l.W.shape) for l in wl.linears]}, G={wl.G} (inputs {time.time() - t0:.1f}s)")
+        f"{[(l.name, l.W.shape) for l in wl.linears]}, G={wl.G} {wl.kind} (inputs {time.time() - t0:.1f}s)")
 
-    sets = [Kernels(wl, dev, torch, cr)]
+    sets = [StepSet(wl, dev, torch, cr)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
-        sets.append(Kernels(wl, dev, torch, cr, template=sets[0]))
-    log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle")
+        sets.append(StepSet(wl, dev, torch, cr, template=sets[0]))
+    ops = sets[0].ops
+    log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
+        f"launches: {[o.name for o in ops]}")
     torch.cuda.synchronize()
 
     if args.copy_mib:
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
@@ -211,7 +398,7 @@ def main():
         sets[i % len(sets)].step()
     torch.cuda.synchronize()
 
-    n_ev = 2 + len(wl.linears) + (2 if wl.extra.get("activation") == "gelu_erf" else 0)
+    n_ev = len(ops) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -222,52 +409,40 @@ def main():
     ms_step = t_total * 1e3 / args.steps
 
     dur = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(n_ev - 1)] for i in range(args.steps)])
-    avg_ms = dur.mean(axis=0)
-    M, K = wl.X.shape
-    in_b = 2 if wl.xdtype == "bf16" else 4
-    out_b = 2 if wl.out_dtype == "bf16" else 4
     kernels = {}
-    pack_bytes = M * K * (in_b + 1) + 4 * M
-    kernels["pack_act"] = {"us": avg_ms[0] * 1e3, "GB/s": pack_bytes / (avg_ms[0] * 1e-3) / 1e9}
-    kernels["pack_act"]["frac_hbm"] = kernels["pack_act"]["GB/s"] / PEAK_HBM_GBS
-    total_ops = 0.0
-    lin_names = [l.name for l in wl.linears]
-    if wl.extra.get("activation") == "gelu_erf":
-        slots = {lin_names[0]: 1, "gelu": 2, "pack_act2": 3, lin_names[1]: 4}
-    else:
-        slots = {n: 1 + j for j, n in enumerate(lin_names)}
-    for j, lin in enumerate(wl.linears):
-        N, Kw = lin.W.shape
-        ops = 2.0 * M * N * Kw
-        total_ops += ops
-        t = avg_ms[slots[lin.name]] * 1e-3
-        gemm_bytes = M * Kw + 4 * M + N * Kw + 8 * N + M * N * out_b
-        kernels[f"linear_{lin.name}"] = {"us": t * 1e6, "TOPS": ops / t / 1e12, "frac_mfma": ops / t / 1e12 / PEAK_I8_TOPS,
-                                         "GB/s": gemm_bytes / t / 1e9, "M": M, "N": N, "K": Kw}
-    if "gelu" in slots:
-        kernels["gelu_torch"] = {"us": avg_ms[slots["gelu"]] * 1e3}
-        Kd = wl.linears[0].W.shape[0]
-        t = avg_ms[slots["pack_act2"]] * 1e-3
-        kernels["pack_act2"] = {"us": t * 1e6, "GB/s": (M * Kd * 3 + 4 * M) / t / 1e9}
+    for j, op in enumerate(ops):
+        us = dur[:, j] * 1e3
+        t = us.mean() * 1e-6
+        k = {"kernel": op.kernel, "us": us.mean(), "us_p10": np.percentile(us, 10), "us_p50": np.median(us),
+             "us_p90": np.percentile(us, 90)}
+        if op.bytes():
+            k["GB/s"] = op.bytes() / t / 1e9
+            k["frac_hbm"] = k["GB/s"] / PEAK_HBM_GBS
+        if op.ops():
+            k["TOPS"] = op.ops() / t / 1e12
+            k["frac_mfma"] = k["TOPS"] / (PEAK_I8_TOPS if op.kind == "int8" else PEAK_BF16_TFLOPS)
+            k.update(M=op.M, N=op.N, K=op.K)
+        kernels[op.name] = k
     for k, v in kernels.items():
         log(f"[bench] {k}: " + ", ".join(f"{a}={b:.4g}" if isinstance(b, float) else f"{a}={b}" for a, b in v.items()))
 
-    # Dominant kernel: the largest linear.
-    big = max(wl.linears, key=lambda l: l.W.shape[0] * l.W.shape[1])
-    kb = kernels[f"linear_{big.name}"]
-    small_m = M <= 16
-    if small_m:
-        roof = {"kernel": f"linear_{big.name}", "bound": "hbm", "achieved": round(kb["GB/s"], 2), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(kb["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None}
+    # Dominant kernel: the linear launch that takes the most time.
+    lin_ops = [op for op in ops if op.kind in ("int8", "bf16")]
+    dom = max(lin_ops, key=lambda o: kernels[o.name]["us"])
+    kd = kernels[dom.name]
+    if dom.M <= SMALL_M:
+        roof = {"kernel": dom.kernel, "launch": dom.name, "bound": "hbm", "achieved": round(kd["GB/s"], 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kd["frac_hbm"], 4)}
     else:
-        roof = {"kernel": f"linear_{big.name}", "bound": "mfma", "achieved": round(kb["TOPS"], 2),
-                "peak": PEAK_I8_TOPS, "unit": "TFLOP/s", "frac": round(kb["TOPS"] / PEAK_I8_TOPS, 4),
-                "traffic": measured_traffic(args.workload)}
+        peak = PEAK_I8_TOPS if dom.kind == "int8" else PEAK_BF16_TFLOPS
+        roof = {"kernel": dom.kernel, "launch": dom.name, "bound": "mfma", "achieved": round(kd["TOPS"], 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(kd["TOPS"] / peak, 4)}
+    roof["traffic"] = measured_traffic(dom.kernel, args.workload)
 
-    value = total_ops / (ms_step * 1e-3) / 1e12
+    value = sum(op.ops() for op in ops) / (ms_step * 1e-3) / 1e12
     result = {
-        "metric": "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM",
-        "value": round(value, 3),
+        "metric": METRIC,
+        "value": round(value, 4),
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
@@ -276,15 +451,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "i8" if any(op.kind == "int8" for op in ops) else "bf16",
         "data": "synthetic (seeded; shapes and outlier structure of the workload, no checkpoint)",
-        "config": {"workload": wl.name, "M": M, "K": K, "N": [l.W.shape[0] for l in wl.linears], "G": wl.G,
-                   "in": wl.xdtype, "out": wl.out_dtype, "buffer_sets": len(sets)},
+        "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
+                   "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
+                   "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
+                   "buffer_sets": len(sets)},
         "roofline": roof,
-        "pack_roofline": {"bound": "hbm", "achieved": round(kernels["pack_act"]["GB/s"], 2), "peak": PEAK_HBM_GBS,
-                          "unit": "GB/s", "frac": round(kernels["pack_act"]["frac_hbm"], 4)},
         "kernels_us": {k: round(v["us"], 3) for k, v in kernels.items()},
     }
+    packs = [op for op in ops if op.kind == "pack"]
+    if packs:
+        kp = kernels[packs[0].name]
+        result["pack_roofline"] = {"kernel": "pack_rows", "launch": packs[0].name, "bound": "hbm",
+                                   "achieved": round(kp["GB/s"], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(kp["frac_hbm"], 4),
+                                   "traffic": measured_traffic("pack_rows", args.workload)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

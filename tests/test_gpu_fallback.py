@@ -15,7 +15,9 @@ from workloads import random_rows
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 2688), (37, 100, 64), (513, 1024, 1040), (5, 7, 16), (1, 300, 2688)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 2688), (37, 100, 64), (513, 1024, 1040), (5, 7, 16), (1, 300, 2688),
+                                   # M <= 16: the weight-streaming kernel (one or several load rounds, K tails)
+                                   (16, 1152, 6912), (4, 6912, 1152), (16, 33, 1040), (2, 24, 16384)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_linear_bf16_parity(cuda, M, N, K, out):
     x = random_rows((M, K), M + K, dtype="bf16")

@@ -25,6 +25,7 @@ GEMM_SHAPES = [
     (40, 8, 1152, 64),
     # small M: the weight-streaming kernel
     (1, 6912, 1152, 64), (4, 1152, 6912, 64), (16, 520, 1024, 256), (3, 17, 80, 16), (16, 16, 64, 4),
+    (2, 40, 40960, 256), (16, 100, 16400, 16),
 ]
 
 

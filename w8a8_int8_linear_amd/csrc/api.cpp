@@ -207,8 +207,11 @@ convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, in
     return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of X or W exceeds %lld bytes",
                 static_cast<long long>(kMaxLdBytes));
   if (M == 0 || N == 0) return ok();
-  const hipError_t e = convrot::launch_gemm_bf16(X, ldx, W, ldw, bias, M, N, K, Y, static_cast<convrot::Elt>(ydt),
-                                                 ldy, static_cast<hipStream_t>(stream));
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const auto s = static_cast<hipStream_t>(stream);
+  const hipError_t e = M <= convrot::kGemvMaxRows
+                           ? convrot::launch_gemv_bf16(X, ldx, W, ldw, bias, M, N, K, Y, out, ldy, s)
+                           : convrot::launch_gemm_bf16(X, ldx, W, ldw, bias, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_bf16");
 }
 

@@ -1,21 +1,29 @@
-// Small-M (decode) quantised linear for gfx950: the same result as the tiled
-// GEMM (exact int32 A = Qx Qw^T, then Y = A s_x[r] s_w[o] + b[o]; "INT8
-// Convrot Safetensors", "Runtime activation quantization"), organised to
-// stream the int8 weight once at full bandwidth.
+// Small-M (decode) linear for gfx950, bound by reading the weight once.
 //
-// With M <= 16 the work is bound by reading Qw (N*K bytes), so the kernel
-// is built around the weight stream rather than around reuse:
-//  * one workgroup per 16 output features; its 4 waves split K between
-//    them (wave w takes 64-byte steps w, w+4, ...);
-//  * every step is one v_mfma_i32_16x16x64_i8 whose row operand is 16 weight
-//    rows (16 bytes per lane, loaded straight from global memory into
-//    VGPRs, no LDS) and whose column operand is the (at most 16) activation
-//    rows; lanes for activation rows >= M re-read the last row and their
-//    outputs are dropped;
-//  * steps are unrolled by 4 so each lane keeps 64 bytes of weight loads in
-//    flight;
-//  * the 4 partial accumulators are summed exactly through LDS and wave 0
-//    applies the epilogue.
+// int8 mode: exact int32 A = Qx Qw^T, then Y = A s_x[r] s_w[o] + b[o] ("INT8
+// Convrot Safetensors", "Runtime activation quantization"); the same result
+// bits as the tiled kernel.  bf16 mode: Y = X W^T + b with fp32 accumulation,
+// the unquantised linear that layers with K % G != 0 keep (sglang PR 34581
+// summary page, kitchen_int8 routing).
+//
+// With M <= 16 the time is the time to stream N*K weight bytes, and at
+// decode sizes (a few MB) that is mostly memory latency.  So the kernel
+// puts every weight byte in flight at once:
+//  * one workgroup per 16 output features; its W waves (4, 8 or 16, chosen
+//    so each wave has at most 8 steps) split the row bytes into W
+//    contiguous ranges;
+//  * a step is 64 bytes of each of the 16 weight rows: one
+//    v_mfma_i32_16x16x64_i8 (or v_mfma_f32_16x16x32_bf16) whose row operand
+//    is the 16 weight rows (16 bytes per lane, straight from global memory)
+//    and whose column operand is the activation rows (rows >= M re-read the
+//    last row; their outputs are dropped);
+//  * a wave issues all loads of its range (up to 8 steps x 2 x 16 bytes per
+//    lane) before its first MFMA, so a whole launch's weight stream is
+//    requested within the first microsecond;
+//  * the W partial accumulators are summed through LDS (exact in int8 mode)
+//    and wave 0 applies the epilogue, writing 4 consecutive outputs per lane.
+// The byte-to-k assignment of a lane is the same for both operands, so each
+// MFMA pairs matching k.
 #include <hip/hip_runtime.h>
 
 #include "launchers.h"
@@ -23,25 +31,48 @@
 namespace convrot {
 namespace {
 
-// Four consecutive outputs go out as one vector store when aligned for it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSteps = 8;        // steps per wave per round of loads
+constexpr int kStepBytes = 64;   // bytes of one weight row per step
+
+template <bool I8>
+struct Mma;
+
+template <>
+struct Mma<true> {
+  using Acc = i32x4;
+  static __device__ __forceinline__ Acc run(i32x4 w, i32x4 x, Acc c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<false> {
+  using Acc = f32x4;
+  static __device__ __forceinline__ Acc run(i32x4 w, i32x4 x, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x), c,
+                                                   0, 0, 0);
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ bool vec_ok(const T* p) {
   return (reinterpret_cast<uintptr_t>(p) & (4 * sizeof(T) - 1)) == 0;
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kUnroll = 4;
-
-template <int OUT, bool KTAIL>
-__global__ __launch_bounds__(kThreads) void gemv_i8_kernel(
-    const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ B, int64_t ldb,
+// A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes]; kbytes =
+// K * element size (a multiple of 16); per = steps per wave.
+template <bool I8, int OUT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     const float* __restrict__ sa, const float* __restrict__ sb, const float* __restrict__ bias, int M, int N,
-    int K, void* __restrict__ C, int64_t ldc) {
-  __shared__ i32x4 partial[kWaves - 1][64];
+    int kbytes, int per, void* __restrict__ C, int64_t ldc) {
+  using Acc = typename Mma<I8>::Acc;
+  __shared__ Acc partial[WAVES > 1 ? WAVES - 1 : 1][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -49,43 +80,37 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(
   const int row = lane & 15;
   const int ch = lane >> 4;
 
-  const int8_t* wrow = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * 16;
-  const int8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
+  const uint8_t* wrow = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * 16;
+  const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
 
-  i32x4 acc = {0, 0, 0, 0};
-  const int nsteps = (K + 63) / 64;
-  int s = wid;
-  for (; s + kWaves * (kUnroll - 1) < nsteps; s += kWaves * kUnroll) {
-    i32x4 w[kUnroll], x[kUnroll];
+  const int nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
+  const int s_begin = wid * per;
+  const int s_end = min(nsteps, s_begin + per);
+
+  Acc acc = {0, 0, 0, 0};
+  for (int s0 = s_begin; s0 < s_end; s0 += kSteps) {
+    i32x4 w[kSteps], x[kSteps];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k = (s + kWaves * u) * 64;
-      if (KTAIL && k + ch * 16 >= K) {
-        w[u] = i32x4{0, 0, 0, 0};
-        x[u] = i32x4{0, 0, 0, 0};
-      } else {
-        w[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + k));
-        x[u] = *reinterpret_cast<const i32x4*>(xrow + k);
+    for (int u = 0; u < kSteps; ++u) {
+      w[u] = i32x4{0, 0, 0, 0};
+      x[u] = i32x4{0, 0, 0, 0};
+      const int byte = (s0 + u) * kStepBytes;
+      if (s0 + u < s_end && byte + ch * 16 < kbytes) {
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + byte));
+        x[u] = *reinterpret_cast<const i32x4*>(xrow + byte);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u], acc, 0, 0, 0);
-  }
-  for (; s < nsteps; s += kWaves) {
-    const int k = s * 64;
-    i32x4 w = {0, 0, 0, 0}, x = {0, 0, 0, 0};
-    if (!KTAIL || k + ch * 16 < K) {
-      w = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + k));
-      x = *reinterpret_cast<const i32x4*>(xrow + k);
-    }
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, acc, 0, 0, 0);
+    for (int u = 0; u < kSteps; ++u) acc = Mma<I8>::run(w[u], x[u], acc);
   }
 
-  if (wid > 0) partial[wid - 1][lane] = acc;
-  __syncthreads();
-  if (wid != 0) return;
+  if (WAVES > 1) {
+    if (wid > 0) partial[wid - 1][lane] = acc;
+    __syncthreads();
+    if (wid != 0) return;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) acc += partial[w][lane];
+    for (int w = 0; w < WAVES - 1; ++w) acc += partial[w][lane];
+  }
 
   // Lane holds output row m = lane & 15 and features n0 + 4 (lane >> 4) + r.
   const int m = row;
@@ -98,14 +123,14 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(
     } else {
       for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[r];
     }
-    return;
   } else {
-    const float s_row = sa[m];
+    const float s_row = I8 ? sa[m] : 1.f;
     float y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int nn = min(n + r, N - 1);
-      y[r] = fmaf(static_cast<float>(acc[r]), s_row * sb[nn], bias ? bias[nn] : 0.f);
+      const float b = bias ? bias[nn] : 0.f;
+      y[r] = I8 ? fmaf(static_cast<float>(acc[r]), s_row * sb[nn], b) : static_cast<float>(acc[r]) + b;
     }
     if constexpr (OUT == 0) {
       float* out = static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n;
@@ -115,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(
         for (int r = 0; r < 4 && n + r < N; ++r) out[r] = y[r];
       }
     } else {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       __bf16* out = static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n;
       if (n + 3 < N && vec_ok(out)) {
         *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
@@ -127,17 +151,36 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(
   }
 }
 
-template <int OUT>
-hipError_t launch_out(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa, const float* sb,
-                      const float* bias, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+template <bool I8, int OUT>
+hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const float* sa, const float* sb,
+                      const float* bias, int64_t M, int64_t N, int64_t kbytes, void* C, int64_t ldc,
                       hipStream_t stream) {
+  const int64_t nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
+  int waves = 16;
+  for (int w : {4, 8}) {
+    if ((nsteps + w - 1) / w <= kSteps) {
+      waves = w;
+      break;
+    }
+  }
+  const int per = static_cast<int>((nsteps + waves - 1) / waves);
   const dim3 grid(static_cast<unsigned>((N + 15) / 16));
-  if (K % 64 == 0) {
-    hipLaunchKernelGGL((gemv_i8_kernel<OUT, false>), grid, dim3(kThreads), 0, stream, A, lda, B, ldb, sa, sb, bias,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), C, ldc);
-  } else {
-    hipLaunchKernelGGL((gemv_i8_kernel<OUT, true>), grid, dim3(kThreads), 0, stream, A, lda, B, ldb, sa, sb, bias,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), C, ldc);
+  const auto* a = static_cast<const uint8_t*>(A);
+  const auto* b = static_cast<const uint8_t*>(B);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
+  switch (waves) {
+    case 4:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4>), grid, dim3(256), 0, stream, a, lda, b, ldb, sa, sb, bias, m, n,
+                         kb, per, C, ldc);
+      break;
+    case 8:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8>), grid, dim3(512), 0, stream, a, lda, b, ldb, sa, sb, bias, m, n,
+                         kb, per, C, ldc);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16>), grid, dim3(1024), 0, stream, a, lda, b, ldb, sa, sb, bias, m,
+                         n, kb, per, C, ldc);
+      break;
   }
   return hipGetLastError();
 }
@@ -149,10 +192,19 @@ hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t
                           int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   switch (out) {
-    case Elt::F32: return launch_out<0>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    case Elt::BF16: return launch_out<1>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    default: return launch_out<2>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
+    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
+    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
+    default: return launch_out<true, 2>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
   }
+}
+
+hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,
+                            int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // Row strides and K in bytes.
+  if (out == Elt::F32)
+    return launch_out<false, 0>(A, 2 * lda, B, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
+  return launch_out<false, 1>(A, 2 * lda, B, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
 }
 
 }  // namespace convrot

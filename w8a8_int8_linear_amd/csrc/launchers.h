@@ -34,12 +34,17 @@ hipError_t launch_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t l
                             const float* bias, int64_t M, int64_t N, int64_t K,
                             void* C, Elt out, int64_t ldc, hipStream_t stream);
 
-// Weight-streaming kernel for small M (M <= kGemvMaxRows); same result bits
-// as launch_gemm_i8.
+// Weight-streaming kernels for small M (M <= kGemvMaxRows).  The int8 one
+// gives the same result bits as launch_gemm_i8; the bf16 one computes the
+// same as launch_gemm_bf16 up to fp32 summation order.
 constexpr int64_t kGemvMaxRows = 16;
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                           const float* sa, const float* sb, const float* bias,
                           int64_t M, int64_t N, int64_t K,
                           void* C, Elt out, int64_t ldc, hipStream_t stream);
+
+hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* C, Elt out, int64_t ldc, hipStream_t stream);
 
 }  // namespace convrot
