@@ -109,6 +109,15 @@ __device__ __forceinline__ void wait_lds_and_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0070);
 #endif
 }
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (lgkmcnt and expcnt are not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
 // One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane
 // l's 16 bytes land at lds + 16 l.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
@@ -145,12 +154,43 @@ template <int N>
 __device__ __forceinline__ void pad() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_sched_barrier(0);
-  static_assert(N == 5 || N == 24, "add the padding length needed");
+  static_assert(N == 5 || N == 16 || N == 24, "add the padding length needed");
   if constexpr (N == 5) {
     asm volatile("s_nop 4" ::);
+  } else if constexpr (N == 16) {
+    asm volatile("s_nop 7\n\ts_nop 7" ::);
   } else {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+// Keeps fragment registers allocated up to this point (no instruction).
+// The MFMAs are inline asm, so the compiler does not know that an MFMA may
+// still be reading its operands several cycles after issue; without this it
+// may hand a register to an unrelated temporary right behind the last MFMA
+// that reads it.
+template <int N>
+__device__ __forceinline__ void keep_live(const i32x4 (&r)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
+#endif
+}
+// Marks an accumulator as rewritten here (no instruction).
+template <typename T>
+__device__ __forceinline__ void touch_acc(T& a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+a"(a));
+#endif
+}
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release semantics would add a wait for every outstanding vector-memory
+// operation; callers wait for exactly what they need before it.
+__device__ __forceinline__ void barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 #endif
 }
@@ -189,9 +229,11 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
+// LDS: three A slices (the activation tile is re-filled one slice
+// further ahead than the weight tile) and two B slices.
 template <int TN>
 constexpr int smem_bytes() {
-  return 2 * (kBM + 32 * TN) * kBK;
+  return 3 * kATileBytes + 2 * (32 * TN) * kBK;
 }
 
 // OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator.
@@ -205,7 +247,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   constexpr int kBN = 32 * TN;
   constexpr int kWN = 16 * TN;
   constexpr int kBTileBytes = kBN * kBK;
-  constexpr int kStageBytes = kATileBytes + kBTileBytes;
+  constexpr int kDmaA = kBM / 32;  // 1 KiB DMA instructions per slice and wave: A part
+  constexpr int kDmas = kDmaA + kBN / 32;
+  constexpr int kBBase = 3 * kATileBytes;  // LDS offset of the B slices
+  static_assert(smem_bytes<TN>() <= 160 * 1024, "LDS budget");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using Op = Mfma<I8>;
   using acc_t = typename Op::acc_t;
@@ -226,34 +271,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   // a slice, lane l writing physical chunk l % 8 of row l / 8.  Wave w
   // fills blocks w, w + 4, ..., so each lane fetches logical chunk
   // (l % 8) ^ (l / 8) of rows 8 (w + 4 i) + l / 8.  Rows past the matrix edge
-  // re-read the last row (their results are never stored).  Offsets are
-  // relative to the tile's first row.
+  // re-read the last row (their results are never stored).
+  //
+  // Issuing a DMA costs no vector ALU work inside the loop: the address is
+  // a wave-uniform base (tile origin + slice offset, scalar registers) plus
+  // a per-lane 32-bit offset computed once here, and the LDS destination
+  // (M0) is derived from the wave-uniform wave id.  When K has a tail, the
+  // last slice uses a second offset set in which chunks past the end of K
+  // point at the row's first chunk (a valid address); fragments of such
+  // chunks are zeroed when read.
   const uint8_t* a_tile = A + static_cast<int64_t>(m_blk) * lda;
   const uint8_t* b_tile = B + static_cast<int64_t>(n_blk) * ldb;
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
   const int dma_ch = (lane & 7) ^ (lane >> 3);
-  int a_off[kBM / 32], b_off[kBN / 32];
+  const int nk = (Kb + kBK - 1) / kBK;
+  const int k_last = (nk - 1) * kBK;
+  uint32_t dma_off[kDmas], dma_off_tail[KTAIL ? kDmas : 1];
 #pragma unroll
-  for (int i = 0; i < kBM / 32; ++i) {
-    const int row = 8 * (wid + 4 * i) + (lane >> 3);
-    a_off[i] = (min(m_blk + row, M - 1) - m_blk) * static_cast<int>(lda) + dma_ch * 16;
+  for (int i = 0; i < kDmas; ++i) {
+    const bool is_a = i < kBM / 32;
+    const int blk = wid + 4 * (is_a ? i : i - kBM / 32);
+    const int row = 8 * blk + (lane >> 3);
+    const int rows = is_a ? M - m_blk : N - n_blk;
+    const int64_t ld = is_a ? lda : ldb;
+    const uint32_t row_off = static_cast<uint32_t>(min(row, rows - 1)) * static_cast<uint32_t>(ld);
+    dma_off[i] = row_off + dma_ch * 16;
+    if constexpr (KTAIL) dma_off_tail[i] = row_off + (k_last + dma_ch * 16 < Kb ? k_last + dma_ch * 16 : 0);
   }
-#pragma unroll
-  for (int i = 0; i < kBN / 32; ++i) {
-    const int row = 8 * (wid + 4 * i) + (lane >> 3);
-    b_off[i] = (min(n_blk + row, N - 1) - n_blk) * static_cast<int>(ldb) + dma_ch * 16;
-  }
-  auto issue_slice = [&](int buf, int k0) {
-    uint8_t* sA = smem + buf * kStageBytes;
-    uint8_t* sB = sA + kATileBytes;
-    // A chunk past the end of K fetches the row's first chunk instead (a
-    // valid address); fragments of such chunks are zeroed when read.
-    const int kk = (KTAIL && k0 + dma_ch * 16 >= Kb) ? -dma_ch * 16 : k0;
-#pragma unroll
-    for (int i = 0; i < kBM / 32; ++i)
-      dma16(a_tile + a_off[i] + kk, sA + (wid + 4 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < kBN / 32; ++i)
-      dma16(b_tile + b_off[i] + kk, sB + (wid + 4 * i) * 1024);
+  // DMA instruction number s of the slice starting at byte k0; A blocks
+  // (s < kDmaA) go to A slice buffer `buf` (of 3), B blocks to B slice
+  // buffer `buf` (of 2).
+  auto dma_block = [&](auto s_c, int buf, int k0, auto tail_c) {
+    constexpr int s = decltype(s_c)::value;
+    constexpr bool kTail = decltype(tail_c)::value;
+    constexpr bool kIsA = s < kDmaA;
+    constexpr int kBlk = kIsA ? s : s - kDmaA;
+    uint8_t* lds = smem + (kIsA ? buf * kATileBytes : kBBase + buf * kBTileBytes) + (wid_u + 4 * kBlk) * 1024;
+    const uint8_t* base = kIsA ? a_tile : b_tile;
+    if constexpr (kTail) {
+      dma16(base + dma_off_tail[s], lds);
+    } else {
+      dma16(base + k0 + dma_off[s], lds);
+    }
+  };
+  // DMA instructions [FIRST, LAST) of the slice at k0 (A into A buffer
+  // abuf, B into B buffer bbuf).
+  auto issue = [&](auto first_c, auto last_c, int abuf, int bbuf, int k0) {
+    constexpr int kFirst = decltype(first_c)::value;
+    constexpr int kLast = decltype(last_c)::value;
+    auto all = [&](auto tail_c) {
+      static_for<kLast - kFirst>([&](auto i_c) {
+        constexpr int s = kFirst + decltype(i_c)::value;
+        dma_block(std::integral_constant<int, s>{}, s < kDmaA ? abuf : bbuf, k0, tail_c);
+      });
+    };
+    if (KTAIL && k0 == k_last) all(std::true_type{}); else all(std::false_type{});
   };
 
   acc_t acc[kTM][TN];
@@ -272,16 +344,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) frag_off[ks] = frag_row * kBK + (((4 * ks + frag_ch) ^ (frag_row & 7)) << 4);
   const uint32_t lds0 = lds_address(smem);
-  auto addr_a = [&](int buf, int ks) -> uint32_t { return lds0 + buf * kStageBytes + wm * kBK + frag_off[ks]; };
+  auto addr_a = [&](int buf, int ks) -> uint32_t { return lds0 + buf * kATileBytes + wm * kBK + frag_off[ks]; };
   auto addr_b = [&](int buf, int ks) -> uint32_t {
-    return lds0 + buf * kStageBytes + kATileBytes + wn * kBK + frag_off[ks];
+    return lds0 + kBBase + buf * kBTileBytes + wn * kBK + frag_off[ks];
   };
 
   // Two register sets of fragments: one feeds the MFMAs while the other is
   // being read from LDS.
   i32x4 fa0[kTM], fb0[TN], fa1[kTM], fb1[TN];
   constexpr int kReads = kTM + TN;              // fragment reads per step
-  constexpr int kDmas = kBM / 32 + kBN / 32;    // DMA instructions per slice and wave
   // Fragment read number s of a step into (fa, fb).
   auto read_frag = [&](auto s_c, i32x4* fa, i32x4* fb, uint32_t aa, uint32_t ab) {
     constexpr int s = decltype(s_c)::value;
@@ -289,17 +360,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       lds_read16<2048 * s>(fa[s], aa);
     } else {
       lds_read16<2048 * (s - kTM)>(fb[s - kTM], ab);
-    }
-  };
-  // DMA instruction number s of a slice.
-  auto dma_block = [&](auto s_c, int buf, int k0) {
-    constexpr int s = decltype(s_c)::value;
-    uint8_t* sA = smem + buf * kStageBytes;
-    const int kk = (KTAIL && k0 + dma_ch * 16 >= Kb) ? -dma_ch * 16 : k0;
-    if constexpr (s < kBM / 32) {
-      dma16(a_tile + a_off[s] + kk, sA + (wid + 4 * s) * 1024);
-    } else {
-      dma16(b_tile + b_off[s - kBM / 32] + kk, sA + kATileBytes + (wid + 4 * (s - kBM / 32)) * 1024);
     }
   };
   // One 64-byte K step: the TM x TN MFMAs on (fa, fb), with op(0..NOPS-1)
@@ -328,70 +388,108 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   using read_ops = std::integral_constant<int, kReads>;
   using dma_read_ops = std::integral_constant<int, kDmas + kReads>;
 
-  // Pipeline per 128-byte slice kt (two 64-byte steps), buffers kt & 1:
-  //   step 0: MFMAs on set 0 | reads of set 1 (slice kt, step 1)
-  //   wait for own LDS reads and for the DMA of slice kt+1; barrier
-  //   step 1: MFMAs on set 1 | DMA of slice kt+2 into kt's buffer, then reads
-  //           of set 0 (slice kt+1, step 0)
-  // The MFMAs never wait on a read issued in the same step, and one barrier
-  // per slice both publishes slice kt+1 and frees kt's buffer.
-  const int nk = (Kb + kBK - 1) / kBK;
-  issue_slice(0, 0);
-  wait_lds_and_vmem();
-  __syncthreads();
-  if (nk > 1) issue_slice(1, kBK);
+  // Pipeline per 128-byte slice kt (two 64-byte steps).  Slice kt lives in
+  // A buffer kt % 3 and B buffer kt % 2.  The vector-memory path moves at
+  // most ~36 bytes per clock into a CU's LDS, so each phase carries half of
+  // a slice's DMA: the A part of slice kt+2 in phase 1, the B part in
+  // phase 2 (a 256 x 256 tile moves 32 KiB per phase, 32 bytes per clock at
+  // the MFMA rate).  The third A buffer is what lets A go out a phase early.
+  //   phase 1: MFMAs on set 0 | DMA A(kt+2) into A buffer (kt+2) % 3,
+  //            reads of set 1 (slice kt, step 1)
+  //   wait for own LDS reads and for own DMAs up to B(kt+1) (A(kt+2) may
+  //   still fly); barrier
+  //   phase 2: MFMAs on set 1 | DMA B(kt+2) into B buffer kt % 2, reads of
+  //            set 0 (slice kt+1, step 0)
+  // A buffer is refilled only after the barrier that follows the last read
+  // of its previous slice: A buffer (kt+2) % 3 held slice kt-1 (last read
+  // before barrier kt-1), B buffer kt % 2 holds slice kt (last read before
+  // barrier kt).  Every slice runs the same code: DMAs of slices past the
+  // end are skipped by uniform branches, and the reads that would feed
+  // slice nk fetch stale LDS data that no MFMA uses.  The loop has one entry
+  // and one exit: the MFMAs are opaque to the compiler, and a second path
+  // into the epilogue would let it place accumulator copies right behind
+  // the last MFMAs, before the hazard padding.
+  using dma_a = std::integral_constant<int, 0>;
+  using dma_mid = std::integral_constant<int, kDmaA>;
+  using dma_end = std::integral_constant<int, kDmas>;
+  issue(dma_a{}, dma_end{}, 0, 0, 0);
+  if (nk > 1) issue(dma_a{}, dma_end{}, 1, 1, kBK);
+  if (nk > 1) wait_vm<kDmas>(); else wait_vm<0>();
+  wait_lds();
+  barrier();
   static_for<kReads>([&](auto s_c) { read_frag(s_c, fa0, fb0, addr_a(0, 0), addr_b(0, 0)); });
 
-  auto slice = [&](int kt, auto with_dma_c) {
-    constexpr bool kWithDma = decltype(with_dma_c)::value;
-    const int cur = kt & 1;
-    const int k0 = kt * kBK;
-    wait_lds();
-    tail_mask(fb0, k0, 0);
-    {
-      const uint32_t aa = addr_a(cur, 1), ab = addr_b(cur, 1);
-      mfma_step(fa0, fb0, read_ops{}, [&](auto s_c) { read_frag(s_c, fa1, fb1, aa, ab); });
-    }
-    wait_lds_and_vmem();
-    __syncthreads();
-    tail_mask(fb1, k0, 1);
-    {
-      const uint32_t aa = addr_a(cur ^ 1, 0), ab = addr_b(cur ^ 1, 0);
-      if constexpr (kWithDma) {
-        mfma_step(fa1, fb1, dma_read_ops{}, [&](auto s_c) {
-          constexpr int s = decltype(s_c)::value;
-          if constexpr (s < kDmas) {
-            dma_block(s_c, cur, k0 + 2 * kBK);
-          } else {
-            read_frag(std::integral_constant<int, s - kDmas>{}, fa0, fb0, aa, ab);
-          }
-        });
-      } else {
-        mfma_step(fa1, fb1, read_ops{}, [&](auto s_c) { read_frag(s_c, fa0, fb0, aa, ab); });
-      }
-    }
-  };
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
-  if (kt + 1 < nk) {
-    slice(kt, std::false_type{});
-    ++kt;
-  }
-  {
-    // Last slice: no DMA, no next slice.
-    const int cur = kt & 1;
+  int a_cur = 0;  // kt % 3
+  do {
+    const int b_cur = kt & 1;
+    const int a_next = a_cur == 2 ? 0 : a_cur + 1;    // (kt+1) % 3
+    const int a_after = a_next == 2 ? 0 : a_next + 1;  // (kt+2) % 3
     const int k0 = kt * kBK;
+    const bool dma = kt + 2 < nk;
     wait_lds();
     tail_mask(fb0, k0, 0);
-    const uint32_t aa = addr_a(cur, 1), ab = addr_b(cur, 1);
-    mfma_step(fa0, fb0, read_ops{}, [&](auto s_c) { read_frag(s_c, fa1, fb1, aa, ab); });
+    {
+      const uint32_t aa = addr_a(a_cur, 1), ab = addr_b(b_cur, 1);
+      mfma_step(fa0, fb0, std::integral_constant<int, kDmaA + kReads>{}, [&](auto s_c) {
+        constexpr int o = decltype(s_c)::value;
+        if constexpr (o < kDmaA) {
+          if (dma) {
+            if (KTAIL && k0 + 2 * kBK == k_last) {
+              dma_block(s_c, a_after, k0 + 2 * kBK, std::true_type{});
+            } else {
+              dma_block(s_c, a_after, k0 + 2 * kBK, std::false_type{});
+            }
+          }
+        } else {
+          read_frag(std::integral_constant<int, o - kDmaA>{}, fa1, fb1, aa, ab);
+        }
+      });
+    }
+    // The operands of the last MFMAs may still be being read: release the
+    // set's registers only after enough wait states (see keep_live).
+    pad<16>();
+    keep_live(fa0);
+    keep_live(fb0);
+    if (dma) wait_vm<kDmaA>(); else wait_vm<0>();
     wait_lds();
+    barrier();
     tail_mask(fb1, k0, 1);
-    mfma_step(fa1, fb1, no_ops{}, [&](auto) {});
-  }
+    {
+      const uint32_t aa = addr_a(a_next, 0), ab = addr_b(b_cur ^ 1, 0);
+      mfma_step(fa1, fb1, std::integral_constant<int, kDmas - kDmaA + kReads>{}, [&](auto s_c) {
+        constexpr int o = decltype(s_c)::value;
+        if constexpr (o < kDmas - kDmaA) {
+          if (dma) {
+            if (KTAIL && k0 + 2 * kBK == k_last) {
+              dma_block(std::integral_constant<int, kDmaA + o>{}, b_cur, k0 + 2 * kBK, std::true_type{});
+            } else {
+              dma_block(std::integral_constant<int, kDmaA + o>{}, b_cur, k0 + 2 * kBK, std::false_type{});
+            }
+          }
+        } else {
+          read_frag(std::integral_constant<int, o - (kDmas - kDmaA)>{}, fa0, fb0, aa, ab);
+        }
+      });
+    }
+    pad<16>();
+    keep_live(fa1);
+    keep_live(fb1);
+    a_cur = a_next;
+    ++kt;
+  } while (kt < nk);
+  // The last reads fetched nothing that is used; let them retire.
+  wait_lds();
   // MFMA results are read below by ordinary instructions: wait out the
-  // longest MFMA write latency first.
+  // longest MFMA write latency first.  The empty statements then redefine
+  // every accumulator after the padding, so no copy of one (which the
+  // register allocator is free to place anywhere after its last write) can
+  // read an MFMA result before it is complete.
   pad<24>();
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) touch_acc(acc[i][j]);
 
   // Epilogue.  Lane holds, for tile (i, j), output row m = m0 + 16 i + (l & 15)
   // and the four consecutive output features n = n0 + 16 j + 4 (l >> 4) + r.
