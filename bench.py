@@ -50,7 +50,23 @@ PEAK_HBM_GBS = 8000.0    # 8 TB/s HBM3E
 COLD_BYTES = 512 << 20
 SMALL_M = 16             # up to this many rows a linear runs on the weight-streaming kernel
 METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
-KERNEL_SOURCE = {"gemm_i8": "gemm.hip", "gemv_i8": "gemv.hip", "gemm_bf16": "gemm.hip", "pack_rows": "pack_rows.hip"}
+# the sources each kernel is compiled from; a traffic summary is valid only for these exact bytes
+KERNEL_SOURCE = {
+    "gemm_i8": ("gemm_kernel.h", "epilogue.h", "gemm_i8.hip"),
+    "gemm_i8_act": ("gemm_kernel.h", "epilogue.h", "gemm_act.hip"),
+    "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
+    "gemm_bf16": ("gemm_kernel.h", "epilogue.h", "gemm_bf16.hip"),
+    "gemv_i8": ("gemv.hip", "epilogue.h"),
+    "pack_rows": ("pack_rows.hip",),
+}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCE[kernel]:
+        with open(os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -69,9 +85,7 @@ def measured_traffic(kernel: str, workload: str):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", KERNEL_SOURCE[kernel])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != digest:
+    if fields.get("source_sha256") != source_digest(kernel):
         return None
     return int(fields["traffic_bytes"])
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 1
+#define CONVROT_ABI_VERSION 2
 
 typedef enum {
   CONVROT_OK = 0,
@@ -89,6 +89,16 @@ typedef enum {
   /* gemma.cpp issue, "Rotation method": (1/sqrt G) H_sylvester D, G = 2^m in {16, 32, ..., 1024}. */
   CONVROT_ROT_RANDOMIZED = 1
 } convrot_rot_kind;
+
+/* Activation applied by a fused epilogue (convrot_linear_act,
+ * convrot_linear_gated), with the erf and tanh of the device math library:
+ *   GELU_ERF   gelu(y) = y/2 (1 + erf(y / sqrt 2))
+ *   GELU_TANH  gelu(y) = y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))  */
+typedef enum {
+  CONVROT_ACT_NONE = 0, /* not accepted by the fused entry points (use convrot_linear) */
+  CONVROT_ACT_GELU_ERF = 1,
+  CONVROT_ACT_GELU_TANH = 2
+} convrot_act;
 
 /* Rotation descriptor.  `signs` is a device vector of K int8 values, each +1
  * or -1 (one sign per input feature, block b using signs[b*G .. b*G+G-1]);
@@ -147,6 +157,38 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w,
                               const float* bias, void* Y, convrot_dtype ydt, int64_t ldy,
                               void* stream);
+
+/* The quantised linear with an activation fused into its epilogue (the
+ * output of the linear is never written unactivated):
+ *   Y[r, o] = fn(A[r, o] * act->scale[r] * w->scale[o] + bias[o])
+ * Arguments, checks and errors as convrot_linear, plus:
+ *   fn    CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH, else
+ *         CONVROT_ERR_INVALID_ARG
+ *   ydt   CONVROT_F32 or CONVROT_BF16 (CONVROT_I32 is rejected with
+ *         CONVROT_ERR_DTYPE).
+ * A packed activation feeds the next layer's linear; this entry point is
+ * for a layer followed by an activation, such as the first linear of an
+ * MLP. */
+convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packed* w, const float* bias,
+                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* stream);
+
+/* A gated pair: two quantised linears that share one packed activation,
+ * combined in the epilogue of a single launch,
+ *   G[r, o] = A_gate[r, o] * act->scale[r] * w_gate->scale[o] + b_gate[o]
+ *   U[r, o] = A_up[r, o]   * act->scale[r] * w_up->scale[o]   + b_up[o]
+ *   Y[r, o] = fn(G[r, o]) * U[r, o]
+ * (the gated feed-forward layer; "INT8 Convrot Safetensors", "Runtime
+ * activation quantization", last paragraph: one packed activation for
+ * every linear that shares the input).
+ *   w_gate, w_up  packed weights [N, K], each checked against `act` as in
+ *                 convrot_linear; they must have the same N
+ *                 (CONVROT_ERR_MISMATCH otherwise)
+ *   b_gate, b_up  [N] fp32 or NULL
+ *   fn, ydt       as convrot_linear_act
+ *   Y             [M, ldy]. */
+convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_packed* w_gate, const float* b_gate,
+                                    const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
+                                    convrot_dtype ydt, int64_t ldy, void* stream);
 
 /* The unquantised path for layers the rotation cannot cover (K % G != 0):
  *   Y[r, o] = sum_i X[r, i] W[o, i] + bias[o]

@@ -80,3 +80,17 @@ def rel_fro(a: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, np.float64)
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(a - ref) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def gelu64(y: np.ndarray, act: str) -> np.ndarray:
+    """GELU in fp64 from its definition: act "gelu_erf" is y/2 (1 + erf(y/sqrt 2)),
+    "gelu_tanh" is y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).  The
+    activation after a linear layer, not part of the method."""
+    from scipy.special import erf
+
+    y = np.asarray(y, np.float64)
+    if act == "gelu_erf":
+        return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+    if act == "gelu_tanh":
+        return 0.5 * y * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (y + 0.044715 * y ** 3)))
+    raise ValueError(act)

@@ -159,6 +159,38 @@ def test_linear_k_overflow_guard(lib):
                          w=packed(rows=4, K=K, G=1024, q=0x40000)) == _lib.ERR_INVALID_ARG
 
 
+def act_status(lib, fn=_lib.ACT_GELU_ERF, ydt=_lib.BF16, act=None, w=None):
+    act = act if act is not None else packed(rows=32)
+    w = w if w is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    return lib.convrot_linear_act(ctypes.byref(act), ctypes.byref(w), None, fn, A16C, ydt, w.rows, None)
+
+
+def gated_status(lib, fn=_lib.ACT_GELU_TANH, ydt=_lib.BF16, up=None, gate=None):
+    act = packed(rows=8)
+    g = gate if gate is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    u = up if up is not None else packed(rows=64, q=0x80000, scale=0x90000)
+    return lib.convrot_linear_gated(ctypes.byref(act), ctypes.byref(g), None, ctypes.byref(u), None, fn, A16C, ydt,
+                                    g.rows, None)
+
+
+def test_linear_act_checks(lib):
+    assert act_status(lib, fn=_lib.ACT_NONE) == _lib.ERR_INVALID_ARG
+    assert act_status(lib, fn=7) == _lib.ERR_INVALID_ARG
+    assert act_status(lib, ydt=_lib.I32) == _lib.ERR_DTYPE        # an activation needs a float output
+    assert act_status(lib, w=packed(rows=64, K=512, q=0x40000)) == _lib.ERR_MISMATCH
+    assert act_status(lib, act=packed(rows=0)) == _lib.OK
+
+
+def test_linear_gated_checks(lib):
+    assert gated_status(lib, fn=_lib.ACT_NONE) == _lib.ERR_INVALID_ARG
+    assert gated_status(lib, ydt=_lib.I32) == _lib.ERR_DTYPE
+    assert gated_status(lib, up=packed(rows=63, q=0x80000)) == _lib.ERR_MISMATCH      # N differs
+    assert gated_status(lib, up=packed(rows=64, G=64, q=0x80000)) == _lib.ERR_MISMATCH  # rotation differs
+    assert gated_status(lib, gate=packed(rows=64, K=512, q=0x40000)) == _lib.ERR_MISMATCH
+    assert lib.convrot_linear_gated(None, None, None, None, None, _lib.ACT_GELU_TANH, A16C, _lib.BF16, 64,
+                                    None) == _lib.ERR_INVALID_ARG
+
+
 def test_linear_bf16_checks(lib):
     f = lib.convrot_linear_bf16
     assert f(A16, 2688, A16B, 2688, None, 8, 16, 2690, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG

@@ -141,6 +141,15 @@ def test_dit_mlp_full(cuda):
     qw_ref, sw_ref = check_weight_pack("up", up.W, pw_up, G, "regular", None)
     y_up = cr.linear(pa, pw_up, to_dev(up.b, torch.float32))
     check_linear("up", pa, pw_up, up.b, S, qx_ref, sx_ref, qw_ref, sw_ref, y_up)
+    # The same layer with GELU fused into its epilogue (the launch the MLP
+    # benchmark times), against GELU of the oracle's Y.
+    St0 = torch.from_numpy(S).to(cuda)
+    g_fused = to_np(cr.linear_act(pa, pw_up, to_dev(up.b, torch.float32), cr.GELU_ERF).index_select(0, St0))
+    ref = O.bf16_round(R.gelu64(O.epilogue64(O.int_gemm(qx_ref, qw_ref), sx_ref, sw_ref, up.b), "gelu_erf")
+                       .astype(np.float32))
+    err = R.rel_fro(g_fused, ref)
+    say(f"  fused up+GELU: Y rel Frobenius {err:.3e}")
+    assert err <= R.Y_RTOL
     h = torch.nn.functional.gelu(y_up)
     del y_up
     St = torch.from_numpy(S).to(cuda)
@@ -210,6 +219,18 @@ def test_decode_ffn_full(cuda, M, G, kind):
         qw_ref, sw_ref = check_weight_pack(lin.name, lin.W, pw, G, kind, sg)
         outs[lin.name] = cr.linear(pa, pw, to_dev(lin.b, torch.float32))
         check_linear(lin.name, pa, pw, lin.b, S, qx_ref, sx_ref, qw_ref, sw_ref, outs[lin.name])
+    # The gated launch (both weights in one pass, the product in the
+    # epilogue) against gelu_tanh(gate) * up of the oracle.
+    pw_g, pw_u = (cr.pack_weight(dev_weight(l), G, kind, sgd) for l in (gate, up))
+    fused = to_np(cr.linear_gated(pa, pw_g, pw_u, to_dev(gate.b, torch.float32), to_dev(up.b, torch.float32),
+                                  cr.GELU_TANH))
+    qg_ref, sg_ref, _ = O.pack(gate.W, G, kind, sg)
+    qu_ref, su_ref, _ = O.pack(up.W, G, kind, sg)
+    ref = O.bf16_round((R.gelu64(O.epilogue64(O.int_gemm(qx_ref, qg_ref), sx_ref, sg_ref, gate.b), "gelu_tanh")
+                        * O.epilogue64(O.int_gemm(qx_ref, qu_ref), sx_ref, su_ref, up.b)).astype(np.float32))
+    err = R.rel_fro(fused, ref)
+    say(f"  gated gate/up: Y rel Frobenius {err:.3e}")
+    assert err <= R.Y_RTOL
     h = F.gelu(outs["gate"], approximate="tanh") * outs["up"]
     pa2 = cr.pack_act(h, G, kind, sdd)
     qh_ref, sh_ref = check_act_pack("h", to_np(h), pa2, S, G, kind, sd)

@@ -48,3 +48,13 @@ def test_scale_and_rows():
     assert abs(R.rotated_row_err(ref + np.array([[1e-6, 0], [0, 0]]), ref) - 5e-7) < 1e-15
     assert R.rotated_row_err(ref + np.array([[0, 0], [1e-9, 0]]), ref) == float("inf")
     assert abs(R.rel_fro(np.array([3.0, 4.0]) * 1.001, np.array([3.0, 4.0])) - 1e-3) < 1e-12
+
+
+def test_gelu_reference_matches_torch():
+    """The fp64 GELU reference agrees with torch's GELU in both forms."""
+    import torch
+
+    y = np.linspace(-8, 8, 4001)
+    t = torch.from_numpy(y)
+    assert np.max(np.abs(R.gelu64(y, "gelu_erf") - torch.nn.functional.gelu(t).numpy())) < 1e-12
+    assert np.max(np.abs(R.gelu64(y, "gelu_tanh") - torch.nn.functional.gelu(t, approximate="tanh").numpy())) < 1e-12

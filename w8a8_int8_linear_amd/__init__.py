@@ -7,7 +7,8 @@ library has not been built.
 """
 
 from .api import (  # noqa: F401
-    RANDOMIZED, REGULAR, Packed, linear, linear_bf16, pack_act, pack_weight, rotate,
+    GELU_ERF, GELU_TANH, RANDOMIZED, REGULAR, Packed, linear, linear_act, linear_bf16, linear_gated, pack_act,
+    pack_weight, rotate,
 )
 from .layer import ConvRotLinear, RoutingLog  # noqa: F401
 from ._lib import ConvrotError  # noqa: F401

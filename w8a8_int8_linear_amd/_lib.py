@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -20,11 +20,15 @@ OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = ra
 F32, BF16, I32 = 0, 1, 2
 # convrot_rot_kind
 ROT_REGULAR, ROT_RANDOMIZED = 0, 1
+# convrot_act
+ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
 
 EXPORTED = (
     "convrot_pack_act",
     "convrot_pack_weight",
     "convrot_linear",
+    "convrot_linear_act",
+    "convrot_linear_gated",
     "convrot_linear_bf16",
     "convrot_rotate",
     "convrot_status_string",
@@ -67,6 +71,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_pack_weight.restype = c_int
     lib.convrot_linear.argtypes = [P, P, vp, vp, c_int, c_i64, vp]
     lib.convrot_linear.restype = c_int
+    lib.convrot_linear_act.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_act.restype = c_int
+    lib.convrot_linear_gated.argtypes = [P, P, vp, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_gated.restype = c_int
     lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp]
     lib.convrot_linear_bf16.restype = c_int
     lib.convrot_rotate.argtypes = [vp, c_int, c_i64, c_i64, c_i64, Rot, vp, c_i64, vp]

@@ -3,7 +3,7 @@
 Every function marshals torch CUDA tensors (device memory) and the current
 torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
 kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
-``linear``, ``linear_bf16``, ``rotate``.
+``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``.
 """
 
 from __future__ import annotations
@@ -19,6 +19,9 @@ REGULAR = "regular"
 RANDOMIZED = "randomized"
 _KIND = {REGULAR: _lib.ROT_REGULAR, RANDOMIZED: _lib.ROT_RANDOMIZED}
 _DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.int32: _lib.I32}
+GELU_ERF = "gelu_erf"
+GELU_TANH = "gelu_tanh"
+_ACT = {GELU_ERF: _lib.ACT_GELU_ERF, GELU_TANH: _lib.ACT_GELU_TANH}
 
 
 @dataclass
@@ -120,6 +123,51 @@ def linear(act: Packed, w: Packed, bias: torch.Tensor | None = None, out_dtype: 
     lib = _lib.load()
     _lib.check(lib.convrot_linear(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
                                   out.data_ptr(), _DT[out.dtype], _ld(out), _stream(out.device)))
+    return out
+
+
+def _out_and_bias(M, N, device, out, out_dtype, bias):
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("output must be float32 or bfloat16")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 vector of length N")
+    return out
+
+
+def _act_code(act: str) -> int:
+    if act not in _ACT:
+        raise ValueError(f"activation must be one of {sorted(_ACT)}")
+    return _ACT[act]
+
+
+def linear_act(act_in: Packed, w: Packed, bias: torch.Tensor | None = None, act: str = GELU_ERF,
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = act(A * s_x * s_w + b) with the activation in the epilogue
+    (convrot_linear_act)."""
+    out = _out_and_bias(act_in.rows, w.rows, act_in.q.device, out, out_dtype, bias)
+    a, b = act_in.descriptor(), w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_act(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
+                                      _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out), _stream(out.device)))
+    return out
+
+
+def linear_gated(act_in: Packed, w_gate: Packed, w_up: Packed, b_gate: torch.Tensor | None = None,
+                 b_up: torch.Tensor | None = None, act: str = GELU_TANH, out_dtype: torch.dtype = torch.bfloat16,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = act(gate) * up for two weights sharing one packed activation, in
+    one launch (convrot_linear_gated)."""
+    out = _out_and_bias(act_in.rows, w_gate.rows, act_in.q.device, out, out_dtype, b_gate)
+    if b_up is not None and (b_up.dtype != torch.float32 or b_up.numel() != w_up.rows or not b_up.is_contiguous()):
+        raise ValueError("b_up must be a contiguous float32 vector of length N")
+    a, g, u = act_in.descriptor(), w_gate.descriptor(), w_up.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_gated(
+        ctypes.byref(a), ctypes.byref(g), b_gate.data_ptr() if b_gate is not None else None, ctypes.byref(u),
+        b_up.data_ptr() if b_up is not None else None, _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out),
+        _stream(out.device)))
     return out
 
 

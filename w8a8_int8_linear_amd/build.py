@@ -21,7 +21,7 @@ LIB_NAME = "libconvrot.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "pack_rows.hip", "gemm.hip", "gemv.hip"]
+SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -51,7 +51,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libconvrot.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
+    jobs = min(len(SOURCES), max(1, os.cpu_count() or 2))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"

@@ -136,6 +136,42 @@ convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int
   return from_hip(e, what);
 }
 
+// Checks shared by the quantised linear entry points: a packed activation
+// and a packed weight that belong together, a bias and an output of Y.
+convrot_status check_linear(const char* fn, const convrot_packed* act, const convrot_packed* w, const float* bias,
+                            const void* Y, convrot_dtype ydt, int64_t ldy, bool i32_ok) {
+  int lga = 0, lgw = 0;
+  convrot_status st = check_packed("activation", act, &lga);
+  if (st != CONVROT_OK) return st;
+  st = check_packed("weight", w, &lgw);
+  if (st != CONVROT_OK) return st;
+  if (act->K != w->K)
+    return fail(CONVROT_ERR_MISMATCH, "activation K = %lld but weight K = %lld", static_cast<long long>(act->K),
+                static_cast<long long>(w->K));
+  if (act->rot.group != w->rot.group || act->rot.kind != w->rot.kind || act->rot.signs != w->rot.signs)
+    return fail(CONVROT_ERR_MISMATCH,
+                "activation and weight were packed with different rotations (G %d/%d, kind %d/%d, signs %p/%p)",
+                act->rot.group, w->rot.group, act->rot.kind, w->rot.kind, static_cast<const void*>(act->rot.signs),
+                static_cast<const void*>(w->rot.signs));
+  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16 && !(i32_ok && ydt == CONVROT_I32))
+    return fail(CONVROT_ERR_DTYPE, "%s: output must be CONVROT_F32 or CONVROT_BF16%s", fn,
+                i32_ok ? " or CONVROT_I32" : "");
+  st = check_matrix("Y", Y, act->rows, w->rows, ldy, elt_size(ydt), false);
+  if (st != CONVROT_OK) return st;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (act->ld > kMaxLdBytes || w->ld > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of a packed operand exceeds %lld bytes",
+                static_cast<long long>(kMaxLdBytes));
+  return CONVROT_OK;
+}
+
+convrot_status check_act(convrot_act fn) {
+  if (fn != CONVROT_ACT_GELU_ERF && fn != CONVROT_ACT_GELU_TANH)
+    return fail(CONVROT_ERR_INVALID_ARG, "activation must be CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH");
+  return CONVROT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,29 +188,9 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
 
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
                               convrot_dtype ydt, int64_t ldy, void* stream) {
-  int lga = 0, lgw = 0;
-  convrot_status st = check_packed("activation", act, &lga);
+  const convrot_status st = check_linear("convrot_linear", act, w, bias, Y, ydt, ldy, true);
   if (st != CONVROT_OK) return st;
-  st = check_packed("weight", w, &lgw);
-  if (st != CONVROT_OK) return st;
-  if (act->K != w->K)
-    return fail(CONVROT_ERR_MISMATCH, "activation K = %lld but weight K = %lld", static_cast<long long>(act->K),
-                static_cast<long long>(w->K));
-  if (act->rot.group != w->rot.group || act->rot.kind != w->rot.kind || act->rot.signs != w->rot.signs)
-    return fail(CONVROT_ERR_MISMATCH,
-                "activation and weight were packed with different rotations (G %d/%d, kind %d/%d, signs %p/%p)",
-                act->rot.group, w->rot.group, act->rot.kind, w->rot.kind, static_cast<const void*>(act->rot.signs),
-                static_cast<const void*>(w->rot.signs));
-  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16 && ydt != CONVROT_I32)
-    return fail(CONVROT_ERR_DTYPE, "convrot_linear: output must be CONVROT_F32, CONVROT_BF16 or CONVROT_I32");
   const int64_t M = act->rows, N = w->rows, K = act->K;
-  st = check_matrix("Y", Y, M, N, ldy, elt_size(ydt), false);
-  if (st != CONVROT_OK) return st;
-  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)
-    return fail(CONVROT_ERR_ALIGN, "bias must be 4-byte aligned");
-  if (act->ld > kMaxLdBytes || w->ld > kMaxLdBytes)
-    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of a packed operand exceeds %lld bytes",
-                static_cast<long long>(kMaxLdBytes));
   if (M == 0 || N == 0) return ok();
   const auto out = static_cast<convrot::Elt>(ydt);
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -185,6 +201,52 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
   return from_hip(e, "convrot_linear");
+}
+
+convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packed* w, const float* bias,
+                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* stream) {
+  convrot_status st = check_act(fn);
+  if (st != CONVROT_OK) return st;
+  st = check_linear("convrot_linear_act", act, w, bias, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  const int64_t M = act->rows, N = w->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const auto a = static_cast<convrot::Act>(fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      M <= convrot::kGemvMaxRows
+          ? convrot::launch_gemv_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
+                                        out, ldy, s)
+          : convrot::launch_gemm_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
+                                        out, ldy, s);
+  return from_hip(e, "convrot_linear_act");
+}
+
+convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_packed* w_gate, const float* b_gate,
+                                    const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
+                                    convrot_dtype ydt, int64_t ldy, void* stream) {
+  convrot_status st = check_act(fn);
+  if (st != CONVROT_OK) return st;
+  st = check_linear("convrot_linear_gated", act, w_gate, b_gate, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  st = check_linear("convrot_linear_gated", act, w_up, b_up, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  if (w_gate->rows != w_up->rows)
+    return fail(CONVROT_ERR_MISMATCH, "gate has %lld output rows but up has %lld",
+                static_cast<long long>(w_gate->rows), static_cast<long long>(w_up->rows));
+  const int64_t M = act->rows, N = w_gate->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const auto a = static_cast<convrot::Act>(fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      M <= convrot::kGemvMaxRows
+          ? convrot::launch_gemv_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
+                                          w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s)
+          : convrot::launch_gemm_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
+                                          w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s);
+  return from_hip(e, "convrot_linear_gated");
 }
 
 convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw, const float* bias,

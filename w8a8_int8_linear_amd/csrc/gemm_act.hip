@@ -1,0 +1,22 @@
+// Quantised linear with an activation fused into the epilogue, on the tiled
+// int8 MFMA kernel (gemm_kernel.h).
+#include "gemm_kernel.h"
+
+namespace convrot {
+
+hipError_t launch_gemm_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
+                              const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
+                              Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const auto* a = reinterpret_cast<const uint8_t*>(A);
+  const auto* b = reinterpret_cast<const uint8_t*>(B);
+  const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_gemm<true, 0, 1, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream)
+               : launch_gemm<true, 1, 1, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream);
+  return f32 ? launch_gemm<true, 0, 2, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream)
+             : launch_gemm<true, 1, 2, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream);
+}
+
+}  // namespace convrot

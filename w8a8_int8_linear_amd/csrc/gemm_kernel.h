@@ -32,12 +32,22 @@
 //    in groups of 8 row-tiles so that concurrent workgroups on one XCD share
 //    A and B panels in that XCD's L2.
 //  * Integer accumulation is exact, so every tiling gives the same bits.
+//  * Fused epilogues (int8 mode): an activation applied to Y (GELU in its erf
+//    or tanh form), or a gated pair: two weights sharing the packed
+//    activation, Y = act(gate) * up.  For the pair, each wave's half of the
+//    B tile holds gate rows and the up rows of the same features, so a lane
+//    ends with both results of an output in registers.
+//
+// This header holds the kernel template; the translation units that
+// instantiate it (plain int8, bf16, fused epilogues) compile in parallel.
+#pragma once
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
+#include "epilogue.h"
 #include "launchers.h"
 
 namespace convrot {
@@ -239,13 +249,23 @@ constexpr int smem_bytes() {
 // OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator.
 // TN: 16-wide output tiles per wave along N; the workgroup tile is
 // 256 x (32 TN), 4 waves in a 2 x 2 grid, each wave 128 x (16 TN).
-template <bool I8, int OUT, bool KTAIL, int TN>
+// ACT: epilogue activation (see activation()).  GATED: the B tile of each
+// wave column holds 8 TN gate rows then the 8 TN up rows of the same
+// features, and the output tile is half as wide.
+template <bool I8, int OUT, bool KTAIL, int TN, int ACT = 0, bool GATED = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    const float* __restrict__ sa, const float* __restrict__ sb, const float* __restrict__ bias, int M, int N,
-    int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool staged) {
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
+    int N, int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool staged) {
+  static_assert(!GATED || (I8 && TN % 2 == 0), "the gated pair is an int8 feature");
+  static_assert((ACT == 0 && !GATED) || OUT != 2, "activations need a float output");
+  const float* __restrict__ sa = epi.sa;
+  const float* __restrict__ sb = epi.sb;
+  const float* __restrict__ bias = epi.bias;
   constexpr int kBN = 32 * TN;
   constexpr int kWN = 16 * TN;
+  constexpr int kTNo = GATED ? TN / 2 : TN;  // output 16-column tiles per wave
+  constexpr int kWNo = 16 * kTNo;            // output columns per wave
+  constexpr int kBNo = 2 * kWNo;             // output columns per tile
   constexpr int kBTileBytes = kBN * kBK;
   constexpr int kDmaA = kBM / 32;  // 1 KiB DMA instructions per slice and wave: A part
   constexpr int kDmas = kDmaA + kBN / 32;
@@ -258,13 +278,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m_blk = tm * kBM;
-  const int n_blk = tn * kBN;
+  const int n_blk = tn * kBNo;  // first output feature of the tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int wm = (wid & 1) * kWM;
-  const int wn = (wid >> 1) * kWN;
+  const int wn = (wid >> 1) * kWN;     // B-tile rows of the wave
+  const int wno = (wid >> 1) * kWNo;   // output columns of the wave
 
   // Global -> LDS without registers (global_load_lds_dwordx4): one
   // instruction fills a contiguous 1 KiB LDS block, i.e. 8 swizzled rows of
@@ -282,7 +303,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   // chunks are zeroed when read.
   const uint8_t* a_tile = A + static_cast<int64_t>(m_blk) * lda;
   const uint8_t* b_tile = B + static_cast<int64_t>(n_blk) * ldb;
+  const uint8_t* b2_tile = GATED ? epi.B2 + static_cast<int64_t>(n_blk) * epi.ldb2 : nullptr;
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  // B DMA instruction i of wave w covers B-tile rows 8 (w + 4 i) .. + 7: a
+  // block of one matrix (gate or up) only, since 8 TN is a multiple of 8.
+  // Its base (wave-uniform) and the feature of its first row:
+  auto b_block = [&](int i, bool& up, int& feat) {
+    const int row0 = 8 * (wid_u + 4 * i);
+    if constexpr (GATED) {
+      const int w = row0 % kWN;
+      up = w >= kWN / 2;
+      feat = (row0 / kWN) * (kWN / 2) + (up ? w - kWN / 2 : w);
+    } else {
+      up = false;
+      feat = row0;
+    }
+  };
   const int dma_ch = (lane & 7) ^ (lane >> 3);
   const int nk = (Kb + kBK - 1) / kBK;
   const int k_last = (nk - 1) * kBK;
@@ -290,10 +326,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
   for (int i = 0; i < kDmas; ++i) {
     const bool is_a = i < kBM / 32;
-    const int blk = wid + 4 * (is_a ? i : i - kBM / 32);
-    const int row = 8 * blk + (lane >> 3);
+    bool up = false;
+    int feat = 0;
+    if (!is_a) b_block(i - kBM / 32, up, feat);
+    const int row = is_a ? 8 * (wid + 4 * i) + (lane >> 3) : feat + (lane >> 3);
     const int rows = is_a ? M - m_blk : N - n_blk;
-    const int64_t ld = is_a ? lda : ldb;
+    const int64_t ld = is_a ? lda : (up ? epi.ldb2 : ldb);
     const uint32_t row_off = static_cast<uint32_t>(min(row, rows - 1)) * static_cast<uint32_t>(ld);
     dma_off[i] = row_off + dma_ch * 16;
     if constexpr (KTAIL) dma_off_tail[i] = row_off + (k_last + dma_ch * 16 < Kb ? k_last + dma_ch * 16 : 0);
@@ -307,7 +345,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     constexpr bool kIsA = s < kDmaA;
     constexpr int kBlk = kIsA ? s : s - kDmaA;
     uint8_t* lds = smem + (kIsA ? buf * kATileBytes : kBBase + buf * kBTileBytes) + (wid_u + 4 * kBlk) * 1024;
-    const uint8_t* base = kIsA ? a_tile : b_tile;
+    const uint8_t* base = a_tile;
+    if constexpr (!kIsA) {
+      bool up = false;
+      int feat = 0;
+      b_block(kBlk, up, feat);
+      base = up ? b2_tile : b_tile;
+    }
     if constexpr (kTail) {
       dma16(base + dma_off_tail[s], lds);
     } else {
@@ -492,35 +536,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     for (int j = 0; j < TN; ++j) touch_acc(acc[i][j]);
 
   // Epilogue.  Lane holds, for tile (i, j), output row m = m0 + 16 i + (l & 15)
-  // and the four consecutive output features n = n0 + 16 j + 4 (l >> 4) + r.
-  // Every scale and bias it needs is requested first, in one batch (16-byte
-  // loads where the columns allow), so the tile pays one memory round trip.
+  // and the four consecutive output features n = n0 + 16 j + 4 (l >> 4) + r
+  // (for the gated pair, tiles j and j + TN/2 are the gate and up results of
+  // the same features).  Every scale and bias it needs is requested first,
+  // in one batch (16-byte loads where the columns allow), so the tile pays
+  // one memory round trip.
   const int n_lane = 4 * (lane >> 4);
   float s_row[kTM];
-  f32x4 s_col[TN], b_col[TN];
+  f32x4 s_col[kTNo], b_col[kTNo], s_col2[GATED ? kTNo : 1], b_col2[GATED ? kTNo : 1];
   if constexpr (OUT != 2) {
-    if (vec_cols && n_blk + kBN <= N) {  // uniform: the whole tile is inside N
+    auto col_loads = [&](const float* s, const float* b, f32x4* sc, f32x4* bc) {
+      if (vec_cols && n_blk + kBNo <= N) {  // uniform: the whole tile is inside N
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n_blk + wn + 16 * j + n_lane;
-        s_col[j] = I8 ? *reinterpret_cast<const f32x4*>(sb + n) : f32x4{1.f, 1.f, 1.f, 1.f};
-        b_col[j] = bias ? *reinterpret_cast<const f32x4*>(bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    } else {
+        for (int j = 0; j < kTNo; ++j) {
+          const int n = n_blk + wno + 16 * j + n_lane;
+          sc[j] = I8 ? *reinterpret_cast<const f32x4*>(s + n) : f32x4{1.f, 1.f, 1.f, 1.f};
+          bc[j] = b ? *reinterpret_cast<const f32x4*>(b + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n_blk + wn + 16 * j + n_lane;
+        for (int j = 0; j < kTNo; ++j) {
+          const int n = n_blk + wno + 16 * j + n_lane;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int nn = min(n + r, N - 1);
-          s_col[j][r] = I8 ? sb[nn] : 1.f;
-          b_col[j][r] = bias ? bias[nn] : 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const int nn = min(n + r, N - 1);
+            sc[j][r] = I8 ? s[nn] : 1.f;
+            bc[j][r] = b ? b[nn] : 0.f;
+          }
         }
       }
-    }
+    };
+    col_loads(sb, bias, s_col, b_col);
+    if constexpr (GATED) col_loads(epi.sb2, epi.bias2, s_col2, b_col2);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) s_row[i] = I8 ? sa[min(m_blk + wm + 16 * i + frag_row, M - 1)] : 1.f;
   }
+  // Output value r of tile (i, j), j < kTNo.
+  auto value = [&](int i, int j, int r) -> float {
+    float y;
+    if constexpr (I8) {
+      y = fmaf(static_cast<float>(acc[i][j][r]), s_row[i] * s_col[j][r], b_col[j][r]);
+    } else {
+      y = acc[i][j][r] + b_col[j][r];
+    }
+    if constexpr (GATED) {
+      const float u = fmaf(static_cast<float>(acc[i][j + kTNo][r]), s_row[i] * s_col2[j][r], b_col2[j][r]);
+      return activation<ACT>(y) * u;
+    } else {
+      return activation<ACT>(y);
+    }
+  };
   // fp32 / bf16 outputs leave through LDS when the destination allows
   // 16-byte stores: each wave writes one 16-row block of its results into a
   // private, padded LDS area and reads it back as 16-byte chunks, so that
@@ -530,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     if (staged) {
       using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
       constexpr int kElt = sizeof(out_t);
-      constexpr int kRowBytes = 16 * TN * kElt;    // one row of the wave's block
+      constexpr int kRowBytes = 16 * kTNo * kElt;  // one row of the wave's block
       constexpr int kPitch = kRowBytes + 32;       // padding spreads rows over banks
       constexpr int kSegs = kRowBytes / 16;        // 16-byte chunks per row
       constexpr int kChunks = 16 * kSegs;          // per 16-row block
@@ -539,17 +604,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const acc_t a = acc[i][j];
+        for (int j = 0; j < kTNo; ++j) {
           float y[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if constexpr (I8) {
-              y[r] = fmaf(static_cast<float>(a[r]), s_row[i] * s_col[j][r], b_col[j][r]);
-            } else {
-              y[r] = a[r] + b_col[j][r];
-            }
-          }
+          for (int r = 0; r < 4; ++r) y[r] = value(i, j, r);
           uint8_t* dst = stage + frag_row * kPitch + (16 * j + n_lane) * kElt;
           if constexpr (OUT == 0) {
             *reinterpret_cast<f32x4*>(dst) = f32x4{y[0], y[1], y[2], y[3]};
@@ -566,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
             const int row = c / kSegs, seg = c % kSegs;
             const i32x4 v = *reinterpret_cast<const i32x4*>(stage + row * kPitch + seg * 16);
             const int m = m_blk + wm + 16 * i + row;
-            const int n = n_blk + wn + seg * (16 / kElt);
+            const int n = n_blk + wno + seg * (16 / kElt);
             if (m < M) {
               out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
               if (n + 16 / kElt <= N) {
@@ -583,15 +641,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n_blk + wn + 16 * j + n_lane;
+  for (int j = 0; j < kTNo; ++j) {
+    const int n = n_blk + wno + 16 * j + n_lane;
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int m = m_blk + wm + 16 * i + frag_row;
       if (m >= M) continue;
-      const acc_t a = acc[i][j];
       if constexpr (OUT == 2) {
+        const acc_t a = acc[i][j];
         int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
         if (n + 3 < N && vec_ok(out)) {
           *reinterpret_cast<i32x4*>(out) = a;
@@ -601,13 +659,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       } else {
         float y[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if constexpr (I8) {
-            y[r] = fmaf(static_cast<float>(a[r]), s_row[i] * s_col[j][r], b_col[j][r]);
-          } else {
-            y[r] = a[r] + b_col[j][r];
-          }
-        }
+        for (int r = 0; r < 4; ++r) y[r] = value(i, j, r);
         if constexpr (OUT == 0) {
           float* out = static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n;
           if (n + 3 < N && vec_ok(out)) {
@@ -631,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   }
 }
 
-int num_cus() {
+inline int num_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -647,8 +699,9 @@ int num_cus() {
 
 // Output-tile width: the candidate minimising (rounds of one tile per CU) x
 // (work per tile), i.e. the fewest idle CU-slots in the last round; ties go
-// to the wider tile (less LDS traffic per MFMA).
-int choose_tn(int64_t M, int64_t N) {
+// to the wider tile (less LDS traffic per MFMA).  `cols` counts B-tile
+// columns (2 N for a gated pair).
+inline int choose_tn(int64_t M, int64_t cols) {
   // CONVROT_GEMM_TN=4|6|8 pins the width (tuning and checking only).
   static const int forced = [] {
     const char* e = std::getenv("CONVROT_GEMM_TN");
@@ -662,7 +715,7 @@ int choose_tn(int64_t M, int64_t N) {
   int64_t best_cost = -1;
   for (int tn : cands) {
     const int64_t bn = 32 * tn;
-    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((cols + bn - 1) / bn);
     const int64_t cost = ((tiles + cus - 1) / cus) * bn;
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -672,11 +725,10 @@ int choose_tn(int64_t M, int64_t N) {
   return best;
 }
 
-template <bool I8, int OUT, bool KTAIL, int TN>
-hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
-                        const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C,
-                        int64_t ldc, hipStream_t stream) {
-  auto kern = gemm_nt_kernel<I8, OUT, KTAIL, TN>;
+template <bool I8, int OUT, bool KTAIL, int TN, int ACT, bool GATED>
+hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi, int64_t M,
+                        int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
+  auto kern = gemm_nt_kernel<I8, OUT, KTAIL, TN, ACT, GATED>;
   constexpr int kSmem = smem_bytes<TN>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -685,61 +737,38 @@ hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  constexpr int kBNo = GATED ? 16 * TN : 32 * TN;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-  const int tiles_n = static_cast<int>((N + 32 * TN - 1) / (32 * TN));
+  const int tiles_n = static_cast<int>((N + kBNo - 1) / kBNo);
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
   // 16-byte scale/bias loads need 16-byte aligned vectors.
-  const bool vec_cols = (reinterpret_cast<uintptr_t>(sb) & 15) == 0 && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec_cols = al16(epi.sb) && al16(epi.bias) && (!GATED || (al16(epi.sb2) && al16(epi.bias2)));
   // Staged stores need 16-byte aligned output rows.
   const int out_elt = OUT == 1 ? 2 : 4;
-  const bool staged = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc * out_elt) % 16 == 0;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kSmem, stream, A, lda, B, ldb, sa, sb, bias, static_cast<int>(M),
+  const bool staged = al16(C) && (ldc * out_elt) % 16 == 0;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kSmem, stream, A, lda, B, ldb, epi, static_cast<int>(M),
                      static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m, tiles_n, vec_cols, staged);
   return hipGetLastError();
 }
 
-template <bool I8, int OUT, bool KTAIL>
-hipError_t launch_tn(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
-                     const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc,
-                     hipStream_t stream) {
-  switch (choose_tn(M, N)) {
-    case 6: return launch_typed<I8, OUT, KTAIL, 6>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
-    case 4: return launch_typed<I8, OUT, KTAIL, 4>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
-    default: return launch_typed<I8, OUT, KTAIL, 8>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+template <bool I8, int OUT, int ACT, bool GATED>
+hipError_t launch_gemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi, int64_t M,
+                       int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
+  const int tn = choose_tn(M, GATED ? 2 * N : N);
+  const bool tail = Kb % kBK != 0;
+#define CONVROT_GEMM_CASE(TN_)                                                                             \
+  case TN_:                                                                                                \
+    return tail ? launch_typed<I8, OUT, true, TN_, ACT, GATED>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream) \
+                : launch_typed<I8, OUT, false, TN_, ACT, GATED>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
+  switch (tn) {
+    CONVROT_GEMM_CASE(6)
+    CONVROT_GEMM_CASE(4)
+    default:
+      CONVROT_GEMM_CASE(8)
   }
-}
-
-template <bool I8, int OUT>
-hipError_t launch_ktail(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
-                        const float* sb, const float* bias, int64_t M, int64_t N, int64_t Kb, void* C,
-                        int64_t ldc, hipStream_t stream) {
-  if (Kb % kBK == 0) return launch_tn<I8, OUT, false>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
-  return launch_tn<I8, OUT, true>(A, lda, B, ldb, sa, sb, bias, M, N, Kb, C, ldc, stream);
+#undef CONVROT_GEMM_CASE
 }
 
 }  // namespace
-
-hipError_t launch_gemm_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
-                          const float* sb, const float* bias, int64_t M, int64_t N, int64_t K, void* C, Elt out,
-                          int64_t ldc, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const uint8_t* a = reinterpret_cast<const uint8_t*>(A);
-  const uint8_t* b = reinterpret_cast<const uint8_t*>(B);
-  switch (out) {
-    case Elt::F32: return launch_ktail<true, 0>(a, lda, b, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    case Elt::BF16: return launch_ktail<true, 1>(a, lda, b, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    default: return launch_ktail<true, 2>(a, lda, b, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-  }
-}
-
-hipError_t launch_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,
-                            int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const uint8_t* a = static_cast<const uint8_t*>(A);
-  const uint8_t* b = static_cast<const uint8_t*>(B);
-  if (out == Elt::F32)
-    return launch_ktail<false, 0>(a, 2 * lda, b, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
-  return launch_ktail<false, 1>(a, 2 * lda, b, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
-}
-
 }  // namespace convrot

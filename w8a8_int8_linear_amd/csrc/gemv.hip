@@ -21,11 +21,16 @@
 //    lane) before its first MFMA, so a whole launch's weight stream is
 //    requested within the first microsecond;
 //  * the W partial accumulators are summed through LDS (exact in int8 mode)
-//    and wave 0 applies the epilogue, writing 4 consecutive outputs per lane.
+//    and wave 0 applies the epilogue, writing 4 consecutive outputs per lane;
+//  * fused epilogues (int8 mode): an activation of Y (GELU, erf or tanh
+//    form), or a gated pair Y = act(gate) * up where the workgroup streams
+//    the same 16 features of both weights against one set of activation
+//    loads.
 // The byte-to-k assignment of a lane is the same for both operands, so each
 // MFMA pairs matching k.
 #include <hip/hip_runtime.h>
 
+#include "epilogue.h"
 #include "launchers.h"
 
 namespace convrot {
@@ -66,13 +71,15 @@ __device__ __forceinline__ bool vec_ok(const T* p) {
 
 // A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes]; kbytes =
 // K * element size (a multiple of 16); per = steps per wave.
-template <bool I8, int OUT, int WAVES>
+template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    const float* __restrict__ sa, const float* __restrict__ sb, const float* __restrict__ bias, int M, int N,
-    int kbytes, int per, void* __restrict__ C, int64_t ldc) {
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
+    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc) {
+  static_assert(!GATED || I8, "the gated pair is an int8 feature");
   using Acc = typename Mma<I8>::Acc;
-  __shared__ Acc partial[WAVES > 1 ? WAVES - 1 : 1][64];
+  constexpr int kSets = GATED ? 2 : 1;  // weight row sets streamed (gate, up)
+  __shared__ Acc partial[kSets][WAVES > 1 ? WAVES - 1 : 1][64];
+  const float* __restrict__ sa = epi.sa;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -80,36 +87,50 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int row = lane & 15;
   const int ch = lane >> 4;
 
-  const uint8_t* wrow = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * 16;
+  const uint8_t* wrow[kSets];
+  wrow[0] = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * 16;
+  if constexpr (GATED) wrow[kSets - 1] = epi.B2 + static_cast<int64_t>(min(n0 + row, N - 1)) * epi.ldb2 + ch * 16;
   const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
 
   const int nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
   const int s_begin = wid * per;
   const int s_end = min(nsteps, s_begin + per);
 
-  Acc acc = {0, 0, 0, 0};
+  Acc acc[kSets];
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) acc[t] = Acc{0, 0, 0, 0};
   for (int s0 = s_begin; s0 < s_end; s0 += kSteps) {
-    i32x4 w[kSteps], x[kSteps];
+    i32x4 w[kSets][kSteps], x[kSteps];
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
-      w[u] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < kSets; ++t) w[t][u] = i32x4{0, 0, 0, 0};
       x[u] = i32x4{0, 0, 0, 0};
       const int byte = (s0 + u) * kStepBytes;
       if (s0 + u < s_end && byte + ch * 16 < kbytes) {
-        w[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + byte));
+#pragma unroll
+        for (int t = 0; t < kSets; ++t)
+          w[t][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t] + byte));
         x[u] = *reinterpret_cast<const i32x4*>(xrow + byte);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) acc = Mma<I8>::run(w[u], x[u], acc);
+    for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+      for (int t = 0; t < kSets; ++t) acc[t] = Mma<I8>::run(w[t][u], x[u], acc[t]);
   }
 
   if (WAVES > 1) {
-    if (wid > 0) partial[wid - 1][lane] = acc;
+    if (wid > 0) {
+#pragma unroll
+      for (int t = 0; t < kSets; ++t) partial[t][wid - 1][lane] = acc[t];
+    }
     __syncthreads();
     if (wid != 0) return;
 #pragma unroll
-    for (int w = 0; w < WAVES - 1; ++w) acc += partial[w][lane];
+    for (int w = 0; w < WAVES - 1; ++w)
+#pragma unroll
+      for (int t = 0; t < kSets; ++t) acc[t] += partial[t][w][lane];
   }
 
   // Lane holds output row m = lane & 15 and features n0 + 4 (lane >> 4) + r.
@@ -119,9 +140,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   if constexpr (OUT == 2) {
     int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
     if (n + 3 < N && vec_ok(out)) {
-      *reinterpret_cast<i32x4*>(out) = acc;
+      *reinterpret_cast<i32x4*>(out) = acc[0];
     } else {
-      for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[r];
+      for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[0][r];
     }
   } else {
     const float s_row = I8 ? sa[m] : 1.f;
@@ -129,8 +150,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int nn = min(n + r, N - 1);
-      const float b = bias ? bias[nn] : 0.f;
-      y[r] = I8 ? fmaf(static_cast<float>(acc[r]), s_row * sb[nn], b) : static_cast<float>(acc[r]) + b;
+      const float b = epi.bias ? epi.bias[nn] : 0.f;
+      y[r] = I8 ? fmaf(static_cast<float>(acc[0][r]), s_row * epi.sb[nn], b) : static_cast<float>(acc[0][r]) + b;
+      if constexpr (GATED) {
+        const float b2 = epi.bias2 ? epi.bias2[nn] : 0.f;
+        const float u = fmaf(static_cast<float>(acc[kSets - 1][r]), s_row * epi.sb2[nn], b2);
+        y[r] = activation<ACT>(y[r]) * u;
+      } else {
+        y[r] = activation<ACT>(y[r]);
+      }
     }
     if constexpr (OUT == 0) {
       float* out = static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n;
@@ -151,10 +179,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   }
 }
 
-template <bool I8, int OUT>
-hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const float* sa, const float* sb,
-                      const float* bias, int64_t M, int64_t N, int64_t kbytes, void* C, int64_t ldc,
-                      hipStream_t stream) {
+template <bool I8, int OUT, int ACT = 0, bool GATED = false>
+hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
+                      int64_t N, int64_t kbytes, void* C, int64_t ldc, hipStream_t stream) {
   const int64_t nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
   int waves = 16;
   for (int w : {4, 8}) {
@@ -170,16 +197,16 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
   switch (waves) {
     case 4:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4>), grid, dim3(256), 0, stream, a, lda, b, ldb, sa, sb, bias, m, n,
-                         kb, per, C, ldc);
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED>), grid, dim3(256), 0, stream, a, lda, b, ldb, epi, m,
+                         n, kb, per, C, ldc);
       break;
     case 8:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8>), grid, dim3(512), 0, stream, a, lda, b, ldb, sa, sb, bias, m, n,
-                         kb, per, C, ldc);
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED>), grid, dim3(512), 0, stream, a, lda, b, ldb, epi, m,
+                         n, kb, per, C, ldc);
       break;
     default:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16>), grid, dim3(1024), 0, stream, a, lda, b, ldb, sa, sb, bias, m,
-                         n, kb, per, C, ldc);
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED>), grid, dim3(1024), 0, stream, a, lda, b, ldb, epi,
+                         m, n, kb, per, C, ldc);
       break;
   }
   return hipGetLastError();
@@ -191,20 +218,48 @@ hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t
                           const float* sb, const float* bias, int64_t M, int64_t N, int64_t K, void* C, Elt out,
                           int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   switch (out) {
-    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
-    default: return launch_out<true, 2>(A, lda, B, ldb, sa, sb, bias, M, N, K, C, ldc, stream);
+    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
   }
+}
+
+hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
+                              const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
+                              Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
+               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
+             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+}
+
+hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg, const float* sbg,
+                                const float* biasg, const int8_t* Bu, int64_t ldbu, const float* sbu,
+                                const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
+                                void* C, Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{sa, sbg, biasg, reinterpret_cast<const uint8_t*>(Bu), ldbu, sbu, biasu};
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
+               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
+  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
+             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
 }
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,
                             int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{nullptr, nullptr, bias, nullptr, 0, nullptr, nullptr};
   // Row strides and K in bytes.
-  if (out == Elt::F32)
-    return launch_out<false, 0>(A, 2 * lda, B, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
-  return launch_out<false, 1>(A, 2 * lda, B, 2 * ldb, nullptr, nullptr, bias, M, N, 2 * K, C, ldc, stream);
+  if (out == Elt::F32) return launch_out<false, 0>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, stream);
+  return launch_out<false, 1>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, stream);
 }
 
 }  // namespace convrot

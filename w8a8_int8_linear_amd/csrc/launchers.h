@@ -9,6 +9,8 @@ namespace convrot {
 
 enum class Elt : int { F32 = 0, BF16 = 1, I32 = 2 };
 enum class RotKind : int { Regular = 0, Randomized = 1 };
+// Activation of a fused epilogue (values of convrot_act).
+enum class Act : int { None = 0, GeluErf = 1, GeluTanh = 2 };
 
 // Fused group rotation + whole-row absmax + int8 quantisation of `rows` rows
 // of X.  When `q` is null the kernel writes the fp32 rotated rows to `xrot`
@@ -34,6 +36,22 @@ hipError_t launch_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t l
                             const float* bias, int64_t M, int64_t N, int64_t K,
                             void* C, Elt out, int64_t ldc, hipStream_t stream);
 
+// int8 mode with a fused activation, Y = act(A sa sb + bias); `act` is
+// GeluErf or GeluTanh and `out` F32 or BF16.
+hipError_t launch_gemm_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                              const float* sa, const float* sb, const float* bias, Act act,
+                              int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                              hipStream_t stream);
+
+// Gated pair sharing the packed activation A:
+//   Y = act(A Bg^T sa sbg + biasg) * (A Bu^T sa sbu + biasu)
+// `act` is GeluErf or GeluTanh and `out` F32 or BF16.
+hipError_t launch_gemm_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg,
+                                const float* sbg, const float* biasg, const int8_t* Bu, int64_t ldbu,
+                                const float* sbu, const float* biasu, const float* sa, Act act,
+                                int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                                hipStream_t stream);
+
 // Weight-streaming kernels for small M (M <= kGemvMaxRows).  The int8 one
 // gives the same result bits as launch_gemm_i8; the bf16 one computes the
 // same as launch_gemm_bf16 up to fp32 summation order.
@@ -46,5 +64,14 @@ hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
                             const float* bias, int64_t M, int64_t N, int64_t K,
                             void* C, Elt out, int64_t ldc, hipStream_t stream);
+hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                              const float* sa, const float* sb, const float* bias, Act act,
+                              int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                              hipStream_t stream);
+hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg,
+                                const float* sbg, const float* biasg, const int8_t* Bu, int64_t ldbu,
+                                const float* sbu, const float* biasu, const float* sa, Act act,
+                                int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                                hipStream_t stream);
 
 }  // namespace convrot
