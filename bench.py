@@ -5,7 +5,10 @@ rows once (rotate + absmax + int8), then run every linear that consumes the
 packed activation; where a workload chains layers (the MLP pair, the gated
 FFN) the intermediate activation is packed again.  Weights are packed once
 before timing (offline, as in a checkpoint).  Layers whose input width is not
-a multiple of G run on the routed bf16 linear.
+a multiple of G run on the routed bf16 linear.  The activation between chained
+layers runs in the producing linear's epilogue (GELU after the MLP up
+projection; gate and up as one gated launch); ``--unfused`` runs it as a
+separate torch op after plain linears instead.
 
 Workloads (``--workload``):
   dit_attn_proj  (default) X bf16 [4096, 3072], 8 outlier channels; fused QKV
@@ -110,29 +113,40 @@ def make_workload(name: str):
 class Op:
     """One timed launch of the step and what it moves or computes."""
 
-    def __init__(self, name, fn, kind, M=0, N=0, K=0, in_b=0, out_b=0):
+    def __init__(self, name, fn, kind, M=0, N=0, K=0, in_b=0, out_b=0, epilogue=""):
         self.name, self.fn, self.kind = name, fn, kind
         self.M, self.N, self.K, self.in_b, self.out_b = M, N, K, in_b, out_b
+        # "" plain, "act" activation in the epilogue, "gated" act(gate) * up:
+        # N output columns from 2N weight rows
+        self.epilogue = epilogue
 
     @property
     def kernel(self):
         if self.kind == "pack":
             return "pack_rows"
         if self.kind == "int8":
-            return "gemv_i8" if self.M <= SMALL_M else "gemm_i8"
+            if self.M <= SMALL_M:
+                return "gemv_i8"
+            return "gemm_i8" + (f"_{self.epilogue}" if self.epilogue else "")
         if self.kind == "bf16":
             return "gemm_bf16"
         return "torch"
 
+    @property
+    def rows(self):
+        """weight rows the launch contracts against"""
+        return 2 * self.N if self.epilogue == "gated" else self.N
+
     def ops(self):
-        return 2.0 * self.M * self.N * self.K if self.kind in ("int8", "bf16") else 0.0
+        return 2.0 * self.M * self.rows * self.K if self.kind in ("int8", "bf16") else 0.0
 
     def bytes(self):
         M, N, K = self.M, self.N, self.K
         if self.kind == "pack":
             return M * K * (self.in_b + 1) + 4 * M
         if self.kind == "int8":
-            return M * K + 4 * M + N * K + 8 * N + M * N * self.out_b
+            R = self.rows
+            return M * K + 4 * M + R * K + 8 * R + M * N * self.out_b
         if self.kind == "bf16":
             return 2 * M * K + 2 * N * K + 4 * N + M * N * self.out_b
         return 0
@@ -141,8 +155,8 @@ class Op:
 class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
-    def __init__(self, wl, dev, torch, cr, template=None):
-        self.torch, self.cr, self.wl = torch, cr, wl
+    def __init__(self, wl, dev, torch, cr, template=None, fused=True):
+        self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
         bf16, f32 = torch.bfloat16, torch.float32
         self.xdt = bf16 if wl.xdtype == "bf16" else f32
         self.odt = bf16 if wl.out_dtype == "bf16" else f32
@@ -235,11 +249,18 @@ class StepSet:
             for n in names:
                 ops.append(self._linear_op(n, src0, self._out(n, M, dev)))
         elif wl.cfg == 3:
-            y_up = self._out("up", M, dev)
-            ops.append(self._linear_op("up", src0, y_up))
-            h = torch.empty_like(y_up)
-            self.bufs.append(h)
-            ops.append(Op("gelu_torch", lambda: gelu(y_up, out=h), "torch"))
+            if self.fused:
+                # GELU in the up projection's epilogue
+                h = self._out("up", M, dev)
+                w, b = self.W["up"], self.b["up"]
+                ops.append(Op("linear_up_gelu", lambda: self.cr.linear_act(src0, w, b, self.cr.GELU_ERF, out=h),
+                              "int8", M=M, N=w.rows, K=w.K, out_b=h.element_size(), epilogue="act"))
+            else:
+                y_up = self._out("up", M, dev)
+                ops.append(self._linear_op("up", src0, y_up))
+                h = torch.empty_like(y_up)
+                self.bufs.append(h)
+                ops.append(Op("gelu_torch", lambda: gelu(y_up, out=h), "torch"))
             pa2 = self._packed(M, h.shape[1], dev)
             ops.append(self._pack_op("pack_act2", h, pa2))
             ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
@@ -248,14 +269,23 @@ class StepSet:
             r = wl.extra["routed"].name
             ops.append(self._linear_op(r, self.X2, self._out(r, M, dev)))
         elif wl.cfg == 5:
-            g = self._out("gate", M, dev)
-            u = self._out("up", M, dev)
-            ops.append(self._linear_op("gate", src0, g))
-            ops.append(self._linear_op("up", src0, u))
-            t, h = torch.empty_like(u), torch.empty_like(u)
-            self.bufs += [t, h]
-            ops.append(Op("gelu_tanh_mul_torch", lambda: torch.mul(gelu(g, approximate="tanh", out=t), u, out=h),
-                          "torch"))
+            wg, wu = self.W["gate"], self.W["up"]
+            if self.fused and isinstance(wg, self.cr.Packed) and isinstance(wu, self.cr.Packed):
+                # gate and up in one launch, gelu_tanh(gate) * up in its epilogue
+                h = self._out("gate", M, dev)
+                bg, bu = self.b["gate"], self.b["up"]
+                ops.append(Op("linear_gate_up", lambda: self.cr.linear_gated(src0, wg, wu, bg, bu, self.cr.GELU_TANH,
+                                                                               out=h),
+                              "int8", M=M, N=wg.rows, K=wg.K, out_b=h.element_size(), epilogue="gated"))
+            else:
+                g = self._out("gate", M, dev)
+                u = self._out("up", M, dev)
+                ops.append(self._linear_op("gate", src0, g))
+                ops.append(self._linear_op("up", src0, u))
+                t, h = torch.empty_like(u), torch.empty_like(u)
+                self.bufs += [t, h]
+                ops.append(Op("gelu_tanh_mul_torch",
+                              lambda: torch.mul(gelu(g, approximate="tanh", out=t), u, out=h), "torch"))
             if isinstance(self.W["down"], self.cr.Packed):
                 pa2 = self._packed(M, h.shape[1], dev)
                 ops.append(self._pack_op("pack_act2", h, pa2))
@@ -373,6 +403,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_attn_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the activation between chained layers as a separate torch op instead of in the "
+                         "linear's epilogue")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -393,9 +426,10 @@ def main():
     log(f"[bench] workload {wl.name}: X {wl.X.shape} {wl.xdtype}, linears "
         f"{[(l.name, l.W.shape) for l in wl.linears]}, G={wl.G} {wl.kind} (inputs {time.time() - t0:.1f}s)")
 
-    sets = [StepSet(wl, dev, torch, cr)]
+    fused = not args.unfused
+    sets = [StepSet(wl, dev, torch, cr, fused=fused)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
-        sets.append(StepSet(wl, dev, torch, cr, template=sets[0]))
+        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -435,7 +469,7 @@ def main():
         if op.ops():
             k["TOPS"] = op.ops() / t / 1e12
             k["frac_mfma"] = k["TOPS"] / (PEAK_I8_TOPS if op.kind == "int8" else PEAK_BF16_TFLOPS)
-            k.update(M=op.M, N=op.N, K=op.K)
+            k.update(M=op.M, N=op.rows, K=op.K)
         kernels[op.name] = k
     for k, v in kernels.items():
         log(f"[bench] {k}: " + ", ".join(f"{a}={b:.4g}" if isinstance(b, float) else f"{a}={b}" for a, b in v.items()))
@@ -469,6 +503,7 @@ def main():
         "data": "synthetic (seeded; shapes and outlier structure of the workload, no checkpoint)",
         "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
+                   "epilogue": "fused" if fused else "separate",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "buffer_sets": len(sets)},
         "roofline": roof,

@@ -369,7 +369,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
         dma_block(std::integral_constant<int, s>{}, s < kDmaA ? abuf : bbuf, k0, tail_c);
       });
     };
-    if (KTAIL && k0 == k_last) all(std::true_type{}); else all(std::false_type{});
+    if constexpr (KTAIL) {
+      if (k0 == k_last) all(std::true_type{}); else all(std::false_type{});
+    } else {
+      all(std::false_type{});
+    }
   };
 
   acc_t acc[kTM][TN];
