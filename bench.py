@@ -28,6 +28,13 @@ Inputs live in HBM before timing starts.  To keep the 256 MB Infinity Cache
 from serving them, each step uses the next of several independent buffer sets
 (activations, packed weights, outputs) whose total exceeds 512 MB.
 
+The timed region is one replay of a HIP graph that holds exactly K steps (the
+launches a serving loop would capture).  Per-launch durations come from one
+graph per launch of the step, holding that launch repeated over the buffer
+sets, timed with events on its stream and divided by the repeat count.
+``--eager`` launches every kernel from Python instead, with an event between
+consecutive launches (at decode sizes that measures the host's launch cost).
+
 Prints one JSON line on stdout; per-kernel details go to stderr.
 """
 
@@ -403,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_attn_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python in the timed region instead of replaying a captured graph")
     ap.add_argument("--unfused", action="store_true",
                     help="run the activation between chained layers as a separate torch op instead of in the "
                          "linear's epilogue")
@@ -447,16 +456,58 @@ def main():
     torch.cuda.synchronize()
 
     n_ev = len(ops) + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        sets[i % len(sets)].step(evs[i])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
+    if args.eager:
+        # Every launch from Python, an event between consecutive launches.
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            sets[i % len(sets)].step(evs[i])
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+    else:
+        # The K steps (cycling through the buffer sets) are captured once as a
+        # HIP graph and replayed: the kernels run back to back, without the
+        # host's per-launch cost between them.  The graph is replayed once,
+        # untimed, before the timed replay.
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for i in range(args.steps):
+                sets[i % len(sets)].step()
+        g_step.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        g_step.replay()
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+        # Per-launch durations (events cannot be recorded inside a captured
+        # graph here): launch j of the step, repeated over the buffer sets in
+        # one graph, between two events on the stream it runs on.
+        reps = max(16, len(sets))
+        per_launch = []
+        for j in range(len(ops)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(reps):
+                    sets[r % len(sets)].ops[j].fn()
+            g.replay()
+            samples = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                samples.append(e0.elapsed_time(e1) / reps)
+            per_launch.append(samples)
+            del g
     ms_step = t_total * 1e3 / args.steps
 
-    dur = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(n_ev - 1)] for i in range(args.steps)])
+    if args.eager:
+        dur = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(n_ev - 1)]
+                        for i in range(args.steps)])
+    else:
+        dur = np.array(per_launch).T  # [sample, launch]
     kernels = {}
     for j, op in enumerate(ops):
         us = dur[:, j] * 1e3
@@ -503,7 +554,7 @@ def main():
         "data": "synthetic (seeded; shapes and outlier structure of the workload, no checkpoint)",
         "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
-                   "epilogue": "fused" if fused else "separate",
+                   "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "buffer_sets": len(sets)},
         "roofline": roof,

@@ -41,8 +41,18 @@
  *   output of the pack and rotate entry points must have a 16-byte aligned
  *   base and a leading dimension whose size in bytes is a multiple of 16.
  *   The Y output of the linear entry points only needs element alignment.
- * - The caller owns every buffer.  The library allocates no device memory
- *   and keeps no mutable global state beyond a thread-local error string.
+ * - The caller owns every input and output buffer.  The only device memory
+ *   the library allocates is one 8 MiB workspace per device, on the first
+ *   linear call with M <= 16 that has fewer 16-feature output tiles than
+ *   the GPU has CUs (it then splits K across workgroups, stores their
+ *   partial sums there and adds them in a second launch).  That allocation
+ *   is skipped while `stream` is being captured into a graph, and such a
+ *   call then uses the unsplit kernel; an allocation failure likewise falls
+ *   back, never errors.  The workspace is held until the process ends and
+ *   needs no clearing, so captured graphs may replay calls that use it.  Two
+ *   such small-M calls must not run at the same time on one device (on
+ *   different streams); calls ordered on one stream, or by events, may.
+ *   Beyond that the library keeps a thread-local error string.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the
  *   default stream).  Inputs must stay alive, and outputs untouched, until
  *   the stream has passed the call.  Outputs must not alias inputs.
@@ -152,8 +162,9 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
  *   Y     [M, ldy] of `ydt`: CONVROT_F32, CONVROT_BF16 (round to nearest
  *         even) or CONVROT_I32 (the raw accumulator A; scales and bias are
  *         then not applied)
- * Small M uses a weight-streaming kernel, larger M a tiled matrix-core
- * kernel; both produce bit-identical A. */
+ * Small M (<= 16) uses a weight-streaming kernel, larger M a tiled
+ * matrix-core kernel; both produce bit-identical A (the small-M kernel's
+ * split over K adds exact int32 partial sums). */
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w,
                               const float* bias, void* Y, convrot_dtype ydt, int64_t ldy,
                               void* stream);

@@ -483,8 +483,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
         constexpr int o = decltype(s_c)::value;
         if constexpr (o < kDmaA) {
           if (dma) {
-            if (KTAIL && k0 + 2 * kBK == k_last) {
-              dma_block(s_c, a_after, k0 + 2 * kBK, std::true_type{});
+            if constexpr (KTAIL) {
+              if (k0 + 2 * kBK == k_last) {
+                dma_block(s_c, a_after, k0 + 2 * kBK, std::true_type{});
+              } else {
+                dma_block(s_c, a_after, k0 + 2 * kBK, std::false_type{});
+              }
             } else {
               dma_block(s_c, a_after, k0 + 2 * kBK, std::false_type{});
             }
@@ -509,10 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
         constexpr int o = decltype(s_c)::value;
         if constexpr (o < kDmas - kDmaA) {
           if (dma) {
-            if (KTAIL && k0 + 2 * kBK == k_last) {
-              dma_block(std::integral_constant<int, kDmaA + o>{}, b_cur, k0 + 2 * kBK, std::true_type{});
+            using blk = std::integral_constant<int, kDmaA + o>;
+            if constexpr (KTAIL) {
+              if (k0 + 2 * kBK == k_last) {
+                dma_block(blk{}, b_cur, k0 + 2 * kBK, std::true_type{});
+              } else {
+                dma_block(blk{}, b_cur, k0 + 2 * kBK, std::false_type{});
+              }
             } else {
-              dma_block(std::integral_constant<int, kDmaA + o>{}, b_cur, k0 + 2 * kBK, std::false_type{});
+              dma_block(blk{}, b_cur, k0 + 2 * kBK, std::false_type{});
             }
           }
         } else {

@@ -25,10 +25,22 @@
 //  * fused epilogues (int8 mode): an activation of Y (GELU, erf or tanh
 //    form), or a gated pair Y = act(gate) * up where the workgroup streams
 //    the same 16 features of both weights against one set of activation
-//    loads.
+//    loads;
+//  * when there are fewer 16-feature tiles than CUs (a down projection has
+//    N = 1152, i.e. 72 tiles), K is also split across workgroups: each
+//    (tile, K range) workgroup stores its partial sums (exact int32 in int8
+//    mode) in a per-device workspace, and a second launch of one wave per
+//    tile adds them in K order and applies the epilogue.  The launch
+//    boundary makes the partials visible; inside one launch that would take
+//    device-scope fences, which on this multi-XCD GPU write back and
+//    invalidate a whole L2 each.  Same result bits as the unsplit kernel in
+//    int8 mode.
 // The byte-to-k assignment of a lane is the same for both operands, so each
 // MFMA pairs matching k.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
 
 #include "epilogue.h"
 #include "launchers.h"
@@ -69,17 +81,75 @@ __device__ __forceinline__ bool vec_ok(const T* p) {
   return (reinterpret_cast<uintptr_t>(p) & (4 * sizeof(T) - 1)) == 0;
 }
 
+// Split-K state of one launch: partials [tile][split][set][64 lanes] x 16
+// bytes, `steps` K steps per split.
+struct SplitArgs {
+  i32x4* part;
+  int splits;
+  int steps;
+};
+
+// Epilogue of one 16-feature tile: lane holds output row m = lane & 15 and
+// features n0 + 4 (lane >> 4) + r of the accumulators acc[set].
+template <bool I8, int OUT, int ACT, bool GATED, typename Acc>
+__device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, const EpiArgs& epi, int M, int N,
+                                              void* __restrict__ C, int64_t ldc) {
+  constexpr int kSets = GATED ? 2 : 1;
+  const int m = lane & 15;
+  const int n = n0 + 4 * (lane >> 4);
+  if (m >= M || n >= N) return;
+  if constexpr (OUT == 2) {
+    int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+    if (n + 3 < N && vec_ok(out)) {
+      *reinterpret_cast<i32x4*>(out) = __builtin_bit_cast(i32x4, acc[0]);
+    } else {
+      for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[0][r];
+    }
+  } else {
+    const float s_row = I8 ? epi.sa[m] : 1.f;
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nn = min(n + r, N - 1);
+      const float b = epi.bias ? epi.bias[nn] : 0.f;
+      y[r] = I8 ? fmaf(static_cast<float>(acc[0][r]), s_row * epi.sb[nn], b) : static_cast<float>(acc[0][r]) + b;
+      if constexpr (GATED) {
+        const float b2 = epi.bias2 ? epi.bias2[nn] : 0.f;
+        const float u = fmaf(static_cast<float>(acc[kSets - 1][r]), s_row * epi.sb2[nn], b2);
+        y[r] = activation<ACT>(y[r]) * u;
+      } else {
+        y[r] = activation<ACT>(y[r]);
+      }
+    }
+    if constexpr (OUT == 0) {
+      float* out = static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n;
+      if (n + 3 < N && vec_ok(out)) {
+        *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+      } else {
+        for (int r = 0; r < 4 && n + r < N; ++r) out[r] = y[r];
+      }
+    } else {
+      __bf16* out = static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n;
+      if (n + 3 < N && vec_ok(out)) {
+        *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
+                                                 static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+      } else {
+        for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<__bf16>(y[r]);
+      }
+    }
+  }
+}
+
 // A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes]; kbytes =
 // K * element size (a multiple of 16); per = steps per wave.
-template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false>
+template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc) {
+    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   using Acc = typename Mma<I8>::Acc;
   constexpr int kSets = GATED ? 2 : 1;  // weight row sets streamed (gate, up)
   __shared__ Acc partial[kSets][WAVES > 1 ? WAVES - 1 : 1][64];
-  const float* __restrict__ sa = epi.sa;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -93,8 +163,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
 
   const int nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
-  const int s_begin = wid * per;
-  const int s_end = min(nsteps, s_begin + per);
+  // K steps [s_lo, s_hi) of this workgroup, `per` of them per wave.
+  const int s_lo = SPLIT ? static_cast<int>(blockIdx.y) * sp.steps : 0;
+  const int s_hi = SPLIT ? min(nsteps, s_lo + sp.steps) : nsteps;
+  const int s_begin = s_lo + wid * per;
+  const int s_end = min(s_hi, s_begin + per);
 
   Acc acc[kSets];
 #pragma unroll
@@ -133,82 +206,140 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
       for (int t = 0; t < kSets; ++t) acc[t] += partial[t][w][lane];
   }
 
-  // Lane holds output row m = lane & 15 and features n0 + 4 (lane >> 4) + r.
-  const int m = row;
-  const int n = n0 + 4 * ch;
-  if (m >= M || n >= N) return;
-  if constexpr (OUT == 2) {
-    int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
-    if (n + 3 < N && vec_ok(out)) {
-      *reinterpret_cast<i32x4*>(out) = acc[0];
-    } else {
-      for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[0][r];
-    }
-  } else {
-    const float s_row = I8 ? sa[m] : 1.f;
-    float y[4];
+  if constexpr (SPLIT) {
+    // This K range's sums, for the combining launch.
+    i32x4* mine = sp.part + ((static_cast<int64_t>(blockIdx.x) * sp.splits + blockIdx.y) * kSets) * 64;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nn = min(n + r, N - 1);
-      const float b = epi.bias ? epi.bias[nn] : 0.f;
-      y[r] = I8 ? fmaf(static_cast<float>(acc[0][r]), s_row * epi.sb[nn], b) : static_cast<float>(acc[0][r]) + b;
-      if constexpr (GATED) {
-        const float b2 = epi.bias2 ? epi.bias2[nn] : 0.f;
-        const float u = fmaf(static_cast<float>(acc[kSets - 1][r]), s_row * epi.sb2[nn], b2);
-        y[r] = activation<ACT>(y[r]) * u;
-      } else {
-        y[r] = activation<ACT>(y[r]);
-      }
-    }
-    if constexpr (OUT == 0) {
-      float* out = static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n;
-      if (n + 3 < N && vec_ok(out)) {
-        *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
-      } else {
-        for (int r = 0; r < 4 && n + r < N; ++r) out[r] = y[r];
-      }
-    } else {
-      __bf16* out = static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n;
-      if (n + 3 < N && vec_ok(out)) {
-        *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
-                                                 static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
-      } else {
-        for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<__bf16>(y[r]);
-      }
-    }
+    for (int t = 0; t < kSets; ++t) mine[t * 64 + lane] = __builtin_bit_cast(i32x4, acc[t]);
+  } else {
+    tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, n0, epi, M, N, C, ldc);
   }
+}
+
+// Second launch of the split path: one wave per tile adds the tile's
+// partials in K order, then applies the epilogue.
+template <bool I8, int OUT, int ACT, bool GATED>
+__global__ __launch_bounds__(64) void gemv_combine_kernel(EpiArgs epi, int M, int N, void* __restrict__ C,
+                                                          int64_t ldc, SplitArgs sp) {
+  using Acc = typename Mma<I8>::Acc;
+  constexpr int kSets = GATED ? 2 : 1;
+  const int lane = threadIdx.x;
+  const i32x4* all = sp.part + static_cast<int64_t>(blockIdx.x) * sp.splits * kSets * 64;
+  Acc acc[kSets];
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) {
+    Acc sum = __builtin_bit_cast(Acc, all[t * 64 + lane]);
+    for (int q = 1; q < sp.splits; ++q) sum += __builtin_bit_cast(Acc, all[(q * kSets + t) * 64 + lane]);
+    acc[t] = sum;
+  }
+  tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, static_cast<int>(blockIdx.x) * 16, epi, M, N, C, ldc);
+}
+
+// Per-device split-K workspace for the partial sums, allocated on the first
+// call that wants it (outside stream capture).  Calls that run at the same
+// time on one device (different streams) must not both take the split path.
+constexpr size_t kWsBytes = 8 << 20;
+
+bool split_workspace(hipStream_t stream, uint8_t** ws) {
+  static std::mutex mu;
+  static uint8_t* bufs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (bufs[dev] == nullptr) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
+    void* p = nullptr;
+    if (hipMalloc(&p, kWsBytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    bufs[dev] = static_cast<uint8_t*>(p);
+  }
+  *ws = bufs[dev];
+  return true;
+}
+
+inline int gemv_num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+           prop.multiProcessorCount > 0)
+              ? prop.multiProcessorCount
+              : 256;
+  }
+  return cus;
+}
+
+template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT>
+void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
+                  const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
+                  hipStream_t stream) {
+  switch (waves) {
+    case 4:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT>), grid, dim3(256), 0, stream, a, lda, b, ldb,
+                         epi, m, n, kb, per, C, ldc, sp);
+      break;
+    case 8:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT>), grid, dim3(512), 0, stream, a, lda, b, ldb,
+                         epi, m, n, kb, per, C, ldc, sp);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED, SPLIT>), grid, dim3(1024), 0, stream, a, lda, b,
+                         ldb, epi, m, n, kb, per, C, ldc, sp);
+      break;
+  }
+}
+
+// Waves per workgroup for `steps` K steps: the fewest of 4, 8, 16 that keep
+// each wave at kSteps steps or less.
+inline int waves_for(int64_t steps) {
+  for (int w : {4, 8}) {
+    if ((steps + w - 1) / w <= kSteps) return w;
+  }
+  return 16;
 }
 
 template <bool I8, int OUT, int ACT = 0, bool GATED = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
                       int64_t N, int64_t kbytes, void* C, int64_t ldc, hipStream_t stream) {
+  constexpr int kSets = GATED ? 2 : 1;
   const int64_t nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
-  int waves = 16;
-  for (int w : {4, 8}) {
-    if ((nsteps + w - 1) / w <= kSteps) {
-      waves = w;
-      break;
-    }
-  }
-  const int per = static_cast<int>((nsteps + waves - 1) / waves);
-  const dim3 grid(static_cast<unsigned>((N + 15) / 16));
+  const int64_t tiles = (N + 15) / 16;
   const auto* a = static_cast<const uint8_t*>(A);
   const auto* b = static_cast<const uint8_t*>(B);
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
-  switch (waves) {
-    case 4:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED>), grid, dim3(256), 0, stream, a, lda, b, ldb, epi, m,
-                         n, kb, per, C, ldc);
-      break;
-    case 8:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED>), grid, dim3(512), 0, stream, a, lda, b, ldb, epi, m,
-                         n, kb, per, C, ldc);
-      break;
-    default:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED>), grid, dim3(1024), 0, stream, a, lda, b, ldb, epi,
-                         m, n, kb, per, C, ldc);
-      break;
+
+  // Split K when there are fewer tiles than CUs: aim at two workgroups per
+  // CU, keep at least 8 steps per split, stay inside the workspace.
+  int64_t splits = 1;
+  const int64_t cus = gemv_num_cus();
+  if (tiles < cus) {
+    splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nsteps / 8);
+    const int64_t cap = static_cast<int64_t>(kWsBytes / (static_cast<size_t>(kSets) * 1024));
+    splits = std::min<int64_t>(splits, cap / tiles);
   }
+  uint8_t* ws = nullptr;
+  if (splits > 1 && split_workspace(stream, &ws)) {
+    const int64_t steps = (nsteps + splits - 1) / splits;
+    splits = (nsteps + steps - 1) / steps;  // no empty split
+    const int waves = waves_for(steps);
+    const int per = static_cast<int>((steps + waves - 1) / waves);
+    const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(steps)};
+    launch_waves<I8, OUT, ACT, GATED, true>(waves, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splits)),
+                                           a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_combine_kernel<I8, OUT, ACT, GATED>), dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
+                       stream, epi, m, n, C, ldc, sp);
+    return hipGetLastError();
+  }
+  const int waves = waves_for(nsteps);
+  const int per = static_cast<int>((nsteps + waves - 1) / waves);
+  launch_waves<I8, OUT, ACT, GATED, false>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n, kb,
+                                          per, C, ldc, SplitArgs{nullptr, 1, 0}, stream);
   return hipGetLastError();
 }
 
