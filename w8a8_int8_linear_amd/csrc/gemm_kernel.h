@@ -10,9 +10,11 @@
 // accumulation of bf16 products, Y = acc + b.
 //
 // Design:
-//  * 256x256 output tile per 256-thread workgroup, 4 waves in a 2x2 grid,
-//    each wave owning a 128x128 sub-tile: 8x8 MFMA tiles of 16x16, i.e. 256
-//    int32/fp32 accumulators per lane.  K advances in 128-byte slices.
+//  * 256 x (32 TN) output tile per 256-thread workgroup (TN in {4, 6, 8},
+//    chosen per shape), 4 waves in a 2x2 grid, each wave owning a
+//    128 x (16 TN) sub-tile: 8 x TN MFMA tiles of 16x16, i.e. up to 256
+//    int32/fp32 accumulators per lane, held in AGPRs.  K advances in
+//    128-byte slices.
 //  * Both instruction kinds consume 16 bytes per lane per operand and cover
 //    64 bytes of K (v_mfma_i32_16x16x64_i8: 64 int8; v_mfma_f32_16x16x32_bf16:
 //    32 bf16), so the data movement is shared and only the MFMA differs.
@@ -20,13 +22,14 @@
 //    the "column" operand, so each lane's four accumulators are four
 //    consecutive output features of one output row (one 16-byte fp32 or
 //    8-byte bf16 store).
-//  * LDS holds two [256][128 B] slices per operand (128 KiB double buffer).
-//    16-byte chunks are XOR-swizzled by (row & 7), which makes both the
-//    coalesced row writes and the MFMA fragment reads (16 rows, one chunk
-//    column) bank-conflict free.
+//  * LDS holds three activation slices and two weight slices ([rows][128 B]
+//    each; 160 KiB at TN = 8).  16-byte chunks are XOR-swizzled by
+//    (row & 7), which makes both the coalesced row writes and the MFMA
+//    fragment reads (16 rows, one chunk column) bank-conflict free.
 //  * Slices move global -> LDS directly (global_load_lds_dwordx4, no
-//    staging registers); slice k+1 is in flight while the MFMAs of slice k
-//    run, with one barrier per slice.
+//    staging registers), two slices ahead of the MFMAs, spread between
+//    them by a compile-time schedule, with one barrier per slice (see the
+//    pipeline comment at the main loop).
 //  * Workgroups are remapped so that each of the 8 XCDs (workgroup id mod 8
 //    on dispatch) works on a contiguous range of tiles, and tiles are walked
 //    in groups of 8 row-tiles so that concurrent workgroups on one XCD share
