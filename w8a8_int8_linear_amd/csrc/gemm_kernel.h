@@ -538,8 +538,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     a_cur = a_next;
     ++kt;
   } while (kt < nk);
-  // The last reads fetched nothing that is used; let them retire.
+  // The last reads fetched nothing that is used; let them retire.  Their
+  // destination registers stay allocated until the wait has passed, so that
+  // no epilogue value is placed in a register an LDS read is still writing.
+  sched_fence();
   wait_lds();
+  sched_fence();
+  keep_live(fa0);
+  keep_live(fb0);
+  keep_live(fa1);
+  keep_live(fb1);
   // MFMA results are read below by ordinary instructions: wait out the
   // longest MFMA write latency first.  The empty statements then redefine
   // every accumulator after the padding, so no copy of one (which the
@@ -646,8 +654,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
               if (n + 16 / kElt <= N) {
                 *reinterpret_cast<i32x4*>(out) = v;
               } else {
-                const out_t* e = reinterpret_cast<const out_t*>(&v);
-                for (int r = 0; r < 16 / kElt && n + r < N; ++r) out[r] = e[r];
+                // ragged right edge: element r of the 16-byte piece, taken
+                // with shifts (taking the vector's address would place it in
+                // scratch memory for every piece, not only the ragged ones)
+                for (int r = 0; r < 16 / kElt && n + r < N; ++r) {
+                  if constexpr (OUT == 0) {
+                    reinterpret_cast<int32_t*>(out)[r] = v[r];
+                  } else {
+                    reinterpret_cast<uint16_t*>(out)[r] = static_cast<uint16_t>(v[r >> 1] >> (16 * (r & 1)));
+                  }
+                }
               }
             }
           }
