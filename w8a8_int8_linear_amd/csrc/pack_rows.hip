@@ -12,26 +12,32 @@
 // transform and scales by 1/sqrt(G).
 //
 // Design (one workgroup per row, the whole row held in VGPRs):
-//  * Each thread owns chunks of 16 contiguous features (two 16-byte loads for
-//    bf16, four for fp32), so one chunk is exactly one 16-byte store of
-//    codes.  A G-group spans G/16 lanes of one wavefront.
-//  * H4 = J/2 - (anti-diagonal), so a radix-4 butterfly on (a0..a3) is
-//    s = a0+a1+a2+a3, y_j = s - 2 a_{3-j} (3 adds + 4 FMAs).  The factor 1/2
-//    of every stage is left out and the total power of two is folded into
-//    the scale at the end, which is bit-identical (binary scaling commutes
-//    with fp32 rounding).
+//  * Each thread owns 1, 2 or 4 chunks of 16 contiguous features (two
+//    16-byte loads per chunk for bf16, four for fp32), so one chunk's codes
+//    are exactly one 16-byte store.  A G-group spans G/16 lanes of one
+//    wavefront.  Rows are accessed through buffer resources sized to the
+//    row: loads past K return zeros and stores past K are dropped.
+//  * H4 = J/2 - (anti-diagonal), so an in-register radix-4 butterfly on
+//    (a0..a3) is s = a0+a1+a2+a3, y_j = s - 2 a_{3-j} (3 adds + 4 FMAs).  The
+//    factor 1/2 of every stage is left out and the total power of two is
+//    folded into the scale at the end, which is bit-identical (binary
+//    scaling commutes with fp32 rounding).
 //  * The two low base-4 digits of a group index live inside a chunk
-//    (in-register butterflies).  Higher digits live in lane bits and are
-//    exchanged with DPP (quad_perm within 4 lanes, row_ror within 16 lanes)
-//    and, for G = 1024, ds_swizzle / ds_bpermute across 64 lanes.  The digit
+//    (in-register butterflies).  Higher digits live in lane bits.  With the
+//    partner lane holding digit 3 - d, y_d = (a_d - a_{3-d}) + (sum of the
+//    other pair): three two-operand instructions per element, each taking
+//    its lane exchange as a DPP source (quad_perm within 4 lanes, row_ror
+//    within 16), or ds_swizzle / a 32-lane exchange for G = 1024.  The digit
 //    held in lane bits 2-3 (and 4-5) is Gray-coded across lanes, so that the
-//    partner holding digit 3-j is always lane ^ 8 (or lane ^ 32) and the
-//    butterfly needs only rotations that DPP provides.
-//  * Absmax: per-thread max, DPP/swizzle wavefront reduction, LDS reduction
-//    across waves.  Quantisation multiplies by 127/amax and rounds with the
-//    1.5*2^23 trick (one FMA rounds to nearest even and leaves the int8 code
-//    in the low byte); three v_perm_b32 pack four codes per dword.
+//    partner holding digit 3-j is always lane ^ 8 (or lane ^ 32).
+//  * Absmax: per-thread max, then an unsigned max over the bit patterns of
+//    the (non-negative) per-lane maxima across the wavefront, then LDS
+//    across wavefronts.  Quantisation multiplies by 127/amax and rounds with
+//    the 1.5*2^23 trick (one FMA rounds to nearest even and leaves the int8
+//    code in the low byte); three v_perm_b32 pack four codes per dword.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "launchers.h"
 
@@ -92,22 +98,27 @@ __device__ __forceinline__ void bfly4(float& a0, float& a1, float& a2, float& a3
 // k = 0: identity digit order within a quad, partner at lane ^ 3.
 // k = 1: Gray-coded digit in lane bits 2-3, partner at lane ^ 8.
 // k = 2: Gray-coded digit in lane bits 4-5, partner at lane ^ 32.
+// With the digit d of this lane and 3 - d held by the partner, the output
+// s - 2 a_{3-d} equals (a_d - a_{3-d}) + (sum of the other pair), and the
+// other pair's sum is held by the lanes one exchange away (lane ^ 1 in a
+// quad, a rotation by 4 within 16 lanes for the Gray-coded digit 1, lane ^ 16
+// for digit 2).  That is three two-operand instructions per element, each
+// taking its lane exchange as a DPP source operand.
 template <int K>
 __device__ __forceinline__ float bfly4_lanes(float x) {
   if constexpr (K == 0) {
-    const float t = x + dpp<kQuadXor1>(x);
-    const float s = t + dpp<kQuadXor2>(t);
-    return fmaf(-2.f, dpp<kQuadXor3>(x), s);
+    const float u = x + dpp<kQuadXor3>(x);
+    const float w = x - dpp<kQuadXor3>(x);
+    return w + dpp<kQuadXor1>(u);
   } else if constexpr (K == 1) {
-    const float p = dpp<kRowRor8>(x);
-    const float t = x + p;
-    const float s = t + dpp<kRowRor4>(t);
-    return fmaf(-2.f, p, s);
+    const float u = x + dpp<kRowRor8>(x);
+    const float w = x - dpp<kRowRor8>(x);
+    return w + dpp<kRowRor4>(u);
   } else {
     const float p = xor32(x);
-    const float t = x + p;
-    const float s = t + swz<kSwzXor16>(t);
-    return fmaf(-2.f, p, s);
+    const float u = x + p;
+    const float w = x - p;
+    return w + swz<kSwzXor16>(u);
   }
 }
 
@@ -133,14 +144,26 @@ __device__ __forceinline__ int chunk_in_group(int pos) {
   }
 }
 
+// Rows are accessed through buffer resources whose size is the row's valid
+// bytes: a load past the end returns zeros and a store past the end is
+// dropped, so chunks beyond K (threads rounded up to whole wavefronts) need
+// no test, no zero fill and no store guard.  Word 3 is the raw-buffer
+// default (32-bit data format).  Cache policy: non-temporal, the row is
+// touched once.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
+}
+
 template <typename InT>
-__device__ __forceinline__ void load_chunk(const InT* p, float v[kChunk]);
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]);
 
 template <>
-__device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float v[kChunk]) {
-  const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
-  const u32x4 a = __builtin_nontemporal_load(p4);
-  const u32x4 b = __builtin_nontemporal_load(p4 + 1);
+__device__ __forceinline__ void load_chunk<uint16_t>(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * elem_off, 0, kNonTemporal);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * elem_off + 16, 0, kNonTemporal);
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -150,12 +173,11 @@ __device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* p, float v[
 }
 
 template <>
-__device__ __forceinline__ void load_chunk<float>(const float* p, float v[kChunk]) {
-  const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+__device__ __forceinline__ void load_chunk<float>(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f32x4 a = __builtin_nontemporal_load(p4 + i);
-    v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, 4 * elem_off + 16 * i, 0, kNonTemporal);
+    v[4 * i] = as_f(a.x); v[4 * i + 1] = as_f(a.y); v[4 * i + 2] = as_f(a.z); v[4 * i + 3] = as_f(a.w);
   }
 }
 
@@ -172,13 +194,21 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, f
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
-__device__ __forceinline__ float wave_max(float m) {
-  m = fmaxf(m, dpp<kQuadXor1>(m));
-  m = fmaxf(m, dpp<kQuadXor2>(m));
-  m = fmaxf(m, dpp<kRowRor4>(m));
-  m = fmaxf(m, dpp<kRowRor8>(m));
-  m = fmaxf(m, swz<kSwzXor16>(m));
-  m = fmaxf(m, xor32(m));
+// Maximum over the wavefront of non-negative values.  For those the IEEE
+// bit patterns order like unsigned integers, so the reduction runs on the
+// bits (an unsigned max takes its lane exchange as a DPP operand and needs
+// none of the NaN canonicalisation a float max would add at every step).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t m) {
+  m = max(m, dpp_u<kQuadXor1>(m));
+  m = max(m, dpp_u<kQuadXor2>(m));
+  m = max(m, dpp_u<kRowRor4>(m));
+  m = max(m, dpp_u<kRowRor8>(m));
+  m = max(m, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(m), kSwzXor16)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
   return m;
 }
 
@@ -192,7 +222,7 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
   static_assert(L <= 64, "a group must fit in one wavefront");
   static_assert(RAND ? (LOG2G >= 4 && LOG2G <= 10) : (LOG2G % 2 == 0 && LOG2G >= 2 && LOG2G <= 10),
                 "unsupported group size");
-  __shared__ float wave_amax[kMaxThreads / 64];
+  __shared__ uint32_t wave_amax[kMaxThreads / 64];
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -200,35 +230,28 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
   const int lane = tid & 63;
   const InT* xrow = X + static_cast<int64_t>(row) * ldx;
 
+  const __amdgpu_buffer_rsrc_t xr = row_rsrc(xrow, K * static_cast<int>(sizeof(InT)));
   float v[CPT][kChunk];
   int off[CPT];
-  bool ok[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int vt = tid + c * T;
     const int grp = vt / L;
     const int pos = vt % L;
     off[c] = (grp * L + chunk_in_group<RAND>(pos)) * kChunk;
-    ok[c] = off[c] < K;
-    if (ok[c]) {
-      load_chunk<InT>(xrow + off[c], v[c]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kChunk; ++e) v[c][e] = 0.f;
-    }
+    load_chunk<InT>(xr, off[c], v[c]);
   }
 
   if constexpr (RAND) {
+    const __amdgpu_buffer_rsrc_t sr = row_rsrc(signs, K);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      if (ok[c]) {
-        const uint4 sv = *reinterpret_cast<const uint4*>(signs + off[c]);
-        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+      const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(sr, off[c], 0, 0);
+      const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const int8_t sgn = static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
-          v[c][e] = sgn < 0 ? -v[c][e] : v[c][e];
-        }
+      for (int e = 0; e < kChunk; ++e) {
+        const int8_t sgn = static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
+        v[c][e] = sgn < 0 ? -v[c][e] : v[c][e];
       }
     }
     // In-register radix-2 stages over element bits 0..3.
@@ -275,18 +298,18 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
         for (int b = 0; b < 4; ++b) bfly4(v[c][b], v[c][4 + b], v[c][8 + b], v[c][12 + b]);
       }
     }
-    // Digits 2.. across lanes.
+    // Digits 2.. across lanes, one digit at a time over all elements (the
+    // independent elements fill the wait states a DPP read needs after the
+    // write of its source).
+    auto lane_stage = [&](auto k_c) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+      for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
-        float x = v[c][e];
-        if constexpr (LOG2G >= 6) x = bfly4_lanes<0>(x);
-        if constexpr (LOG2G >= 8) x = bfly4_lanes<1>(x);
-        if constexpr (LOG2G >= 10) x = bfly4_lanes<2>(x);
-        v[c][e] = x;
-      }
-    }
+        for (int e = 0; e < kChunk; ++e) v[c][e] = bfly4_lanes<decltype(k_c)::value>(v[c][e]);
+    };
+    if constexpr (LOG2G >= 6) lane_stage(std::integral_constant<int, 0>{});
+    if constexpr (LOG2G >= 8) lane_stage(std::integral_constant<int, 1>{});
+    if constexpr (LOG2G >= 10) lane_stage(std::integral_constant<int, 2>{});
   }
 
   // Scale that turns the unnormalised transform into the orthonormal one:
@@ -296,15 +319,13 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
                           : __builtin_ldexpf(1.0f, -(LOG2G / 2));
 
   if constexpr (!QUANT) {
-    float* rrow = xrot + static_cast<int64_t>(row) * ldr;
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(xrot + static_cast<int64_t>(row) * ldr, 4 * K);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      if (!ok[c]) continue;
-      float4* o4 = reinterpret_cast<float4*>(rrow + off[c]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o4[i] = make_float4(v[c][4 * i] * norm, v[c][4 * i + 1] * norm, v[c][4 * i + 2] * norm,
-                            v[c][4 * i + 3] * norm);
+        const f32x4 o = {v[c][4 * i] * norm, v[c][4 * i + 1] * norm, v[c][4 * i + 2] * norm, v[c][4 * i + 3] * norm};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rr, 4 * off[c] + 16 * i, 0, 0);
       }
     }
     return;
@@ -315,28 +336,33 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
 #pragma unroll
       for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
     }
-    m = wave_max(m);
+    // Every lane ends with its wavefront's maximum; rows of several
+    // wavefronts combine theirs through LDS (uniform branch: T is the
+    // workgroup size).
+    uint32_t amax_bits = wave_max_bits(as_u(m));
     const int nwaves = T >> 6;
-    if (lane == 0) wave_amax[tid >> 6] = m;
-    __syncthreads();
-    float amax_u = wave_amax[0];
-    for (int w = 1; w < nwaves; ++w) amax_u = fmaxf(amax_u, wave_amax[w]);
+    if (nwaves > 1) {
+      if (lane == 0) wave_amax[tid >> 6] = amax_bits;
+      __syncthreads();
+      amax_bits = wave_amax[0];
+      for (int w = 1; w < nwaves; ++w) amax_bits = max(amax_bits, wave_amax[w]);
+    }
+    const float amax_u = as_f(amax_bits);
 
     // Unnormalised codes: y_u * (127 / amax_u) == y / s exactly up to the
     // rounding of the reciprocal; all-zero rows give inv = 0 and codes 0.
     const float inv = amax_u > 0.f ? 127.0f / amax_u : 0.f;
     if (tid == 0) scale[row] = (amax_u * norm) / 127.0f;
 
-    int8_t* qrow = q + static_cast<int64_t>(row) * ldq;
+    const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      if (!ok[c]) continue;
       u32x4 o;
       o.x = quant4(v[c][0], v[c][1], v[c][2], v[c][3], inv);
       o.y = quant4(v[c][4], v[c][5], v[c][6], v[c][7], inv);
       o.z = quant4(v[c][8], v[c][9], v[c][10], v[c][11], inv);
       o.w = quant4(v[c][12], v[c][13], v[c][14], v[c][15], inv);
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qrow + off[c]));
+      __builtin_amdgcn_raw_buffer_store_b128(o, qr, off[c], 0, kNonTemporal);
     }
   }
 }
@@ -346,7 +372,13 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
                         int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
                         hipStream_t stream) {
   const int64_t nvt = K / kChunk;  // chunks in a row
+  // Chunks per thread: more of them spread the per-wavefront fixed work (the
+  // reductions, the scale division, addressing) over more elements; take 2
+  // or 4 while the row keeps at least two whole wavefronts (one wavefront
+  // per row was measured slower: less parallelism per row), and as many as
+  // needed to stay within one workgroup.
   int cpt = 1;
+  while (cpt < 4 && nvt % (128 * cpt) == 0) cpt *= 2;
   while ((nvt + cpt - 1) / cpt > kMaxThreads) cpt *= 2;
   const int64_t threads = ((nvt + cpt - 1) / cpt + 63) / 64 * 64;
   const dim3 grid(static_cast<unsigned>(rows));
