@@ -625,6 +625,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       constexpr int kChunks = 16 * kSegs;          // per 16-row block
       __syncthreads();  // every wave is done reading the slice buffers
       uint8_t* stage = smem + wid * 16 * kPitch;
+      constexpr int kPasses = (kChunks + 63) / 64;
+      const bool full = m_blk + kBM <= M && n_blk + kBNo <= N;  // uniform
+      // Lane l's store of pass p in 16-row block 0 (blocks follow at
+      // block_stride bytes).
+      uint8_t* pass_base[kPasses];
+      const int64_t block_stride = 16 * ldc * kElt;
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int c = min(64 * p + lane, kChunks - 1);
+        const int row = c / kSegs, seg = c % kSegs;
+        pass_base[p] = static_cast<uint8_t*>(C) +
+                       (static_cast<int64_t>(m_blk + wm + row) * ldc + n_blk + wno) * kElt + seg * 16;
+      }
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
 #pragma unroll
@@ -640,6 +653,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
             *reinterpret_cast<bf16x4*>(dst) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
                                                      static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
           }
+        }
+        if (full) {
+          // Whole tile inside the output: no bound checks, addresses step by
+          // a uniform 16-row stride from the per-pass bases.
+#pragma unroll
+          for (int p = 0; p < kPasses; ++p) {
+            const int c = 64 * p + lane;
+            if (kChunks % 64 == 0 || c < kChunks) {
+              const int row = c / kSegs, seg = c % kSegs;
+              const i32x4 v = *reinterpret_cast<const i32x4*>(stage + row * kPitch + seg * 16);
+              *reinterpret_cast<i32x4*>(pass_base[p] + static_cast<int64_t>(i) * block_stride) = v;
+            }
+          }
+          continue;
         }
 #pragma unroll
         for (int c0 = 0; c0 < kChunks; c0 += 64) {
