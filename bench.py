@@ -62,10 +62,10 @@ SMALL_M = 16             # up to this many rows a linear runs on the weight-stre
 METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
 # the sources each kernel is compiled from; a traffic summary is valid only for these exact bytes
 KERNEL_SOURCE = {
-    "gemm_i8": ("gemm_kernel.h", "epilogue.h", "gemm_i8.hip"),
-    "gemm_i8_act": ("gemm_kernel.h", "epilogue.h", "gemm_act.hip"),
+    "gemm_i8": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_i8.hip"),
+    "gemm_i8_act": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_act.hip"),
     "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
-    "gemm_bf16": ("gemm_kernel.h", "epilogue.h", "gemm_bf16.hip"),
+    "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_bf16.hip"),
     "gemv_i8": ("gemv.hip", "epilogue.h"),
     "pack_rows": ("pack_rows.hip",),
 }

@@ -1,6 +1,8 @@
-// Quantised linear with an activation fused into the epilogue, on the tiled
-// int8 MFMA kernel (gemm_kernel.h).
+// Quantised linear with an activation fused into the epilogue: the
+// eight-wave kernel (gemm_pp.h) for whole 128-byte K slices, the four-wave
+// kernel (gemm_kernel.h) for a K tail.
 #include "gemm_kernel.h"
+#include "gemm_pp.h"
 
 namespace convrot {
 
@@ -12,6 +14,13 @@ hipError_t launch_gemm_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int
   const auto* b = reinterpret_cast<const uint8_t*>(B);
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   const bool f32 = out == Elt::F32;
+  if (pp_eligible(K)) {
+    if (act == Act::GeluErf)
+      return f32 ? launch_gemm_pp<true, 0, 1>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream)
+                 : launch_gemm_pp<true, 1, 1>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream);
+    return f32 ? launch_gemm_pp<true, 0, 2>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream)
+               : launch_gemm_pp<true, 1, 2>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream);
+  }
   if (act == Act::GeluErf)
     return f32 ? launch_gemm<true, 0, 1, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream)
                : launch_gemm<true, 1, 1, false>(a, lda, b, ldb, epi, M, N, K, C, ldc, stream);

@@ -1,0 +1,399 @@
+// Eight-wave "ping-pong" matrix-core GEMM for gfx950: C = A B^T, both
+// operands K-contiguous, fused scale/bias (and activation) epilogue.  Same
+// operation, modes and result bits as gemm_nt_kernel (gemm_kernel.h); it
+// runs every linear with whole 128-byte K slices (the four-wave kernel keeps
+// K tails and the gated pair).
+//
+// Why eight waves.  A wave issues in order, and a global -> LDS transfer
+// (global_load_lds_dwordx4, 1 KiB) holds its wave's issue for about 50
+// cycles, so MFMAs interleaved with transfers in one wave leave the matrix
+// core idle a third of the time.  Transfers and LDS reads issued by
+// *another* wave on the same SIMD do not slow that wave's MFMAs at all.  So
+// each SIMD runs two waves that take turns: while one issues its memory
+// phase (its share of the transfers and the LDS reads of its next
+// fragments), the other runs a compute phase of MFMAs on fragments already
+// in registers, and a workgroup barrier swaps the roles.  The second group
+// starts one phase late (one extra barrier) and so stays a phase behind.
+//
+// Shapes.  Workgroup tile 256 (A rows, tokens) x 64 TN (B rows, features),
+// TN in {2, 3, 4}; 8 waves, wave w owning tokens 64 (w % 4) .. + 63 and B
+// rows 32 TN (w / 4) .. + 32 TN - 1, i.e. 4 x 2 TN MFMA tiles of 16 x 16
+// (v_mfma_i32_16x16x64_i8, or v_mfma_f32_16x16x32_bf16 in bf16 mode; both
+// take 16 bytes of K per lane and operand).  That is at most 128
+// accumulators per lane, so two waves fit on a SIMD.  The 16 x 16 x 64
+// form is used rather than 32 x 32 x 32 because on random int8 operands it
+// runs at a higher clock under the power limit (2.06 against 1.68 GHz
+// at the same utilisation): less energy per operation.
+//
+// Data movement.  K advances in 128-byte slices ([rows][128 B], 16-byte
+// chunks XOR-swizzled by row & 7); one slice is two 64-byte steps, one step
+// per memory/compute phase pair.  LDS holds three A slices and two B
+// slices.  In the period of slice p each wave issues the B part of slice
+// p + 1 in its first memory phase and the A part of slice p + 2 in its
+// second, so every transfer has at least two phases to land; each wave
+// waits for its own transfers (vmcnt) before the barrier that publishes
+// them.  A buffer (p + 2) % 3 and B buffer (p + 1) % 2 held slices p - 1,
+// whose last reads precede the barrier that opens period p.
+//
+// Epilogue.  Weights are the MFMA "row" operand, so each lane's four
+// accumulators of a tile hold four consecutive output features of one
+// token.  Scales and biases are loaded before the main loop.  Values are
+// multiplied by their row scale in that layout, staged as fp32 rows in a
+// private LDS area per wave, and read back so that each lane finishes fixed
+// 4-feature segments (column scale, bias, activation, conversion) and
+// stores whole row pieces.
+#pragma once
+#include "gemm_kernel.h"
+
+namespace convrot {
+namespace {
+
+constexpr int kPPThreads = 512;
+
+// Largest power of two dividing both v and 64.
+constexpr int gcd_pow2_64(int v) { return (v & -v) < 64 ? (v & -v) : 64; }
+
+template <int TN>
+constexpr int pp_smem_bytes() {
+  return 3 * kATileBytes + 2 * (64 * TN) * kBK;
+}
+
+// OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator (int8 mode only).
+// ACT: epilogue activation (see activation() in epilogue.h).
+template <bool I8, int OUT, int TN, int ACT>
+__global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
+    int N, int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool vec_out) {
+  static_assert(TN >= 2 && TN <= 4, "tile width");
+  static_assert(I8 || OUT != 2, "raw accumulators are an int8 feature");
+  static_assert(ACT == 0 || OUT != 2, "activations need a float output");
+  constexpr int kBN = 64 * TN;          // B-tile rows (output features)
+  constexpr int kWN = 32 * TN;          // B rows per wave
+  constexpr int kBTileBytes = kBN * kBK;
+  constexpr int kBBase = 3 * kATileBytes;
+  constexpr int kDmaA = kBM / 64;       // 1 KiB transfers per wave and slice: A part
+  constexpr int kDmaB = kBN / 64;       // and B part
+  static_assert(pp_smem_bytes<TN>() <= 160 * 1024, "LDS budget");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using Op = Mfma<I8>;
+  using acc_t = typename Op::acc_t;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m_blk = tm * kBM;
+  const int n_blk = tn * kBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int grp = wid >> 2;            // 0: leads, 1: one phase behind
+  const int wm = (wid & 3) * 64;       // tokens of the wave within the tile
+  const int wn = grp * kWN;            // features of the wave within the tile
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  const int grp_u = wid_u >> 2;
+
+  // Transfers: instruction i of wave w fills 1 KiB block w + 8 i of a slice
+  // (8 rows; lane l writes physical chunk l % 8 of row l / 8, which holds
+  // logical chunk (l % 8) ^ (l / 8)).  Rows past the matrix edge re-read
+  // the last row; their results are never stored.
+  const int dma_ch = (lane & 7) ^ (lane >> 3);
+  uint32_t off_a[kDmaA], off_b[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int row = 8 * (wid + 8 * i) + (lane >> 3);
+    off_a[i] = static_cast<uint32_t>(min(row, M - m_blk - 1)) * static_cast<uint32_t>(lda) + dma_ch * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int row = 8 * (wid + 8 * i) + (lane >> 3);
+    off_b[i] = static_cast<uint32_t>(min(row, N - n_blk - 1)) * static_cast<uint32_t>(ldb) + dma_ch * 16;
+  }
+  const uint8_t* a_tile = A + static_cast<int64_t>(m_blk) * lda;
+  const uint8_t* b_tile = B + static_cast<int64_t>(n_blk) * ldb;
+  auto dma_a = [&](int slice, int buf) {
+    const uint8_t* g = a_tile + slice * kBK;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) dma16(g + off_a[i], smem + buf * kATileBytes + (wid_u + 8 * i) * 1024);
+  };
+  auto dma_b = [&](int slice, int buf) {
+    const uint8_t* g = b_tile + slice * kBK;
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i)
+      dma16(g + off_b[i], smem + kBBase + buf * kBTileBytes + (wid_u + 8 * i) * 1024);
+  };
+
+  // Fragment reads: lane l takes row l % 16 of a 16-row tile and 16-byte
+  // chunk l / 16 of the 64-byte K step; step s of a slice is chunks 4 s ..
+  // 4 s + 3.  The swizzle depends on the lane only, so there is one base
+  // address per step and operand; tiles are immediate offsets (16 rows =
+  // 2 KiB).
+  const int frow = lane & 15;
+  const int fk = lane >> 4;
+  const uint32_t lds0 = lds_address(smem);
+  uint32_t base_a[2], base_b[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const uint32_t off = frow * kBK + (((4 * st + fk) ^ (frow & 7)) << 4);
+    base_a[st] = lds0 + wm * kBK + off;
+    base_b[st] = lds0 + kBBase + wn * kBK + off;
+  }
+
+  constexpr int kTF = 2 * TN;  // 16-feature tiles per wave
+  acc_t acc[4][kTF];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int f = 0; f < kTF; ++f) acc[t][f] = acc_t{};
+  pad<5>();  // the zeroing is VALU work read by the first MFMAs
+
+  // One fragment set: a wave reads it in a memory phase and consumes it in
+  // the next phase; the overlap comes from the other wave on the SIMD.
+  i32x4 fa[4], fb[kTF];
+  auto read_step = [&](int st, int abuf, int bbuf) {
+    const uint32_t aa = base_a[st] + abuf * kATileBytes, ab = base_b[st] + bbuf * kBTileBytes;
+    static_for<4>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      lds_read16<2048 * t>(fa[t], aa);
+    });
+    static_for<kTF>([&](auto f_c) {
+      constexpr int f = decltype(f_c)::value;
+      lds_read16<2048 * f>(fb[f], ab);
+    });
+  };
+  auto compute_step = [&]() {
+    static_for<4>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      static_for<kTF>([&](auto f_c) {
+        constexpr int f = decltype(f_c)::value;
+        Op::run(acc[t][f], fb[f], fa[t]);
+      });
+    });
+    // Keep the fragment registers allocated up to here: the MFMAs are opaque
+    // to the compiler, which must not hand their source registers to a
+    // temporary while they may still be read.  (The next writes to them are
+    // LDS reads behind a barrier; the accumulators, read as SrcC, are only
+    // touched again after the padding in front of the epilogue.)
+    keep_live(fa);
+    keep_live(fb);
+  };
+
+  // Epilogue operands, requested before the main loop so that their latency
+  // hides behind it.  Per lane: the row scale of its four tokens (MFMA
+  // layout, token = l % 16 of each 16-token tile), and the column scales and
+  // biases of the 4-feature output segments it finishes (row layout, see
+  // the epilogue).
+  constexpr int kSegs = kWN / 4;                       // 4-feature segments per wave row
+  constexpr int kLaneSegs = kSegs / gcd_pow2_64(kSegs);  // distinct segments per lane
+  float s_row[4] = {1.f, 1.f, 1.f, 1.f};
+  f32x4 s_col[kLaneSegs], b_col[kLaneSegs];
+  if constexpr (OUT != 2) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s_row[t] = epi.sa[min(m_blk + wm + 16 * t + frow, M - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kLaneSegs; ++j) {
+      const int n = n_blk + wn + 4 * ((64 * j + lane) % kSegs);
+      const bool vec = vec_cols && n_blk + kBN <= N;
+      auto load4 = [&](const float* v, float dflt) -> f32x4 {
+        if (v == nullptr) return f32x4{dflt, dflt, dflt, dflt};
+        if (vec) return *reinterpret_cast<const f32x4*>(v + n);
+        f32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = v[min(n + i, N - 1)];
+        return r;
+      };
+      s_col[j] = I8 ? load4(epi.sb, 1.f) : f32x4{1.f, 1.f, 1.f, 1.f};
+      b_col[j] = load4(epi.bias, 0.f);
+    }
+  }
+
+  const int nk = Kb / kBK;
+  dma_a(0, 0);
+  dma_b(0, 0);
+  if (nk > 1) dma_a(1, 1);
+  if (nk > 1) wait_vm<kDmaA>(); else wait_vm<0>();
+  barrier();
+  if (grp_u == 1) barrier();  // the second group runs one phase behind
+
+  int p = 0;
+  int a_cur = 0;  // p % 3
+  do {
+    const int b_cur = p & 1;
+    const int a_next = a_cur == 2 ? 0 : a_cur + 1;
+    const int a_after = a_next == 2 ? 0 : a_next + 1;  // (p + 2) % 3
+    // memory phase: fragments of step 0 of slice p, then the B part of slice
+    // p + 1 (LDS reads queued behind transfers wait for them; in this order
+    // the transfers issue while the reads are in flight)
+    read_step(0, a_cur, b_cur);
+    if (p + 1 < nk) dma_b(p + 1, b_cur ^ 1);
+    wait_lds();
+    barrier();
+    compute_step();
+    barrier();
+    // memory phase: fragments of step 1 of slice p, then the A part of slice
+    // p + 2; every transfer but that A part must have landed before the
+    // barrier
+    read_step(1, a_cur, b_cur);
+    if (p + 2 < nk) dma_a(p + 2, a_after);
+    if (p + 2 < nk) wait_vm<kDmaA>(); else wait_vm<0>();
+    wait_lds();
+    barrier();
+    compute_step();
+    if (grp_u == 0 || p + 1 < nk) barrier();
+    a_cur = a_next;
+    ++p;
+  } while (p < nk);
+
+  // MFMA results are read below by ordinary instructions: wait out the
+  // longest MFMA write latency, then redefine every accumulator so no copy
+  // of one can be placed before the padding.
+  pad<24>();
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int f = 0; f < kTF; ++f) touch_acc(acc[t][f]);
+
+  // Epilogue.  Lane l holds, for tile (t, f), token m = m0 + 16 t + l % 16
+  // and features n = n0 + 16 f + 4 (l / 16) + r, r = 0..3.
+  const int n_lane = 4 * fk;
+  if constexpr (OUT == 2) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int m = m_blk + wm + 16 * t + frow;
+      if (m >= M) continue;
+#pragma unroll
+      for (int f = 0; f < kTF; ++f) {
+        const int n = n_blk + wn + 16 * f + n_lane;
+        int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+        const i32x4 a = acc[t][f];
+        if (n + 3 < N && vec_ok(out)) {
+          *reinterpret_cast<i32x4*>(out) = a;
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) out[r] = a[r];
+        }
+      }
+    }
+  } else {
+    // Per 32 tokens (two 16-token tiles): the accumulators go to a private
+    // LDS area of the wave as fp32 rows, with each row's scale in the row's
+    // padding (every slice read finished before the last barrier); each lane
+    // then takes 4-feature segments of those rows, whose column scale and
+    // bias it already holds, finishes them and stores whole row pieces.  The
+    // value is fma(acc, s_x s_w, b), the same expression in the same
+    // precision as the other linear kernels, so the result bits do not depend
+    // on which kernel a shape runs on.
+    using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
+    constexpr int kPitch = kWN * 4 + 16;  // fp32 row of the wave + its scale, padded across banks
+    constexpr int kPasses = 32 * kSegs / 64;
+    static_assert(8 * 32 * kPitch <= pp_smem_bytes<TN>(), "staging area");
+    uint8_t* stage = smem + wid * 32 * kPitch;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 2 * u + h;
+        uint8_t* row_ptr = stage + (16 * h + frow) * kPitch;
+#pragma unroll
+        for (int f = 0; f < kTF; ++f) {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = static_cast<float>(acc[t][f][r]);
+          *reinterpret_cast<f32x4*>(row_ptr + (16 * f + n_lane) * 4) = v;
+        }
+        if (fk == 0) *reinterpret_cast<float*>(row_ptr + kWN * 4) = s_row[t];
+      }
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int c = 64 * p + lane;
+        const int row = c / kSegs, seg = c % kSegs;
+        const int j = p % kLaneSegs;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * kPitch + seg * 16);
+        const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = I8 ? fmaf(v[r], sr * s_col[j][r], b_col[j][r]) : v[r] + b_col[j][r];
+          y[r] = activation<ACT>(a);
+        }
+        const int m = m_blk + wm + 32 * u + row;
+        const int n = n_blk + wn + 4 * seg;
+        if (m < M) {
+          out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+          if (vec_out && n + 3 < N) {
+            if constexpr (OUT == 0) {
+              *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+            } else {
+              typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+              *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
+                                                       static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+            }
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Tile width for the eight-wave kernel: the fewest idle CU-slots in the
+// last round (ties to the wider tile), as choose_tn does for the four-wave
+// kernel.
+inline int choose_tn_pp(int64_t M, int64_t cols) {
+  const int cands[] = {4, 3, 2};
+  const int64_t cus = num_cus();
+  int best = 4;
+  int64_t best_cost = -1;
+  for (int tn : cands) {
+    const int64_t bn = 64 * tn;
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((cols + bn - 1) / bn);
+    const int64_t cost = ((tiles + cus - 1) / cus) * bn;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = tn;
+    }
+  }
+  return best;
+}
+
+template <bool I8, int OUT, int TN, int ACT>
+hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi,
+                           int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
+  auto kern = gemm_pp_kernel<I8, OUT, TN, ACT>;
+  constexpr int kSmem = pp_smem_bytes<TN>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+  const int tiles_n = static_cast<int>((N + 64 * TN - 1) / (64 * TN));
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec_cols = al16(epi.sb) && al16(epi.bias);
+  // Four consecutive outputs go out as one store when rows keep them aligned.
+  const int out_elt = OUT == 1 ? 2 : 4;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(C) % (4 * out_elt)) == 0 && ldc % 4 == 0;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(kPPThreads), kSmem, stream, A, lda, B,
+                     ldb, epi, static_cast<int>(M), static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m,
+                     tiles_n, vec_cols, vec_out);
+  return hipGetLastError();
+}
+
+// Whether the eight-wave kernel takes this shape: whole 128-byte K slices.
+inline bool pp_eligible(int64_t Kb) { return Kb % kBK == 0 && Kb > 0; }
+
+template <bool I8, int OUT, int ACT = 0>
+hipError_t launch_gemm_pp(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi, int64_t M,
+                          int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
+  switch (choose_tn_pp(M, N)) {
+    case 2: return launch_pp_typed<I8, OUT, 2, ACT>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
+    case 3: return launch_pp_typed<I8, OUT, 3, ACT>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
+    default: return launch_pp_typed<I8, OUT, 4, ACT>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
+  }
+}
+
+}  // namespace
+}  // namespace convrot
