@@ -288,6 +288,19 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     constexpr int kPasses = 32 * kSegs / 64;
     static_assert(8 * 32 * kPitch <= pp_smem_bytes<TN>(), "staging area");
     uint8_t* stage = smem + wid * 32 * kPitch;
+    // Tiles wholly inside the output take a path without per-store checks:
+    // lane l's segment and row in pass p repeat with period kLaneSegs, the
+    // row advancing by kRowStep, so a few per-lane bases and uniform strides
+    // give every address.
+    const bool full = vec_out && m_blk + kBM <= M && n_blk + kBN <= N;  // uniform
+    constexpr int kRowStep = 64 * kLaneSegs / kSegs;
+    out_t* lane_base[kLaneSegs];
+#pragma unroll
+    for (int j = 0; j < kLaneSegs; ++j) {
+      const int c = 64 * j + lane;
+      lane_base[j] = static_cast<out_t*>(C) + static_cast<int64_t>(m_blk + wm + c / kSegs) * ldc + n_blk + wn +
+                     4 * (c % kSegs);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -315,6 +328,17 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
         for (int r = 0; r < 4; ++r) {
           const float a = I8 ? fmaf(v[r], sr * s_col[j][r], b_col[j][r]) : v[r] + b_col[j][r];
           y[r] = activation<ACT>(a);
+        }
+        if (full) {
+          out_t* out = lane_base[j] + static_cast<int64_t>(32 * u + (p / kLaneSegs) * kRowStep) * ldc;
+          if constexpr (OUT == 0) {
+            *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
+                                                     static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+          }
+          continue;
         }
         const int m = m_blk + wm + 32 * u + row;
         const int n = n_blk + wn + 4 * seg;
