@@ -37,11 +37,11 @@
 //
 // Epilogue.  Weights are the MFMA "row" operand, so each lane's four
 // accumulators of a tile hold four consecutive output features of one
-// token.  Scales and biases are loaded before the main loop.  Values are
-// multiplied by their row scale in that layout, staged as fp32 rows in a
-// private LDS area per wave, and read back so that each lane finishes fixed
-// 4-feature segments (column scale, bias, activation, conversion) and
-// stores whole row pieces.
+// token.  Scales and biases are loaded before the main loop.  The
+// accumulators are staged as fp32 rows (each row's scale in its padding) in
+// a private LDS area per wave and read back so that each lane finishes fixed
+// 4-feature segments (both scales, bias, activation, conversion) and stores
+// whole row pieces.
 #pragma once
 #include "gemm_kernel.h"
 
