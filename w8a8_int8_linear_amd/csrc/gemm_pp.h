@@ -37,10 +37,10 @@
 //
 // Epilogue.  Weights are the MFMA "row" operand, so each lane's four
 // accumulators of a tile hold four consecutive output features of one
-// token.  Scales and biases are loaded before the main loop.  The
-// accumulators are staged as fp32 rows (each row's scale in its padding) in
-// a private LDS area per wave and read back so that each lane finishes fixed
-// 4-feature segments (both scales, bias, activation, conversion) and stores
+// token.  Scales and biases are loaded before the main loop.  The raw
+// accumulators are staged as rows (each row's scale in its padding) in a
+// private LDS area per wave and read back so that each lane finishes fixed
+// 4-feature segments (conversion, both scales, bias, activation) and stores
 // whole row pieces.
 #pragma once
 #include "gemm_kernel.h"
@@ -275,22 +275,23 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
       }
     }
   } else {
-    // Per 32 tokens (two 16-token tiles): the accumulators go to a private
-    // LDS area of the wave as fp32 rows, with each row's scale in the row's
-    // padding (every slice read finished before the last barrier); each lane
-    // then takes 4-feature segments of those rows, whose column scale and
-    // bias it already holds, finishes them and stores whole row pieces.  The
-    // value is fma(acc, s_x s_w, b), the same expression in the same
-    // precision as the other linear kernels, so the result bits do not depend
-    // on which kernel a shape runs on.
+    // Per 32 tokens (two 16-token tiles): the raw accumulators go to a
+    // private LDS area of the wave as rows, with each row's scale in the
+    // row's padding (every slice read finished before the last barrier);
+    // each lane then takes 4-feature segments of those rows, whose column
+    // scale and bias it already holds, converts, finishes them and stores
+    // whole row pieces.  The value is fma(acc, s_x s_w, b), the same
+    // expression in the same precision as the other linear kernels, so the
+    // result bits do not depend on which kernel a shape runs on.
     using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
-    constexpr int kPitch = kWN * 4 + 16;  // fp32 row of the wave + its scale, padded across banks
+    constexpr int kPitch = kWN * 4 + 16;  // one row of the wave + its scale, padded across banks
     constexpr int kPasses = 32 * kSegs / 64;
     static_assert(8 * 32 * kPitch <= pp_smem_bytes<TN>(), "staging area");
     uint8_t* stage = smem + wid * 32 * kPitch;
-    // Tiles wholly inside the output take a path without per-store checks:
-    // lane l's segment and row in pass p repeat with period kLaneSegs, the
-    // row advancing by kRowStep, so a few per-lane bases and uniform strides
+    // Tiles wholly inside the output take a branch-free pass loop (so the
+    // LDS reads of later passes can issue ahead of earlier stores): lane l's
+    // segment and row in pass p repeat with period kLaneSegs, the row
+    // advancing by kRowStep, so a few per-lane bases and uniform strides
     // give every address.
     const bool full = vec_out && m_blk + kBM <= M && n_blk + kBN <= N;  // uniform
     constexpr int kRowStep = 64 * kLaneSegs / kSegs;
@@ -301,6 +302,33 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
       lane_base[j] = static_cast<out_t*>(C) + static_cast<int64_t>(m_blk + wm + c / kSegs) * ldc + n_blk + wn +
                      4 * (c % kSegs);
     }
+    // Segment of pass p: converted, scaled, biased and activated outputs.
+    auto finish = [&](int p, float y[4]) {
+      const int c = 64 * p + lane;
+      const int row = c / kSegs, seg = c % kSegs;
+      const int j = p % kLaneSegs;
+      const acc_t a = *reinterpret_cast<const acc_t*>(stage + row * kPitch + seg * 16);
+      const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = static_cast<float>(a[r]);
+        const float z = I8 ? fmaf(v, sr * s_col[j][r], b_col[j][r]) : v + b_col[j][r];
+        y[r] = activation<ACT>(z);
+      }
+    };
+    auto store4 = [](out_t* out, const float y[4]) {
+      if constexpr (OUT == 0) {
+        *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+      } else {
+        // Two pairs, each one packed round-to-nearest-even conversion.
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+        *reinterpret_cast<u32x2*>(out) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+    };
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -308,52 +336,31 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
         const int t = 2 * u + h;
         uint8_t* row_ptr = stage + (16 * h + frow) * kPitch;
 #pragma unroll
-        for (int f = 0; f < kTF; ++f) {
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = static_cast<float>(acc[t][f][r]);
-          *reinterpret_cast<f32x4*>(row_ptr + (16 * f + n_lane) * 4) = v;
-        }
+        for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (16 * f + n_lane) * 4) = acc[t][f];
         if (fk == 0) *reinterpret_cast<float*>(row_ptr + kWN * 4) = s_row[t];
       }
+      if (full) {
 #pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        const int c = 64 * p + lane;
-        const int row = c / kSegs, seg = c % kSegs;
-        const int j = p % kLaneSegs;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * kPitch + seg * 16);
-        const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
-        float y[4];
+        for (int p = 0; p < kPasses; ++p) {
+          float y[4];
+          finish(p, y);
+          store4(lane_base[p % kLaneSegs] + static_cast<int64_t>(32 * u + (p / kLaneSegs) * kRowStep) * ldc, y);
+        }
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = I8 ? fmaf(v[r], sr * s_col[j][r], b_col[j][r]) : v[r] + b_col[j][r];
-          y[r] = activation<ACT>(a);
-        }
-        if (full) {
-          out_t* out = lane_base[j] + static_cast<int64_t>(32 * u + (p / kLaneSegs) * kRowStep) * ldc;
-          if constexpr (OUT == 0) {
-            *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
-          } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
-                                                     static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
-          }
-          continue;
-        }
-        const int m = m_blk + wm + 32 * u + row;
-        const int n = n_blk + wn + 4 * seg;
-        if (m < M) {
-          out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
-          if (vec_out && n + 3 < N) {
-            if constexpr (OUT == 0) {
-              *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+        for (int p = 0; p < kPasses; ++p) {
+          float y[4];
+          finish(p, y);
+          const int c = 64 * p + lane;
+          const int m = m_blk + wm + 32 * u + c / kSegs;
+          const int n = n_blk + wn + 4 * (c % kSegs);
+          if (m < M) {
+            out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+            if (vec_out && n + 3 < N) {
+              store4(out, y);
             } else {
-              typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-              *reinterpret_cast<bf16x4*>(out) = bf16x4{static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1]),
-                                                       static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+              for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
             }
-          } else {
-            for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
           }
         }
       }
