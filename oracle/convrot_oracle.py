@@ -27,6 +27,11 @@ define, written from the formulas:
 * sglang PR 34581 summary page, section on implementation
   (kitchen_int8 layer routing): layers whose input width is not a multiple of
   the group size stay on the unquantised BF16 linear.
+* stable-diffusion.cpp PR "load ConvRot int4 and per-channel int8
+  safetensors", sections "Solution" and "The rotation": int4 weights are the
+  rotated weight quantised to [-7, 7] with one scale per output channel,
+  adjacent code pairs packed into one byte (W4A8 here: the int8 activation
+  codes against those weight codes, same accumulation and epilogue).
 
 Readings taken where the pages are silent (all listed in the design notes of
 the repository):
@@ -47,8 +52,10 @@ Pins (tests/test_oracle.py, CPU-only) tie every function here to something
 other than itself: the printed H4, exact orthogonality/symmetry, the base-4
 digit closed form, scipy's Sylvester matrix, rotation invariance in fp64,
 Parseval, a one-hot worked example whose output is known in closed form,
-brute-force integer loops, and torch's bf16 rounding.  Nothing here is
-"parity unpinned".
+brute-force integer loops, and torch's bf16 rounding; for int4, the page's
+code range, exact-tie rounding, a hand-packed nibble example, every byte
+decoded, and the page's correlation check of rotated against un-rotated
+weights.  Nothing here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -238,6 +245,84 @@ def pack(X: np.ndarray, G: int, kind: str = REGULAR,
     xr = rotate(X, G, kind, signs)
     q, s = quantize_rows(xr)
     return q, s, xr
+
+
+# ---------------------------------------------------------------------------
+# int4 weights (W4A8)
+# ---------------------------------------------------------------------------
+#
+# stable-diffusion.cpp PR "load ConvRot int4 and per-channel int8
+# safetensors", sections "Solution" and "The rotation": ConvRot int4 weights
+# are the rotated weight W R quantised to integers in [-7, 7] with one scale
+# per output channel, and the payload packs adjacent pairs of codes into one
+# byte.  Readings taken where the page is silent:
+#   * the int4 rule is the int8 rule with 7 in place of 127:
+#     s = max |x| / 7 (fp32 division), q = clamp(round_half_even(x / s), -7, 7);
+#   * a byte holds element 2j in its low nibble and element 2j + 1 in its high
+#     nibble, each as a 4-bit two's complement value (the page's "+8 bias
+#     lands inside Q4_0's nibble range" implies signed nibbles).
+
+QMAX4 = 7
+
+
+def quantize_rows_int4(Xr32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row absmax int4 quantisation of fp32 rows.
+
+        s[r]    = max_i |x[r, i]| / 7              (fp32 IEEE division)
+        q[r, i] = clamp(round(x[r, i] / s[r]), -7, 7)
+    round = half-to-even, the division in fp32; an all-zero row gets s = 0 and
+    q = 0.  Returns (q int8 [rows, K] with values in [-7, 7], s fp32 [rows]).
+    """
+    x = np.asarray(Xr32)
+    if x.dtype != np.float32:
+        raise TypeError("quantize_rows_int4 expects the fp32 rotated rows")
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    s = (amax / np.float32(QMAX4)).astype(np.float32)
+    q = np.zeros(x.shape, dtype=np.int8)
+    nz = s > 0
+    if np.any(nz):
+        v = (x[nz] / s[nz][:, None]).astype(np.float32)
+        q[nz] = np.clip(np.rint(v), -QMAX4, QMAX4).astype(np.int8)
+    return q, s
+
+
+def pack_nibbles(q4: np.ndarray) -> np.ndarray:
+    """Pack int4 codes [rows, K] (K even) into bytes [rows, K / 2]: byte j holds
+    code 2j in its low nibble and code 2j + 1 in its high nibble, each as 4-bit
+    two's complement."""
+    q = np.asarray(q4)
+    if q.dtype != np.int8 or q.ndim != 2 or q.shape[1] % 2:
+        raise ValueError("pack_nibbles expects int8 codes [rows, even K]")
+    if np.any(q < -8) or np.any(q > 7):
+        raise ValueError("codes outside the 4-bit range")
+    u = q.astype(np.int16) & 0xF
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles: bytes [rows, K / 2] -> int8 codes [rows, K]."""
+    b = np.asarray(b)
+    if b.dtype != np.uint8 or b.ndim != 2:
+        raise ValueError("unpack_nibbles expects uint8 [rows, bytes]")
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    q = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int8)
+    q[:, 0::2] = lo
+    q[:, 1::2] = hi
+    return q
+
+
+def pack_weight_int4(W: np.ndarray, G: int, kind: str = REGULAR,
+                     signs: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Offline int4 weight: rotate, quantise to [-7, 7] per output row, pack
+    nibble pairs.  Returns (bytes uint8 [N, K / 2], s fp32 [N], codes int8,
+    rotated fp32 rows).  A W4A8 linear is then int_gemm(Qx,
+    unpack_nibbles(bytes)) followed by the same epilogue as the int8 weight."""
+    wr = rotate(W, G, kind, signs)
+    q, s = quantize_rows_int4(wr)
+    return pack_nibbles(q), s, q, wr
 
 
 # ---------------------------------------------------------------------------

@@ -328,6 +328,85 @@ def check_routing():
         assert not O.routes_to_fallback(K, consts["randomized_block"])
 
 
+
+# -- int4 weights (W4A8) ------------------------------------------------------
+
+def check_qmax4_from_pages():
+    assert O.QMAX4 == page_constants()["qmax_int4"]
+
+
+def check_int4_ties_half_even():
+    # amax 7 gives s == 1 exactly, so the codes are rint of the values.
+    x = np.array([[7.0, 2.5, 3.5, -2.5, 0.5, -1.5, 6.5, -0.5]], dtype=np.float32)
+    q, s = O.quantize_rows_int4(x)
+    assert s[0] == 1.0
+    assert q[0].tolist() == [7, 2, 4, -2, 0, -2, 6, 0]
+
+
+def check_int4_invariants(seed: int = 11):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((6, 96)) * g.uniform(0.01, 50, (6, 1))).astype(np.float32)
+    x[2] = 0.0
+    q, s = O.quantize_rows_int4(x)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert s[2] == 0 and not np.any(q[2])
+    for r in (0, 1, 3, 4, 5):
+        assert np.max(np.abs(q[r])) == 7
+        assert abs(int(q[r, np.argmax(np.abs(x[r]))])) == 7
+        assert s[r] == np.float32(np.max(np.abs(x[r])) / np.float32(7))
+        err = np.abs(q[r].astype(np.float64) * float(s[r]) - x[r].astype(np.float64))
+        assert np.max(err) <= 0.5 * float(s[r]) * (1 + 1e-4)
+
+
+def check_nibble_worked_example():
+    # By hand: byte j = (code 2j mod 16) + 16 (code 2j+1 mod 16).
+    # (1, -1) -> 0x1 + 0xF0; (7, -7) -> 0x7 + 0x90; (0, 5) -> 0x50; (-3, 2) -> 0xD + 0x20
+    q = np.array([[1, -1, 7, -7, 0, 5, -3, 2]], dtype=np.int8)
+    b = O.pack_nibbles(q)
+    assert b.dtype == np.uint8 and b.shape == (1, 4)
+    assert b[0].tolist() == [0xF1, 0x97, 0x50, 0x2D]
+    assert np.array_equal(O.unpack_nibbles(b), q)
+
+
+def check_nibble_bytes_exhaustive():
+    # Every byte decodes to (low, high) nibble as 4-bit two's complement:
+    # a nibble n means n - 16 when its top bit is set.
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = O.unpack_nibbles(b)
+    for v in range(256):
+        lo = (v & 0xF) - 16 if v & 0x8 else v & 0xF
+        hi = (v >> 4) - 16 if v & 0x80 else v >> 4
+        assert (int(q[0, 2 * v]), int(q[0, 2 * v + 1])) == (lo, hi)
+    codes = np.array([[a, c] for a in range(-7, 8) for c in range(-7, 8)], dtype=np.int8)
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(codes)), codes)
+
+
+def check_int4_rotation_correlation(seed: int = 12):
+    """The PR's verification: dequantised int4 weights of W R correlate with
+    W only once un-rotated by R (R is symmetric and orthogonal).  Read as-is
+    the correlation is trace(R) / K = 2^-n for G = 4^n (1/16 at G = 256), the
+    page's 0.06."""
+    consts = page_constants()
+    g = np.random.default_rng(seed)
+    G = 256
+    W = g.standard_normal((96, 2 * G)).astype(np.float32)
+    b, s, q, _ = O.pack_weight_int4(W, G)
+    deq = O.unpack_nibbles(b).astype(np.float64) * s[:, None].astype(np.float64)
+    unrot = O.rotate64(deq, G)  # R is its own inverse
+    corr = lambda a, c: float(np.corrcoef(a.ravel(), c.ravel())[0, 1])
+    assert abs(corr(deq, W) - 1.0 / 16) < 0.03
+    assert abs(corr(deq, W) - consts["int4_corr_as_is"]) < 0.03
+    assert corr(unrot, W) >= consts["int4_corr_unrotated_min"]
+
+
+def check_w4a8_int_gemm_bruteforce(seed: int = 13):
+    g = np.random.default_rng(seed)
+    Qx = g.integers(-127, 128, (3, 32)).astype(np.int8)
+    Qw = g.integers(-7, 8, (5, 32)).astype(np.int8)
+    A = O.int_gemm(Qx, O.unpack_nibbles(O.pack_nibbles(Qw)))
+    assert np.array_equal(A, O.int_gemm_bruteforce(Qx, Qw))
+
+
 ALL_CHECKS = [
     ("r4_printed", check_r4_printed, ()),
     *[(f"regular_structure_G{G}", check_regular_structure, (G,)) for G in REGULAR_GS],
@@ -353,6 +432,13 @@ ALL_CHECKS = [
     ("bf16_round", check_bf16_round, ()),
     ("fallback_bruteforce", check_fallback_bruteforce, ()),
     ("routing", check_routing, ()),
+    ("qmax4_from_pages", check_qmax4_from_pages, ()),
+    ("int4_ties_half_even", check_int4_ties_half_even, ()),
+    ("int4_invariants", check_int4_invariants, ()),
+    ("nibble_worked_example", check_nibble_worked_example, ()),
+    ("nibble_bytes_exhaustive", check_nibble_bytes_exhaustive, ()),
+    ("int4_rotation_correlation", check_int4_rotation_correlation, ()),
+    ("w4a8_int_gemm_bruteforce", check_w4a8_int_gemm_bruteforce, ()),
 ]
 
 

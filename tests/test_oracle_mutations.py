@@ -134,6 +134,52 @@ def _sylvester_wrong_sign(G):
     return h
 
 
+
+_quantize_rows_int4 = O.quantize_rows_int4
+_pack_nibbles = O.pack_nibbles
+_unpack_nibbles = O.unpack_nibbles
+
+
+def _quant4_divides_by_8(x):
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(8)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    q[nz] = np.clip(np.rint(x[nz] / s[nz][:, None]), -7, 7).astype(np.int8)
+    return q, s
+
+
+def _quant4_half_away(x):
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(7)).astype(np.float32)
+    q = np.zeros(x.shape, np.int8)
+    nz = s > 0
+    v = x[nz] / s[nz][:, None]
+    q[nz] = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -7, 7).astype(np.int8)
+    return q, s
+
+
+def _nibbles_high_first(q4):
+    u = np.asarray(q4).astype(np.int16) & 0xF
+    return ((u[:, 0::2] << 4) | u[:, 1::2]).astype(np.uint8)
+
+
+def _unpack_unsigned(b):
+    q = np.empty((b.shape[0], 2 * b.shape[1]), np.int16)
+    q[:, 0::2] = b & 0xF
+    q[:, 1::2] = b >> 4
+    return q.astype(np.int8)
+
+
+def _unpack_swapped(b):
+    q = _unpack_nibbles(b)
+    out = q.copy()
+    out[:, 0::2], out[:, 1::2] = q[:, 1::2], q[:, 0::2]
+    return out
+
+
 MUTATIONS = {
     "h4_sign_flip": ("h4", _h4_sign_flip),
     "h4_unnormalised": ("h4", _h4_unnormalised),
@@ -152,6 +198,11 @@ MUTATIONS = {
     "gemm_wrong_operand_order": ("int_gemm", _gemm_untransposed),
     "gemm_float32_accumulation": ("int_gemm", _gemm_float32),
     "bf16_truncates": ("bf16_round", _bf16_truncate),
+    "quant4_divides_by_8": ("quantize_rows_int4", _quant4_divides_by_8),
+    "quant4_half_away": ("quantize_rows_int4", _quant4_half_away),
+    "nibbles_high_first": ("pack_nibbles", _nibbles_high_first),
+    "unpack_without_sign": ("unpack_nibbles", _unpack_unsigned),
+    "unpack_swapped_nibbles": ("unpack_nibbles", _unpack_swapped),
 }
 
 
