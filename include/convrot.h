@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 2
+#define CONVROT_ABI_VERSION 3
 
 typedef enum {
   CONVROT_OK = 0,
@@ -134,6 +134,25 @@ typedef struct {
   int64_t ld;
   convrot_rot rot;
 } convrot_packed;
+
+/* A packed int4 weight (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
+ * per-channel int8 safetensors", sections "Solution" and "The rotation"):
+ * the rotated weight W R quantised to codes in [-7, 7] with one fp32 scale
+ * per output row (row max / 7), two codes per byte.
+ *   q      [rows, ld] bytes, row-major; byte j of a row holds element 2j in
+ *          its low nibble and element 2j + 1 in its high nibble, each as
+ *          4-bit two's complement; ld >= K / 2 and ld % 8 == 0 (bytes; the rows
+ *          are read in 8-byte units), q 16-byte aligned
+ *   scale  [rows] fp32
+ * Both buffers are caller-owned device memory. */
+typedef struct {
+  uint8_t* q;
+  float* scale;
+  int64_t rows;
+  int64_t K;
+  int64_t ld;
+  convrot_rot rot;
+} convrot_packed_w4;
 
 /* Rotate and quantise activation rows ("Runtime activation quantization").
  *   X     [out->rows, ldx] of `xdt` (CONVROT_F32 or CONVROT_BF16), K = out->K
@@ -214,6 +233,47 @@ convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, in
  *   X [M, ldx] of `xdt`, Xrot [M, ldr] fp32. */
 convrot_status convrot_rotate(const void* X, convrot_dtype xdt, int64_t M, int64_t K, int64_t ldx,
                               convrot_rot rot, float* Xrot, int64_t ldr, void* stream);
+
+/* Rotate, quantise to int4 and pack weight rows offline: the transform of
+ * convrot_pack_weight, then s = row max / 7 and codes rounded to nearest
+ * even and clamped to [-7, 7], written as nibble pairs.  Arguments, checks
+ * and errors as convrot_pack_weight, with `out` an int4 descriptor. */
+convrot_status convrot_pack_weight_w4(const void* W, convrot_dtype wdt, int64_t ldw, const convrot_packed_w4* out,
+                                      void* stream);
+
+/* W4A8 linear: int8 activation codes against int4 weight codes,
+ *   Y[r, o] = fn(A[r, o] * act->scale[r] * w->scale[o] + bias[o]),
+ *   A = act->q (expanded w->q)^T, exact int32
+ * (the same accumulation and epilogue as convrot_linear and
+ * convrot_linear_act).
+ *   act        packed activation [M, K]; act->K == w->K and equal rotation
+ *              descriptors, else CONVROT_ERR_MISMATCH
+ *   w          packed int4 weight [N, K]
+ *   fn         CONVROT_ACT_NONE (plain linear; ydt may then also be
+ *              CONVROT_I32, the raw accumulator), CONVROT_ACT_GELU_ERF or
+ *              CONVROT_ACT_GELU_TANH
+ *   workspace  M <= 16: unused (may be NULL); the weight-streaming kernel
+ *              reads the nibbles (half the bytes of an int8 weight) and
+ *              expands them in registers.  M > 16: caller-owned device
+ *              memory of at least workspace_bytes >= N * K bytes, 16-byte
+ *              aligned, not shared with a concurrent call; the weight is
+ *              expanded there to int8 codes and the tiled kernel runs.  Too
+ *              small or NULL: CONVROT_ERR_INVALID_ARG. */
+convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed_w4* w, const float* bias,
+                                 convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Gated pair with int4 weights, Y = fn(G) * U as in convrot_linear_gated;
+ * fn must be CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH.  For M > 16 the
+ * workspace holds both expanded weights: workspace_bytes >= 2 * N * K. */
+convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_packed_w4* w_gate,
+                                       const float* b_gate, const convrot_packed_w4* w_up, const float* b_up,
+                                       convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                       int64_t workspace_bytes, void* stream);
+
+/* Expand int4 codes to int8 codes (for checking, or to keep an int8 copy):
+ *   dst [w->rows, ldd] int8, ldd >= w->K, ldd % 16 == 0, 16-byte aligned. */
+convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_t ldd, void* stream);
 
 /* Static description of a status code. */
 const char* convrot_status_string(convrot_status status);

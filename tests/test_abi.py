@@ -224,3 +224,62 @@ def test_python_layer_raises_on_error():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+# -- int4 weights (W4A8) -------------------------------------------------------
+
+def packed_w4(rows=64, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=0x40000, scale=0x50000):
+    return _lib.PackedW4(q, scale, rows, K, ld if ld is not None else K // 2, _lib.Rot(G, kind, signs))
+
+
+def test_w4_struct_layout():
+    assert ctypes.sizeof(_lib.PackedW4) == ctypes.sizeof(_lib.Packed) == 56
+    assert _lib.PackedW4.rot.offset == 40
+
+
+def w4_status(lib, act=None, w=None, fn=_lib.ACT_NONE, ydt=_lib.BF16, ws=None, ws_bytes=0):
+    act = act if act is not None else packed(rows=32)
+    w = w if w is not None else packed_w4()
+    return lib.convrot_linear_w4(ctypes.byref(act), ctypes.byref(w), None, fn, A16C, ydt, w.rows, ws, ws_bytes, None)
+
+
+def test_w4_pack_checks(lib):
+    def st(out, wdt=_lib.BF16, ldw=256):
+        return lib.convrot_pack_weight_w4(A16C, wdt, ldw, ctypes.byref(out), None)
+    assert st(packed_w4(ld=120)) == _lib.ERR_INVALID_ARG      # ld < K / 2
+    assert st(packed_w4(ld=132)) == _lib.ERR_ALIGN            # ld % 8
+    # an 8-byte pitch passes the descriptor checks (the dtype check after them fails)
+    assert st(packed_w4(ld=136), wdt=_lib.I32) == _lib.ERR_DTYPE
+    assert st(packed_w4(q=MIS)) == _lib.ERR_ALIGN
+    assert st(packed_w4(G=128)) == _lib.ERR_GROUP
+    assert st(packed_w4(), wdt=_lib.I32) == _lib.ERR_DTYPE
+    assert st(packed_w4(rows=0)) == _lib.OK
+
+
+def test_w4_linear_needs_a_workspace_above_16_rows(lib):
+    assert w4_status(lib) == _lib.ERR_INVALID_ARG
+    assert b"workspace" in lib.convrot_last_error()
+    assert w4_status(lib, ws=0x80000, ws_bytes=64 * 256 - 1) == _lib.ERR_INVALID_ARG
+    assert w4_status(lib, ws=0x80008, ws_bytes=64 * 256) == _lib.ERR_ALIGN
+
+
+def test_w4_linear_checks(lib):
+    assert w4_status(lib, w=packed_w4(K=512, ld=256)) == _lib.ERR_MISMATCH
+    assert w4_status(lib, w=packed_w4(G=64)) == _lib.ERR_MISMATCH
+    assert w4_status(lib, fn=7) == _lib.ERR_INVALID_ARG
+    assert w4_status(lib, fn=_lib.ACT_GELU_ERF, ydt=_lib.I32) == _lib.ERR_DTYPE
+    assert w4_status(lib, act=packed(rows=0)) == _lib.OK
+    g = packed_w4()
+    u = packed_w4(rows=32, q=0x90000, scale=0xA0000)
+    act = packed(rows=8)
+    assert lib.convrot_linear_w4_gated(ctypes.byref(act), ctypes.byref(g), None, ctypes.byref(u), None,
+                                       _lib.ACT_GELU_TANH, A16C, _lib.BF16, 64, None, 0, None) == _lib.ERR_MISMATCH
+    assert lib.convrot_linear_w4_gated(ctypes.byref(act), ctypes.byref(g), None, ctypes.byref(g), None,
+                                       _lib.ACT_NONE, A16C, _lib.BF16, 64, None, 0, None) == _lib.ERR_INVALID_ARG
+
+
+def test_w4_unpack_checks(lib):
+    w = packed_w4()
+    assert lib.convrot_unpack_w4(ctypes.byref(w), A16C, 128, None) == _lib.ERR_INVALID_ARG  # ldd < K
+    assert lib.convrot_unpack_w4(ctypes.byref(w), MIS, 256, None) == _lib.ERR_ALIGN
+    assert lib.convrot_unpack_w4(ctypes.byref(packed_w4(rows=0)), A16C, 256, None) == _lib.OK

@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -31,6 +31,10 @@ EXPORTED = (
     "convrot_linear_gated",
     "convrot_linear_bf16",
     "convrot_rotate",
+    "convrot_pack_weight_w4",
+    "convrot_linear_w4",
+    "convrot_linear_w4_gated",
+    "convrot_unpack_w4",
     "convrot_status_string",
     "convrot_last_error",
     "convrot_abi_version",
@@ -42,6 +46,17 @@ class Rot(ctypes.Structure):
 
 
 class Packed(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("ld", ctypes.c_int64),
+        ("rot", Rot),
+    ]
+
+
+class PackedW4(ctypes.Structure):
     _fields_ = [
         ("q", ctypes.c_void_p),
         ("scale", ctypes.c_void_p),
@@ -79,6 +94,15 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_linear_bf16.restype = c_int
     lib.convrot_rotate.argtypes = [vp, c_int, c_i64, c_i64, c_i64, Rot, vp, c_i64, vp]
     lib.convrot_rotate.restype = c_int
+    P4 = ctypes.POINTER(PackedW4)
+    lib.convrot_pack_weight_w4.argtypes = [vp, c_int, c_i64, P4, vp]
+    lib.convrot_pack_weight_w4.restype = c_int
+    lib.convrot_linear_w4.argtypes = [P, P4, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
+    lib.convrot_linear_w4.restype = c_int
+    lib.convrot_linear_w4_gated.argtypes = [P, P4, vp, P4, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
+    lib.convrot_linear_w4_gated.restype = c_int
+    lib.convrot_unpack_w4.argtypes = [P4, vp, c_i64, vp]
+    lib.convrot_unpack_w4.restype = c_int
     lib.convrot_status_string.argtypes = [c_int]
     lib.convrot_status_string.restype = ctypes.c_char_p
     lib.convrot_last_error.argtypes = []

@@ -3,7 +3,9 @@
 Every function marshals torch CUDA tensors (device memory) and the current
 torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
 kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
-``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``.
+``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``,
+and for int4 weights (W4A8) ``pack_weight_w4``, ``linear_w4``,
+``linear_w4_gated``, ``unpack_w4``.
 """
 
 from __future__ import annotations
@@ -204,4 +206,110 @@ def rotate(x: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.
     lib = _lib.load()
     _lib.check(lib.convrot_rotate(x.data_ptr(), _DT[x.dtype], M, K, _ld(x), _rot(group, kind, signs),
                                   out.data_ptr(), _ld(out), _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# int4 weights (W4A8)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PackedW4:
+    """int4 weight: nibble pairs (element 2j in the low nibble of byte j),
+    one fp32 scale per output row (row max / 7), and the rotation."""
+    q: torch.Tensor          # [rows, K / 2] uint8 (row stride may exceed K / 2)
+    scale: torch.Tensor      # [rows] fp32
+    K: int
+    group: int
+    kind: str = REGULAR
+    signs: torch.Tensor | None = None
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    def descriptor(self) -> _lib.PackedW4:
+        if self.q.dtype != torch.uint8 or self.q.shape[1] * 2 != self.K:
+            raise ValueError("q must be uint8 [rows, K / 2]")
+        return _lib.PackedW4(self.q.data_ptr(), self.scale.data_ptr(), self.q.shape[0], self.K, _ld(self.q),
+                             _rot(self.group, self.kind, self.signs))
+
+
+def pack_weight_w4(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
+                   out: PackedW4 | None = None) -> PackedW4:
+    """Rotate, quantise to int4 and pack weight rows offline (convrot_pack_weight_w4)."""
+    _need_cuda(w, "w")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    rows, K = w.shape
+    _check_signs(signs, K, kind)
+    if out is None:
+        out = PackedW4(torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device),
+                       torch.empty((rows,), dtype=torch.float32, device=w.device), K, group, kind, signs)
+    desc = out.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_pack_weight_w4(w.data_ptr(), _DT[w.dtype], _ld(w), ctypes.byref(desc), _stream(w.device)))
+    return out
+
+
+def _w4_workspace(M: int, N: int, K: int, sets: int, device, workspace):
+    if M <= 16:
+        return workspace
+    need = sets * N * K
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.int8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return workspace
+
+
+def linear_w4(act_in: Packed, w: PackedW4, bias: torch.Tensor | None = None, act: str | None = None,
+              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8 linear Y = act(A * s_x * s_w + b), act None for the plain linear
+    (convrot_linear_w4).  For more than 16 rows the expanded int8 weight goes
+    to ``workspace`` (allocated here when not given)."""
+    M, N = act_in.rows, w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=act_in.q.device)
+    if out.dtype not in _DT or (act is not None and out.dtype == torch.int32):
+        raise ValueError("output must be float32 or bfloat16 (or int32 without an activation)")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 vector of length N")
+    ws = _w4_workspace(M, N, w.K, 1, out.device, workspace)
+    a, b = act_in.descriptor(), w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_w4(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
+                                     _lib.ACT_NONE if act is None else _act_code(act), out.data_ptr(), _DT[out.dtype],
+                                     _ld(out), ws.data_ptr() if ws is not None else None,
+                                     ws.numel() * ws.element_size() if ws is not None else 0, _stream(out.device)))
+    return out
+
+
+def linear_w4_gated(act_in: Packed, w_gate: PackedW4, w_up: PackedW4, b_gate: torch.Tensor | None = None,
+                    b_up: torch.Tensor | None = None, act: str = GELU_TANH, out_dtype: torch.dtype = torch.bfloat16,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = act(gate) * up with int4 weights sharing one packed activation
+    (convrot_linear_w4_gated)."""
+    out = _out_and_bias(act_in.rows, w_gate.rows, act_in.q.device, out, out_dtype, b_gate)
+    if b_up is not None and (b_up.dtype != torch.float32 or b_up.numel() != w_up.rows or not b_up.is_contiguous()):
+        raise ValueError("b_up must be a contiguous float32 vector of length N")
+    ws = _w4_workspace(act_in.rows, w_gate.rows, w_gate.K, 2, out.device, workspace)
+    a, g, u = act_in.descriptor(), w_gate.descriptor(), w_up.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_w4_gated(
+        ctypes.byref(a), ctypes.byref(g), b_gate.data_ptr() if b_gate is not None else None, ctypes.byref(u),
+        b_up.data_ptr() if b_up is not None else None, _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out),
+        ws.data_ptr() if ws is not None else None, ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(out.device)))
+    return out
+
+
+def unpack_w4(w: PackedW4, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 codes [rows, K] of an int4 weight (convrot_unpack_w4)."""
+    if out is None:
+        out = torch.empty((w.rows, w.K), dtype=torch.int8, device=w.q.device)
+    desc = w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_unpack_w4(ctypes.byref(desc), out.data_ptr(), _ld(out), _stream(out.device)))
     return out

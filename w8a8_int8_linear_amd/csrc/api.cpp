@@ -166,6 +166,45 @@ convrot_status check_linear(const char* fn, const convrot_packed* act, const con
   return CONVROT_OK;
 }
 
+convrot_status check_packed_w4(const char* name, const convrot_packed_w4* p, int* log2G) {
+  if (p == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+  convrot_status st = check_k(p->K, kMaxK);
+  if (st != CONVROT_OK) return st;
+  st = check_rot(p->rot, p->K, log2G);
+  if (st != CONVROT_OK) return st;
+  // Nibble rows are read and written in 8-byte units: base 16-byte aligned,
+  // row pitch a multiple of 8 bytes (K / 2 always is).
+  if (p->rows > 0 && p->q == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s is NULL", name);
+  if (p->rows < 0 || p->rows > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad row count", name);
+  if (p->ld < p->K / 2)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: leading dimension %lld < K / 2 = %lld bytes", name,
+                static_cast<long long>(p->ld), static_cast<long long>(p->K / 2));
+  if (!aligned16(p->q)) return fail(CONVROT_ERR_ALIGN, "%s must be 16-byte aligned", name);
+  if (p->ld % 8 != 0) return fail(CONVROT_ERR_ALIGN, "%s: leading dimension must be a multiple of 8 bytes", name);
+  if (p->rows > 0 && p->scale == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s scale is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(p->scale) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "%s scale must be 4-byte aligned", name);
+  if (p->ld > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: leading dimension exceeds %lld bytes", name,
+                static_cast<long long>(kMaxLdBytes));
+  return CONVROT_OK;
+}
+
+// An int4 weight seen through the int8 descriptor checks of check_linear:
+// the same K, rotation and row count (the code pointer is only compared).
+convrot_packed as_int8_view(const convrot_packed_w4& w) {
+  return convrot_packed{reinterpret_cast<int8_t*>(w.q), w.scale, w.rows, w.K, w.K, w.rot};
+}
+
+// M > 16 with int4 weights: the expanded codes go to the caller's workspace.
+convrot_status check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
+  if (ws == nullptr || ws_bytes < need)
+    return fail(CONVROT_ERR_INVALID_ARG, "this call needs a workspace of %lld bytes (got %lld)",
+                static_cast<long long>(need), static_cast<long long>(ws == nullptr ? 0 : ws_bytes));
+  if (!aligned16(ws)) return fail(CONVROT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return CONVROT_OK;
+}
+
 convrot_status check_act(convrot_act fn) {
   if (fn != CONVROT_ACT_GELU_ERF && fn != CONVROT_ACT_GELU_TANH)
     return fail(CONVROT_ERR_INVALID_ARG, "activation must be CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH");
@@ -295,6 +334,117 @@ convrot_status convrot_rotate(const void* X, convrot_dtype xdt, int64_t M, int64
                                                  static_cast<convrot::RotKind>(rot.kind), rot.signs, nullptr, 0,
                                                  nullptr, Xrot, ldr, static_cast<hipStream_t>(stream));
   return from_hip(e, "convrot_rotate");
+}
+
+convrot_status convrot_pack_weight_w4(const void* W, convrot_dtype wdt, int64_t ldw, const convrot_packed_w4* out,
+                                      void* stream) {
+  const char* what = "convrot_pack_weight_w4";
+  int log2G = 0;
+  if (out == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: output descriptor is NULL", what);
+  convrot_status st = check_k(out->K, kMaxPackK);
+  if (st != CONVROT_OK) return st;
+  st = check_packed_w4("packed output", out, &log2G);
+  if (st != CONVROT_OK) return st;
+  if (wdt != CONVROT_F32 && wdt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
+  st = check_matrix("input", W, out->rows, out->K, ldw, elt_size(wdt));
+  if (st != CONVROT_OK) return st;
+  if (out->rows == 0) return ok();
+  const hipError_t e = convrot::launch_pack_rows_w4(W, static_cast<convrot::Elt>(wdt), out->rows, out->K, ldw, log2G,
+                                                    static_cast<convrot::RotKind>(out->rot.kind), out->rot.signs,
+                                                    out->q, out->ld, out->scale, static_cast<hipStream_t>(stream));
+  return from_hip(e, what);
+}
+
+convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed_w4* w, const float* bias,
+                                 convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  const char* what = "convrot_linear_w4";
+  if (fn != CONVROT_ACT_NONE) {
+    convrot_status st = check_act(fn);
+    if (st != CONVROT_OK) return st;
+  }
+  int lg = 0;
+  convrot_status st = check_packed_w4("weight", w, &lg);
+  if (st != CONVROT_OK) return st;
+  const convrot_packed wv = as_int8_view(*w);
+  st = check_linear(what, act, &wv, bias, Y, ydt, ldy, fn == CONVROT_ACT_NONE);
+  if (st != CONVROT_OK) return st;
+  const int64_t M = act->rows, N = w->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const auto a = static_cast<convrot::Act>(fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= convrot::kGemvMaxRows) {
+    return from_hip(convrot::launch_gemv_w4(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
+                                            out, ldy, s),
+                    what);
+  }
+  st = check_workspace(workspace, workspace_bytes, N * K);
+  if (st != CONVROT_OK) return st;
+  int8_t* w8 = static_cast<int8_t*>(workspace);
+  hipError_t e = convrot::launch_unpack_w4(w->q, w->ld, N, K, w8, K, s);
+  if (e == hipSuccess) {
+    e = fn == CONVROT_ACT_NONE
+            ? convrot::launch_gemm_i8(act->q, act->ld, w8, K, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s)
+            : convrot::launch_gemm_i8_act(act->q, act->ld, w8, K, act->scale, w->scale, bias, a, M, N, K, Y, out,
+                                          ldy, s);
+  }
+  return from_hip(e, what);
+}
+
+convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_packed_w4* w_gate,
+                                       const float* b_gate, const convrot_packed_w4* w_up, const float* b_up,
+                                       convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                       int64_t workspace_bytes, void* stream) {
+  const char* what = "convrot_linear_w4_gated";
+  convrot_status st = check_act(fn);
+  if (st != CONVROT_OK) return st;
+  int lg = 0;
+  st = check_packed_w4("gate weight", w_gate, &lg);
+  if (st != CONVROT_OK) return st;
+  st = check_packed_w4("up weight", w_up, &lg);
+  if (st != CONVROT_OK) return st;
+  const convrot_packed gv = as_int8_view(*w_gate), uv = as_int8_view(*w_up);
+  st = check_linear(what, act, &gv, b_gate, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  st = check_linear(what, act, &uv, b_up, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  if (w_gate->rows != w_up->rows)
+    return fail(CONVROT_ERR_MISMATCH, "gate has %lld output rows but up has %lld",
+                static_cast<long long>(w_gate->rows), static_cast<long long>(w_up->rows));
+  const int64_t M = act->rows, N = w_gate->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const auto a = static_cast<convrot::Act>(fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= convrot::kGemvMaxRows) {
+    return from_hip(convrot::launch_gemv_w4_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate,
+                                                  w_up->q, w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y,
+                                                  out, ldy, s),
+                    what);
+  }
+  st = check_workspace(workspace, workspace_bytes, 2 * N * K);
+  if (st != CONVROT_OK) return st;
+  int8_t* g8 = static_cast<int8_t*>(workspace);
+  int8_t* u8 = g8 + N * K;
+  hipError_t e = convrot::launch_unpack_w4(w_gate->q, w_gate->ld, N, K, g8, K, s);
+  if (e == hipSuccess) e = convrot::launch_unpack_w4(w_up->q, w_up->ld, N, K, u8, K, s);
+  if (e == hipSuccess)
+    e = convrot::launch_gemm_i8_gated(act->q, act->ld, g8, K, w_gate->scale, b_gate, u8, K, w_up->scale, b_up,
+                                      act->scale, a, M, N, K, Y, out, ldy, s);
+  return from_hip(e, what);
+}
+
+convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_t ldd, void* stream) {
+  int lg = 0;
+  convrot_status st = check_packed_w4("weight", w, &lg);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("dst", dst, w->rows, w->K, ldd, 1);
+  if (st != CONVROT_OK) return st;
+  if (w->rows == 0) return ok();
+  return from_hip(convrot::launch_unpack_w4(w->q, w->ld, w->rows, w->K, dst, ldd, static_cast<hipStream_t>(stream)),
+                  "convrot_unpack_w4");
 }
 
 const char* convrot_status_string(convrot_status status) {

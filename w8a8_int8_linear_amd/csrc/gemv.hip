@@ -35,15 +35,23 @@
 //    device-scope fences, which on this multi-XCD GPU write back and
 //    invalidate a whole L2 each.  Same result bits as the unsplit kernel in
 //    int8 mode.
+//  * int4 weights (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
+//    per-channel int8 safetensors", sections "Solution" and "The rotation":
+//    codes in [-7, 7], one scale per output row, adjacent pairs in a byte):
+//    a lane loads the 8 bytes holding its 16 codes of a step, half the int8
+//    stream, and expands them in registers to the 16 int8 codes the same
+//    MFMA takes; the accumulator and epilogue are unchanged.
 // The byte-to-k assignment of a lane is the same for both operands, so each
 // MFMA pairs matching k.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "epilogue.h"
 #include "launchers.h"
+#include "w4_codec.h"
 
 namespace convrot {
 namespace {
@@ -140,14 +148,17 @@ __device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, 
   }
 }
 
-// A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes]; kbytes =
-// K * element size (a multiple of 16); per = steps per wave.
-template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false>
+// A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes] (int4
+// mode: K / 2 bytes of nibble pairs per row); kbytes = K * element size of A
+// (a multiple of 16); per = steps per wave.
+template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false, bool W4 = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
     int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
+  static_assert(!W4 || I8, "int4 weights pair with int8 activations");
   using Acc = typename Mma<I8>::Acc;
+  constexpr int kWDiv = W4 ? 2 : 1;  // activation bytes per weight byte
   constexpr int kSets = GATED ? 2 : 1;  // weight row sets streamed (gate, up)
   __shared__ Acc partial[kSets][WAVES > 1 ? WAVES - 1 : 1][64];
   const int tid = threadIdx.x;
@@ -158,8 +169,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int ch = lane >> 4;
 
   const uint8_t* wrow[kSets];
-  wrow[0] = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * 16;
-  if constexpr (GATED) wrow[kSets - 1] = epi.B2 + static_cast<int64_t>(min(n0 + row, N - 1)) * epi.ldb2 + ch * 16;
+  wrow[0] = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * (16 / kWDiv);
+  if constexpr (GATED)
+    wrow[kSets - 1] = epi.B2 + static_cast<int64_t>(min(n0 + row, N - 1)) * epi.ldb2 + ch * (16 / kWDiv);
   const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
 
   const int nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
@@ -172,25 +184,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   Acc acc[kSets];
 #pragma unroll
   for (int t = 0; t < kSets; ++t) acc[t] = Acc{0, 0, 0, 0};
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  using WLoad = typename std::conditional<W4, u32x2, i32x4>::type;
   for (int s0 = s_begin; s0 < s_end; s0 += kSteps) {
-    i32x4 w[kSets][kSteps], x[kSteps];
+    WLoad w[kSets][kSteps];
+    i32x4 x[kSteps];
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) w[t][u] = i32x4{0, 0, 0, 0};
+      for (int t = 0; t < kSets; ++t) w[t][u] = WLoad{};
       x[u] = i32x4{0, 0, 0, 0};
       const int byte = (s0 + u) * kStepBytes;
       if (s0 + u < s_end && byte + ch * 16 < kbytes) {
 #pragma unroll
         for (int t = 0; t < kSets; ++t)
-          w[t][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t] + byte));
+          w[t][u] = __builtin_nontemporal_load(reinterpret_cast<const WLoad*>(wrow[t] + byte / kWDiv));
         x[u] = *reinterpret_cast<const i32x4*>(xrow + byte);
       }
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u)
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) acc[t] = Mma<I8>::run(w[t][u], x[u], acc[t]);
+      for (int t = 0; t < kSets; ++t) {
+        if constexpr (W4) {
+          acc[t] = Mma<I8>::run(expand_w4(w[t][u].x, w[t][u].y), x[u], acc[t]);
+        } else {
+          acc[t] = Mma<I8>::run(w[t][u], x[u], acc[t]);
+        }
+      }
   }
 
   if (WAVES > 1) {
@@ -273,21 +294,21 @@ inline int gemv_num_cus() {
   return cus;
 }
 
-template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT>
+template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
                   const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
                   hipStream_t stream) {
   switch (waves) {
     case 4:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT>), grid, dim3(256), 0, stream, a, lda, b, ldb,
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4>), grid, dim3(256), 0, stream, a, lda, b, ldb,
                          epi, m, n, kb, per, C, ldc, sp);
       break;
     case 8:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT>), grid, dim3(512), 0, stream, a, lda, b, ldb,
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4>), grid, dim3(512), 0, stream, a, lda, b, ldb,
                          epi, m, n, kb, per, C, ldc, sp);
       break;
     default:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED, SPLIT>), grid, dim3(1024), 0, stream, a, lda, b,
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED, SPLIT, W4>), grid, dim3(1024), 0, stream, a, lda, b,
                          ldb, epi, m, n, kb, per, C, ldc, sp);
       break;
   }
@@ -302,7 +323,7 @@ inline int waves_for(int64_t steps) {
   return 16;
 }
 
-template <bool I8, int OUT, int ACT = 0, bool GATED = false>
+template <bool I8, int OUT, int ACT = 0, bool GATED = false, bool W4 = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
                       int64_t N, int64_t kbytes, void* C, int64_t ldc, hipStream_t stream) {
   constexpr int kSets = GATED ? 2 : 1;
@@ -328,7 +349,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const int waves = waves_for(steps);
     const int per = static_cast<int>((steps + waves - 1) / waves);
     const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(steps)};
-    launch_waves<I8, OUT, ACT, GATED, true>(waves, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splits)),
+    launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splits)),
                                            a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -338,7 +359,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   }
   const int waves = waves_for(nsteps);
   const int per = static_cast<int>((nsteps + waves - 1) / waves);
-  launch_waves<I8, OUT, ACT, GATED, false>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n, kb,
+  launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n, kb,
                                           per, C, ldc, SplitArgs{nullptr, 1, 0}, stream);
   return hipGetLastError();
 }
@@ -382,6 +403,40 @@ hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, 
                : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
   return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
              : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
+}
+
+hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
+                          const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
+                          Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
+  if (act == Act::None) {
+    switch (out) {
+      case Elt::F32: return launch_out<true, 0, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+      case Elt::BF16: return launch_out<true, 1, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+      default: return launch_out<true, 2, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    }
+  }
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out<true, 0, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
+               : launch_out<true, 1, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+  return f32 ? launch_out<true, 0, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
+             : launch_out<true, 1, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+}
+
+hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
+                                const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
+                                const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
+                                void* C, Elt out, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const EpiArgs epi{sa, sbg, biasg, Bu, ldbu, sbu, biasu};
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out<true, 0, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
+               : launch_out<true, 1, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
+  return f32 ? launch_out<true, 0, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
+             : launch_out<true, 1, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
 }
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,

@@ -20,6 +20,16 @@ hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int
                             int8_t* q, int64_t ldq, float* scale,
                             float* xrot, int64_t ldr, hipStream_t stream);
 
+// The same kernel in int4 weight mode: codes clamped to [-7, 7], scale =
+// row max / 7, written as nibble pairs (K / 2 bytes per row of q).
+hipError_t launch_pack_rows_w4(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
+                               RotKind kind, const int8_t* signs, uint8_t* q, int64_t ldq, float* scale,
+                               hipStream_t stream);
+
+// int4 nibble pairs [rows, ldq bytes] -> int8 codes [rows, ldd].
+hipError_t launch_unpack_w4(const uint8_t* q, int64_t ldq, int64_t rows, int64_t K, int8_t* dst, int64_t ldd,
+                            hipStream_t stream);
+
 // Tiled matrix-core GEMM, C = A B^T with both operands K-contiguous.
 //   int8 mode : A = Qx [M, K] int8, B = Qw [N, K] int8, exact int32
 //               accumulation, epilogue acc * sa[m] * sb[n] + bias[n]
@@ -73,5 +83,16 @@ hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, 
                                 const float* sbu, const float* biasu, const float* sa, Act act,
                                 int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
                                 hipStream_t stream);
+
+// Small-M kernels with int4 weights (nibble pairs, ldb in bytes): the same
+// accumulators as the int8 kernels on the expanded codes.  `act` may be
+// None (then `out` may be I32) for the plain linear.
+hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
+                          const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
+                          Elt out, int64_t ldc, hipStream_t stream);
+hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
+                                const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
+                                const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
+                                void* C, Elt out, int64_t ldc, hipStream_t stream);
 
 }  // namespace convrot

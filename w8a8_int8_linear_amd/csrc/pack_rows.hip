@@ -9,7 +9,11 @@
 // clamped to [-127, 127].  The randomized kind ("Add experimental W8A8 MatMul
 // with optional QuaRot-style rotation", section "Rotation method") multiplies
 // each block by fixed +-1 signs, applies the natural-order Walsh-Hadamard
-// transform and scales by 1/sqrt(G).
+// transform and scales by 1/sqrt(G).  The int4 weight mode
+// (stable-diffusion.cpp PR "load ConvRot int4 and per-channel int8
+// safetensors", sections "Solution" and "The rotation") takes the largest
+// rotated magnitude over 7, clamps to [-7, 7] and packs adjacent codes into
+// the low and high nibble of one byte.
 //
 // Design (one workgroup per row, the whole row held in VGPRs):
 //  * Each thread owns 1, 2 or 4 chunks of 16 contiguous features (two
@@ -194,6 +198,17 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, f
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
+// Sixteen codes of one chunk as int4 nibble pairs (element 2j in the low,
+// 2j + 1 in the high nibble of byte j): the even and the odd codes are each
+// gathered into a dword of bytes by quant4, and one bit-field insert merges
+// their low nibbles.  |code| <= 7, so the low nibble of a code's byte is its
+// 4-bit two's complement.
+__device__ __forceinline__ uint32_t quant8_nibbles(const float* v, float inv) {
+  const uint32_t even = quant4(v[0], v[2], v[4], v[6], inv);
+  const uint32_t odd = quant4(v[1], v[3], v[5], v[7], inv);
+  return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
+}
+
 // Maximum over the wavefront of non-negative values.  For those the IEEE
 // bit patterns order like unsigned integers, so the reduction runs on the
 // bits (an unsigned max takes its lane exchange as a DPP operand and needs
@@ -212,7 +227,9 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t m) {
   return m;
 }
 
-template <typename InT, int LOG2G, bool RAND, bool QUANT, int CPT>
+// QMODE: 0 rotation only (fp32 rows to xrot), 1 int8 codes, 2 int4 codes
+// (nibble pairs, K / 2 bytes per row, scale = max / 7).
+template <typename InT, int LOG2G, bool RAND, int QMODE, int CPT>
 __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     const InT* __restrict__ X, int64_t ldx, int K, const int8_t* __restrict__ signs,
     int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
@@ -318,7 +335,7 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
   const float norm = RAND ? (1.0f / __builtin_sqrtf(static_cast<float>(G)))
                           : __builtin_ldexpf(1.0f, -(LOG2G / 2));
 
-  if constexpr (!QUANT) {
+  if constexpr (QMODE == 0) {
     const __amdgpu_buffer_rsrc_t rr = row_rsrc(xrot + static_cast<int64_t>(row) * ldr, 4 * K);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -349,25 +366,36 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     }
     const float amax_u = as_f(amax_bits);
 
-    // Unnormalised codes: y_u * (127 / amax_u) == y / s exactly up to the
+    // Unnormalised codes: y_u * (qmax / amax_u) == y / s exactly up to the
     // rounding of the reciprocal; all-zero rows give inv = 0 and codes 0.
-    const float inv = amax_u > 0.f ? 127.0f / amax_u : 0.f;
-    if (tid == 0) scale[row] = (amax_u * norm) / 127.0f;
+    constexpr float kQMax = QMODE == 2 ? 7.0f : 127.0f;
+    const float inv = amax_u > 0.f ? kQMax / amax_u : 0.f;
+    if (tid == 0) scale[row] = (amax_u * norm) / kQMax;
 
-    const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K);
+    if constexpr (QMODE == 1) {
+      const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      u32x4 o;
-      o.x = quant4(v[c][0], v[c][1], v[c][2], v[c][3], inv);
-      o.y = quant4(v[c][4], v[c][5], v[c][6], v[c][7], inv);
-      o.z = quant4(v[c][8], v[c][9], v[c][10], v[c][11], inv);
-      o.w = quant4(v[c][12], v[c][13], v[c][14], v[c][15], inv);
-      __builtin_amdgcn_raw_buffer_store_b128(o, qr, off[c], 0, kNonTemporal);
+      for (int c = 0; c < CPT; ++c) {
+        u32x4 o;
+        o.x = quant4(v[c][0], v[c][1], v[c][2], v[c][3], inv);
+        o.y = quant4(v[c][4], v[c][5], v[c][6], v[c][7], inv);
+        o.z = quant4(v[c][8], v[c][9], v[c][10], v[c][11], inv);
+        o.w = quant4(v[c][12], v[c][13], v[c][14], v[c][15], inv);
+        __builtin_amdgcn_raw_buffer_store_b128(o, qr, off[c], 0, kNonTemporal);
+      }
+    } else {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K / 2);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const u32x2 o = {quant8_nibbles(&v[c][0], inv), quant8_nibbles(&v[c][8], inv)};
+        __builtin_amdgcn_raw_buffer_store_b64(o, qr, off[c] / 2, 0, kNonTemporal);
+      }
     }
   }
 }
 
-template <typename InT, int LOG2G, bool RAND, bool QUANT>
+template <typename InT, int LOG2G, bool RAND, int QMODE>
 hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, const int8_t* signs,
                         int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
                         hipStream_t stream) {
@@ -386,15 +414,15 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
   const InT* x = static_cast<const InT*>(X);
   switch (cpt) {
     case 1:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 1>), grid, block, 0, stream, x, ldx,
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 1>), grid, block, 0, stream, x, ldx,
                          static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
       break;
     case 2:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 2>), grid, block, 0, stream, x, ldx,
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 2>), grid, block, 0, stream, x, ldx,
                          static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
       break;
     case 4:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QUANT, 4>), grid, block, 0, stream, x, ldx,
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 4>), grid, block, 0, stream, x, ldx,
                          static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
       break;
     default:
@@ -403,13 +431,13 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
   return hipGetLastError();
 }
 
-template <typename InT, bool RAND, bool QUANT>
+template <typename InT, bool RAND, int QMODE>
 hipError_t dispatch_group(int log2G, const void* X, int64_t rows, int64_t K, int64_t ldx,
                           const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot,
                           int64_t ldr, hipStream_t stream) {
 #define CONVROT_PACK_CASE(LG)                                                                   \
   case LG:                                                                                      \
-    return dispatch_cpt<InT, LG, RAND, QUANT>(X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, \
+    return dispatch_cpt<InT, LG, RAND, QMODE>(X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, \
                                               stream);
   if constexpr (RAND) {
     switch (log2G) {
@@ -435,16 +463,22 @@ hipError_t dispatch_group(int log2G, const void* X, int64_t rows, int64_t K, int
 #undef CONVROT_PACK_CASE
 }
 
-template <typename InT>
-hipError_t dispatch_kind(int log2G, RotKind kind, bool quant, const void* X, int64_t rows, int64_t K,
-                         int64_t ldx, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
-                         float* xrot, int64_t ldr, hipStream_t stream) {
-  if (kind == RotKind::Randomized) {
-    return quant ? dispatch_group<InT, true, true>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream)
-                 : dispatch_group<InT, true, false>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
-  }
-  return quant ? dispatch_group<InT, false, true>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream)
-               : dispatch_group<InT, false, false>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+template <typename InT, int QMODE>
+hipError_t dispatch_kind(int log2G, RotKind kind, const void* X, int64_t rows, int64_t K, int64_t ldx,
+                         const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
+                         hipStream_t stream) {
+  if (kind == RotKind::Randomized)
+    return dispatch_group<InT, true, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+  return dispatch_group<InT, false, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+}
+
+template <int QMODE>
+hipError_t dispatch_input(Elt xdt, int log2G, RotKind kind, const void* X, int64_t rows, int64_t K, int64_t ldx,
+                          const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
+                          hipStream_t stream) {
+  if (xdt == Elt::BF16)
+    return dispatch_kind<uint16_t, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+  return dispatch_kind<float, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
 }
 
 }  // namespace
@@ -453,11 +487,17 @@ hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int
                             RotKind kind, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
                             float* xrot, int64_t ldr, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const bool quant = q != nullptr;
-  if (xdt == Elt::BF16) {
-    return dispatch_kind<uint16_t>(log2G, kind, quant, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
-  }
-  return dispatch_kind<float>(log2G, kind, quant, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+  if (q != nullptr)
+    return dispatch_input<1>(xdt, log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, nullptr, 0, stream);
+  return dispatch_input<0>(xdt, log2G, kind, X, rows, K, ldx, signs, nullptr, 0, scale, xrot, ldr, stream);
+}
+
+hipError_t launch_pack_rows_w4(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
+                               RotKind kind, const int8_t* signs, uint8_t* q, int64_t ldq, float* scale,
+                               hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  return dispatch_input<2>(xdt, log2G, kind, X, rows, K, ldx, signs, reinterpret_cast<int8_t*>(q), ldq, scale,
+                           nullptr, 0, stream);
 }
 
 }  // namespace convrot

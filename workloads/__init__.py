@@ -195,3 +195,15 @@ def random_codes(shape, seed: int) -> np.ndarray:
         flat[0] = 127
         flat[-1] = -127
     return q
+
+
+def random_codes4(shape, seed: int) -> np.ndarray:
+    """Seeded int4 codes in [-7, 7] (held as int8), with both extremes forced
+    present."""
+    g = np.random.default_rng(seed)
+    q = g.integers(-7, 8, size=shape).astype(np.int8)
+    if q.size >= 2:
+        flat = q.reshape(-1)
+        flat[0] = 7
+        flat[-1] = -7
+    return q
