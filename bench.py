@@ -21,7 +21,8 @@ Workloads (``--workload``):
                  [6912, 1152] share one pack, h = gelu_tanh(gate) * up feeds
                  W_down [1152, 6912]; G in {16, 64, 1024}, "r" = randomized
                  block rotation (G = 128).  G = 1024 divides neither width,
-                 so every linear routes to bf16.
+                 so every linear routes to bf16.  Suffix "_w4": the same layer
+                 with int4 weights (W4A8; codes in [-7, 7], nibble pairs).
   unit_layer     X fp32 [64, 1024], W [1024, 1024], fp32 output.
 
 Inputs live in HBM before timing starts.  To keep the 256 MB Infinity Cache
@@ -67,6 +68,7 @@ KERNEL_SOURCE = {
     "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
     "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_bf16.hip"),
     "gemv_i8": ("gemv.hip", "epilogue.h"),
+    "gemv_w4": ("gemv.hip", "epilogue.h", "w4_codec.h"),
     "pack_rows": ("pack_rows.hip",),
 }
 
@@ -109,9 +111,13 @@ def make_workload(name: str):
         return W.config3()
     if name == "large_m_qkv":
         return W.config4(with_routed=True)
-    m = re.fullmatch(r"decode_m(\d+)_g(\d+)(r?)", name)
+    m = re.fullmatch(r"decode_m(\d+)_g(\d+)(r?)(_w4)?", name)
     if m:
-        return W.config5(M=int(m.group(1)), G=int(m.group(2)), kind="randomized" if m.group(3) else "regular")
+        wl = W.config5(M=int(m.group(1)), G=int(m.group(2)), kind="randomized" if m.group(3) else "regular")
+        if m.group(4):
+            wl.name += "_w4"
+            wl.extra["wbits"] = 4
+        return wl
     if name == "unit_layer":
         return W.config1()
     raise SystemExit(f"unknown workload {name}")
@@ -131,9 +137,9 @@ class Op:
     def kernel(self):
         if self.kind == "pack":
             return "pack_rows"
-        if self.kind == "int8":
+        if self.kind in ("int8", "int4"):
             if self.M <= SMALL_M:
-                return "gemv_i8"
+                return "gemv_i8" if self.kind == "int8" else "gemv_w4"
             return "gemm_i8" + (f"_{self.epilogue}" if self.epilogue else "")
         if self.kind == "bf16":
             return "gemm_bf16"
@@ -145,15 +151,16 @@ class Op:
         return 2 * self.N if self.epilogue == "gated" else self.N
 
     def ops(self):
-        return 2.0 * self.M * self.rows * self.K if self.kind in ("int8", "bf16") else 0.0
+        return 2.0 * self.M * self.rows * self.K if self.kind in ("int8", "int4", "bf16") else 0.0
 
     def bytes(self):
         M, N, K = self.M, self.N, self.K
         if self.kind == "pack":
             return M * K * (self.in_b + 1) + 4 * M
-        if self.kind == "int8":
+        if self.kind in ("int8", "int4"):
             R = self.rows
-            return M * K + 4 * M + R * K + 8 * R + M * N * self.out_b
+            wb = R * K if self.kind == "int8" else R * K // 2  # int4: two codes per byte
+            return M * K + 4 * M + wb + 8 * R + M * N * self.out_b
         if self.kind == "bf16":
             return 2 * M * K + 2 * N * K + 4 * N + M * N * self.out_b
         return 0
@@ -188,6 +195,8 @@ class StepSet:
                 wd = up(lin.W, bf16 if lin.wdtype == "bf16" else f32)
                 if lin is routed or K % G != 0:
                     self.W[lin.name] = wd.to(bf16)
+                elif wl.extra.get("wbits") == 4:
+                    self.W[lin.name] = cr.pack_weight_w4(wd, G, kind, self.signs.get(K))
                 else:
                     self.W[lin.name] = cr.pack_weight(wd, G, kind, self.signs.get(K))
                     del wd
@@ -197,11 +206,23 @@ class StepSet:
             self.signs = template.signs
             self.X = template.X.clone()
             self.W = {k: (cr.Packed(v.q.clone(), v.scale.clone(), v.group, v.kind, v.signs)
-                          if isinstance(v, cr.Packed) else v.clone()) for k, v in template.W.items()}
+                          if isinstance(v, cr.Packed) else
+                          cr.PackedW4(v.q.clone(), v.scale.clone(), v.K, v.group, v.kind, v.signs)
+                          if isinstance(v, cr.PackedW4) else v.clone()) for k, v in template.W.items()}
             self.b = template.b
             self.X2 = template.X2.clone() if template.X2 is not None else None
         self.bufs = []
         self.ops = self._plan(dev)
+
+    def _quant(self, w):
+        """A packed (int8 or int4) weight, as opposed to a routed bf16 tensor."""
+        return isinstance(w, (self.cr.Packed, self.cr.PackedW4))
+
+    def _workspace(self, nbytes, dev):
+        """Expanded-weight workspace of the int4 path above 16 rows."""
+        ws = self.torch.empty(nbytes, dtype=self.torch.int8, device=dev)
+        self.bufs.append(ws)
+        return ws
 
     # -- buffers -----------------------------------------------------------
     def _packed(self, rows, K, dev):
@@ -213,7 +234,7 @@ class StepSet:
 
     def _out(self, name, rows, dev):
         w = self.W[name]
-        N = w.rows if isinstance(w, self.cr.Packed) else w.shape[0]
+        N = w.rows if self._quant(w) else w.shape[0]
         y = self.torch.empty((rows, N), dtype=self.odt, device=dev)
         self.bufs.append(y)
         return y
@@ -221,7 +242,7 @@ class StepSet:
     def nbytes(self):
         t = [self.X, *self.bufs] + ([self.X2] if self.X2 is not None else [])
         for v in self.W.values():
-            t.append(v.q if isinstance(v, self.cr.Packed) else v)
+            t.append(v.q if self._quant(v) else v)
         return sum(x.numel() * x.element_size() for x in t)
 
     # -- launches ----------------------------------------------------------
@@ -238,6 +259,10 @@ class StepSet:
         if isinstance(w, cr.Packed):
             return Op(f"linear_{name}", lambda: cr.linear(src, w, b, out=y), "int8", M=src.rows, N=w.rows, K=w.K,
                       out_b=ob)
+        if isinstance(w, cr.PackedW4):
+            ws = self._workspace(w.rows * w.K, y.device) if src.rows > SMALL_M else None
+            return Op(f"linear_{name}", lambda: cr.linear_w4(src, w, b, out=y, workspace=ws), "int4", M=src.rows,
+                      N=w.rows, K=w.K, out_b=ob)
         return Op(f"linear_{name}", lambda: cr.linear_bf16(src, w, b, out=y), "bf16", M=src.shape[0],
                   N=w.shape[0], K=w.shape[1], out_b=ob)
 
@@ -247,7 +272,7 @@ class StepSet:
         M, K = self.X.shape
         ops = []
         names = [l.name for l in wl.linears]
-        if isinstance(self.W[names[0]], self.cr.Packed):
+        if self._quant(self.W[names[0]]):
             src0 = self._packed(M, K, dev)
             ops.append(self._pack_op("pack_act", self.X, src0))
         else:
@@ -277,7 +302,15 @@ class StepSet:
             ops.append(self._linear_op(r, self.X2, self._out(r, M, dev)))
         elif wl.cfg == 5:
             wg, wu = self.W["gate"], self.W["up"]
-            if self.fused and isinstance(wg, self.cr.Packed) and isinstance(wu, self.cr.Packed):
+            if self.fused and isinstance(wg, self.cr.PackedW4) and isinstance(wu, self.cr.PackedW4):
+                # int4 gate and up in one launch
+                h = self._out("gate", M, dev)
+                bg, bu = self.b["gate"], self.b["up"]
+                ws = self._workspace(2 * wg.rows * wg.K, dev) if M > SMALL_M else None
+                ops.append(Op("linear_gate_up", lambda: self.cr.linear_w4_gated(
+                    src0, wg, wu, bg, bu, self.cr.GELU_TANH, out=h, workspace=ws),
+                    "int4", M=M, N=wg.rows, K=wg.K, out_b=h.element_size(), epilogue="gated"))
+            elif self.fused and isinstance(wg, self.cr.Packed) and isinstance(wu, self.cr.Packed):
                 # gate and up in one launch, gelu_tanh(gate) * up in its epilogue
                 h = self._out("gate", M, dev)
                 bg, bu = self.b["gate"], self.b["up"]
@@ -293,7 +326,7 @@ class StepSet:
                 self.bufs += [t, h]
                 ops.append(Op("gelu_tanh_mul_torch",
                               lambda: torch.mul(gelu(g, approximate="tanh", out=t), u, out=h), "torch"))
-            if isinstance(self.W["down"], self.cr.Packed):
+            if self._quant(self.W["down"]):
                 pa2 = self._packed(M, h.shape[1], dev)
                 ops.append(self._pack_op("pack_act2", h, pa2))
                 ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
@@ -348,15 +381,21 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     def sg(K):
         return signs.get(K) if kind == "randomized" else None
 
+    w4 = wl.extra.get("wbits") == 4
     packed = {}
     for n, l in lin.items():
         K = l.W.shape[1]
         if l is not routed and K % G == 0:
-            q, s, _ = O.pack(l.W, G, kind, sg(K))
-            packed[n] = (q, s)
+            if w4:
+                nib, s, _, _ = O.pack_weight_int4(l.W, G, kind, sg(K))
+                packed[n] = (nib, s)
+            else:
+                q, s, _ = O.pack(l.W, G, kind, sg(K))
+                packed[n] = (q, s)
 
     def gemm(name, qx, sx):
-        return O.epilogue64(O.int_gemm(qx, packed[name][0]), sx, packed[name][1], lin[name].b).astype(np.float32)
+        q = O.unpack_nibbles(packed[name][0]) if w4 else packed[name][0]
+        return O.epilogue64(O.int_gemm(qx, q), sx, packed[name][1], lin[name].b).astype(np.float32)
 
     def layer(name, x):
         if name in packed:
@@ -519,7 +558,7 @@ def main():
             k["frac_hbm"] = k["GB/s"] / PEAK_HBM_GBS
         if op.ops():
             k["TOPS"] = op.ops() / t / 1e12
-            k["frac_mfma"] = k["TOPS"] / (PEAK_I8_TOPS if op.kind == "int8" else PEAK_BF16_TFLOPS)
+            k["frac_mfma"] = k["TOPS"] / (PEAK_BF16_TFLOPS if op.kind == "bf16" else PEAK_I8_TOPS)
             k.update(M=op.M, N=op.rows, K=op.K)
         kernels[op.name] = k
     for k, v in kernels.items():
@@ -528,7 +567,7 @@ def main():
     # Dominant kernel: the linear launch with the most algorithmic work
     # (weight bytes at decode sizes, ops otherwise); ties go to the earlier
     # launch, so the choice does not flip with timing noise.
-    lin_ops = [op for op in ops if op.kind in ("int8", "bf16")]
+    lin_ops = [op for op in ops if op.kind in ("int8", "int4", "bf16")]
     small = all(op.M <= SMALL_M for op in lin_ops)
     dom = max(lin_ops, key=lambda o: (o.bytes() if small else o.ops(), -ops.index(o)))
     kd = kernels[dom.name]
@@ -536,7 +575,7 @@ def main():
         roof = {"kernel": dom.kernel, "launch": dom.name, "bound": "hbm", "achieved": round(kd["GB/s"], 2),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kd["frac_hbm"], 4)}
     else:
-        peak = PEAK_I8_TOPS if dom.kind == "int8" else PEAK_BF16_TFLOPS
+        peak = PEAK_BF16_TFLOPS if dom.kind == "bf16" else PEAK_I8_TOPS
         roof = {"kernel": dom.kernel, "launch": dom.name, "bound": "mfma", "achieved": round(kd["TOPS"], 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(kd["TOPS"] / peak, 4)}
     roof["traffic"] = measured_traffic(dom.kernel, args.workload)
@@ -553,12 +592,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if any(op.kind == "int8" for op in ops) else "bf16",
+        "dtype": "i8" if any(op.kind in ("int8", "int4") for op in ops) else "bf16",
         "data": "synthetic (seeded; shapes and outlier structure of the workload, no checkpoint)",
         "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
                    "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
+                   "weights": "int4" if wl.extra.get("wbits") == 4 else "int8",
                    "buffer_sets": len(sets)},
         "roofline": roof,
         "kernels_us": {k: round(v["us"], 3) for k, v in kernels.items()},
