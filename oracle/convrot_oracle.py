@@ -32,6 +32,9 @@ define, written from the formulas:
   rotated weight quantised to [-7, 7] with one scale per output channel,
   adjacent code pairs packed into one byte (W4A8 here: the int8 activation
   codes against those weight codes, same accumulation and epilogue).
+* "Add experimental W8A8 MatMul ..." (gemma.cpp issue), the maintainer's
+  review comment: data-free smoothing scales of an FFN's intermediate
+  channels (L2 or max norms), applied to the weights before the rotation.
 
 Readings taken where the pages are silent (all listed in the design notes of
 the repository):
@@ -55,7 +58,9 @@ Parseval, a one-hot worked example whose output is known in closed form,
 brute-force integer loops, and torch's bf16 rounding; for int4, the page's
 code range, exact-tie rounding, a hand-packed nibble example, every byte
 decoded, and the page's correlation check of rotated against un-rotated
-weights.  Nothing here is "parity unpinned".
+weights; for smoothing, closed forms on scaled unit rows, the norms after
+scaling, the zero-norm rule and the gated FFN's invariance.  Nothing here is
+"parity unpinned".
 """
 
 from __future__ import annotations
@@ -323,6 +328,57 @@ def pack_weight_int4(W: np.ndarray, G: int, kind: str = REGULAR,
     wr = rotate(W, G, kind, signs)
     q, s = quantize_rows_int4(wr)
     return pack_nibbles(q), s, q, wr
+
+
+# ---------------------------------------------------------------------------
+# Data-free smoothing of an FFN's intermediate channels
+# ---------------------------------------------------------------------------
+#
+# "Add experimental W8A8 MatMul with optional QuaRot-style rotation"
+# (gemma.cpp issue), maintainer's review comment: scale the weights before
+# the rotation without calibration data -- max norms as in SmoothQuant and
+# DuQuant++, or the square root of the ratio of the W_up to W_down L2 column
+# norms -- so the quantisation range shrinks, the factor being pulled into the
+# per-row scales.  Readings taken where the comment is silent:
+#   * the scaled channel j is an intermediate channel of the FFN: row j of
+#     W_up [F, K] and column j of W_down [K_out, F];
+#   * s_j = sqrt(n_up[j] / n_down[j]) with n the L2 norm ("l2") or the largest
+#     magnitude ("max"); W_up row j is divided by s_j and W_down column j
+#     multiplied by it, which leaves both with norm sqrt(n_up n_down) and the
+#     layer unchanged wherever up enters the intermediate linearly (the gated
+#     FFN h = act(gate) * up);
+#   * s_j = 1 where either norm is 0;
+#   * s is computed in fp64 and stored as fp32; the scaled weights are the
+#     fp64 quotient / product with that fp32 s, rounded once to fp32.
+
+
+def smoothing_scales(W_up: np.ndarray, W_down: np.ndarray, norm: str = "l2") -> np.ndarray:
+    """Per-channel smoothing scales s [F] (fp32) of an FFN with W_up [F, K]
+    and W_down [K_out, F]."""
+    up = np.asarray(W_up, np.float64)
+    dn = np.asarray(W_down, np.float64)
+    if up.ndim != 2 or dn.ndim != 2 or dn.shape[1] != up.shape[0]:
+        raise ValueError("W_up [F, K] and W_down [K_out, F] expected")
+    if norm == "l2":
+        n_up = np.sqrt(np.sum(up * up, axis=1))
+        n_dn = np.sqrt(np.sum(dn * dn, axis=0))
+    elif norm == "max":
+        n_up = np.max(np.abs(up), axis=1)
+        n_dn = np.max(np.abs(dn), axis=0)
+    else:
+        raise ValueError(f"unknown norm {norm!r}")
+    ok = (n_up > 0) & (n_dn > 0)
+    s = np.ones(up.shape[0], np.float64)
+    s[ok] = np.sqrt(n_up[ok] / n_dn[ok])
+    return s.astype(np.float32)
+
+
+def apply_smoothing(W_up: np.ndarray, W_down: np.ndarray, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """(W_up / s per row, W_down * s per column), fp64 then rounded once to fp32."""
+    s64 = np.asarray(s, np.float32).astype(np.float64)
+    up = (np.asarray(W_up, np.float64) / s64[:, None]).astype(np.float32)
+    dn = (np.asarray(W_down, np.float64) * s64[None, :]).astype(np.float32)
+    return up, dn
 
 
 # ---------------------------------------------------------------------------

@@ -407,6 +407,67 @@ def check_w4a8_int_gemm_bruteforce(seed: int = 13):
     assert np.array_equal(A, O.int_gemm_bruteforce(Qx, Qw))
 
 
+
+# -- data-free smoothing (FFN intermediate channels) ---------------------------
+
+def _unit_ffn(seed: int):
+    """W_up row j = c_j u_j and W_down column j = d_j v_j with unit u, v (L2)."""
+    g = np.random.default_rng(seed)
+    F, K, Ko = 6, 32, 24
+    u = g.standard_normal((F, K))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    v = g.standard_normal((Ko, F))
+    v /= np.linalg.norm(v, axis=0, keepdims=True)
+    c = np.array([1.0, 4.0, 0.25, 9.0, 2.0, 0.5])
+    d = np.array([1.0, 1.0, 4.0, 0.01, 8.0, 0.5])
+    return u * c[:, None], v * d[None, :], c, d
+
+
+def check_smoothing_closed_form(seed: int = 14):
+    up, dn, c, d = _unit_ffn(seed)
+    s = O.smoothing_scales(up, dn, "l2")
+    assert s.dtype == np.float32
+    assert np.allclose(s, np.sqrt(c / d), rtol=1e-6)
+    up2, dn2 = O.apply_smoothing(up, dn, s)
+    target = np.sqrt(c * d)
+    assert np.allclose(np.linalg.norm(up2.astype(np.float64), axis=1), target, rtol=1e-5)
+    assert np.allclose(np.linalg.norm(dn2.astype(np.float64), axis=0), target, rtol=1e-5)
+
+
+def check_smoothing_max_norm():
+    up = np.zeros((3, 8)); dn = np.zeros((5, 3))
+    up[0, 2], up[1, 7], up[2, 0] = -8.0, 2.0, 0.5
+    dn[4, 0], dn[0, 1], dn[2, 2] = 2.0, -0.5, 0.5
+    up[0, 3], dn[1, 0] = 1.0, 0.1   # smaller entries do not change the max
+    s = O.smoothing_scales(up, dn, "max")
+    assert s.tolist() == [2.0, 2.0, 1.0]
+
+
+def check_smoothing_zero_channel():
+    up = np.ones((3, 4)); dn = np.ones((4, 3))   # equal norms (2) where nothing is zero
+    up[1] = 0.0
+    dn[:, 2] = 0.0
+    assert O.smoothing_scales(up, dn, "l2").tolist() == [1.0, 1.0, 1.0]
+
+
+def check_smoothing_preserves_gated_ffn(seed: int = 15):
+    """y = W_down (gelu(W_gate x) * (W_up x)) is unchanged by smoothing."""
+    from scipy.special import erf
+    g = np.random.default_rng(seed)
+    F, K = 64, 48
+    x = g.standard_normal((5, K))
+    Wg = g.standard_normal((F, K))
+    Wu = g.standard_normal((F, K)) * np.exp(g.standard_normal(F))[:, None]
+    Wd = g.standard_normal((K, F)) * np.exp(g.standard_normal(F))[None, :]
+    gelu = lambda t: 0.5 * t * (1 + erf(t / np.sqrt(2)))
+    ffn = lambda wu, wd: (gelu(x @ Wg.T) * (x @ np.asarray(wu, np.float64).T)) @ np.asarray(wd, np.float64).T
+    s = O.smoothing_scales(Wu, Wd, "l2")
+    assert np.max(np.abs(s - 1)) > 0.1
+    up2, dn2 = O.apply_smoothing(Wu, Wd, s)
+    y0, y1 = ffn(Wu.astype(np.float32), Wd.astype(np.float32)), ffn(up2, dn2)
+    assert np.linalg.norm(y1 - y0) <= 1e-5 * np.linalg.norm(y0)
+
+
 ALL_CHECKS = [
     ("r4_printed", check_r4_printed, ()),
     *[(f"regular_structure_G{G}", check_regular_structure, (G,)) for G in REGULAR_GS],
@@ -439,6 +500,10 @@ ALL_CHECKS = [
     ("nibble_bytes_exhaustive", check_nibble_bytes_exhaustive, ()),
     ("int4_rotation_correlation", check_int4_rotation_correlation, ()),
     ("w4a8_int_gemm_bruteforce", check_w4a8_int_gemm_bruteforce, ()),
+    ("smoothing_closed_form", check_smoothing_closed_form, ()),
+    ("smoothing_max_norm", check_smoothing_max_norm, ()),
+    ("smoothing_zero_channel", check_smoothing_zero_channel, ()),
+    ("smoothing_preserves_gated_ffn", check_smoothing_preserves_gated_ffn, ()),
 ]
 
 

@@ -180,6 +180,37 @@ def _unpack_swapped(b):
     return out
 
 
+
+_smoothing_scales = O.smoothing_scales
+_apply_smoothing = O.apply_smoothing
+
+
+def _smooth_inverted_ratio(W_up, W_down, norm="l2"):
+    s = _smoothing_scales(W_up, W_down, norm)
+    return (1.0 / s).astype(np.float32)
+
+
+def _smooth_no_sqrt(W_up, W_down, norm="l2"):
+    s = _smoothing_scales(W_up, W_down, norm).astype(np.float64)
+    return (s * s).astype(np.float32)
+
+
+def _smooth_applied_backwards(W_up, W_down, s):
+    s64 = np.asarray(s, np.float64)
+    return ((np.asarray(W_up, np.float64) * s64[:, None]).astype(np.float32),
+            (np.asarray(W_down, np.float64) / s64[None, :]).astype(np.float32))
+
+
+def _smooth_rows_of_down(W_up, W_down, norm="l2"):
+    # norms of W_down's rows instead of its columns (only shapes with K_out == F survive)
+    up = np.asarray(W_up, np.float64)
+    dn = np.asarray(W_down, np.float64)
+    n_up = np.sqrt(np.sum(up * up, axis=1)) if norm == "l2" else np.max(np.abs(up), axis=1)
+    n_dn = np.sqrt(np.sum(dn * dn, axis=1)) if norm == "l2" else np.max(np.abs(dn), axis=1)
+    n_dn = np.resize(n_dn, n_up.shape)
+    return np.sqrt(np.where(n_dn > 0, n_up / np.where(n_dn > 0, n_dn, 1), 1)).astype(np.float32)
+
+
 MUTATIONS = {
     "h4_sign_flip": ("h4", _h4_sign_flip),
     "h4_unnormalised": ("h4", _h4_unnormalised),
@@ -203,6 +234,10 @@ MUTATIONS = {
     "nibbles_high_first": ("pack_nibbles", _nibbles_high_first),
     "unpack_without_sign": ("unpack_nibbles", _unpack_unsigned),
     "unpack_swapped_nibbles": ("unpack_nibbles", _unpack_swapped),
+    "smooth_inverted_ratio": ("smoothing_scales", _smooth_inverted_ratio),
+    "smooth_no_sqrt": ("smoothing_scales", _smooth_no_sqrt),
+    "smooth_rows_of_down": ("smoothing_scales", _smooth_rows_of_down),
+    "smooth_applied_backwards": ("apply_smoothing", _smooth_applied_backwards),
 }
 
 
