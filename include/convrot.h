@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 3
+#define CONVROT_ABI_VERSION 4
 
 typedef enum {
   CONVROT_OK = 0,
@@ -109,6 +109,12 @@ typedef enum {
   CONVROT_ACT_GELU_ERF = 1,
   CONVROT_ACT_GELU_TANH = 2
 } convrot_act;
+
+/* Norm of the data-free smoothing scales (convrot_smooth_ffn). */
+typedef enum {
+  CONVROT_SMOOTH_L2 = 0, /* s_j = sqrt(||W_up[j, :]||_2 / ||W_down[:, j]||_2) */
+  CONVROT_SMOOTH_MAX = 1 /* the same with the largest magnitudes */
+} convrot_smooth_norm;
 
 /* Rotation descriptor.  `signs` is a device vector of K int8 values, each +1
  * or -1 (one sign per input feature, block b using signs[b*G .. b*G+G-1]);
@@ -274,6 +280,29 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
 /* Expand int4 codes to int8 codes (for checking, or to keep an int8 copy):
  *   dst [w->rows, ldd] int8, ldd >= w->K, ldd % 16 == 0, 16-byte aligned. */
 convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_t ldd, void* stream);
+
+/* Data-free smoothing of an FFN's intermediate channels, offline, before
+ * the weights are packed (gemma.cpp issue "Add experimental W8A8 MatMul with
+ * optional QuaRot-style rotation", the maintainer's review comment: scaling
+ * without calibration data, by max norms or by the square root of the ratio
+ * of the W_up to W_down L2 column norms, pulled into the per-row scales).
+ * For channel j (row j of W_up, column j of W_down):
+ *   s[j]           = sqrt(n_up[j] / n_down[j]), 1 where either norm is 0
+ *   W_up_out[j, :] = W_up[j, :] / s[j],   W_down_out[:, j] = W_down[:, j] * s[j]
+ * Norms accumulate in fp64; s is rounded once to fp32; each output weight is
+ * the fp64 quotient or product with that s, rounded once to fp32.  Exact
+ * for a gated FFN (h = act(gate) * up); the scaled weights are then packed
+ * with convrot_pack_weight or convrot_pack_weight_w4.
+ *   W_up      [F, ldu] of up_dt (CONVROT_F32 or CONVROT_BF16), K columns
+ *   W_down    [K_out, ldd] of down_dt, F columns
+ *   s         [F] fp32 (written)
+ *   W_up_out  [F, ldu_out] fp32, or NULL to skip
+ *   W_down_out [K_out, ldd_out] fp32, or NULL to skip
+ * Only element alignment is required.  F == 0 is a no-op. */
+convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t ldu, const void* W_down,
+                                  convrot_dtype down_dt, int64_t ldd, int64_t F, int64_t K, int64_t K_out,
+                                  convrot_smooth_norm norm, float* s, float* W_up_out, int64_t ldu_out,
+                                  float* W_down_out, int64_t ldd_out, void* stream);
 
 /* Static description of a status code. */
 const char* convrot_status_string(convrot_status status);

@@ -283,3 +283,25 @@ def test_w4_unpack_checks(lib):
     assert lib.convrot_unpack_w4(ctypes.byref(w), A16C, 128, None) == _lib.ERR_INVALID_ARG  # ldd < K
     assert lib.convrot_unpack_w4(ctypes.byref(w), MIS, 256, None) == _lib.ERR_ALIGN
     assert lib.convrot_unpack_w4(ctypes.byref(packed_w4(rows=0)), A16C, 256, None) == _lib.OK
+
+
+
+# -- data-free smoothing ------------------------------------------------------
+
+def smooth_status(lib, up=A16, up_dt=_lib.BF16, ldu=64, dn=A16B, dn_dt=_lib.BF16, ldd=32, F=32, K=64, K_out=48,
+                  norm=_lib.SMOOTH_L2, s=A16C, uo=None, lduo=0, do=None, lddo=0):
+    return lib.convrot_smooth_ffn(up, up_dt, ldu, dn, dn_dt, ldd, F, K, K_out, norm, s, uo, lduo, do, lddo, None)
+
+
+def test_smooth_checks(lib):
+    assert smooth_status(lib, F=0) == _lib.OK
+    assert smooth_status(lib, up_dt=_lib.I32) == _lib.ERR_DTYPE
+    assert smooth_status(lib, norm=3) == _lib.ERR_INVALID_ARG
+    assert smooth_status(lib, s=None) == _lib.ERR_INVALID_ARG
+    assert smooth_status(lib, s=A16C + 2) == _lib.ERR_ALIGN
+    assert smooth_status(lib, ldu=32) == _lib.ERR_INVALID_ARG          # ldu < K
+    assert smooth_status(lib, ldd=16) == _lib.ERR_INVALID_ARG          # ldd < F
+    assert smooth_status(lib, up=A16 + 1) == _lib.ERR_ALIGN            # bf16 element alignment
+    assert smooth_status(lib, uo=0x40000, lduo=32) == _lib.ERR_INVALID_ARG
+    assert smooth_status(lib, do=0x50000, lddo=16) == _lib.ERR_INVALID_ARG
+    assert smooth_status(lib, F=-1) == _lib.ERR_INVALID_ARG

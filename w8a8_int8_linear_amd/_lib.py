@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -22,6 +22,8 @@ F32, BF16, I32 = 0, 1, 2
 ROT_REGULAR, ROT_RANDOMIZED = 0, 1
 # convrot_act
 ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
+# convrot_smooth_norm
+SMOOTH_L2, SMOOTH_MAX = 0, 1
 
 EXPORTED = (
     "convrot_pack_act",
@@ -35,6 +37,7 @@ EXPORTED = (
     "convrot_linear_w4",
     "convrot_linear_w4_gated",
     "convrot_unpack_w4",
+    "convrot_smooth_ffn",
     "convrot_status_string",
     "convrot_last_error",
     "convrot_abi_version",
@@ -103,6 +106,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_linear_w4_gated.restype = c_int
     lib.convrot_unpack_w4.argtypes = [P4, vp, c_i64, vp]
     lib.convrot_unpack_w4.restype = c_int
+    lib.convrot_smooth_ffn.argtypes = [vp, c_int, c_i64, vp, c_int, c_i64, c_i64, c_i64, c_i64, c_int, vp, vp, c_i64,
+                                       vp, c_i64, vp]
+    lib.convrot_smooth_ffn.restype = c_int
     lib.convrot_status_string.argtypes = [c_int]
     lib.convrot_status_string.restype = ctypes.c_char_p
     lib.convrot_last_error.argtypes = []

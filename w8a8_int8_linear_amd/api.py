@@ -4,8 +4,8 @@ Every function marshals torch CUDA tensors (device memory) and the current
 torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
 kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
 ``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``,
-and for int4 weights (W4A8) ``pack_weight_w4``, ``linear_w4``,
-``linear_w4_gated``, ``unpack_w4``.
+for int4 weights (W4A8) ``pack_weight_w4``, ``linear_w4``,
+``linear_w4_gated``, ``unpack_w4``, and the offline ``smooth_ffn``.
 """
 
 from __future__ import annotations
@@ -313,3 +313,36 @@ def unpack_w4(w: PackedW4, out: torch.Tensor | None = None) -> torch.Tensor:
     lib = _lib.load()
     _lib.check(lib.convrot_unpack_w4(ctypes.byref(desc), out.data_ptr(), _ld(out), _stream(out.device)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Data-free smoothing of an FFN's intermediate channels (offline)
+# ---------------------------------------------------------------------------
+
+_SMOOTH = {"l2": _lib.SMOOTH_L2, "max": _lib.SMOOTH_MAX}
+
+
+def smooth_ffn(w_up: torch.Tensor, w_down: torch.Tensor, norm: str = "l2", scaled: bool = True):
+    """s [F] = sqrt(n_up / n_down) per intermediate channel and, with
+    ``scaled``, the fp32 weights W_up / s (rows) and W_down * s (columns)
+    ready to pack (convrot_smooth_ffn).  Returns (s, up, down) or s."""
+    for t, name in ((w_up, "w_up"), (w_down, "w_down")):
+        _need_cuda(t, name)
+        if t.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"{name} must be float32 or bfloat16")
+    if norm not in _SMOOTH:
+        raise ValueError(f"norm must be one of {sorted(_SMOOTH)}")
+    F, K = w_up.shape
+    K_out = w_down.shape[0]
+    if w_down.shape[1] != F:
+        raise ValueError("w_down must be [K_out, F] with F = w_up.shape[0]")
+    dev = w_up.device
+    s = torch.empty(F, dtype=torch.float32, device=dev)
+    up = torch.empty((F, K), dtype=torch.float32, device=dev) if scaled else None
+    dn = torch.empty((K_out, F), dtype=torch.float32, device=dev) if scaled else None
+    lib = _lib.load()
+    _lib.check(lib.convrot_smooth_ffn(
+        w_up.data_ptr(), _DT[w_up.dtype], _ld(w_up), w_down.data_ptr(), _DT[w_down.dtype], _ld(w_down), F, K, K_out,
+        _SMOOTH[norm], s.data_ptr(), up.data_ptr() if up is not None else None, _ld(up) if up is not None else 0,
+        dn.data_ptr() if dn is not None else None, _ld(dn) if dn is not None else 0, _stream(dev)))
+    return (s, up, dn) if scaled else s

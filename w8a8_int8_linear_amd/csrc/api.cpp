@@ -447,6 +447,38 @@ convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_
                   "convrot_unpack_w4");
 }
 
+convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t ldu, const void* W_down,
+                                  convrot_dtype down_dt, int64_t ldd, int64_t F, int64_t K, int64_t K_out,
+                                  convrot_smooth_norm norm, float* s, float* W_up_out, int64_t ldu_out,
+                                  float* W_down_out, int64_t ldd_out, void* stream) {
+  const char* what = "convrot_smooth_ffn";
+  if (F < 0 || K < 0 || K_out < 0 || F > kMaxRows || K_out > kMaxRows)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: bad sizes", what);
+  if ((up_dt != CONVROT_F32 && up_dt != CONVROT_BF16) || (down_dt != CONVROT_F32 && down_dt != CONVROT_BF16))
+    return fail(CONVROT_ERR_DTYPE, "%s: weights must be CONVROT_F32 or CONVROT_BF16", what);
+  if (norm != CONVROT_SMOOTH_L2 && norm != CONVROT_SMOOTH_MAX)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: unknown norm %d", what, static_cast<int>(norm));
+  if (F == 0) return ok();
+  if (s == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: s is NULL", what);
+  if ((reinterpret_cast<uintptr_t>(s) & 3u) != 0) return fail(CONVROT_ERR_ALIGN, "s must be 4-byte aligned");
+  convrot_status st = check_matrix("W_up", W_up, F, K, ldu, elt_size(up_dt), false);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("W_down", W_down, K_out, F, ldd, elt_size(down_dt), false);
+  if (st != CONVROT_OK) return st;
+  if (W_up_out != nullptr) {
+    st = check_matrix("W_up_out", W_up_out, F, K, ldu_out, 4, false);
+    if (st != CONVROT_OK) return st;
+  }
+  if (W_down_out != nullptr) {
+    st = check_matrix("W_down_out", W_down_out, K_out, F, ldd_out, 4, false);
+    if (st != CONVROT_OK) return st;
+  }
+  const hipError_t e = convrot::launch_smooth_ffn(
+      W_up, static_cast<convrot::Elt>(up_dt), ldu, W_down, static_cast<convrot::Elt>(down_dt), ldd, F, K, K_out,
+      norm == CONVROT_SMOOTH_MAX, s, W_up_out, ldu_out, W_down_out, ldd_out, static_cast<hipStream_t>(stream));
+  return from_hip(e, what);
+}
+
 const char* convrot_status_string(convrot_status status) {
   switch (status) {
     case CONVROT_OK: return "CONVROT_OK";

@@ -84,6 +84,13 @@ hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, 
                                 int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
                                 hipStream_t stream);
 
+// Data-free smoothing of an FFN's intermediate channels (offline): s [F]
+// and, where the outputs are non-null, the scaled fp32 weights
+// W_up / s (rows) and W_down * s (columns).
+hipError_t launch_smooth_ffn(const void* up, Elt up_dt, int64_t ldu, const void* dn, Elt dn_dt, int64_t ldd, int64_t F,
+                             int64_t K, int64_t K_out, bool max_norm, float* s, float* up_out, int64_t ldu_out,
+                             float* dn_out, int64_t ldd_out, hipStream_t stream);
+
 // Small-M kernels with int4 weights (nibble pairs, ldb in bytes): the same
 // accumulators as the int8 kernels on the expanded codes.  `act` may be
 // None (then `out` may be I32) for the plain linear.

@@ -207,3 +207,17 @@ def random_codes4(shape, seed: int) -> np.ndarray:
         flat[0] = 7
         flat[-1] = -7
     return q
+
+
+def smoothing_study_ffn(M: int = 64, K: int = 3072, F: int = 8192, sigma_c: float = 1.5, seed: int = 9):
+    """Gated FFN whose intermediate channels are imbalanced: X bf16 [M, K]
+    ~N(0,1) with 4 channels x30; W_gate [F, K] ~N(0, 0.02); W_up row j
+    ~N(0, 0.02 c_j) and W_down [K, F] column j ~N(0, 0.02 / c_j) with
+    c_j = exp(sigma_c z_j), z ~N(0,1).  All bf16 values."""
+    g = np.random.default_rng(seed)
+    c = np.exp(sigma_c * g.standard_normal(F)).astype(np.float32)
+    X = to_bf16_values(column_outliers(g.standard_normal((M, K)).astype(np.float32), seed, 4, 30.0))
+    Wg = to_bf16_values((g.standard_normal((F, K)) * 0.02).astype(np.float32))
+    Wu = to_bf16_values((g.standard_normal((F, K)) * 0.02 * c[:, None]).astype(np.float32))
+    Wd = to_bf16_values((g.standard_normal((K, F)) * 0.02 / c[None, :]).astype(np.float32))
+    return X, Wg, Wu, Wd
