@@ -67,7 +67,7 @@ KERNEL_SOURCE = {
     "gemm_i8_act": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_act.hip"),
     "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
     "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_bf16.hip"),
-    "gemv_i8": ("gemv.hip", "epilogue.h"),
+    "gemv_i8": ("gemv.hip", "epilogue.h", "w4_codec.h"),
     "gemv_w4": ("gemv.hip", "epilogue.h", "w4_codec.h"),
     "pack_rows": ("pack_rows.hip",),
 }

@@ -167,3 +167,23 @@ def test_w4a8_decode_layer_full_size(cuda):
     ah = cr.pack_act(h, G)
     y_ref = O.epilogue64(O.int_gemm(to_np(ah.q), qd), to_np(ah.scale), to_np(pd.scale))
     assert R.rel_fro(y, y_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16400, 1024), (3, 17000, 2080), (1, 16384, 512)])
+def test_small_m_two_tile_workgroups(cuda, M, N, K):
+    """Small M with at least four 16-feature tiles per CU (256 CUs): the
+    weight-streaming kernel computes two tiles per workgroup (int8, int4 and
+    bf16 weights; ragged last pair)."""
+    qx, sx, q4, sw, b = _operands(M, N, K, N + K)
+    q8 = random_codes((N, K), N + K + 2)
+    a = cr.Packed(to_dev(qx, torch.int8), to_dev(sx, torch.float32), 16)
+    assert np.array_equal(to_np(cr.linear_w4(a, _w4(q4, sw, 16), out_dtype=torch.int32)), O.int_gemm(qx, q4))
+    w8 = cr.Packed(to_dev(q8, torch.int8), to_dev(sw, torch.float32), 16)
+    assert np.array_equal(to_np(cr.linear(a, w8, out_dtype=torch.int32)), O.int_gemm(qx, q8))
+    bd = to_dev(b, torch.float32)
+    y = to_np(cr.linear_w4(a, _w4(q4, sw, 16), bd, cr.GELU_ERF, out_dtype=torch.float32))
+    assert R.rel_fro(y, R.gelu64(O.epilogue64(O.int_gemm(qx, q4), sx, sw, b), "gelu_erf")) <= 1e-5
+    xb = to_bf16_values(random_rows((M, K), 3))
+    wb = to_bf16_values(random_rows((N, K), 4) * np.float32(0.05))
+    yb = to_np(cr.linear_bf16(to_dev(xb, torch.bfloat16), to_dev(wb, torch.bfloat16), out_dtype=torch.float32))
+    assert R.rel_fro(yb, O.linear_unquantized64(xb, wb)) <= 1e-5

@@ -6,27 +6,29 @@
 // the unquantised linear that layers with K % G != 0 keep (sglang PR 34581
 // summary page, kitchen_int8 routing).
 //
-// With M <= 16 the time is the time to stream N*K weight bytes, and at
-// decode sizes (a few MB) that is mostly memory latency.  So the kernel
-// puts every weight byte in flight at once:
-//  * one workgroup per 16 output features; its W waves (4, 8 or 16, chosen
-//    so each wave has at most 8 steps) split the row bytes into W
-//    contiguous ranges;
-//  * a step is 64 bytes of each of the 16 weight rows: one
-//    v_mfma_i32_16x16x64_i8 (or v_mfma_f32_16x16x32_bf16) whose row operand
-//    is the 16 weight rows (16 bytes per lane, straight from global memory)
-//    and whose column operand is the activation rows (rows >= M re-read the
-//    last row; their outputs are dropped);
-//  * a wave issues all loads of its range (up to 8 steps x 2 x 16 bytes per
-//    lane) before its first MFMA, so a whole launch's weight stream is
-//    requested within the first microsecond;
-//  * the W partial accumulators are summed through LDS (exact in int8 mode)
-//    and wave 0 applies the epilogue, writing 4 consecutive outputs per lane;
-//  * fused epilogues (int8 mode): an activation of Y (GELU, erf or tanh
+// With M <= 16 the time is the time to stream N*K weight bytes.  Every
+// vector load of an MFMA operand touches 16 rows (16 cache lines), so the
+// CU's memory pipeline, counted in lines, is what streams: the structure
+// keeps the lines per MFMA low and many of them in flight.
+//  * A workgroup computes one 16-feature tile, or two that share every
+//    activation fragment (plain launches with at least four tiles per CU);
+//    its waves (4, or 8 where a wave would stream more than 32 K units)
+//    split K.
+//  * A K unit is 64 bytes of each of the 16 weight rows: one
+//    v_mfma_i32_16x16x64_i8 (or v_mfma_f32_16x16x32_bf16) per tile whose row
+//    operand is the 16 weight rows (16 bytes per lane, straight from global
+//    memory) and whose column operand is the activation rows (rows >= M
+//    re-read the last row; their outputs are dropped).
+//  * Loads come in double-buffered rounds: the next round is requested
+//    before the current one is multiplied.
+//  * The partial accumulators of the waves are summed through LDS (exact in
+//    int8 mode) and wave 0 applies the epilogue, writing 4 consecutive
+//    outputs per lane.
+//  * Fused epilogues (int8 mode): an activation of Y (GELU, erf or tanh
 //    form), or a gated pair Y = act(gate) * up where the workgroup streams
 //    the same 16 features of both weights against one set of activation
-//    loads;
-//  * when there are fewer 16-feature tiles than CUs (a down projection has
+//    loads.
+//  * When there are fewer 16-feature tiles than CUs (a down projection has
 //    N = 1152, i.e. 72 tiles), K is also split across workgroups: each
 //    (tile, K range) workgroup stores its partial sums (exact int32 in int8
 //    mode) in a per-device workspace, and a second launch of one wave per
@@ -38,10 +40,10 @@
 //  * int4 weights (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
 //    per-channel int8 safetensors", sections "Solution" and "The rotation":
 //    codes in [-7, 7], one scale per output row, adjacent pairs in a byte):
-//    a lane loads the 8 bytes holding its 16 codes of a step, half the int8
-//    stream, and expands them in registers to the 16 int8 codes the same
-//    MFMA takes; the accumulator and epilogue are unchanged.
-// The byte-to-k assignment of a lane is the same for both operands, so each
+//    a K unit is 128 codes, one 16-byte load per lane and tile (half the
+//    int8 lines per MFMA), expanded in registers to the int8 codes of two
+//    MFMAs; the accumulator and epilogue are unchanged.
+// The assignment of k to (MFMA, lane) is the same for both operands, so each
 // MFMA pairs matching k.
 #include <hip/hip_runtime.h>
 
@@ -61,7 +63,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSteps = 8;        // steps per wave per round of loads
 constexpr int kStepBytes = 64;   // bytes of one weight row per step
 
 template <bool I8>
@@ -150,90 +151,163 @@ __device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, 
 
 // A: activation rows [M, lda bytes]; B: weight rows [N, ldb bytes] (int4
 // mode: K / 2 bytes of nibble pairs per row); kbytes = K * element size of A
-// (a multiple of 16); per = steps per wave.
-template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false, bool W4 = false>
+// (a multiple of 16); per = K units per wave.  A workgroup computes TILES
+// consecutive 16-feature tiles that share each activation fragment.
+//
+// K unit: 64 activation bytes (one MFMA per tile), or in int4 mode 128 codes
+// (two MFMAs per tile), where lane (row, ch) takes codes 32 ch .. 32 ch + 31
+// of the unit from one 16-byte weight load (bytes 16 ch .. 16 ch + 15 of the
+// unit's 64 nibble bytes) and two 16-byte activation loads; codes 0-15 of
+// that range feed the first MFMA and 16-31 the second.  Both operands follow
+// the same assignment of k to (MFMA, lane), so every product pairs matching
+// k; the int32 sum does not depend on the order.
+template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false, bool W4 = false,
+          int TILES = 1>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
     int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   static_assert(!W4 || I8, "int4 weights pair with int8 activations");
+  static_assert(TILES == 1 || (!GATED && !SPLIT), "several tiles per workgroup only on the plain unsplit path");
   using Acc = typename Mma<I8>::Acc;
-  constexpr int kWDiv = W4 ? 2 : 1;  // activation bytes per weight byte
-  constexpr int kSets = GATED ? 2 : 1;  // weight row sets streamed (gate, up)
-  __shared__ Acc partial[kSets][WAVES > 1 ? WAVES - 1 : 1][64];
+  constexpr int kSets = GATED ? 2 : 1;         // weight row sets streamed (gate, up)
+  constexpr int kUnit = W4 ? 128 : kStepBytes;  // activation bytes per K unit
+  constexpr int kRound = TILES == 1 ? 4 : 2;    // units per round of loads (two rounds in flight per wave)
+  __shared__ Acc partial[kSets * TILES][WAVES > 1 ? WAVES - 1 : 1][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * TILES;
   const int row = lane & 15;
   const int ch = lane >> 4;
 
-  const uint8_t* wrow[kSets];
-  wrow[0] = B + static_cast<int64_t>(min(n0 + row, N - 1)) * ldb + ch * (16 / kWDiv);
-  if constexpr (GATED)
-    wrow[kSets - 1] = epi.B2 + static_cast<int64_t>(min(n0 + row, N - 1)) * epi.ldb2 + ch * (16 / kWDiv);
-  const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * 16;
+  // Weight rows: TILES tiles of each set; in int4 mode 16 nibble bytes per
+  // lane and unit, else 16 weight bytes per lane and step.
+  const uint8_t* wrow[kSets][TILES];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    const int64_t n = min(n0 + 16 * i + row, N - 1);
+    wrow[0][i] = B + n * ldb + ch * 16;
+    if constexpr (GATED) wrow[kSets - 1][i] = epi.B2 + n * epi.ldb2 + ch * 16;
+  }
+  const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * (W4 ? 32 : 16);
 
-  const int nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
-  // K steps [s_lo, s_hi) of this workgroup, `per` of them per wave.
-  const int s_lo = SPLIT ? static_cast<int>(blockIdx.y) * sp.steps : 0;
-  const int s_hi = SPLIT ? min(nsteps, s_lo + sp.steps) : nsteps;
-  const int s_begin = s_lo + wid * per;
-  const int s_end = min(s_hi, s_begin + per);
+  const int nunits = (kbytes + kUnit - 1) / kUnit;
+  // K units [u_lo, u_hi) of this workgroup, `per` of them per wave.
+  const int u_lo = SPLIT ? static_cast<int>(blockIdx.y) * sp.steps : 0;
+  const int u_hi = SPLIT ? min(nunits, u_lo + sp.steps) : nunits;
+  const int u_begin = u_lo + wid * per;
+  const int u_end = min(u_hi, u_begin + per);
 
-  Acc acc[kSets];
+  Acc acc[kSets][TILES];
 #pragma unroll
-  for (int t = 0; t < kSets; ++t) acc[t] = Acc{0, 0, 0, 0};
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  using WLoad = typename std::conditional<W4, u32x2, i32x4>::type;
-  for (int s0 = s_begin; s0 < s_end; s0 += kSteps) {
-    WLoad w[kSets][kSteps];
-    i32x4 x[kSteps];
+  for (int t = 0; t < kSets; ++t)
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
+    for (int i = 0; i < TILES; ++i) acc[t][i] = Acc{0, 0, 0, 0};
+  // Rounds of kRound units, double-buffered: the loads of the next round are
+  // issued before the MFMAs of the current one, so a wave keeps its weight
+  // stream in flight while it multiplies.
+  struct Round {
+    i32x4 w[kSets][TILES][kRound];
+    i32x4 x[kRound][W4 ? 2 : 1];
+  };
+  auto load = [&](int u0, Round& r) {
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) w[t][u] = WLoad{};
-      x[u] = i32x4{0, 0, 0, 0};
-      const int byte = (s0 + u) * kStepBytes;
-      if (s0 + u < s_end && byte + ch * 16 < kbytes) {
+    for (int u = 0; u < kRound; ++u) {
+#pragma unroll
+      for (int t = 0; t < kSets; ++t)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) r.w[t][i][u] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < (W4 ? 2 : 1); ++h) r.x[u][h] = i32x4{0, 0, 0, 0};
+      if (u0 + u >= u_end) continue;
+      const int byte = (u0 + u) * kUnit;  // activation byte of the unit
+      if constexpr (W4) {
+        // K is a multiple of 16: each 16-code half is wholly in or out.
+        const bool lo = byte + ch * 32 + 16 <= kbytes, hi = byte + ch * 32 + 32 <= kbytes;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        if (lo) {
+#pragma unroll
+          for (int t = 0; t < kSets; ++t)
+#pragma unroll
+            for (int i = 0; i < TILES; ++i) {
+              const uint8_t* p = wrow[t][i] + byte / 2;
+              if (hi) {
+                r.w[t][i][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+              } else {
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+                r.w[t][i][u] = i32x4{static_cast<int>(v.x), static_cast<int>(v.y), 0, 0};
+              }
+            }
+          r.x[u][0] = *reinterpret_cast<const i32x4*>(xrow + byte);
+        }
+        if (hi) r.x[u][1] = *reinterpret_cast<const i32x4*>(xrow + byte + 16);
+      } else if (byte + ch * 16 < kbytes) {
 #pragma unroll
         for (int t = 0; t < kSets; ++t)
-          w[t][u] = __builtin_nontemporal_load(reinterpret_cast<const WLoad*>(wrow[t] + byte / kWDiv));
-        x[u] = *reinterpret_cast<const i32x4*>(xrow + byte);
+#pragma unroll
+          for (int i = 0; i < TILES; ++i)
+            r.w[t][i][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t][i] + byte));
+        r.x[u][0] = *reinterpret_cast<const i32x4*>(xrow + byte);
       }
     }
+  };
+  auto mma = [&](const Round& r) {
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u)
+    for (int u = 0; u < kRound; ++u)
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) {
-        if constexpr (W4) {
-          acc[t] = Mma<I8>::run(expand_w4(w[t][u].x, w[t][u].y), x[u], acc[t]);
-        } else {
-          acc[t] = Mma<I8>::run(w[t][u], x[u], acc[t]);
+      for (int t = 0; t < kSets; ++t)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) {
+          const i32x4 w = r.w[t][i][u];
+          if constexpr (W4) {
+            acc[t][i] = Mma<I8>::run(expand_w4(w.x, w.y), r.x[u][0], acc[t][i]);
+            acc[t][i] = Mma<I8>::run(expand_w4(w.z, w.w), r.x[u][1], acc[t][i]);
+          } else {
+            acc[t][i] = Mma<I8>::run(w, r.x[u][0], acc[t][i]);
+          }
         }
-      }
+  };
+  Round ra, rb;
+  if (u_begin < u_end) load(u_begin, ra);
+  for (int u0 = u_begin; u0 < u_end; u0 += 2 * kRound) {
+    if (u0 + kRound < u_end) load(u0 + kRound, rb);
+    mma(ra);
+    if (u0 + kRound >= u_end) break;
+    if (u0 + 2 * kRound < u_end) load(u0 + 2 * kRound, ra);
+    mma(rb);
   }
 
   if (WAVES > 1) {
     if (wid > 0) {
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) partial[t][wid - 1][lane] = acc[t];
+      for (int t = 0; t < kSets; ++t)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) partial[t * TILES + i][wid - 1][lane] = acc[t][i];
     }
     __syncthreads();
     if (wid != 0) return;
 #pragma unroll
     for (int w = 0; w < WAVES - 1; ++w)
 #pragma unroll
-      for (int t = 0; t < kSets; ++t) acc[t] += partial[t][w][lane];
+      for (int t = 0; t < kSets; ++t)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) acc[t][i] += partial[t * TILES + i][w][lane];
   }
 
   if constexpr (SPLIT) {
     // This K range's sums, for the combining launch.
     i32x4* mine = sp.part + ((static_cast<int64_t>(blockIdx.x) * sp.splits + blockIdx.y) * kSets) * 64;
 #pragma unroll
-    for (int t = 0; t < kSets; ++t) mine[t * 64 + lane] = __builtin_bit_cast(i32x4, acc[t]);
+    for (int t = 0; t < kSets; ++t) mine[t * 64 + lane] = __builtin_bit_cast(i32x4, acc[t][0]);
   } else {
-    tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, n0, epi, M, N, C, ldc);
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+      Acc tile[kSets];
+#pragma unroll
+      for (int t = 0; t < kSets; ++t) tile[t] = acc[t][i];
+      tile_epilogue<I8, OUT, ACT, GATED>(tile, lane, n0 + 16 * i, epi, M, N, C, ldc);
+    }
   }
 }
 
@@ -294,73 +368,78 @@ inline int gemv_num_cus() {
   return cus;
 }
 
-template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4>
+template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
                   const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
                   hipStream_t stream) {
   switch (waves) {
     case 4:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4>), grid, dim3(256), 0, stream, a, lda, b, ldb,
-                         epi, m, n, kb, per, C, ldc, sp);
-      break;
-    case 8:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4>), grid, dim3(512), 0, stream, a, lda, b, ldb,
-                         epi, m, n, kb, per, C, ldc, sp);
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES>), grid, dim3(256), 0, stream, a,
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
       break;
     default:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 16, ACT, GATED, SPLIT, W4>), grid, dim3(1024), 0, stream, a, lda, b,
-                         ldb, epi, m, n, kb, per, C, ldc, sp);
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES>), grid, dim3(512), 0, stream, a,
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
       break;
   }
 }
 
-// Waves per workgroup for `steps` K steps: the fewest of 4, 8, 16 that keep
-// each wave at kSteps steps or less.
-inline int waves_for(int64_t steps) {
-  for (int w : {4, 8}) {
-    if ((steps + w - 1) / w <= kSteps) return w;
-  }
-  return 16;
-}
+// Waves per workgroup for `units` K units: four, eight where a wave would
+// otherwise stream more than kMaxUnits units (a workgroup's waves split K,
+// so fewer waves mean more resident workgroups per CU; a wave's rounds are
+// pipelined, so a long range costs no extra latency).
+constexpr int kMaxUnits = 32;
+inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 8; }
 
 template <bool I8, int OUT, int ACT = 0, bool GATED = false, bool W4 = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
                       int64_t N, int64_t kbytes, void* C, int64_t ldc, hipStream_t stream) {
   constexpr int kSets = GATED ? 2 : 1;
-  const int64_t nsteps = (kbytes + kStepBytes - 1) / kStepBytes;
+  constexpr int kUnit = W4 ? 128 : kStepBytes;
+  constexpr int kStepsPerUnit = kUnit / kStepBytes;
+  const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
   const auto* a = static_cast<const uint8_t*>(A);
   const auto* b = static_cast<const uint8_t*>(B);
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
 
   // Split K when there are fewer tiles than CUs: aim at two workgroups per
-  // CU, keep at least 8 steps per split, stay inside the workspace.
+  // CU, keep at least 8 MFMA steps per split, stay inside the workspace.
   int64_t splits = 1;
   const int64_t cus = gemv_num_cus();
   if (tiles < cus) {
-    splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nsteps / 8);
+    splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nunits * kStepsPerUnit / 8);
     const int64_t cap = static_cast<int64_t>(kWsBytes / (static_cast<size_t>(kSets) * 1024));
     splits = std::min<int64_t>(splits, cap / tiles);
   }
   uint8_t* ws = nullptr;
   if (splits > 1 && split_workspace(stream, &ws)) {
-    const int64_t steps = (nsteps + splits - 1) / splits;
-    splits = (nsteps + steps - 1) / steps;  // no empty split
-    const int waves = waves_for(steps);
-    const int per = static_cast<int>((steps + waves - 1) / waves);
-    const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(steps)};
+    const int64_t units = (nunits + splits - 1) / splits;
+    splits = (nunits + units - 1) / units;  // no empty split
+    const int waves = waves_for(units);
+    const int per = static_cast<int>((units + waves - 1) / waves);
+    const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(units)};
     launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splits)),
-                                           a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, stream);
+                                                a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_combine_kernel<I8, OUT, ACT, GATED>), dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
                        stream, epi, m, n, C, ldc, sp);
     return hipGetLastError();
   }
-  const int waves = waves_for(nsteps);
-  const int per = static_cast<int>((nsteps + waves - 1) / waves);
-  launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n, kb,
-                                          per, C, ldc, SplitArgs{nullptr, 1, 0}, stream);
+  const int waves = waves_for(nunits);
+  const int per = static_cast<int>((nunits + waves - 1) / waves);
+  // Two tiles per workgroup share every activation fragment once there are
+  // at least four tiles per CU (plain launches only; with fewer, the
+  // workgroups of two tiles spread unevenly over the CUs).
+  if (!GATED && tiles >= 4 * cus) {
+    launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2>(
+        waves, dim3(static_cast<unsigned>((tiles + 1) / 2)), a, lda, b, ldb, epi, m, n, kb, per, C, ldc,
+        SplitArgs{nullptr, 1, 0}, stream);
+    return hipGetLastError();
+  }
+  launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n,
+                                               kb, per, C, ldc, SplitArgs{nullptr, 1, 0}, stream);
   return hipGetLastError();
 }
 
