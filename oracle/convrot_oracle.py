@@ -35,6 +35,9 @@ define, written from the formulas:
 * "Add experimental W8A8 MatMul ..." (gemma.cpp issue), the maintainer's
   review comment: data-free smoothing scales of an FFN's intermediate
   channels (L2 or max norms), applied to the weights before the rotation.
+* "INT8 Convrot Safetensors", LoRA paragraph: the runtime adapter
+  correction computed from the unrotated activation and added to the base
+  output.
 
 Readings taken where the pages are silent (all listed in the design notes of
 the repository):
@@ -59,8 +62,10 @@ brute-force integer loops, and torch's bf16 rounding; for int4, the page's
 code range, exact-tie rounding, a hand-packed nibble example, every byte
 decoded, and the page's correlation check of rotated against un-rotated
 weights; for smoothing, closed forms on scaled unit rows, the norms after
-scaling, the zero-norm rule and the gated FFN's invariance.  Nothing here is
-"parity unpinned".
+scaling, the zero-norm rule and the gated FFN's invariance; for LoRA, the
+merged-weight identity on values that bf16 holds exactly, a one-hot closed
+form, the bf16 rounding of the intermediate and a brute-force loop.
+Nothing here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -379,6 +384,35 @@ def apply_smoothing(W_up: np.ndarray, W_down: np.ndarray, s: np.ndarray) -> tupl
     up = (np.asarray(W_up, np.float64) / s64[:, None]).astype(np.float32)
     dn = (np.asarray(W_down, np.float64) * s64[None, :]).astype(np.float32)
     return up, dn
+
+
+# ---------------------------------------------------------------------------
+# Runtime LoRA correction from the unrotated activation
+# ---------------------------------------------------------------------------
+#
+# "INT8 Convrot Safetensors", LoRA paragraph: adapters are applied at run
+# time without touching the int8 weights; the convrot path computes the base
+# output and the adapter computes its correction from the original,
+# unrotated activation and adds it to that output.  Readings taken where the
+# page is silent:
+#   * the adapter is the low-rank pair A [r, K] (down) and B [N, r] (up) with
+#     a scalar scale (alpha / r):  dY = scale (X A^T) B^T;
+#   * the rank-r intermediate T = X A^T is held in bf16 (the adapter's own
+#     precision), the product T B^T accumulates in fp32 and scale multiplies
+#     the sum; the correction is added to the base output in the output's
+#     precision (fp32, or the sum rounded to bf16).
+
+
+def lora_intermediate(X: np.ndarray, A: np.ndarray) -> np.ndarray:
+    """T = X A^T in fp64, rounded once to bf16 (returned as fp32 values)."""
+    T = np.asarray(X, np.float64) @ np.asarray(A, np.float64).T
+    return bf16_round(T.astype(np.float32)) if T.size else T.astype(np.float32)
+
+
+def lora_delta64(X: np.ndarray, A: np.ndarray, B: np.ndarray, scale: float) -> np.ndarray:
+    """dY = scale (bf16(X A^T)) B^T in fp64."""
+    T = lora_intermediate(X, A).astype(np.float64)
+    return float(np.float32(scale)) * (T @ np.asarray(B, np.float64).T)
 
 
 # ---------------------------------------------------------------------------

@@ -468,6 +468,58 @@ def check_smoothing_preserves_gated_ffn(seed: int = 15):
     assert np.linalg.norm(y1 - y0) <= 1e-5 * np.linalg.norm(y0)
 
 
+
+# -- runtime LoRA correction ------------------------------------------------------
+
+def check_lora_merged_identity(seed: int = 16):
+    """On small integers (exact in bf16 and in the products), the correction
+    equals the linear with the merged weight scale B A minus the base."""
+    g = np.random.default_rng(seed)
+    X = g.integers(-3, 4, (5, 32)).astype(np.float32)
+    A = g.integers(-2, 3, (4, 32)).astype(np.float32)
+    B = g.integers(-2, 3, (24, 4)).astype(np.float32)
+    W = g.integers(-5, 6, (24, 32)).astype(np.float32)
+    scale = 0.5
+    merged = O.linear_unquantized64(X, W + scale * (B.astype(np.float64) @ A.astype(np.float64)))
+    base = O.linear_unquantized64(X, W)
+    assert np.array_equal(base + O.lora_delta64(X, A, B, scale), merged)
+
+
+def check_lora_one_hot():
+    X = np.zeros((2, 16), np.float32); X[0, 3] = 2.0; X[1, 7] = -1.0
+    A = np.zeros((2, 16), np.float32); A[1, 3] = 0.25; A[0, 7] = 4.0
+    B = np.zeros((5, 2), np.float32); B[2, 1] = 3.0; B[4, 0] = -1.0
+    d = O.lora_delta64(X, A, B, 2.0)
+    want = np.zeros((2, 5)); want[0, 2] = 2.0 * (2.0 * 0.25) * 3.0; want[1, 4] = 2.0 * (-4.0) * -1.0
+    assert np.array_equal(d, want)
+
+
+def check_lora_intermediate_rounds_to_bf16():
+    # 1 + 2^-9 is below half a bf16 ulp above 1 (ulp 2^-7): it rounds to 1;
+    # 1 + 3 * 2^-8 rounds up to 1 + 2^-6 (ties and nearest, bf16 keeps 8 bits).
+    X = np.array([[1.0, 2.0 ** -9], [1.0, 3 * 2.0 ** -8]], np.float32)
+    A = np.array([[1.0, 1.0]], np.float32)
+    T = O.lora_intermediate(X, A)
+    assert T[:, 0].tolist() == [1.0, 1.0 + 2.0 ** -6]
+
+
+def check_lora_bruteforce(seed: int = 17):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((3, 16)).astype(np.float32)
+    A = g.standard_normal((2, 16)).astype(np.float32)
+    B = g.standard_normal((4, 2)).astype(np.float32)
+    T = O.lora_intermediate(X, A).astype(np.float64)
+    for m in range(3):
+        for j in range(2):
+            t = sum(float(X[m, k]) * float(A[j, k]) for k in range(16))
+            assert T[m, j] == O.bf16_round(np.array([t], np.float32))[0]
+    d = O.lora_delta64(X, A, B, 0.75)
+    for m in range(3):
+        for n in range(4):
+            ref = 0.75 * sum(T[m, j] * float(B[n, j]) for j in range(2))
+            assert abs(d[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
 ALL_CHECKS = [
     ("r4_printed", check_r4_printed, ()),
     *[(f"regular_structure_G{G}", check_regular_structure, (G,)) for G in REGULAR_GS],
@@ -504,6 +556,10 @@ ALL_CHECKS = [
     ("smoothing_max_norm", check_smoothing_max_norm, ()),
     ("smoothing_zero_channel", check_smoothing_zero_channel, ()),
     ("smoothing_preserves_gated_ffn", check_smoothing_preserves_gated_ffn, ()),
+    ("lora_merged_identity", check_lora_merged_identity, ()),
+    ("lora_one_hot", check_lora_one_hot, ()),
+    ("lora_intermediate_bf16", check_lora_intermediate_rounds_to_bf16, ()),
+    ("lora_bruteforce", check_lora_bruteforce, ()),
 ]
 
 

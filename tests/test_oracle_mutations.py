@@ -211,6 +211,27 @@ def _smooth_rows_of_down(W_up, W_down, norm="l2"):
     return np.sqrt(np.where(n_dn > 0, n_up / np.where(n_dn > 0, n_dn, 1), 1)).astype(np.float32)
 
 
+
+_lora_intermediate = O.lora_intermediate
+_lora_delta64 = O.lora_delta64
+
+
+def _lora_no_bf16(X, A):
+    return (np.asarray(X, np.float64) @ np.asarray(A, np.float64).T).astype(np.float32)
+
+
+def _lora_up_read_as_rn(X, A, B, scale):
+    # B [N, r] read as if it were stored [r, N] row-major (a layout mistake)
+    T = _lora_intermediate(X, A).astype(np.float64)
+    Bw = np.asarray(B, np.float64)
+    Bs = Bw.ravel().reshape(Bw.shape[1], Bw.shape[0]).T
+    return float(scale) * (T @ Bs.T)
+
+
+def _lora_no_scale(X, A, B, scale):
+    return _lora_delta64(X, A, B, 1.0)
+
+
 MUTATIONS = {
     "h4_sign_flip": ("h4", _h4_sign_flip),
     "h4_unnormalised": ("h4", _h4_unnormalised),
@@ -238,6 +259,9 @@ MUTATIONS = {
     "smooth_no_sqrt": ("smoothing_scales", _smooth_no_sqrt),
     "smooth_rows_of_down": ("smoothing_scales", _smooth_rows_of_down),
     "smooth_applied_backwards": ("apply_smoothing", _smooth_applied_backwards),
+    "lora_intermediate_not_rounded": ("lora_intermediate", _lora_no_bf16),
+    "lora_up_read_as_rn": ("lora_delta64", _lora_up_read_as_rn),
+    "lora_scale_dropped": ("lora_delta64", _lora_no_scale),
 }
 
 
