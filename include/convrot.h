@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 4
+#define CONVROT_ABI_VERSION 5
 
 typedef enum {
   CONVROT_OK = 0,
@@ -303,6 +303,32 @@ convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t
                                   convrot_dtype down_dt, int64_t ldd, int64_t F, int64_t K, int64_t K_out,
                                   convrot_smooth_norm norm, float* s, float* W_up_out, int64_t ldu_out,
                                   float* W_down_out, int64_t ldd_out, void* stream);
+
+/* Runtime LoRA correction added to a linear's output ("INT8 Convrot
+ * Safetensors", LoRA paragraph: adapters are applied at run time without
+ * touching the int8 weights; the correction is computed from the original,
+ * unrotated activation and added to the base output):
+ *   T = X A^T                 fp32 accumulation (in an unspecified order),
+ *                             held in bf16
+ *   Y[m, n] += scale * sum_j T[m, j] B[n, j]   (fp32 sum, one fused
+ *                             multiply-add into Y; bf16 Y rounded to
+ *                             nearest even)
+ *   X   [M, ldx] bf16, the layer's unrotated input (K columns)
+ *   A   [r, lda] bf16 (adapter down), B [N, ldb] bf16 (adapter up, r columns)
+ *   r   rank, a positive multiple of 16, at most 256; K a positive multiple
+ *       of 16
+ *   Y   [M, ldy] of ydt (CONVROT_F32 or CONVROT_BF16), read and written
+ *   workspace  caller-owned device memory of workspace_bytes >= M * r * 2
+ *       bytes, 16-byte aligned, for T; not shared with a concurrent call
+ * X, A, B: 16-byte aligned bases and rows.  Two launches on `stream` (the
+ * down product into the workspace, then the up product with the add).  A
+ * layer whose
+ * output goes through a fused activation must run the plain linear, this
+ * call, and the activation afterwards. */
+convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, int64_t N, int64_t r, float scale, void* Y,
+                                convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /* Static description of a status code. */
 const char* convrot_status_string(convrot_status status);

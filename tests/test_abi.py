@@ -305,3 +305,27 @@ def test_smooth_checks(lib):
     assert smooth_status(lib, uo=0x40000, lduo=32) == _lib.ERR_INVALID_ARG
     assert smooth_status(lib, do=0x50000, lddo=16) == _lib.ERR_INVALID_ARG
     assert smooth_status(lib, F=-1) == _lib.ERR_INVALID_ARG
+
+
+
+# -- runtime LoRA correction ----------------------------------------------------
+
+def lora_status(lib, X=A16, ldx=64, M=32, K=64, A=A16B, lda=64, B=A16C, ldb=16, N=48, r=16, Y=0x40000,
+                ydt=_lib.BF16, ldy=48, ws=0x50000, ws_bytes=32 * 16 * 2):
+    return lib.convrot_lora_add(X, ldx, M, K, A, lda, B, ldb, N, r, ctypes.c_float(0.5), Y, ydt, ldy, ws, ws_bytes,
+                                None)
+
+
+def test_lora_checks(lib):
+    assert lora_status(lib, r=8) == _lib.ERR_INVALID_ARG
+    assert lora_status(lib, r=0) == _lib.ERR_INVALID_ARG
+    assert lora_status(lib, r=272, ldb=272) == _lib.ERR_INVALID_ARG   # rank above 256
+    assert lora_status(lib, K=40, ldx=40, lda=40) == _lib.ERR_INVALID_ARG
+    assert lora_status(lib, ydt=_lib.I32) == _lib.ERR_DTYPE
+    assert lora_status(lib, X=MIS) == _lib.ERR_ALIGN
+    assert lora_status(lib, ldb=12) == _lib.ERR_INVALID_ARG           # ldb < r
+    assert lora_status(lib, ldb=20) == _lib.ERR_ALIGN                 # 40-byte rows
+    assert lora_status(lib, ws=None) == _lib.ERR_INVALID_ARG
+    assert lora_status(lib, ws_bytes=32 * 16 * 2 - 2) == _lib.ERR_INVALID_ARG
+    assert lora_status(lib, ws=0x50008) == _lib.ERR_ALIGN
+    assert lora_status(lib, M=0) == _lib.OK

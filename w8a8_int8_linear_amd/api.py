@@ -5,7 +5,8 @@ torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
 kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
 ``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``,
 for int4 weights (W4A8) ``pack_weight_w4``, ``linear_w4``,
-``linear_w4_gated``, ``unpack_w4``, and the offline ``smooth_ffn``.
+``linear_w4_gated``, ``unpack_w4``, the offline ``smooth_ffn`` and the
+runtime adapter correction ``lora_add``.
 """
 
 from __future__ import annotations
@@ -346,3 +347,33 @@ def smooth_ffn(w_up: torch.Tensor, w_down: torch.Tensor, norm: str = "l2", scale
         _SMOOTH[norm], s.data_ptr(), up.data_ptr() if up is not None else None, _ld(up) if up is not None else 0,
         dn.data_ptr() if dn is not None else None, _ld(dn) if dn is not None else 0, _stream(dev)))
     return (s, up, dn) if scaled else s
+
+
+# ---------------------------------------------------------------------------
+# Runtime LoRA correction
+# ---------------------------------------------------------------------------
+
+def lora_add(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor, scale: float, y: torch.Tensor,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y += scale * (x a^T) b^T in place, from the unrotated bf16 input x
+    [M, K], the adapter's down a [r, K] and up b [N, r] (convrot_lora_add).
+    The rank-r intermediate goes to ``workspace`` (allocated here when not
+    given)."""
+    for t, name in ((x, "x"), (a, "a"), (b, "b")):
+        _need_cuda(t, name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    M, K = x.shape
+    r = a.shape[0]
+    N = b.shape[0]
+    if a.shape[1] != K or b.shape[1] != r or tuple(y.shape) != (M, N):
+        raise ValueError("shapes must be x [M, K], a [r, K], b [N, r], y [M, N]")
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("y must be float32 or bfloat16")
+    if workspace is None:
+        workspace = torch.empty((max(M, 1) * r,), dtype=torch.bfloat16, device=x.device)
+    lib = _lib.load()
+    _lib.check(lib.convrot_lora_add(x.data_ptr(), _ld(x), M, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), N, r,
+                                    float(scale), y.data_ptr(), _DT[y.dtype], _ld(y), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(x.device)))
+    return y

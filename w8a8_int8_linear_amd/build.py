@@ -21,7 +21,7 @@ LIB_NAME = "libconvrot.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip", "w4.hip", "smooth.hip"]
+SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip", "w4.hip", "smooth.hip", "lora.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

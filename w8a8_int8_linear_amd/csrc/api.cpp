@@ -479,6 +479,40 @@ convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t
   return from_hip(e, what);
 }
 
+convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, int64_t N, int64_t r, float scale, void* Y,
+                                convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  const char* what = "convrot_lora_add";
+  convrot_status st = check_k(K, int64_t{1} << 30);
+  if (st != CONVROT_OK) return st;
+  if (r <= 0 || r % 16 != 0 || r > 256)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: rank r = %lld must be a positive multiple of 16, at most 256", what,
+                static_cast<long long>(r));
+  if (M < 0 || N < 0 || M > kMaxRows || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad M or N", what);
+  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "%s: Y must be CONVROT_F32 or CONVROT_BF16", what);
+  st = check_matrix("X", X, M, K, ldx, 2);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("A", A, r, K, lda, 2);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("B", B, N, r, ldb, 2);
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("Y", Y, M, N, ldy, elt_size(ydt), false);
+  if (st != CONVROT_OK) return st;
+  if (2 * ldx > kMaxLdBytes || 2 * lda > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of X or A exceeds %lld bytes",
+                static_cast<long long>(kMaxLdBytes));
+  if (M == 0 || N == 0) return ok();
+  st = check_workspace(workspace, workspace_bytes, 2 * M * r);
+  if (st != CONVROT_OK) return st;
+  const auto s = static_cast<hipStream_t>(stream);
+  hipError_t e = convrot::launch_lora_down(X, ldx, A, lda, M, K, r, workspace, r, s);
+  if (e == hipSuccess)
+    e = convrot::launch_lora_up(workspace, r, B, ldb, M, N, r, scale, Y, static_cast<convrot::Elt>(ydt), ldy, s);
+  return from_hip(e, what);
+}
+
 const char* convrot_status_string(convrot_status status) {
   switch (status) {
     case CONVROT_OK: return "CONVROT_OK";

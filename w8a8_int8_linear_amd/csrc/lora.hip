@@ -1,0 +1,194 @@
+// Runtime LoRA correction added to a linear's output, for gfx950.
+//
+// "INT8 Convrot Safetensors", LoRA paragraph: adapters are applied at run
+// time without touching the int8 weights; the correction is computed from
+// the original, unrotated activation and added to the base output.  With the
+// adapter's down and up matrices A [r, K] and B [N, r]:
+//   T = X A^T              rank-r intermediate, fp32 accumulation, held in
+//                          bf16 (the bf16 linear kernels of this library)
+//   Y[m, n] += scale * sum_j T[m, j] B[n, j]
+// Both products are here, each bound by one operand's bytes:
+//  * down (T = X A^T, r <= 256): a workgroup takes 16 rows of X and all r
+//    columns; its four waves split K, stream their X range through
+//    v_mfma_f32_16x16x32_bf16 (A's rows as the row operand, from L2), and
+//    add their partial sums through LDS; T is rounded to bf16 once;
+//  * up (Y += scale T B^T): K = r is small, so a launch is bound by reading
+//    and writing Y.  A workgroup owns a 64 x 64 block of Y; each wave takes 16
+//    rows and four 16-feature MFMA tiles; the block is staged in LDS so that
+//    each thread reads, updates and writes 16 contiguous features of one row
+//    (whole lines of Y); one fused multiply-add per element (bf16 Y: rounded
+//    to nearest even).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "launchers.h"
+
+namespace convrot {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 8 bf16 of row `row` at element k (zeros when k is past r).
+__device__ __forceinline__ i32x4 load8(const __bf16* base, int64_t ld, int row, int k, int r) {
+  if (k >= r) return i32x4{0, 0, 0, 0};
+  return *reinterpret_cast<const i32x4*>(base + static_cast<int64_t>(row) * ld + k);
+}
+
+// T = X A^T for 16 rows of X per workgroup (r <= kMaxRank, r % 16 == 0).
+constexpr int kMaxRank = 256;
+
+template <int RT>  // 16-feature tiles of r
+__global__ __launch_bounds__(256) void lora_down_kernel(const __bf16* __restrict__ X, int64_t ldx,
+                                                        const __bf16* __restrict__ A, int64_t lda, int M, int K,
+                                                        int r, __bf16* __restrict__ T, int64_t ldt) {
+  __shared__ f32x4 partial[3][RT][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row = lane & 15, ch = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int mx = min(m0 + row, M - 1);
+  const int steps = (K + 31) / 32;
+  const int per = (steps + 3) / 4;
+  const int s0 = wid * per, s1 = min(steps, s0 + per);
+  f32x4 acc[RT] = {};
+  for (int st = s0; st < s1; ++st) {
+    const int k = 32 * st + 8 * ch;
+    const i32x4 x = load8(X, ldx, mx, k, K);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      if (16 * j >= r) break;
+      const i32x4 w = load8(A, lda, 16 * j + row, k, K);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x),
+                                                       acc[j], 0, 0, 0);
+    }
+  }
+  if (wid > 0) {
+#pragma unroll
+    for (int j = 0; j < RT; ++j) partial[wid - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wid != 0) return;
+  // Lane holds row m0 + row and features 16 j + 4 ch + e.
+  const int m = m0 + row;
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    if (16 * j >= r) break;
+    const f32x4 v = acc[j] + partial[0][j][lane] + partial[1][j][lane] + partial[2][j][lane];
+    if (m < M) {
+      *reinterpret_cast<bf16x4*>(T + static_cast<int64_t>(m) * ldt + 16 * j + 4 * ch) =
+          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                 static_cast<__bf16>(v[3])};
+    }
+  }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void lora_up_kernel(const __bf16* __restrict__ T, int64_t ldt,
+                                                      const __bf16* __restrict__ Bw, int64_t ldb, int M, int N, int r,
+                                                      float scale, void* __restrict__ Y, int64_t ldy) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row = lane & 15, ch = lane >> 4;
+  const int m0 = blockIdx.y * 64 + wid * 16;
+  const int n0 = blockIdx.x * 64;
+  const int mt = min(m0 + row, M - 1);  // rows past the end re-read the last one; their outputs are dropped
+  // The workgroup's 64 B rows of each 32-wide k step are loaded once (one
+  // 16-byte piece per thread) into LDS and shared by the four waves.
+  constexpr int kBPitch = 40;  // bf16 per staged B row (32 + padding across banks)
+  __shared__ __bf16 bstage[64 * kBPitch];
+  const int br = threadIdx.x >> 2, bp = 8 * (threadIdx.x & 3);
+  const int brow = min(n0 + br, N - 1);
+  f32x4 acc[4] = {};
+  for (int k0 = 0; k0 < r; k0 += 32) {
+    const int k = k0 + 8 * ch;
+    const i32x4 t = load8(T, ldt, mt, k, r);
+    *reinterpret_cast<i32x4*>(&bstage[br * kBPitch + bp]) = load8(Bw, ldb, brow, k0 + bp, r);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x4 b = *reinterpret_cast<const i32x4*>(&bstage[(16 * j + row) * kBPitch + 8 * ch]);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t), __builtin_bit_cast(bf16x8, b),
+                                                       acc[j], 0, 0, 0);
+    }
+    __syncthreads();  // the next step overwrites the staged rows
+  }
+  // Lane holds rows 4 ch + e (e = 0..3) of the wave's 16 and feature
+  // 16 j + row: stage the workgroup's 64 x 64 block in LDS, then every
+  // thread updates 16 contiguous features of one row, so each row's 64
+  // features of Y are read and written as whole lines.
+  __shared__ float stage[64][64 + 4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) stage[16 * wid + 4 * ch + e][16 * j + row] = acc[j][e];
+  __syncthreads();
+  const int tr = threadIdx.x >> 2, tc = 16 * (threadIdx.x & 3);
+  const int m = blockIdx.y * 64 + tr;
+  const int n = n0 + tc;
+  if (m >= M || n >= N) return;
+  using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
+  out_t* y = static_cast<out_t*>(Y) + static_cast<int64_t>(m) * ldy + n;
+  const float* v = &stage[tr][tc];
+  if (n + 15 < N && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+    if constexpr (OUT == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 o = reinterpret_cast<f32x4*>(y)[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(scale, v[4 * q + e], o[e]);
+        reinterpret_cast<f32x4*>(y)[q] = o;
+      }
+    } else {
+      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8v o = reinterpret_cast<bf16x8v*>(y)[q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(fmaf(scale, v[8 * q + e], static_cast<float>(o[e])));
+        reinterpret_cast<bf16x8v*>(y)[q] = o;
+      }
+    }
+  } else {
+    for (int e = 0; e < 16 && n + e < N; ++e) y[e] = static_cast<out_t>(fmaf(scale, v[e], static_cast<float>(y[e])));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lora_down(const void* X, int64_t ldx, const void* A, int64_t lda, int64_t M, int64_t K, int64_t r,
+                            void* T, int64_t ldt, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((M + 15) / 16));
+  const auto* x = static_cast<const __bf16*>(X);
+  const auto* a = static_cast<const __bf16*>(A);
+  auto* t = static_cast<__bf16*>(T);
+  const int m = static_cast<int>(M), k = static_cast<int>(K), rr = static_cast<int>(r);
+  if (r <= 32)
+    hipLaunchKernelGGL(lora_down_kernel<2>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
+  else if (r <= 64)
+    hipLaunchKernelGGL(lora_down_kernel<4>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
+  else if (r <= 128)
+    hipLaunchKernelGGL(lora_down_kernel<8>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
+  else
+    hipLaunchKernelGGL(lora_down_kernel<16>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_up(const void* T, int64_t ldt, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t r,
+                          float scale, void* Y, Elt out, int64_t ldy, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64));
+  const auto* t = static_cast<const __bf16*>(T);
+  const auto* b = static_cast<const __bf16*>(B);
+  if (out == Elt::F32)
+    hipLaunchKernelGGL(lora_up_kernel<0>, grid, dim3(256), 0, stream, t, ldt, b, ldb, static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(r), scale, Y, ldy);
+  else
+    hipLaunchKernelGGL(lora_up_kernel<1>, grid, dim3(256), 0, stream, t, ldt, b, ldb, static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(r), scale, Y, ldy);
+  return hipGetLastError();
+}
+
+}  // namespace convrot
