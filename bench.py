@@ -13,6 +13,9 @@ separate torch op after plain linears instead.
 Workloads (``--workload``):
   dit_attn_proj  (default) X bf16 [4096, 3072], 8 outlier channels; fused QKV
                  W [9216, 3072] and a second W [3072, 3072] share one pack.
+                 Suffix "_lora{r}": a rank-r adapter on the QKV layer, its
+                 correction computed from the unrotated X and added to the
+                 QKV output (two launches after the linear).
   dit_mlp        X bf16 [8192, 3072]; W_up [12288, 3072], GELU, W_down
                  [3072, 12288].
   large_m_qkv    X bf16 [32700, 6144]; W [18432, 6144]; plus the routed layer
@@ -107,6 +110,12 @@ def make_workload(name: str):
 
     if name == "dit_attn_proj":
         return W.config2()
+    m = re.fullmatch(r"dit_attn_proj_lora(\d+)", name)
+    if m:
+        wl = W.config2()
+        wl.name += f"_lora{m.group(1)}"
+        wl.extra["lora_rank"] = int(m.group(1))
+        return wl
     if name == "dit_mlp":
         return W.config3()
     if name == "large_m_qkv":
@@ -132,6 +141,7 @@ class Op:
         # "" plain, "act" activation in the epilogue, "gated" act(gate) * up:
         # N output columns from 2N weight rows
         self.epilogue = epilogue
+        self.epilogue_rank = 0  # LoRA rank of a "lora" launch
 
     @property
     def kernel(self):
@@ -143,6 +153,8 @@ class Op:
             return "gemm_i8" + (f"_{self.epilogue}" if self.epilogue else "")
         if self.kind == "bf16":
             return "gemm_bf16"
+        if self.kind == "lora":
+            return "lora"
         return "torch"
 
     @property
@@ -163,6 +175,10 @@ class Op:
             return M * K + 4 * M + wb + 8 * R + M * N * self.out_b
         if self.kind == "bf16":
             return 2 * M * K + 2 * N * K + 4 * N + M * N * self.out_b
+        if self.kind == "lora":
+            # X and A read, T written and read, B read, Y read and written (K here is the rank's input width)
+            r = self.epilogue_rank
+            return 2 * M * K + 2 * r * K + 4 * M * r + 2 * N * r + 2 * M * N * self.out_b
         return 0
 
 
@@ -202,7 +218,14 @@ class StepSet:
                     del wd
                 self.b[lin.name] = up(lin.b, f32) if lin.b is not None else None
             self.X2 = up(wl.extra["X_routed"], bf16) if "X_routed" in wl.extra else None
+            self.lora = None
+            if wl.extra.get("lora_rank"):
+                import workloads as Wmod
+                qkv = wl.linears[0]
+                A, Bm = Wmod.lora_adapter(qkv.W.shape[1], qkv.W.shape[0], wl.extra["lora_rank"])
+                self.lora = (up(A, bf16), up(Bm, bf16))
         else:
+            self.lora = template.lora
             self.signs = template.signs
             self.X = template.X.clone()
             self.W = {k: (cr.Packed(v.q.clone(), v.scale.clone(), v.group, v.kind, v.signs)
@@ -279,7 +302,17 @@ class StepSet:
             src0 = self.X
         if wl.cfg in (1, 2):
             for n in names:
-                ops.append(self._linear_op(n, src0, self._out(n, M, dev)))
+                y = self._out(n, M, dev)
+                ops.append(self._linear_op(n, src0, y))
+                if self.lora is not None and n == names[0]:
+                    A, Bm = self.lora
+                    r = A.shape[0]
+                    ws = torch.empty(M * r, dtype=torch.bfloat16, device=dev)
+                    self.bufs.append(ws)
+                    op = Op(f"lora_{n}", lambda y=y, ws=ws: self.cr.lora_add(self.X, A, Bm, 0.5, y, workspace=ws),
+                            "lora", M=M, N=y.shape[1], K=K, out_b=y.element_size())
+                    op.epilogue_rank = r
+                    ops.append(op)
         elif wl.cfg == 3:
             if self.fused:
                 # GELU in the up projection's epilogue
@@ -409,11 +442,19 @@ def cpu_baseline(wl, budget_s: float = 12.0):
             return [gemm(n, qx, sx) for n in names]
         return [layer(n, x) for n in names]
 
+    adapter = None
+    if wl.extra.get("lora_rank"):
+        import workloads as Wmod
+        qkv = wl.linears[0]
+        adapter = Wmod.lora_adapter(qkv.W.shape[1], qkv.W.shape[0], wl.extra["lora_rank"])
+
     def run(m):
         t0 = time.perf_counter()
         x = wl.X[:m]
         if wl.cfg in (1, 2):
-            shared(list(l.name for l in wl.linears), x)
+            ys = shared(list(l.name for l in wl.linears), x)
+            if adapter is not None:
+                ys[0] = ys[0] + O.lora_delta64(x, adapter[0], adapter[1], 0.5).astype(np.float32)
         elif wl.cfg == 3:
             layer("down", _gelu_erf(layer("up", x)).astype(np.float32))
         elif wl.cfg == 4:

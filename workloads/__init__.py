@@ -221,3 +221,12 @@ def smoothing_study_ffn(M: int = 64, K: int = 3072, F: int = 8192, sigma_c: floa
     Wu = to_bf16_values((g.standard_normal((F, K)) * 0.02 * c[:, None]).astype(np.float32))
     Wd = to_bf16_values((g.standard_normal((K, F)) * 0.02 / c[None, :]).astype(np.float32))
     return X, Wg, Wu, Wd
+
+
+def lora_adapter(K: int, N: int, r: int, seed: int = 31):
+    """Seeded bf16 LoRA pair for a layer [N, K]: A [r, K] ~N(0, 1/K) (down),
+    B [N, r] ~N(0, 0.02) (up)."""
+    g = np.random.default_rng(seed)
+    A = to_bf16_values((g.standard_normal((r, K)) / np.sqrt(K)).astype(np.float32))
+    B = to_bf16_values((g.standard_normal((N, r)) * 0.02).astype(np.float32))
+    return A, B
