@@ -8,10 +8,11 @@
 //                          bf16 (the bf16 linear kernels of this library)
 //   Y[m, n] += scale * sum_j T[m, j] B[n, j]
 // Both products are here, each bound by one operand's bytes:
-//  * down (T = X A^T, r <= 256): a workgroup takes 16 rows of X and all r
-//    columns; its four waves split K, stream their X range through
-//    v_mfma_f32_16x16x32_bf16 (A's rows as the row operand, from L2), and
-//    add their partial sums through LDS; T is rounded to bf16 once;
+//  * down (T = X A^T, r <= 256): a workgroup takes up to 64 rows of X and
+//    all r columns; each wave multiplies its row tiles by every fragment of
+//    A it loads (v_mfma_f32_16x16x32_bf16, A's rows as the row operand, from
+//    L2), its eight waves split K and add their partial sums through LDS; T
+//    is rounded to bf16 once;
 //  * up (Y += scale T B^T): K = r is small, so a launch is bound by reading
 //    and writing Y.  A workgroup owns a 64 x 64 block of Y; each wave takes 16
 //    rows and four 16-feature MFMA tiles; the block is staged in LDS so that
@@ -38,49 +39,80 @@ __device__ __forceinline__ i32x4 load8(const __bf16* base, int64_t ld, int row, 
   return *reinterpret_cast<const i32x4*>(base + static_cast<int64_t>(row) * ld + k);
 }
 
-// T = X A^T for 16 rows of X per workgroup (r <= kMaxRank, r % 16 == 0).
+// T = X A^T for 16 MT rows of X per workgroup (r <= kMaxRank, r % 16 == 0):
+// each wave multiplies its MT row tiles by every fragment of A it loads, and
+// the eight waves split K.
 constexpr int kMaxRank = 256;
+constexpr int kDownWaves = 8;
 
-template <int RT>  // 16-feature tiles of r
-__global__ __launch_bounds__(256) void lora_down_kernel(const __bf16* __restrict__ X, int64_t ldx,
-                                                        const __bf16* __restrict__ A, int64_t lda, int M, int K,
-                                                        int r, __bf16* __restrict__ T, int64_t ldt) {
-  __shared__ f32x4 partial[3][RT][64];
+template <int RT, int MT>  // 16-feature tiles of r, 16-row tiles of X per wave
+__global__ __launch_bounds__(64 * kDownWaves) void lora_down_kernel(const __bf16* __restrict__ X, int64_t ldx,
+                                                                    const __bf16* __restrict__ A, int64_t lda,
+                                                                    int M, int K, int r, __bf16* __restrict__ T,
+                                                                    int64_t ldt) {
+  __shared__ f32x4 partial[kDownWaves - 1][MT * RT][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int row = lane & 15, ch = lane >> 4;
-  const int m0 = blockIdx.x * 16;
-  const int mx = min(m0 + row, M - 1);
+  const int m0 = blockIdx.x * 16 * MT;
   const int steps = (K + 31) / 32;
-  const int per = (steps + 3) / 4;
+  const int per = (steps + kDownWaves - 1) / kDownWaves;
   const int s0 = wid * per, s1 = min(steps, s0 + per);
-  f32x4 acc[RT] = {};
-  for (int st = s0; st < s1; ++st) {
+  f32x4 acc[MT][RT] = {};
+  // One k step of fragments; the next step's are requested before the
+  // current step is multiplied.
+  struct Frags {
+    i32x4 x[MT];
+    i32x4 w[RT];
+  };
+  auto load = [&](int st, Frags& f) {
     const int k = 32 * st + 8 * ch;
-    const i32x4 x = load8(X, ldx, mx, k, K);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) f.x[i] = load8(X, ldx, min(m0 + 16 * i + row, M - 1), k, K);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) f.w[j] = 16 * j < r ? load8(A, lda, 16 * j + row, k, K) : i32x4{0, 0, 0, 0};
+  };
+  auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
       if (16 * j >= r) break;
-      const i32x4 w = load8(A, lda, 16 * j + row, k, K);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x),
-                                                       acc[j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.w[j]),
+                                                            __builtin_bit_cast(bf16x8, f.x[i]), acc[i][j], 0, 0, 0);
     }
+  };
+  Frags fa, fb;
+  if (s0 < s1) load(s0, fa);
+  for (int st = s0; st < s1; st += 2) {
+    if (st + 1 < s1) load(st + 1, fb);
+    mma(fa);
+    if (st + 1 >= s1) break;
+    if (st + 2 < s1) load(st + 2, fa);
+    mma(fb);
   }
   if (wid > 0) {
 #pragma unroll
-    for (int j = 0; j < RT; ++j) partial[wid - 1][j][lane] = acc[j];
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < RT; ++j) partial[wid - 1][i * RT + j][lane] = acc[i][j];
   }
   __syncthreads();
   if (wid != 0) return;
-  // Lane holds row m0 + row and features 16 j + 4 ch + e.
-  const int m = m0 + row;
+  // Lane holds row m0 + 16 i + row and features 16 j + 4 ch + e.
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    if (16 * j >= r) break;
-    const f32x4 v = acc[j] + partial[0][j][lane] + partial[1][j][lane] + partial[2][j][lane];
-    if (m < M) {
-      *reinterpret_cast<bf16x4*>(T + static_cast<int64_t>(m) * ldt + 16 * j + 4 * ch) =
-          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                 static_cast<__bf16>(v[3])};
+  for (int i = 0; i < MT; ++i) {
+    const int m = m0 + 16 * i + row;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      if (16 * j >= r) break;
+      f32x4 v = acc[i][j];
+#pragma unroll
+      for (int w = 0; w < kDownWaves - 1; ++w) v += partial[w][i * RT + j][lane];
+      if (m < M) {
+        *reinterpret_cast<bf16x4*>(T + static_cast<int64_t>(m) * ldt + 16 * j + 4 * ch) =
+            bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                   static_cast<__bf16>(v[3])};
+      }
     }
   }
 }
@@ -160,19 +192,26 @@ __global__ __launch_bounds__(256) void lora_up_kernel(const __bf16* __restrict__
 hipError_t launch_lora_down(const void* X, int64_t ldx, const void* A, int64_t lda, int64_t M, int64_t K, int64_t r,
                             void* T, int64_t ldt, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((M + 15) / 16));
   const auto* x = static_cast<const __bf16*>(X);
   const auto* a = static_cast<const __bf16*>(A);
   auto* t = static_cast<__bf16*>(T);
   const int m = static_cast<int>(M), k = static_cast<int>(K), rr = static_cast<int>(r);
-  if (r <= 32)
-    hipLaunchKernelGGL(lora_down_kernel<2>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
-  else if (r <= 64)
-    hipLaunchKernelGGL(lora_down_kernel<4>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
-  else if (r <= 128)
-    hipLaunchKernelGGL(lora_down_kernel<8>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
-  else
-    hipLaunchKernelGGL(lora_down_kernel<16>, grid, dim3(256), 0, stream, x, ldx, a, lda, m, k, rr, t, ldt);
+  const dim3 block(64 * kDownWaves);
+  // Row tiles per wave: enough to share A's fragments, few enough to keep
+  // 128 or more workgroups at M = 4096 and the LDS partials within 112 KiB.
+  if (r <= 32) {
+    hipLaunchKernelGGL((lora_down_kernel<2, 2>), dim3(static_cast<unsigned>((M + 31) / 32)), block, 0, stream, x,
+                       ldx, a, lda, m, k, rr, t, ldt);
+  } else if (r <= 64) {
+    hipLaunchKernelGGL((lora_down_kernel<4, 4>), dim3(static_cast<unsigned>((M + 63) / 64)), block, 0, stream, x,
+                       ldx, a, lda, m, k, rr, t, ldt);
+  } else if (r <= 128) {
+    hipLaunchKernelGGL((lora_down_kernel<8, 2>), dim3(static_cast<unsigned>((M + 31) / 32)), block, 0, stream, x,
+                       ldx, a, lda, m, k, rr, t, ldt);
+  } else {
+    hipLaunchKernelGGL((lora_down_kernel<16, 1>), dim3(static_cast<unsigned>((M + 15) / 16)), block, 0, stream, x,
+                       ldx, a, lda, m, k, rr, t, ldt);
+  }
   return hipGetLastError();
 }
 
