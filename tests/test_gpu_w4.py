@@ -187,3 +187,22 @@ def test_small_m_two_tile_workgroups(cuda, M, N, K):
     wb = to_bf16_values(random_rows((N, K), 4) * np.float32(0.05))
     yb = to_np(cr.linear_bf16(to_dev(xb, torch.bfloat16), to_dev(wb, torch.bfloat16), out_dtype=torch.float32))
     assert R.rel_fro(yb, O.linear_unquantized64(xb, wb)) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 3200, 8192), (8, 2000, 4112), (5, 6912, 1152), (16, 1300, 3136),
+                                   (2, 17000, 2080)])
+def test_small_m_int8_staged_weights(cuda, M, N, K):
+    """int8 weights staged through LDS in whole lines (waves streaming five
+    or more K steps): with split K (3200 x 8192), K tails inside a two-step
+    round (4112, 3136), odd step counts per wave, and two tiles per
+    workgroup (17000); plain and gated, against the exact accumulator."""
+    qx, sx, _, sw, b = _operands(M, N, K, 7 * N + K)
+    qg, qu = random_codes((N, K), N + 5), random_codes((N, K), N + 6)
+    a = cr.Packed(to_dev(qx, torch.int8), to_dev(sx, torch.float32), 16)
+    wg = cr.Packed(to_dev(qg, torch.int8), to_dev(sw, torch.float32), 16)
+    wu = cr.Packed(to_dev(qu, torch.int8), to_dev(sw, torch.float32), 16)
+    assert np.array_equal(to_np(cr.linear(a, wg, out_dtype=torch.int32)), O.int_gemm(qx, qg))
+    g64 = O.epilogue64(O.int_gemm(qx, qg), sx, sw)
+    u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
+    y = to_np(cr.linear_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))
+    assert R.rel_fro(y, R.gelu64(g64, "gelu_tanh") * u64) <= 1e-5

@@ -21,6 +21,10 @@
 //    re-read the last row; their outputs are dropped).
 //  * Loads come in double-buffered rounds: the next round is requested
 //    before the current one is multiplied.
+//  * int8 weights, where a wave streams at least five steps: each row's
+//    128-byte line goes global -> LDS whole (global_load_lds_dwordx4, 8 rows
+//    per transfer, chunks XOR-swizzled by row) and the MFMA fragments are
+//    read from LDS, so a line is touched once instead of twice.
 //  * The partial accumulators of the waves are summed through LDS (exact in
 //    int8 mode) and wave 0 applies the epilogue, writing 4 consecutive
 //    outputs per lane.
@@ -88,6 +92,20 @@ struct Mma<false> {
 template <typename T>
 __device__ __forceinline__ bool vec_ok(const T* p) {
   return (reinterpret_cast<uintptr_t>(p) & (4 * sizeof(T) - 1)) == 0;
+}
+
+typedef __attribute__((address_space(3))) void* gemv_lds_ptr_t;
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds + 16 l.
+__device__ __forceinline__ void gemv_dma16(const uint8_t* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (gemv_lds_ptr_t)lds, 16, 0, 0);
+}
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void gemv_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Split-K state of one launch: partials [tile][split][set][64 lanes] x 16
@@ -162,7 +180,7 @@ __device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, 
 // the same assignment of k to (MFMA, lane), so every product pairs matching
 // k; the int32 sum does not depend on the order.
 template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false, bool W4 = false,
-          int TILES = 1>
+          int TILES = 1, bool DMA = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
     int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp) {
@@ -174,6 +192,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   constexpr int kUnit = W4 ? 128 : kStepBytes;  // activation bytes per K unit
   constexpr int kRound = TILES == 1 ? 4 : 2;    // units per round of loads (two rounds in flight per wave)
   __shared__ Acc partial[kSets * TILES][WAVES > 1 ? WAVES - 1 : 1][64];
+  static_assert(!DMA || (I8 && !W4), "LDS staging is the int8-weight path");
+  constexpr bool kDma = DMA;  // int8 weights staged through LDS in whole lines
+  __shared__ __attribute__((aligned(16))) uint8_t wring[kDma ? WAVES : 1][2][kDma ? kSets * TILES : 1][kDma ? 2048 : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -268,6 +289,87 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
           }
         }
   };
+  if constexpr (kDma) {
+    // int8 weights through LDS in whole lines.  A round is two K steps: one
+    // 128-byte line of each of the 16 rows of every (set, tile), fetched by
+    // two transfers of 8 rows x 128 bytes (lane l: row l / 8 of the half,
+    // 16-byte chunk (l % 8) ^ (row % 8) of the line, so that the fragment
+    // reads below spread over the LDS banks).  Rounds are double-buffered
+    // in the wave's own LDS ring.  Every round issues the same number of
+    // transfers and activation loads (addresses clamped into the rows), so
+    // a fixed vmcnt retires exactly the previous round; chunks past K or
+    // past the wave's range meet zero activations.
+    constexpr int kSlots = kSets * TILES;
+    constexpr int kOpsPerRound = 2 * kSlots + 2;  // transfers + activation loads
+    uint8_t* ring = &wring[wid][0][0][0];
+    const int drow = lane >> 3;
+    const int dchunk = (lane & 7) ^ drow;
+    const uint8_t* dbase[kSets][TILES][2];
+#pragma unroll
+    for (int t = 0; t < kSets; ++t)
+#pragma unroll
+      for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t n = min(n0 + 16 * i + 8 * h + drow, N - 1);
+          dbase[t][i][h] = (t == 0 ? B + n * ldb : epi.B2 + n * epi.ldb2);
+        }
+    auto issue = [&](int u0, int buf, i32x4 (&x)[2], bool (&xv)[2]) {
+      const int byte = u0 * kStepBytes;
+      const int off = byte + dchunk * 16 + 16 <= kbytes ? byte + dchunk * 16 : 0;
+#pragma unroll
+      for (int t = 0; t < kSets; ++t)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) gemv_dma16(dbase[t][i][h] + off, ring + (buf * kSlots + t * TILES + i) * 2048 + h * 1024);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int b = byte + q * kStepBytes;
+        xv[q] = u0 + q < u_end && b + ch * 16 < kbytes;
+        x[q] = *reinterpret_cast<const i32x4*>(xrow + (xv[q] ? b : 0));
+      }
+    };
+    auto consume = [&](int buf, const i32x4 (&x)[2], const bool (&xv)[2]) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const i32x4 xq = xv[q] ? x[q] : i32x4{0, 0, 0, 0};
+        const int off = row * 128 + (((4 * q + ch) ^ (row & 7)) << 4);
+#pragma unroll
+        for (int t = 0; t < kSets; ++t)
+#pragma unroll
+          for (int i = 0; i < TILES; ++i) {
+            const i32x4 w = *reinterpret_cast<const i32x4*>(ring + (buf * kSlots + t * TILES + i) * 2048 + off);
+            acc[t][i] = Mma<I8>::run(w, xq, acc[t][i]);
+          }
+      }
+    };
+    i32x4 xa[2], xb[2];
+    bool va[2], vb[2];
+    if (u_begin < u_end) issue(u_begin, 0, xa, va);
+    int buf = 0;
+    for (int u0 = u_begin; u0 < u_end; u0 += 4) {
+      const bool more = u0 + 2 < u_end;
+      if (more) {
+        issue(u0 + 2, buf ^ 1, xb, vb);
+        gemv_wait_vm<kOpsPerRound>();
+      } else {
+        gemv_wait_vm<0>();
+      }
+      consume(buf, xa, va);
+      if (!more) break;
+      buf ^= 1;
+      const bool more2 = u0 + 4 < u_end;
+      if (more2) {
+        issue(u0 + 4, buf ^ 1, xa, va);
+        gemv_wait_vm<kOpsPerRound>();
+      } else {
+        gemv_wait_vm<0>();
+      }
+      consume(buf, xb, vb);
+      buf ^= 1;
+    }
+  } else {
   Round ra, rb;
   if (u_begin < u_end) load(u_begin, ra);
   for (int u0 = u_begin; u0 < u_end; u0 += 2 * kRound) {
@@ -276,6 +378,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     if (u0 + kRound >= u_end) break;
     if (u0 + 2 * kRound < u_end) load(u0 + 2 * kRound, ra);
     mma(rb);
+  }
   }
 
   if (WAVES > 1) {
@@ -368,17 +471,17 @@ inline int gemv_num_cus() {
   return cus;
 }
 
-template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1>
+template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1, bool DMA = false>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
                   const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
                   hipStream_t stream) {
   switch (waves) {
     case 4:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES>), grid, dim3(256), 0, stream, a,
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(256), 0, stream, a,
                          lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
       break;
     default:
-      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES>), grid, dim3(512), 0, stream, a,
+      hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(512), 0, stream, a,
                          lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
       break;
   }
@@ -397,6 +500,10 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   constexpr int kSets = GATED ? 2 : 1;
   constexpr int kUnit = W4 ? 128 : kStepBytes;
   constexpr int kStepsPerUnit = kUnit / kStepBytes;
+  // int8 weights go through LDS in whole lines when a wave streams enough
+  // steps for the staging to pay (a round is two steps).
+  constexpr bool kStageable = I8 && !W4;
+  constexpr int kStageMinUnits = 5;
   const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
   const auto* a = static_cast<const uint8_t*>(A);
@@ -419,8 +526,13 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const int waves = waves_for(units);
     const int per = static_cast<int>((units + waves - 1) / waves);
     const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(units)};
-    launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splits)),
-                                                a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, stream);
+    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splits));
+    if (kStageable && per >= kStageMinUnits)
+      launch_waves<I8, OUT, ACT, GATED, true, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
+                                                                 ldc, sp, stream);
+    else
+      launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp,
+                                                  stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_combine_kernel<I8, OUT, ACT, GATED>), dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
@@ -432,14 +544,25 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   // Two tiles per workgroup share every activation fragment once there are
   // at least four tiles per CU (plain launches only; with fewer, the
   // workgroups of two tiles spread unevenly over the CUs).
+  const bool stage = kStageable && per >= kStageMinUnits;
+  const SplitArgs none{nullptr, 1, 0};
   if (!GATED && tiles >= 4 * cus) {
-    launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2>(
-        waves, dim3(static_cast<unsigned>((tiles + 1) / 2)), a, lda, b, ldb, epi, m, n, kb, per, C, ldc,
-        SplitArgs{nullptr, 1, 0}, stream);
+    const dim3 grid(static_cast<unsigned>((tiles + 1) / 2));
+    if (stage)
+      launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n,
+                                                                              kb, per, C, ldc, none, stream);
+    else
+      launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
+                                                                  ldc, none, stream);
     return hipGetLastError();
   }
-  launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, dim3(static_cast<unsigned>(tiles)), a, lda, b, ldb, epi, m, n,
-                                               kb, per, C, ldc, SplitArgs{nullptr, 1, 0}, stream);
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (stage)
+    launch_waves<I8, OUT, ACT, GATED, false, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
+                                                                ldc, none, stream);
+  else
+    launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none,
+                                                 stream);
   return hipGetLastError();
 }
 
