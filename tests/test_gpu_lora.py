@@ -84,3 +84,26 @@ def test_convrot_layer_with_adapter(cuda):
     cr.lora_add(xd, to_dev(a, torch.bfloat16), to_dev(b, torch.bfloat16), 0.5, y)
     ref = O.linear(x, *O.pack(W, G)[:2], None, G)["y64"] + O.lora_delta64(x, a, b, 0.5)
     assert R.rel_fro(to_np(y), ref) <= R.Y_RTOL
+
+
+def test_layer_int4_weights_with_adapter(cuda):
+    """ConvRotLinear with int4 weights and an attached adapter, on a 3-D
+    input: the W4A8 linear of the packed input plus the adapter's
+    correction from the unrotated input."""
+    B_, S, K, N, r, G = 2, 24, 1024, 640, 16, 256
+    g = np.random.default_rng(41)
+    x = to_bf16_values(g.standard_normal((B_ * S, K)).astype(np.float32))
+    W = to_bf16_values((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bias = (g.standard_normal(N) * 0.01).astype(np.float32)
+    _, a, b = _adapter(1, K, N, r, 42)
+    layer = cr.ConvRotLinear.from_dense(to_dev(W, torch.bfloat16), to_dev(bias, torch.float32), G, weight_bits=4)
+    layer.add_lora(to_dev(a, torch.bfloat16), to_dev(b, torch.bfloat16), 0.5)
+    assert layer.weight_bits == 4 and layer.quantized
+    y = layer(to_dev(x, torch.bfloat16).reshape(B_, S, K), out_dtype=torch.float32)
+    assert tuple(y.shape) == (B_, S, N)
+    nib, s_w, q4, _ = O.pack_weight_int4(W, G)
+    qx, sx, _ = O.pack(x, G)
+    ref = O.epilogue64(O.int_gemm(qx, O.unpack_nibbles(nib)), sx, s_w, bias) + O.lora_delta64(x, a, b, 0.5)
+    assert R.rel_fro(to_np(y).reshape(B_ * S, N), ref) <= R.Y_RTOL
+    with pytest.raises(ValueError):
+        layer(layer.pack_input(to_dev(x, torch.bfloat16)))
