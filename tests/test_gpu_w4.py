@@ -206,3 +206,20 @@ def test_small_m_int8_staged_weights(cuda, M, N, K):
     u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
     y = to_np(cr.linear_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))
     assert R.rel_fro(y, R.gelu64(g64, "gelu_tanh") * u64) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 3200, 8192), (5, 6912, 4096), (12, 9000, 5152), (3, 17000, 2080)])
+def test_small_m_int4_staged_weights(cuda, M, N, K):
+    """int4 weights staged through LDS in whole lines (waves streaming five
+    or more 128-code units, K % 32 == 0): split K (3200 x 8192), a K tail
+    inside a unit with ragged N (9000 x 5152), two tiles per workgroup
+    (17000); plain and gated, against the exact accumulator."""
+    qx, sx, qg, sw, _ = _operands(M, N, K, 11 * N + K)
+    qu = random_codes4((N, K), N + 9)
+    a = cr.Packed(to_dev(qx, torch.int8), to_dev(sx, torch.float32), 16)
+    wg, wu = _w4(qg, sw, 16), _w4(qu, sw, 16)
+    assert np.array_equal(to_np(cr.linear_w4(a, wg, out_dtype=torch.int32)), O.int_gemm(qx, qg))
+    g64 = O.epilogue64(O.int_gemm(qx, qg), sx, sw)
+    u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
+    y = to_np(cr.linear_w4_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))
+    assert R.rel_fro(y, R.gelu64(g64, "gelu_tanh") * u64) <= 1e-5

@@ -21,10 +21,11 @@
 //    re-read the last row; their outputs are dropped).
 //  * Loads come in double-buffered rounds: the next round is requested
 //    before the current one is multiplied.
-//  * int8 weights, where a wave streams at least five steps: each row's
-//    128-byte line goes global -> LDS whole (global_load_lds_dwordx4, 8 rows
-//    per transfer, chunks XOR-swizzled by row) and the MFMA fragments are
-//    read from LDS, so a line is touched once instead of twice.
+//  * Where a wave streams at least five K units, each weight row's 128-byte
+//    line goes global -> LDS whole (global_load_lds_dwordx4, 8 rows per
+//    transfer, chunks XOR-swizzled by row) and the MFMA fragments are read
+//    from LDS, so a line is touched once instead of twice (int8 weights, and
+//    int4 weights with K % 32 == 0).
 //  * The partial accumulators of the waves are summed through LDS (exact in
 //    int8 mode) and wave 0 applies the epilogue, writing 4 consecutive
 //    outputs per lane.
@@ -192,8 +193,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   constexpr int kUnit = W4 ? 128 : kStepBytes;  // activation bytes per K unit
   constexpr int kRound = TILES == 1 ? 4 : 2;    // units per round of loads (two rounds in flight per wave)
   __shared__ Acc partial[kSets * TILES][WAVES > 1 ? WAVES - 1 : 1][64];
-  static_assert(!DMA || (I8 && !W4), "LDS staging is the int8-weight path");
-  constexpr bool kDma = DMA;  // int8 weights staged through LDS in whole lines
+  static_assert(!DMA || I8, "LDS staging is for int8 and int4 weights");
+  constexpr bool kDma = DMA;  // weights staged through LDS in whole lines
   __shared__ __attribute__((aligned(16))) uint8_t wring[kDma ? WAVES : 1][2][kDma ? kSets * TILES : 1][kDma ? 2048 : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -290,17 +291,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
         }
   };
   if constexpr (kDma) {
-    // int8 weights through LDS in whole lines.  A round is two K steps: one
-    // 128-byte line of each of the 16 rows of every (set, tile), fetched by
-    // two transfers of 8 rows x 128 bytes (lane l: row l / 8 of the half,
-    // 16-byte chunk (l % 8) ^ (row % 8) of the line, so that the fragment
-    // reads below spread over the LDS banks).  Rounds are double-buffered
-    // in the wave's own LDS ring.  Every round issues the same number of
-    // transfers and activation loads (addresses clamped into the rows), so
-    // a fixed vmcnt retires exactly the previous round; chunks past K or
-    // past the wave's range meet zero activations.
+    // Weights through LDS in whole lines.  A round is two K units: one
+    // 128-byte line of each of the 16 rows of every (set, tile) (two int8
+    // steps, or 256 int4 codes), fetched by two transfers of 8 rows x 128
+    // bytes (lane l: row l / 8 of the half, 16-byte chunk (l % 8) ^ (row % 8)
+    // of the line, so that the fragment reads below spread over the LDS
+    // banks).  Rounds are double-buffered in the wave's own LDS ring.  Every
+    // round issues the same number of transfers and activation loads
+    // (addresses clamped into the rows), so a fixed vmcnt retires exactly
+    // the previous round; chunks past K or past the wave's range meet zero
+    // activations (int4: K % 32 == 0, so a chunk is wholly in or out).
     constexpr int kSlots = kSets * TILES;
-    constexpr int kOpsPerRound = 2 * kSlots + 2;  // transfers + activation loads
+    constexpr int kXH = W4 ? 2 : 1;                    // activation loads per unit
+    constexpr int kOpsPerRound = 2 * kSlots + 2 * kXH;  // transfers + activation loads
+    const int wbytes = W4 ? kbytes / 2 : kbytes;        // weight bytes of a row
     uint8_t* ring = &wring[wid][0][0][0];
     const int drow = lane >> 3;
     const int dchunk = (lane & 7) ^ drow;
@@ -314,38 +318,48 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
           const int64_t n = min(n0 + 16 * i + 8 * h + drow, N - 1);
           dbase[t][i][h] = (t == 0 ? B + n * ldb : epi.B2 + n * epi.ldb2);
         }
-    auto issue = [&](int u0, int buf, i32x4 (&x)[2], bool (&xv)[2]) {
-      const int byte = u0 * kStepBytes;
-      const int off = byte + dchunk * 16 + 16 <= kbytes ? byte + dchunk * 16 : 0;
+    auto issue = [&](int u0, int buf, i32x4 (&x)[2][kXH], bool (&xv)[2][kXH]) {
+      const int wb = u0 * 64;  // weight byte of the round's line
+      const int off = wb + dchunk * 16 + 16 <= wbytes ? wb + dchunk * 16 : 0;
 #pragma unroll
       for (int t = 0; t < kSets; ++t)
 #pragma unroll
         for (int i = 0; i < TILES; ++i)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) gemv_dma16(dbase[t][i][h] + off, ring + (buf * kSlots + t * TILES + i) * 2048 + h * 1024);
+          for (int h = 0; h < 2; ++h)
+            gemv_dma16(dbase[t][i][h] + off, ring + (buf * kSlots + t * TILES + i) * 2048 + h * 1024);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int b = byte + q * kStepBytes;
-        xv[q] = u0 + q < u_end && b + ch * 16 < kbytes;
-        x[q] = *reinterpret_cast<const i32x4*>(xrow + (xv[q] ? b : 0));
-      }
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int hh = 0; hh < kXH; ++hh) {
+          const int b = (u0 + q) * kUnit + 16 * hh;  // from this lane's activation base
+          xv[q][hh] = u0 + q < u_end && (u0 + q) * kUnit + ch * 16 * kXH + 16 * (hh + 1) <= kbytes;
+          x[q][hh] = *reinterpret_cast<const i32x4*>(xrow + (xv[q][hh] ? b : 0));
+        }
     };
-    auto consume = [&](int buf, const i32x4 (&x)[2], const bool (&xv)[2]) {
+    auto consume = [&](int buf, const i32x4 (&x)[2][kXH], const bool (&xv)[2][kXH]) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const i32x4 xq = xv[q] ? x[q] : i32x4{0, 0, 0, 0};
         const int off = row * 128 + (((4 * q + ch) ^ (row & 7)) << 4);
+        i32x4 xq[kXH];
+#pragma unroll
+        for (int hh = 0; hh < kXH; ++hh) xq[hh] = xv[q][hh] ? x[q][hh] : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < kSets; ++t)
 #pragma unroll
           for (int i = 0; i < TILES; ++i) {
             const i32x4 w = *reinterpret_cast<const i32x4*>(ring + (buf * kSlots + t * TILES + i) * 2048 + off);
-            acc[t][i] = Mma<I8>::run(w, xq, acc[t][i]);
+            if constexpr (W4) {
+              acc[t][i] = Mma<I8>::run(expand_w4(w.x, w.y), xq[0], acc[t][i]);
+              acc[t][i] = Mma<I8>::run(expand_w4(w.z, w.w), xq[kXH - 1], acc[t][i]);
+            } else {
+              acc[t][i] = Mma<I8>::run(w, xq[0], acc[t][i]);
+            }
           }
       }
     };
-    i32x4 xa[2], xb[2];
-    bool va[2], vb[2];
+    i32x4 xa[2][kXH], xb[2][kXH];
+    bool va[2][kXH], vb[2][kXH];
     if (u_begin < u_end) issue(u_begin, 0, xa, va);
     int buf = 0;
     for (int u0 = u_begin; u0 < u_end; u0 += 4) {
@@ -500,10 +514,12 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   constexpr int kSets = GATED ? 2 : 1;
   constexpr int kUnit = W4 ? 128 : kStepBytes;
   constexpr int kStepsPerUnit = kUnit / kStepBytes;
-  // int8 weights go through LDS in whole lines when a wave streams enough
-  // steps for the staging to pay (a round is two steps).
-  constexpr bool kStageable = I8 && !W4;
+  // Weights go through LDS in whole lines when a wave streams enough units
+  // for the staging to pay (a round is two units); int4 rows also need
+  // K % 32 == 0 so that no 16-byte chunk straddles K.
+  constexpr bool kStageable = I8;
   constexpr int kStageMinUnits = 5;
+  const bool stage_ok = !W4 || kbytes % 32 == 0;
   const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
   const auto* a = static_cast<const uint8_t*>(A);
@@ -527,7 +543,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const int per = static_cast<int>((units + waves - 1) / waves);
     const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(units)};
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splits));
-    if (kStageable && per >= kStageMinUnits)
+    if (kStageable && stage_ok && per >= kStageMinUnits)
       launch_waves<I8, OUT, ACT, GATED, true, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
                                                                  ldc, sp, stream);
     else
@@ -544,7 +560,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   // Two tiles per workgroup share every activation fragment once there are
   // at least four tiles per CU (plain launches only; with fewer, the
   // workgroups of two tiles spread unevenly over the CUs).
-  const bool stage = kStageable && per >= kStageMinUnits;
+  const bool stage = kStageable && stage_ok && per >= kStageMinUnits;
   const SplitArgs none{nullptr, 1, 0};
   if (!GATED && tiles >= 4 * cus) {
     const dim3 grid(static_cast<unsigned>((tiles + 1) / 2));
