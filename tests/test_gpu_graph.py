@@ -1,10 +1,12 @@
 """The path under HIP graph capture: a captured step replays to the same bits
 as the same launches made eagerly.
 
-Two steps are captured with torch.cuda.graph: a decode step of a gated
+Steps captured with torch.cuda.graph: a decode step of a gated
 feed-forward layer (pack the activation, gate and up in one gated launch,
-pack the product, down projection) and a DiT-sized step (one pack shared by
-two linears, 256-row tiles with ragged edges).  Each graph is replayed three
+pack the product, down projection), the same step with int4 weights (also
+at a width where the weights are staged through LDS), a DiT-sized step
+(one pack shared by two linears, 256-row tiles with ragged edges), and a
+linear followed by a LoRA correction.  Each graph is replayed three
 times; before each replay the captured input buffer is refilled eagerly,
 the same launches run eagerly into separate outputs, and the replay's
 outputs must equal them bit for bit (the kernels are deterministic, so any
@@ -22,13 +24,14 @@ from workloads import random_rows
 pytestmark = pytest.mark.gpu
 
 
-def _weights(shapes, G, seed, dev):
+def _weights(shapes, G, seed, dev, bits=8):
     g = np.random.default_rng(seed)
     out = []
+    pack = cr.pack_weight if bits == 8 else cr.pack_weight_w4
     for n, k in shapes:
         w = torch.from_numpy((g.standard_normal((n, k)) * 0.05).astype(np.float32)).to(torch.bfloat16).to(dev)
         b = torch.from_numpy((g.standard_normal(n) * 0.1).astype(np.float32)).to(dev)
-        out.append((cr.pack_weight(w, G), b))
+        out.append((pack(w, G), b))
     return out
 
 
@@ -43,6 +46,15 @@ def _decode_step(x, ws, bufs, G):
     cr.linear_gated(pa, wg, wu, bg, bu, cr.GELU_TANH, out=h)
     cr.pack_act(h, G, out=pa2)
     cr.linear(pa2, wd, bd, out=y)
+
+
+def _decode_step_w4(x, ws, bufs, G):
+    (wg, bg), (wu, bu), (wd, bd) = ws
+    pa, h, pa2, y = bufs
+    cr.pack_act(x, G, out=pa)
+    cr.linear_w4_gated(pa, wg, wu, bg, bu, cr.GELU_TANH, out=h)
+    cr.pack_act(h, G, out=pa2)
+    cr.linear_w4(pa2, wd, bd, out=y)
 
 
 def _decode_bufs(M, K, F, G, dev):
@@ -103,3 +115,32 @@ def test_dit_step_graph(cuda):
     M, K, N1, N2, G = 600, 1024, 1000, 520, 256
     ws = _weights([(N1, K), (N2, K)], G, 7, cuda)
     _replay_matches_eager(_dit_step, lambda: _dit_bufs(M, K, N1, N2, G, cuda), ws, M, K, G, 200, cuda)
+
+
+@pytest.mark.parametrize("M,K,F", [(16, 1152, 6912), (4, 4096, 6912)])
+def test_decode_step_w4_graph(cuda, M, K, F):
+    G = 64
+    ws = _weights([(F, K), (F, K), (K, F)], G, 9, cuda, bits=4)
+    _replay_matches_eager(_decode_step_w4, lambda: _decode_bufs(M, K, F, G, cuda), ws, M, K, G, 300 + M, cuda)
+
+
+def test_lora_step_graph(cuda):
+    M, K, N, r, G = 300, 1024, 700, 32, 256
+    ws = _weights([(N, K)], G, 11, cuda)
+    g = np.random.default_rng(12)
+    a = torch.from_numpy((g.standard_normal((r, K)) / 32).astype(np.float32)).to(torch.bfloat16).to(cuda)
+    bu = torch.from_numpy((g.standard_normal((N, r)) * 0.05).astype(np.float32)).to(torch.bfloat16).to(cuda)
+
+    def step(x, ws_, bufs, G_):
+        (w, b), = ws_
+        pa, y, t = bufs
+        cr.pack_act(x, G_, out=pa)
+        cr.linear(pa, w, b, out=y)
+        cr.lora_add(x, a, bu, 0.5, y, workspace=t)
+
+    def bufs():
+        return (cr.Packed(torch.empty((M, K), dtype=torch.int8, device=cuda),
+                          torch.empty(M, dtype=torch.float32, device=cuda), G),
+                torch.empty((M, N), dtype=torch.bfloat16, device=cuda),
+                torch.empty(M * r, dtype=torch.bfloat16, device=cuda))
+    _replay_matches_eager(step, bufs, ws, M, K, G, 400, cuda)

@@ -223,3 +223,17 @@ def test_small_m_int4_staged_weights(cuda, M, N, K):
     u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
     y = to_np(cr.linear_w4_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))
     assert R.rel_fro(y, R.gelu64(g64, "gelu_tanh") * u64) <= 1e-5
+
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 16), (1, 1, 32), (20, 7, 48), (0, 9, 64), (16, 33, 16)])
+def test_linear_w4_edges(cuda, M, N, K):
+    """Smallest K (one 16-code chunk), a single output, M = 0, and the
+    expanded-weight path at tiny sizes."""
+    qx, sx, q4, sw, b = _operands(max(M, 1), N, K, 3 * N + K + M)
+    qx, sx = qx[:M], sx[:M]
+    a = cr.Packed(to_dev(qx.reshape(M, K), torch.int8), to_dev(sx, torch.float32), 16)
+    y = cr.linear_w4(a, _w4(q4, sw, 16), out_dtype=torch.int32)
+    assert tuple(y.shape) == (M, N)
+    if M:
+        assert np.array_equal(to_np(y), O.int_gemm(qx, q4))
