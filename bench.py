@@ -13,6 +13,10 @@ separate torch op after plain linears instead.
 Workloads (``--workload``):
   dit_attn_proj  (default) X bf16 [4096, 3072], 8 outlier channels; fused QKV
                  W [9216, 3072] and a second W [3072, 3072] share one pack.
+                 Both run as one launch over the concatenated packed weight
+                 (per-row packing makes it the concatenation of the two packed
+                 weights), each output a column view of one buffer;
+                 ``--separate-linears`` launches them one by one.
                  Suffix "_lora{r}": a rank-r adapter on the QKV layer, its
                  correction computed from the unrotated X and added to the
                  QKV output (two launches after the linear).
@@ -185,8 +189,11 @@ class Op:
 class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
-    def __init__(self, wl, dev, torch, cr, template=None, fused=True):
+    def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
+        # linears that share the packed activation run as one launch over the
+        # concatenated weight (configs whose linears all read the same input)
+        self.merge = merge and wl.cfg == 2 and all(l.W.shape[1] % wl.G == 0 for l in wl.linears)
         bf16, f32 = torch.bfloat16, torch.float32
         self.xdt = bf16 if wl.xdtype == "bf16" else f32
         self.odt = bf16 if wl.out_dtype == "bf16" else f32
@@ -206,7 +213,14 @@ class StepSet:
             self.X = up(wl.X, self.xdt)
             self.W, self.b = {}, {}
             routed = wl.extra.get("routed")
-            for lin in list(wl.linears) + ([routed] if routed is not None else []):
+            lins = list(wl.linears) + ([routed] if routed is not None else [])
+            if self.merge:
+                from workloads import Linear as _Lin
+                cat = _Lin("_".join(l.name for l in wl.linears), np.concatenate([l.W for l in wl.linears]),
+                           np.concatenate([l.b for l in wl.linears]) if all(l.b is not None for l in wl.linears)
+                           else None, wl.linears[0].wdtype)
+                lins = [cat]
+            for lin in lins:
                 K = lin.W.shape[1]
                 wd = up(lin.W, bf16 if lin.wdtype == "bf16" else f32)
                 if lin is routed or K % G != 0:
@@ -295,12 +309,28 @@ class StepSet:
         M, K = self.X.shape
         ops = []
         names = [l.name for l in wl.linears]
-        if self._quant(self.W[names[0]]):
+        first = "_".join(names) if self.merge else names[0]
+        if self._quant(self.W[first]):
             src0 = self._packed(M, K, dev)
             ops.append(self._pack_op("pack_act", self.X, src0))
         else:
             src0 = self.X
-        if wl.cfg in (1, 2):
+        if self.merge:
+            # one launch; each linear's output is a column view of its buffer
+            n = "_".join(names)
+            y = self._out(n, M, dev)
+            ops.append(self._linear_op(n, src0, y))
+            if self.lora is not None:
+                A, Bm = self.lora
+                r = A.shape[0]
+                yq = y[:, :wl.linears[0].W.shape[0]]
+                ws = torch.empty(M * r, dtype=torch.bfloat16, device=dev)
+                self.bufs.append(ws)
+                op = Op(f"lora_{names[0]}", lambda yq=yq, ws=ws: self.cr.lora_add(self.X, A, Bm, 0.5, yq, workspace=ws),
+                        "lora", M=M, N=yq.shape[1], K=K, out_b=y.element_size())
+                op.epilogue_rank = r
+                ops.append(op)
+        elif wl.cfg in (1, 2):
             for n in names:
                 y = self._out(n, M, dev)
                 ops.append(self._linear_op(n, src0, y))
@@ -495,6 +525,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run the activation between chained layers as a separate torch op instead of in the "
                          "linear's epilogue")
+    ap.add_argument("--separate-linears", action="store_true",
+                    help="launch linears that share one packed activation one by one instead of as one launch over "
+                         "the concatenated weight")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -516,9 +549,10 @@ def main():
         f"{[(l.name, l.W.shape) for l in wl.linears]}, G={wl.G} {wl.kind} (inputs {time.time() - t0:.1f}s)")
 
     fused = not args.unfused
-    sets = [StepSet(wl, dev, torch, cr, fused=fused)]
+    merge = not args.separate_linears
+    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
-        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused))
+        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -638,6 +672,7 @@ def main():
         "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
                    "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
+                   "shared_pack_linears": "one launch" if sets[0].merge else "one launch each",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "weights": "int4" if wl.extra.get("wbits") == 4 else "int8",
                    "buffer_sets": len(sets)},

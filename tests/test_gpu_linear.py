@@ -119,6 +119,26 @@ def test_row_split_bit_exact(cuda):
     assert torch.equal(again, full)
 
 
+@pytest.mark.parametrize("M", [700, 16])
+def test_concatenated_weights_one_launch(cuda, M):
+    """Weights are packed row by row, so linears that share one packed
+    activation can run as one launch over the concatenated weight: the packed
+    concatenation is the concatenation of the packed weights, and each column
+    slice of the one output equals that linear's own launch bit for bit."""
+    K, G = 1024, 256
+    x = to_dev(random_rows((M, K), 21, dtype="bf16"), torch.bfloat16)
+    ws = [to_dev(random_rows((n, K), 22 + n, sigma=0.02, dtype="bf16"), torch.bfloat16) for n in (600, 200)]
+    bs = [torch.randn(w.shape[0], device=cuda) * 0.01 for w in ws]
+    parts = [cr.pack_weight(w, G) for w in ws]
+    cat = cr.pack_weight(torch.cat(ws), G)
+    assert torch.equal(cat.q, torch.cat([p.q for p in parts]))
+    assert torch.equal(cat.scale, torch.cat([p.scale for p in parts]))
+    pa = cr.pack_act(x, G)
+    y = cr.linear(pa, cat, torch.cat(bs))
+    assert torch.equal(y[:, :600], cr.linear(pa, parts[0], bs[0]))
+    assert torch.equal(y[:, 600:], cr.linear(pa, parts[1], bs[1]))
+
+
 def test_strided_output(cuda):
     qx, qw = random_codes((100, 512), 11), random_codes((200, 512), 12)
     a = _packed_from_codes(qx, np.ones(100, np.float32), 256, cuda)
