@@ -368,21 +368,26 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
   }
 }
 
-// Tile width for the eight-wave kernel: the fewest idle CU-slots in the
-// last round (ties to the wider tile), as choose_tn does for the four-wave
-// kernel.
+// Tile width for the eight-wave kernel: the least estimated time, counted as
+// rounds of tiles over the CUs times the tile width times a cost per output
+// column that depends on the width.  Wider tiles read fewer LDS bytes per
+// MFMA and spread the prologue and epilogue over more columns; measured with
+// the same number of rounds (K = 3072 and 6144, M from 4096 to 32700), a
+// column of a 192-wide tile costs 1.14-1.17x one of a 256-wide tile, and a
+// 128-wide tile 1.39-1.40x.  Ties go to the wider tile.
 inline int choose_tn_pp(int64_t M, int64_t cols) {
-  const int cands[] = {4, 3, 2};
+  constexpr int cands[] = {4, 3, 2};
+  constexpr int64_t col_cost[] = {100, 116, 140};
   const int64_t cus = num_cus();
   int best = 4;
   int64_t best_cost = -1;
-  for (int tn : cands) {
-    const int64_t bn = 64 * tn;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t bn = 64 * cands[i];
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((cols + bn - 1) / bn);
-    const int64_t cost = ((tiles + cus - 1) / cus) * bn;
+    const int64_t cost = ((tiles + cus - 1) / cus) * bn * col_cost[i];
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
-      best = tn;
+      best = cands[i];
     }
   }
   return best;
