@@ -120,11 +120,26 @@ def test_dit_attn_proj_full(cuda):
     pa = cr.pack_act(xd, G)
     S = rows_to_check(X, 2)
     qx_ref, sx_ref = check_act_pack("X", X[S], pa, S, G, "regular", None)
+    packs, refs = [], []
     for lin in wl.linears:
         pw = cr.pack_weight(dev_weight(lin), G)
         qw_ref, sw_ref = check_weight_pack(lin.name, lin.W, pw, G, "regular", None)
         y = cr.linear(pa, pw, to_dev(lin.b, torch.float32))
         check_linear(lin.name, pa, pw, lin.b, S, qx_ref, sx_ref, qw_ref, sw_ref, y)
+        packs.append(pw)
+        refs.append((qw_ref, sw_ref))
+    # The benchmark runs both linears as one launch over the concatenated
+    # packed weight ([12288, 3072], 256 x 256 tiles); each output is a column
+    # slice of that launch.
+    Wc = np.concatenate([lin.W for lin in wl.linears])
+    bc = np.concatenate([lin.b for lin in wl.linears])
+    pwc = cr.pack_weight(to_dev(Wc, torch.bfloat16), G)
+    assert torch.equal(pwc.q, torch.cat([p.q for p in packs]))
+    assert torch.equal(pwc.scale, torch.cat([p.scale for p in packs]))
+    del packs
+    y = cr.linear(pa, pwc, to_dev(bc, torch.float32))
+    check_linear("qkv+second", pa, pwc, bc, S, qx_ref, sx_ref, np.concatenate([r[0] for r in refs]),
+                 np.concatenate([r[1] for r in refs]), y)
 
 
 def test_dit_mlp_full(cuda):
