@@ -324,7 +324,7 @@ class StepSet:
                 A, Bm = self.lora
                 r = A.shape[0]
                 yq = y[:, :wl.linears[0].W.shape[0]]
-                ws = torch.empty(M * r, dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(self.cr.lora_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
                 self.bufs.append(ws)
                 op = Op(f"lora_{names[0]}", lambda yq=yq, ws=ws: self.cr.lora_add(self.X, A, Bm, 0.5, yq, workspace=ws),
                         "lora", M=M, N=yq.shape[1], K=K, out_b=y.element_size())
@@ -337,7 +337,7 @@ class StepSet:
                 if self.lora is not None and n == names[0]:
                     A, Bm = self.lora
                     r = A.shape[0]
-                    ws = torch.empty(M * r, dtype=torch.bfloat16, device=dev)
+                    ws = torch.empty(self.cr.lora_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
                     self.bufs.append(ws)
                     op = Op(f"lora_{n}", lambda y=y, ws=ws: self.cr.lora_add(self.X, A, Bm, 0.5, y, workspace=ws),
                             "lora", M=M, N=y.shape[1], K=K, out_b=y.element_size())

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 5
+#define CONVROT_ABI_VERSION 6
 
 typedef enum {
   CONVROT_OK = 0,
@@ -318,13 +318,21 @@ convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t
  *   r   rank, a positive multiple of 16, at most 256; K a positive multiple
  *       of 16
  *   Y   [M, ldy] of ydt (CONVROT_F32 or CONVROT_BF16), read and written
- *   workspace  caller-owned device memory of workspace_bytes >= M * r * 2
- *       bytes, 16-byte aligned, for T; not shared with a concurrent call
- * X, A, B: 16-byte aligned bases and rows.  Two launches on `stream` (the
- * down product into the workspace, then the up product with the add).  A
- * layer whose
- * output goes through a fused activation must run the plain linear, this
- * call, and the activation afterwards. */
+ *   workspace  caller-owned device memory, 16-byte aligned, of at least
+ *       convrot_lora_workspace_bytes(M, K, r) bytes; not shared with a
+ *       concurrent call.  T [M, r] bf16 is left at its start.
+ * X, A, B: 16-byte aligned bases and rows.  Two or three launches on
+ * `stream`: the down product into the workspace (split over K when the rows
+ * alone give fewer workgroups than CUs, with a reduction of the fp32 block
+ * partials in block order), then the up product with the add.  A smaller
+ * workspace is CONVROT_ERR_INVALID_ARG.  A layer whose output goes through a
+ * fused activation must run the plain linear, this call, and the activation
+ * afterwards. */
+/* Workspace bytes convrot_lora_add needs for X [M, K] and rank r on the
+ * current device (0 when M == 0); the same argument checks as that call.
+ * The size depends on the device's CU count through the K split. */
+convrot_status convrot_lora_workspace_bytes(int64_t M, int64_t K, int64_t r, int64_t* bytes);
+
 convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K, const void* A, int64_t lda,
                                 const void* B, int64_t ldb, int64_t N, int64_t r, float scale, void* Y,
                                 convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,

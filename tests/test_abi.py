@@ -329,3 +329,27 @@ def test_lora_checks(lib):
     assert lora_status(lib, ws_bytes=32 * 16 * 2 - 2) == _lib.ERR_INVALID_ARG
     assert lora_status(lib, ws=0x50008) == _lib.ERR_ALIGN
     assert lora_status(lib, M=0) == _lib.OK
+
+
+def lora_ws(lib, M, K, r):
+    out = ctypes.c_int64(-1)
+    st = lib.convrot_lora_workspace_bytes(M, K, r, ctypes.byref(out))
+    return st, out.value
+
+
+def test_lora_workspace_query(lib):
+    # one K block: bf16 T only, rounded up to 256 bytes
+    assert lora_ws(lib, 32, 64, 16) == (_lib.OK, 1024)
+    assert lora_ws(lib, 3, 64, 16) == (_lib.OK, 256)
+    assert lora_ws(lib, 0, 64, 16) == (_lib.OK, 0)
+    # 4096 rows of K = 3072 at r = 32 split K into 4 blocks on 256 CUs:
+    # T (256 KiB) plus 4 x 4096 x 32 fp32 partials
+    st, n = lora_ws(lib, 4096, 3072, 32)
+    assert st == _lib.OK and n >= 4096 * 32 * 2 and (n - 4096 * 32 * 2) % (4096 * 32 * 4) == 0
+    assert lora_ws(lib, 32, 64, 8)[0] == _lib.ERR_INVALID_ARG
+    assert lora_ws(lib, 32, 40, 16)[0] == _lib.ERR_INVALID_ARG
+    assert lora_ws(lib, -1, 64, 16)[0] == _lib.ERR_INVALID_ARG
+    assert lib.convrot_lora_workspace_bytes(32, 64, 16, None) == _lib.ERR_INVALID_ARG
+    # the call itself rejects a workspace one byte short of the query
+    assert lora_status(lib, M=4096, ldx=3072, K=3072, lda=3072, r=32, ldb=32, N=48, ldy=48, ws_bytes=n - 1) \
+        == _lib.ERR_INVALID_ARG

@@ -142,5 +142,5 @@ def test_lora_step_graph(cuda):
         return (cr.Packed(torch.empty((M, K), dtype=torch.int8, device=cuda),
                           torch.empty(M, dtype=torch.float32, device=cuda), G),
                 torch.empty((M, N), dtype=torch.bfloat16, device=cuda),
-                torch.empty(M * r, dtype=torch.bfloat16, device=cuda))
+                torch.empty(cr.lora_workspace_bytes(M, K, r), dtype=torch.uint8, device=cuda))
     _replay_matches_eager(step, bufs, ws, M, K, G, 400, cuda)

@@ -34,7 +34,8 @@ def _adapter(M, K, N, r, seed):
 
 @pytest.mark.parametrize("M,K,N,r", [(1, 1024, 520, 16), (16, 1152, 6912, 32), (17, 256, 100, 16),
                                      (300, 3072, 1000, 64), (513, 2048, 777, 128), (70, 1040, 64, 256),
-                                     (33, 512, 300, 48)])
+                                     (33, 512, 300, 48), (20, 512, 130, 64), (9, 1024, 200, 128),
+                                     (128, 2048, 96, 32)])
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 def test_lora_add(cuda, M, K, N, r, ydt):
     x, a, b = _adapter(M, K, N, r, M + K + N + r)
@@ -45,10 +46,10 @@ def test_lora_add(cuda, M, K, N, r, ydt):
     if ydt == "bf16":
         y0 = to_bf16_values(y0)
     y = to_dev(y0, tdt)
-    ws = torch.empty(M * r, dtype=torch.bfloat16, device=cuda)
+    ws = torch.empty((cr.lora_workspace_bytes(M, K, r) + 1) // 2, dtype=torch.bfloat16, device=cuda)
     cr.lora_add(xd, ad, bd, scale, y, workspace=ws)
-    # the call leaves its bf16 intermediate T [M, r] in the workspace
-    T = to_np(ws.view(M, r))
+    # the call leaves its bf16 intermediate T [M, r] at the workspace's start
+    T = to_np(ws[:M * r].view(M, r))
     T_ref = O.lora_intermediate(x, a)
     assert np.all(np.abs(T - T_ref) <= np.abs(T_ref) * 2.0 ** -7 + 1e-30)
     got = to_np(y).astype(np.float64)

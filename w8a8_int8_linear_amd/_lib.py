@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -38,6 +38,7 @@ EXPORTED = (
     "convrot_linear_w4_gated",
     "convrot_unpack_w4",
     "convrot_smooth_ffn",
+    "convrot_lora_workspace_bytes",
     "convrot_lora_add",
     "convrot_status_string",
     "convrot_last_error",
@@ -110,6 +111,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_smooth_ffn.argtypes = [vp, c_int, c_i64, vp, c_int, c_i64, c_i64, c_i64, c_i64, c_int, vp, vp, c_i64,
                                        vp, c_i64, vp]
     lib.convrot_smooth_ffn.restype = c_int
+    lib.convrot_lora_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.POINTER(c_i64)]
+    lib.convrot_lora_workspace_bytes.restype = c_int
     lib.convrot_lora_add.argtypes = [vp, c_i64, c_i64, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, ctypes.c_float, vp,
                                      c_int, c_i64, vp, c_i64, vp]
     lib.convrot_lora_add.restype = c_int

@@ -353,12 +353,22 @@ def smooth_ffn(w_up: torch.Tensor, w_down: torch.Tensor, norm: str = "l2", scale
 # Runtime LoRA correction
 # ---------------------------------------------------------------------------
 
+def lora_workspace_bytes(M: int, K: int, r: int) -> int:
+    """Bytes of device workspace ``lora_add`` needs for an input [M, K] and
+    rank r on the current device (convrot_lora_workspace_bytes)."""
+    lib = _lib.load()
+    out = ctypes.c_int64(0)
+    _lib.check(lib.convrot_lora_workspace_bytes(M, K, r, ctypes.byref(out)))
+    return out.value
+
+
 def lora_add(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor, scale: float, y: torch.Tensor,
              workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y += scale * (x a^T) b^T in place, from the unrotated bf16 input x
     [M, K], the adapter's down a [r, K] and up b [N, r] (convrot_lora_add).
-    The rank-r intermediate goes to ``workspace`` (allocated here when not
-    given)."""
+    The rank-r intermediate T (bf16 [M, r]) is left at the start of
+    ``workspace``, which holds at least ``lora_workspace_bytes(M, K, r)``
+    bytes (allocated here when not given)."""
     for t, name in ((x, "x"), (a, "a"), (b, "b")):
         _need_cuda(t, name)
         if t.dtype != torch.bfloat16:
@@ -371,7 +381,8 @@ def lora_add(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor, scale: float, y:
     if y.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("y must be float32 or bfloat16")
     if workspace is None:
-        workspace = torch.empty((max(M, 1) * r,), dtype=torch.bfloat16, device=x.device)
+        with torch.cuda.device(x.device):
+            workspace = torch.empty((max(lora_workspace_bytes(M, K, r), 16),), dtype=torch.uint8, device=x.device)
     lib = _lib.load()
     _lib.check(lib.convrot_lora_add(x.data_ptr(), _ld(x), M, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), N, r,
                                     float(scale), y.data_ptr(), _DT[y.dtype], _ld(y), workspace.data_ptr(),

@@ -479,17 +479,41 @@ convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t
   return from_hip(e, what);
 }
 
-convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K, const void* A, int64_t lda,
-                                const void* B, int64_t ldb, int64_t N, int64_t r, float scale, void* Y,
-                                convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
-                                void* stream) {
-  const char* what = "convrot_lora_add";
+namespace {
+// Workspace of the LoRA correction: bf16 T [M, r] first, then (when the down
+// product splits K) the fp32 partials from the next 256-byte boundary.
+int64_t lora_t_bytes(int64_t M, int64_t r) { return (2 * M * r + 255) / 256 * 256; }
+int64_t lora_ws_bytes(int64_t M, int64_t K, int64_t r) {
+  const int nb = convrot::lora_down_blocks(M, K, r);
+  return lora_t_bytes(M, r) + (nb > 1 ? 4 * static_cast<int64_t>(nb) * M * r : 0);
+}
+convrot_status check_lora_shape(const char* what, int64_t M, int64_t K, int64_t r) {
   convrot_status st = check_k(K, int64_t{1} << 30);
   if (st != CONVROT_OK) return st;
   if (r <= 0 || r % 16 != 0 || r > 256)
     return fail(CONVROT_ERR_INVALID_ARG, "%s: rank r = %lld must be a positive multiple of 16, at most 256", what,
                 static_cast<long long>(r));
-  if (M < 0 || N < 0 || M > kMaxRows || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad M or N", what);
+  if (M < 0 || M > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad M", what);
+  return CONVROT_OK;
+}
+}  // namespace
+
+convrot_status convrot_lora_workspace_bytes(int64_t M, int64_t K, int64_t r, int64_t* bytes) {
+  if (bytes == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "convrot_lora_workspace_bytes: bytes is NULL");
+  const convrot_status st = check_lora_shape("convrot_lora_workspace_bytes", M, K, r);
+  if (st != CONVROT_OK) return st;
+  *bytes = M == 0 ? 0 : lora_ws_bytes(M, K, r);
+  return ok();
+}
+
+convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, int64_t N, int64_t r, float scale, void* Y,
+                                convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  const char* what = "convrot_lora_add";
+  convrot_status st = check_lora_shape(what, M, K, r);
+  if (st != CONVROT_OK) return st;
+  if (N < 0 || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad N", what);
   if (ydt != CONVROT_F32 && ydt != CONVROT_BF16)
     return fail(CONVROT_ERR_DTYPE, "%s: Y must be CONVROT_F32 or CONVROT_BF16", what);
   st = check_matrix("X", X, M, K, ldx, 2);
@@ -504,10 +528,11 @@ convrot_status convrot_lora_add(const void* X, int64_t ldx, int64_t M, int64_t K
     return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of X or A exceeds %lld bytes",
                 static_cast<long long>(kMaxLdBytes));
   if (M == 0 || N == 0) return ok();
-  st = check_workspace(workspace, workspace_bytes, 2 * M * r);
+  st = check_workspace(workspace, workspace_bytes, lora_ws_bytes(M, K, r));
   if (st != CONVROT_OK) return st;
   const auto s = static_cast<hipStream_t>(stream);
-  hipError_t e = convrot::launch_lora_down(X, ldx, A, lda, M, K, r, workspace, r, s);
+  auto* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + lora_t_bytes(M, r));
+  hipError_t e = convrot::launch_lora_down(X, ldx, A, lda, M, K, r, workspace, r, partials, s);
   if (e == hipSuccess)
     e = convrot::launch_lora_up(workspace, r, B, ldb, M, N, r, scale, Y, static_cast<convrot::Elt>(ydt), ldy, s);
   return from_hip(e, what);

@@ -91,10 +91,14 @@ hipError_t launch_smooth_ffn(const void* up, Elt up_dt, int64_t ldu, const void*
                              int64_t K, int64_t K_out, bool max_norm, float* s, float* up_out, int64_t ldu_out,
                              float* dn_out, int64_t ldd_out, hipStream_t stream);
 
+// Number of K blocks the down product splits K into on the current device
+// (1: no split).  With nb > 1 it needs nb * M * r fp32 partials.
+int lora_down_blocks(int64_t M, int64_t K, int64_t r);
 // T = X A^T rounded to bf16: X bf16 [M, K], A bf16 [r, K] (r % 16 == 0,
-// r <= 256), T bf16 [M, ldt].
+// r <= 256), T bf16 [M, ldt]; `partials` (16-byte aligned) holds
+// lora_down_blocks(M, K, r) * M * r floats when that count is above 1.
 hipError_t launch_lora_down(const void* X, int64_t ldx, const void* A, int64_t lda, int64_t M, int64_t K, int64_t r,
-                            void* T, int64_t ldt, hipStream_t stream);
+                            void* T, int64_t ldt, float* partials, hipStream_t stream);
 // Y[m, n] += scale * sum_j T[m, j] B[n, j]: T bf16 [M, r], B bf16 [N, r]
 // (r % 16 == 0, rows 16-byte aligned), Y fp32 or bf16 [M, ldy], in place.
 hipError_t launch_lora_up(const void* T, int64_t ldt, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t r,

@@ -8,11 +8,15 @@
 //                          bf16 (the bf16 linear kernels of this library)
 //   Y[m, n] += scale * sum_j T[m, j] B[n, j]
 // Both products are here, each bound by one operand's bytes:
-//  * down (T = X A^T, r <= 256): a workgroup takes up to 64 rows of X and
-//    all r columns; each wave multiplies its row tiles by every fragment of
-//    A it loads (v_mfma_f32_16x16x32_bf16, A's rows as the row operand, from
-//    L2), its eight waves split K and add their partial sums through LDS; T
-//    is rounded to bf16 once;
+//  * down (T = X A^T, r <= 256): a workgroup takes up to 64 rows of X, all r
+//    columns and one block of K; each wave multiplies its row tiles by every
+//    fragment of A it loads (v_mfma_f32_16x16x32_bf16, A's rows as the row
+//    operand, from L2), its eight waves split the block and add their partial
+//    sums through LDS.  Every workgroup reads A's columns of its block, so the
+//    row blocks are made large (A read fewer times) and K is split over
+//    workgroups until the grid covers the CUs; the fp32 partials of the K
+//    blocks are then added in block order by a small reduction.  T is rounded
+//    to bf16 once;
 //  * up (Y += scale T B^T): K = r is small, so a launch is bound by reading
 //    and writing Y.  A workgroup owns a 64 x 64 block of Y; each wave takes 16
 //    rows and four 16-feature MFMA tiles; the block is staged in LDS so that
@@ -21,6 +25,7 @@
 //    to nearest even).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "launchers.h"
@@ -39,24 +44,28 @@ __device__ __forceinline__ i32x4 load8(const __bf16* base, int64_t ld, int row, 
   return *reinterpret_cast<const i32x4*>(base + static_cast<int64_t>(row) * ld + k);
 }
 
-// T = X A^T for 16 MT rows of X per workgroup (r <= kMaxRank, r % 16 == 0):
-// each wave multiplies its MT row tiles by every fragment of A it loads, and
-// the eight waves split K.
+// T = X A^T for 16 MT rows of X per workgroup (r <= kMaxRank, r % 16 == 0)
+// and the 32-wide k steps [spb y, spb (y + 1)) of K, y = blockIdx.y: each
+// wave multiplies its MT row tiles by every fragment of A it loads, and the
+// eight waves split the block's steps.  SPLIT: the block's fp32 sum goes to
+// P [gridDim.y][M][r]; otherwise (one block) it is rounded into T.
 constexpr int kMaxRank = 256;
 constexpr int kDownWaves = 8;
 
-template <int RT, int MT>  // 16-feature tiles of r, 16-row tiles of X per wave
+template <int RT, int MT, bool SPLIT>  // 16-feature tiles of r, 16-row tiles of X per wave
 __global__ __launch_bounds__(64 * kDownWaves) void lora_down_kernel(const __bf16* __restrict__ X, int64_t ldx,
                                                                     const __bf16* __restrict__ A, int64_t lda,
-                                                                    int M, int K, int r, __bf16* __restrict__ T,
-                                                                    int64_t ldt) {
+                                                                    int M, int K, int r, int spb,
+                                                                    __bf16* __restrict__ T, int64_t ldt,
+                                                                    float* __restrict__ P) {
   __shared__ f32x4 partial[kDownWaves - 1][MT * RT][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int row = lane & 15, ch = lane >> 4;
   const int m0 = blockIdx.x * 16 * MT;
   const int steps = (K + 31) / 32;
-  const int per = (steps + kDownWaves - 1) / kDownWaves;
-  const int s0 = wid * per, s1 = min(steps, s0 + per);
+  const int b0 = blockIdx.y * spb, b1 = min(steps, b0 + spb);
+  const int per = (b1 - b0 + kDownWaves - 1) / kDownWaves;
+  const int s0 = b0 + wid * per, s1 = min(b1, s0 + per);
   f32x4 acc[MT][RT] = {};
   // One k step of fragments; the next step's are requested before the
   // current step is multiplied.
@@ -109,12 +118,31 @@ __global__ __launch_bounds__(64 * kDownWaves) void lora_down_kernel(const __bf16
 #pragma unroll
       for (int w = 0; w < kDownWaves - 1; ++w) v += partial[w][i * RT + j][lane];
       if (m < M) {
-        *reinterpret_cast<bf16x4*>(T + static_cast<int64_t>(m) * ldt + 16 * j + 4 * ch) =
-            bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                   static_cast<__bf16>(v[3])};
+        if constexpr (SPLIT) {
+          *reinterpret_cast<f32x4*>(P + (static_cast<int64_t>(blockIdx.y) * M + m) * r + 16 * j + 4 * ch) = v;
+        } else {
+          *reinterpret_cast<bf16x4*>(T + static_cast<int64_t>(m) * ldt + 16 * j + 4 * ch) =
+              bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                     static_cast<__bf16>(v[3])};
+        }
       }
     }
   }
+}
+
+// T = bf16 of the sum of the nb K blocks' fp32 partials P [nb][M][r], added
+// in block order; one thread per 4 features of a row.
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restrict__ P, int M, int r, int nb,
+                                                          __bf16* __restrict__ T, int64_t ldt) {
+  const int q = r / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * q) return;
+  const int64_t m = i / q;
+  const int c = 4 * static_cast<int>(i % q);
+  f32x4 v = *reinterpret_cast<const f32x4*>(P + m * r + c);
+  for (int b = 1; b < nb; ++b) v += *reinterpret_cast<const f32x4*>(P + (static_cast<int64_t>(b) * M + m) * r + c);
+  *reinterpret_cast<bf16x4*>(T + m * ldt + c) = bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                                                        static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
 }
 
 template <int OUT>
@@ -189,28 +217,85 @@ __global__ __launch_bounds__(256) void lora_up_kernel(const __bf16* __restrict__
 
 }  // namespace
 
+// Row tiles per wave by rank: enough to share A's fragments, few enough to
+// keep the accumulators in registers and the LDS partials within 112 KiB.
+static int lora_row_tiles(int64_t r) { return r <= 64 ? 4 : r <= 128 ? 2 : 1; }
+
+int lora_down_blocks(int64_t M, int64_t K, int64_t r) {
+  // Below 128 rows the product takes a few microseconds and the reduction's
+  // launch costs more than the split saves (16 rows, K = 1152: 7.5 us
+  // unsplit, 8.2 us split in two).
+  if (M < 128 || K <= 0) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t rows = 16 * lora_row_tiles(r);
+  const int64_t row_blocks = (M + rows - 1) / rows;
+  const int64_t steps = (K + 31) / 32;
+  // enough K blocks for one workgroup per CU, each block at least two k
+  // steps per wave
+  int64_t nb = (cus + row_blocks - 1) / row_blocks;
+  nb = std::min<int64_t>(nb, std::max<int64_t>(1, steps / (2 * kDownWaves)));
+  nb = std::min<int64_t>(nb, 16);
+  // no empty block: as many blocks as the per-block step count needs
+  const int64_t spb = (steps + nb - 1) / nb;
+  return static_cast<int>((steps + spb - 1) / spb);
+}
+
+namespace {
+template <int RT, int MT>
+void launch_down_typed(const __bf16* x, int64_t ldx, const __bf16* a, int64_t lda, int m, int k, int r, int nb,
+                       __bf16* t, int64_t ldt, float* p, hipStream_t stream) {
+  const int steps = (k + 31) / 32;
+  const int spb = (steps + nb - 1) / nb;
+  const dim3 grid(static_cast<unsigned>((m + 16 * MT - 1) / (16 * MT)), static_cast<unsigned>(nb));
+  if (nb > 1)
+    hipLaunchKernelGGL((lora_down_kernel<RT, MT, true>), grid, dim3(64 * kDownWaves), 0, stream, x, ldx, a, lda, m,
+                       k, r, spb, t, ldt, p);
+  else
+    hipLaunchKernelGGL((lora_down_kernel<RT, MT, false>), grid, dim3(64 * kDownWaves), 0, stream, x, ldx, a, lda, m,
+                       k, r, spb, t, ldt, p);
+}
+
+// mt row tiles per wave, at most MTMAX (a power of two).
+template <int RT, int MTMAX>
+void launch_down_rt(int mt, const __bf16* x, int64_t ldx, const __bf16* a, int64_t lda, int m, int k, int r, int nb,
+                    __bf16* t, int64_t ldt, float* p, hipStream_t stream) {
+  if (MTMAX >= 4 && mt >= 4)
+    launch_down_typed<RT, (MTMAX >= 4 ? 4 : 1)>(x, ldx, a, lda, m, k, r, nb, t, ldt, p, stream);
+  else if (MTMAX >= 2 && mt >= 2)
+    launch_down_typed<RT, (MTMAX >= 2 ? 2 : 1)>(x, ldx, a, lda, m, k, r, nb, t, ldt, p, stream);
+  else
+    launch_down_typed<RT, 1>(x, ldx, a, lda, m, k, r, nb, t, ldt, p, stream);
+}
+}  // namespace
+
 hipError_t launch_lora_down(const void* X, int64_t ldx, const void* A, int64_t lda, int64_t M, int64_t K, int64_t r,
-                            void* T, int64_t ldt, hipStream_t stream) {
+                            void* T, int64_t ldt, float* partials, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const auto* x = static_cast<const __bf16*>(X);
   const auto* a = static_cast<const __bf16*>(A);
   auto* t = static_cast<__bf16*>(T);
   const int m = static_cast<int>(M), k = static_cast<int>(K), rr = static_cast<int>(r);
-  const dim3 block(64 * kDownWaves);
-  // Row tiles per wave: enough to share A's fragments, few enough to keep
-  // 128 or more workgroups at M = 4096 and the LDS partials within 112 KiB.
-  if (r <= 32) {
-    hipLaunchKernelGGL((lora_down_kernel<2, 2>), dim3(static_cast<unsigned>((M + 31) / 32)), block, 0, stream, x,
-                       ldx, a, lda, m, k, rr, t, ldt);
-  } else if (r <= 64) {
-    hipLaunchKernelGGL((lora_down_kernel<4, 4>), dim3(static_cast<unsigned>((M + 63) / 64)), block, 0, stream, x,
-                       ldx, a, lda, m, k, rr, t, ldt);
-  } else if (r <= 128) {
-    hipLaunchKernelGGL((lora_down_kernel<8, 2>), dim3(static_cast<unsigned>((M + 31) / 32)), block, 0, stream, x,
-                       ldx, a, lda, m, k, rr, t, ldt);
-  } else {
-    hipLaunchKernelGGL((lora_down_kernel<16, 1>), dim3(static_cast<unsigned>((M + 15) / 16)), block, 0, stream, x,
-                       ldx, a, lda, m, k, rr, t, ldt);
+  const int nb = lora_down_blocks(M, K, r);
+  if (nb > 1 && partials == nullptr) return hipErrorInvalidValue;
+  // fewer row tiles when M is small, so a workgroup loads no rows twice
+  int mt = lora_row_tiles(r);
+  while (mt > 1 && 16 * (mt / 2) >= M) mt /= 2;
+  static_assert(kMaxRank == 256, "rank dispatch below covers r <= 256");
+  if (r <= 32)
+    launch_down_rt<2, 4>(mt, x, ldx, a, lda, m, k, rr, nb, t, ldt, partials, stream);
+  else if (r <= 64)
+    launch_down_rt<4, 4>(mt, x, ldx, a, lda, m, k, rr, nb, t, ldt, partials, stream);
+  else if (r <= 128)
+    launch_down_rt<8, 2>(mt, x, ldx, a, lda, m, k, rr, nb, t, ldt, partials, stream);
+  else
+    launch_down_rt<16, 1>(mt, x, ldx, a, lda, m, k, rr, nb, t, ldt, partials, stream);
+  if (nb > 1) {
+    const int64_t pieces = M * (r / 4);
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, stream,
+                       partials, m, rr, nb, t, ldt);
   }
   return hipGetLastError();
 }
