@@ -67,3 +67,51 @@ def test_packed_activation_reuse(cuda):
     lb = cr.ConvRotLinear.from_dense(to_dev(random_rows((100, 1024), 7, sigma=0.02, dtype="bf16"), torch.bfloat16))
     pa = la.pack_input(x)
     assert torch.equal(la(pa), la(x)) and torch.equal(lb(pa), lb(x))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_merged_layers_one_launch(cuda, bits):
+    """Layers on one input merged into one launch over their stacked packed
+    weights: each output is a column view equal bit for bit to the layer's
+    own output; packed activations reuse works on the merged layer too."""
+    K, G = 1024, 256
+    x = to_dev(random_rows((300, K), 31, dtype="bf16"), torch.bfloat16)
+    layers = []
+    for i, n in enumerate((384, 128, 200)):
+        w = to_dev(random_rows((n, K), 40 + i, sigma=0.02, dtype="bf16"), torch.bfloat16)
+        b = torch.randn(n, device=cuda) * 0.01 if i != 1 else None
+        layers.append(cr.ConvRotLinear.from_dense(w, b, G, name=f"l{i}", weight_bits=bits))
+    merged = cr.ConvRotLinear.merge(layers)
+    assert merged.N == 712 and merged.splits == [384, 128, 200]
+    for m in (300, 7):
+        ys = merged.split(merged(x[:m]))
+        for l, y in zip(layers, ys):
+            assert torch.equal(y, l(x[:m])), (l.name, m)
+    pa = merged.pack_input(x)
+    assert torch.equal(merged(pa), merged(x))
+    twice = cr.ConvRotLinear.merge([merged, layers[0]])
+    assert twice.splits == [384, 128, 200, 384]
+    assert torch.equal(twice.split(twice(x))[3], layers[0](x))
+
+
+def test_merge_rejects_mismatched_layers(cuda):
+    K = 512
+    w = to_dev(random_rows((64, K), 50, sigma=0.02, dtype="bf16"), torch.bfloat16)
+    a = cr.ConvRotLinear.from_dense(w, group=256, name="a")
+    with pytest.raises(ValueError, match="group"):
+        cr.ConvRotLinear.merge([a, cr.ConvRotLinear.from_dense(w, group=64, name="b")])
+    with pytest.raises(ValueError, match="weight width"):
+        cr.ConvRotLinear.merge([a, cr.ConvRotLinear.from_dense(w, group=256, name="c", weight_bits=4)])
+    routed = cr.ConvRotLinear.from_dense(w[:, :500], group=256, name="r")
+    with pytest.raises(ValueError, match="routed"):
+        cr.ConvRotLinear.merge([a, routed])
+    signs = torch.where(torch.arange(K, device=cuda) % 3 == 0, -1, 1).to(torch.int8)
+    rz = cr.ConvRotLinear.from_dense(w, group=256, kind=cr.RANDOMIZED, signs=signs, name="z")
+    with pytest.raises(ValueError):
+        cr.ConvRotLinear.merge([a, rz])
+    lo = cr.ConvRotLinear.from_dense(w, group=256, name="lo")
+    lo.add_lora(torch.zeros(16, K, device=cuda), torch.zeros(64, 16, device=cuda), 1.0)
+    with pytest.raises(ValueError, match="adapters"):
+        cr.ConvRotLinear.merge([a, lo])
+    with pytest.raises(ValueError):
+        cr.ConvRotLinear.merge([])

@@ -12,6 +12,13 @@ per-channel int8 safetensors").  LoRA adapters attached with ``add_lora``
 are applied at run time from the unrotated input and added to the base
 output ("INT8 Convrot Safetensors", LoRA paragraph); the packed weight is
 never modified.
+
+Layers that read the same input can share one packed activation (the
+stable-diffusion.cpp reuse rule); ``ConvRotLinear.merge`` goes one step
+further and runs them as one launch over their stacked packed weights.
+Weights are packed row by row, so stacking packed weights equals packing the
+stacked weights, and each layer's output is a column slice of the merged
+output (``split``).
 """
 
 from __future__ import annotations
@@ -54,6 +61,7 @@ class ConvRotLinear:
         self.w_bf16 = w_bf16
         self.bias = bias
         self.adapters: list[tuple[torch.Tensor, torch.Tensor, float]] = []
+        self.splits: list[int] = [N]
 
     @property
     def quantized(self) -> bool:
@@ -79,6 +87,48 @@ class ConvRotLinear:
             packed = pack(w.contiguous(), group, kind, signs)
             return cls(name, N, K, group, kind, packed, None, b)
         return cls(name, N, K, group, kind, None, w.to(torch.bfloat16).contiguous(), b)
+
+    @classmethod
+    def merge(cls, layers: "list[ConvRotLinear]", name: str | None = None) -> "ConvRotLinear":
+        """One layer over the stacked packed weights of ``layers``, which must
+        all be quantised with the same K, group, rotation (kind and signs) and
+        weight width, and carry no adapters.  Its output holds the layers'
+        outputs side by side, in order; ``split`` returns them as views."""
+        if not layers:
+            raise ValueError("merge needs at least one layer")
+        first = layers[0]
+        for l in layers:
+            if not l.quantized:
+                raise ValueError(f"{l.name} is routed to bf16 and cannot be merged")
+            if l.adapters:
+                raise ValueError(f"{l.name} has LoRA adapters; merge the base layers, then attach adapters")
+            if (l.K, l.group, l.kind, l.weight_bits) != (first.K, first.group, first.kind, first.weight_bits):
+                raise ValueError(f"{l.name} differs from {first.name} in K, group, rotation or weight width")
+            s0, s1 = first.packed.signs, l.packed.signs
+            if (s0 is None) != (s1 is None) or (s0 is not None and not torch.equal(s0, s1)):
+                raise ValueError(f"{l.name} and {first.name} use different sign vectors")
+            if l.packed.q.shape[1] != first.packed.q.shape[1]:
+                raise ValueError(f"{l.name} and {first.name} have different packed row pitches")
+        q = torch.cat([l.packed.q for l in layers])
+        scale = torch.cat([l.packed.scale for l in layers])
+        p0 = first.packed
+        if isinstance(p0, api.PackedW4):
+            packed = api.PackedW4(q, scale, p0.K, p0.group, p0.kind, p0.signs)
+        else:
+            packed = api.Packed(q, scale, p0.group, p0.kind, p0.signs)
+        bias = None
+        if any(l.bias is not None for l in layers):
+            bias = torch.cat([l.bias if l.bias is not None else torch.zeros(l.N, dtype=torch.float32,
+                                                                            device=q.device) for l in layers])
+        merged = cls(name or "+".join(l.name for l in layers), sum(l.N for l in layers), first.K, first.group,
+                     first.kind, packed, None, bias)
+        merged.splits = [n for l in layers for n in l.splits]
+        return merged
+
+    def split(self, y: torch.Tensor) -> tuple[torch.Tensor, ...]:
+        """The outputs of the layers a merged layer was made from, as column
+        views of its output y."""
+        return torch.split(y, self.splits, dim=-1)
 
     def add_lora(self, a: torch.Tensor, b: torch.Tensor, scale: float) -> None:
         """Attach an adapter: a [r, K] (down), b [N, r] (up), bf16; its
