@@ -20,9 +20,9 @@
 //  * up (Y += scale T B^T): K = r is small, so a launch is bound by reading
 //    and writing Y.  A workgroup owns a 64 x 64 block of Y; each wave takes 16
 //    rows and four 16-feature MFMA tiles; the block is staged in LDS so that
-//    each thread reads, updates and writes 16 contiguous features of one row
-//    (whole lines of Y); one fused multiply-add per element (bf16 Y: rounded
-//    to nearest even).
+//    Y is read and written in 16-byte pieces whose every instruction covers
+//    whole 128-byte lines; one fused multiply-add per element (bf16 Y:
+//    rounded to nearest even).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -175,43 +175,49 @@ __global__ __launch_bounds__(256) void lora_up_kernel(const __bf16* __restrict__
     __syncthreads();  // the next step overwrites the staged rows
   }
   // Lane holds rows 4 ch + e (e = 0..3) of the wave's 16 and feature
-  // 16 j + row: stage the workgroup's 64 x 64 block in LDS, then every
-  // thread updates 16 contiguous features of one row, so each row's 64
-  // features of Y are read and written as whole lines.
+  // 16 j + row: stage the workgroup's 64 x 64 block in LDS, then update Y in
+  // 16-byte pieces laid out so that every load and store instruction of a
+  // wave covers whole 128-byte lines (8 rows of 8 bf16 pieces, or 4 rows of
+  // 16 fp32 pieces); all of a thread's pieces are requested before any is
+  // written.
   __shared__ float stage[64][64 + 4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) stage[16 * wid + 4 * ch + e][16 * j + row] = acc[j][e];
   __syncthreads();
-  const int tr = threadIdx.x >> 2, tc = 16 * (threadIdx.x & 3);
-  const int m = blockIdx.y * 64 + tr;
-  const int n = n0 + tc;
-  if (m >= M || n >= N) return;
   using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
-  out_t* y = static_cast<out_t*>(Y) + static_cast<int64_t>(m) * ldy + n;
-  const float* v = &stage[tr][tc];
-  if (n + 15 < N && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
-    if constexpr (OUT == 0) {
+  constexpr int kVec = 16 / static_cast<int>(sizeof(out_t));  // elements per piece
+  constexpr int kPer = 64 / kVec;                              // threads per row of the block
+  constexpr int kRows = 256 / kPer;                            // rows per pass
+  constexpr int kPasses = 64 / kRows;
+  typedef out_t vec_t __attribute__((ext_vector_type(kVec)));
+  const int pr = threadIdx.x / kPer, pc = (threadIdx.x % kPer) * kVec;
+  const int n = n0 + pc;
+  vec_t old[kPasses];
+  bool full[kPasses];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 o = reinterpret_cast<f32x4*>(y)[q];
+  for (int p = 0; p < kPasses; ++p) {
+    const int m = blockIdx.y * 64 + p * kRows + pr;
+    const out_t* y = static_cast<const out_t*>(Y) + static_cast<int64_t>(min(m, M - 1)) * ldy + n;
+    full[p] = m < M && n + kVec <= N && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    if (full[p]) old[p] = *reinterpret_cast<const vec_t*>(y);
+  }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = fmaf(scale, v[4 * q + e], o[e]);
-        reinterpret_cast<f32x4*>(y)[q] = o;
-      }
+  for (int p = 0; p < kPasses; ++p) {
+    const int tr = p * kRows + pr;
+    const int m = blockIdx.y * 64 + tr;
+    if (m >= M) continue;
+    out_t* y = static_cast<out_t*>(Y) + static_cast<int64_t>(m) * ldy + n;
+    const float* v = &stage[tr][pc];
+    if (full[p]) {
+      vec_t o = old[p];
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) o[e] = static_cast<out_t>(fmaf(scale, v[e], static_cast<float>(o[e])));
+      *reinterpret_cast<vec_t*>(y) = o;
     } else {
-      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        bf16x8v o = reinterpret_cast<bf16x8v*>(y)[q];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(fmaf(scale, v[8 * q + e], static_cast<float>(o[e])));
-        reinterpret_cast<bf16x8v*>(y)[q] = o;
-      }
+      for (int e = 0; e < kVec && n + e < N; ++e) y[e] = static_cast<out_t>(fmaf(scale, v[e], static_cast<float>(y[e])));
     }
-  } else {
-    for (int e = 0; e < 16 && n + e < N; ++e) y[e] = static_cast<out_t>(fmaf(scale, v[e], static_cast<float>(y[e])));
   }
 }
 
