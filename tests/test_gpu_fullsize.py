@@ -142,6 +142,53 @@ def test_dit_attn_proj_full(cuda):
                  np.concatenate([r[1] for r in refs]), y)
 
 
+@pytest.mark.parametrize("r", [32, 128])
+def test_dit_attn_proj_lora_full(cuda, r):
+    """The LoRA workloads' correction at full size, as the benchmark runs it:
+    X [4096, 3072], rank r on the QKV's 9216 columns, added in place into the
+    QKV's column view of the one launch over both linears (row pitch 12288).
+    T is checked on sampled rows within one bf16 ulp plus the fp32 summation
+    bound of the oracle's; Y on
+    those rows against bf16(Y0 + scale T B^T) from the GPU's own T, and the
+    other linear's columns must stay untouched."""
+    wl = W.config2()
+    G, X = wl.G, wl.X
+    qkv = wl.linears[0]
+    K, N = qkv.W.shape[1], qkv.W.shape[0]
+    A, B = W.lora_adapter(K, N, r)
+    xd = to_dev(X, torch.bfloat16)
+    Wc = np.concatenate([lin.W for lin in wl.linears])
+    bc = np.concatenate([lin.b for lin in wl.linears])
+    y = cr.linear(cr.pack_act(xd, G), cr.pack_weight(to_dev(Wc, torch.bfloat16), G), to_dev(bc, torch.float32))
+    y0 = y.clone()
+    ws = torch.empty((cr.lora_workspace_bytes(X.shape[0], K, r) + 1) // 2, dtype=torch.bfloat16, device=cuda)
+    cr.lora_add(xd, to_dev(A, torch.bfloat16), to_dev(B, torch.bfloat16), 0.5, y[:, :N], workspace=ws)
+    S = rows_to_check(X, 5)
+    St = torch.from_numpy(S).to(cuda)
+    T = to_np(ws[:X.shape[0] * r].view(X.shape[0], r).index_select(0, St))
+    T_ref = O.lora_intermediate(X[S], A)
+    # T is an fp32 sum of K products in an unspecified order, rounded to bf16:
+    # one bf16 ulp plus the worst-case fp32 summation error K 2^-24 sum|x a|
+    # (the outlier channels make some sums cancel far below their terms).
+    mag = np.abs(X[S].astype(np.float64)) @ np.abs(A.astype(np.float64)).T
+    bound = np.abs(T_ref) * 2.0 ** -7 + K * 2.0 ** -24 * mag + 1e-30
+    d = np.abs(T.astype(np.float64) - T_ref)
+    say(f"  lora r={r}: T max |d| / bound {float(np.max(d / bound)):.3f}, "
+        f"{np.count_nonzero(d > np.abs(T_ref) * 2.0 ** -7)} of {d.size} beyond one bf16 ulp")
+    assert np.all(d <= bound)
+    got = to_np(y.index_select(0, St))
+    base = to_np(y0.index_select(0, St))
+    want = O.bf16_round((base[:, :N].astype(np.float64) + 0.5 * (T.astype(np.float64) @ B.astype(np.float64).T))
+                        .astype(np.float32))
+    ulp = bf16_ulp_dist(got[:, :N], want)
+    err = R.rel_fro(got[:, :N], base[:, :N] + O.lora_delta64(X[S], A, B, 0.5))
+    say(f"  lora r={r}: {len(S)} rows; Y max ulp {int(ulp.max())}, "
+        f"{np.count_nonzero(ulp) / ulp.size:.2e} off; rel Frobenius vs oracle delta {err:.3e}")
+    assert ulp.max() <= 1 and np.count_nonzero(ulp) / ulp.size <= EPI_ULP_FRAC
+    assert err <= 2e-3
+    assert torch.equal(y[:, N:], y0[:, N:])
+
+
 def test_dit_mlp_full(cuda):
     """X bf16 [8192, 3072] with a Student-t tail -> up [12288, 3072] -> GELU
     (torch) -> pack of the [8192, 12288] intermediate -> down [3072, 12288]."""
