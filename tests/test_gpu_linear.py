@@ -119,6 +119,22 @@ def test_row_split_bit_exact(cuda):
     assert torch.equal(again, full)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (513, 264, 3072), (4096, 1024, 3072), (64, 8, 12288)])
+def test_accumulator_matches_vendor_int8_gemm(cuda, M, N, K):
+    """The int32 accumulator equals the vendor's int8 GEMM (torch._int_mm on
+    hipBLASLt) on the same codes, bit for bit: an integer product has one
+    answer."""
+    qx = to_dev(random_codes((M, K), seed=M + K), torch.int8)
+    qw = to_dev(random_codes((N, K), seed=N + 3 * K), torch.int8)
+    try:
+        ref = torch._int_mm(qx, qw.t())
+    except RuntimeError as e:  # a shape the vendor call does not take
+        pytest.skip(f"torch._int_mm: {e}")
+    a = cr.Packed(qx, torch.ones(M, device=cuda), 256)
+    w = cr.Packed(qw, torch.ones(N, device=cuda), 256)
+    assert torch.equal(cr.linear(a, w, out_dtype=torch.int32), ref)
+
+
 @pytest.mark.parametrize("M", [700, 16])
 def test_concatenated_weights_one_launch(cuda, M):
     """Weights are packed row by row, so linears that share one packed
