@@ -532,8 +532,9 @@ def main():
                     help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is data parallel over rows "
-              "and multi-GPU runs are not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is data parallel over "
+              "rows, so each GPU runs the same one-GPU step on its own rows, and this library has no multi-GPU "
+              "driver.", file=sys.stderr)
         sys.exit(2)
 
     import torch
