@@ -211,6 +211,34 @@ def check_quant_ties_half_even():
     assert q[0].tolist() == [127, 2, 4, -2, 0, 0, 2, 126]
 
 
+def check_code_values(seed: int = 18):
+    """``code_values`` is the value the quantiser rounds.  Rounded half to
+    even and clamped it gives ``quantize_rows``' codes (int8) and
+    ``quantize_rows_int4``' codes (int4), on rows of mixed magnitude, a
+    zero row and a row with s = 1 and exact ties.  Each v is the correctly
+    rounded fp32 quotient x / s: an fp64 division rounded once to fp32 is
+    that quotient (53 >= 2 * 24 + 2 bits, so the double rounding is
+    innocuous).  A zero row gives v = 0."""
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((12, 384)) * g.uniform(1e-3, 300, (12, 1))).astype(np.float32)
+    x[2] = 0.0
+    x[5, :8] = [127.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 126.5]
+    x[5, 8:] = np.clip(x[5, 8:], -100, 100)
+    q, s = O.quantize_rows(x)
+    v = O.code_values(x, s)
+    assert v.dtype == np.float32 and v.shape == x.shape
+    assert np.array_equal(np.clip(np.rint(v), -127, 127).astype(np.int8), q)
+    assert s[5] == 1.0 and np.array_equal(v[5], x[5])
+    assert np.all(v[2] == 0)
+    nz = s > 0
+    exact = (x[nz].astype(np.float64) / s[nz, None].astype(np.float64)).astype(np.float32)
+    assert np.array_equal(v[nz], exact)
+    q4, s4 = O.quantize_rows_int4(x)
+    v4 = O.code_values(x, s4)
+    assert np.array_equal(np.clip(np.rint(v4), -7, 7).astype(np.int8), q4)
+    assert np.all(v4[2] == 0)
+
+
 def check_qmax_from_pages():
     consts = page_constants()
     assert O.QMAX == consts["qmax"]
@@ -537,6 +565,7 @@ ALL_CHECKS = [
     ("quant_invariants", check_quant_invariants, ()),
     ("quant_ties_half_even", check_quant_ties_half_even, ()),
     ("qmax_from_pages", check_qmax_from_pages, ()),
+    ("code_values", check_code_values, ()),
     ("int_gemm_bruteforce", check_int_gemm_bruteforce, ()),
     ("int_gemm_extremes", check_int_gemm_extremes, ()),
     ("int_gemm_large_random", check_int_gemm_large_random, ()),

@@ -4,10 +4,11 @@ Readings of the tolerances (see the design notes):
 
 * Codes (Q_x, Q_w): a GPU code may differ from the oracle's by exactly 1,
   and only where the oracle's fp32 code value v lies within
-  TIE_REL * 127 of a rounding tie (|v - (floor(v) + 1/2)| <= 1.27e-4 code
-  units, i.e. within 1e-6 of the row's full-scale code); at most
-  FLIP_FRAC of all elements may differ.  The count under the stricter
-  reading (|v - tie| <= 1e-6 |v|) is reported as well.
+  TIE_REL * qmax of a rounding tie, i.e. within 1e-6 of the row's
+  full-scale code (qmax = 127 for int8: 1.27e-4 code units; qmax = 7 for
+  int4 weights: 7e-6 code units); at most FLIP_FRAC of all elements may
+  differ.  The count under the stricter reading (|v - tie| <= 1e-6 |v|) is
+  reported as well.
 * Scales: relative difference <= 1e-5.
 * Rotated fp32 rows: per row, max |diff| <= 1e-5 * max |oracle row|.
 * The int32 accumulator: bit-exact.
@@ -45,14 +46,14 @@ class CodeReport:
                 f"{self.outside_window} outside the tie window, {self.strict_outside} outside the strict window")
 
 
-def compare_codes(q_gpu: np.ndarray, q_ref: np.ndarray, v_ref: np.ndarray) -> CodeReport:
+def compare_codes(q_gpu: np.ndarray, q_ref: np.ndarray, v_ref: np.ndarray, qmax: int = 127) -> CodeReport:
     q_gpu = np.asarray(q_gpu).astype(np.int16)
     q_ref = np.asarray(q_ref).astype(np.int16)
     d = q_gpu - q_ref
     idx = np.nonzero(d)
     v = np.asarray(v_ref, np.float64)[idx]
     tie_dist = np.abs(v - (np.floor(v) + 0.5))
-    outside = int(np.count_nonzero(tie_dist > TIE_REL * 127))
+    outside = int(np.count_nonzero(tie_dist > TIE_REL * qmax))
     strict = int(np.count_nonzero(tie_dist > TIE_REL * np.abs(v)))
     return CodeReport(int(q_ref.size), int(idx[0].size), int(np.max(np.abs(d))) if d.size else 0, outside, strict)
 

@@ -181,7 +181,8 @@ def test_dit_attn_proj_lora_full(cuda, r):
     want = O.bf16_round((base[:, :N].astype(np.float64) + 0.5 * (T.astype(np.float64) @ B.astype(np.float64).T))
                         .astype(np.float32))
     ulp = bf16_ulp_dist(got[:, :N], want)
-    err = R.rel_fro(got[:, :N], base[:, :N] + O.lora_delta64(X[S], A, B, 0.5))
+    err = R.rel_fro(got[:, :N], O.bf16_round((base[:, :N].astype(np.float64) + O.lora_delta64(X[S], A, B, 0.5))
+                                              .astype(np.float32)))
     say(f"  lora r={r}: {len(S)} rows; Y max ulp {int(ulp.max())}, "
         f"{np.count_nonzero(ulp) / ulp.size:.2e} off; rel Frobenius vs oracle delta {err:.3e}")
     assert ulp.max() <= 1 and np.count_nonzero(ulp) / ulp.size <= EPI_ULP_FRAC

@@ -68,8 +68,21 @@ def test_lora_add_strided_output_and_untouched_padding(cuda):
     buf = torch.full((M, N + 24), -3.0, dtype=torch.float32, device=cuda)
     y = buf[:, 8:8 + N]
     y.zero_()
-    cr.lora_add(*(to_dev(t, torch.bfloat16) for t in (x, a, b)), 2.0, y)
-    assert R.rel_fro(to_np(y), O.lora_delta64(x, a, b, 2.0)) <= 5e-3
+    ws = torch.empty((cr.lora_workspace_bytes(M, K, r) + 1) // 2, dtype=torch.bfloat16, device=cuda)
+    cr.lora_add(*(to_dev(t, torch.bfloat16) for t in (x, a, b)), 2.0, y, workspace=ws)
+    T = to_np(ws[:M * r].view(M, r)).astype(np.float64)
+    got = to_np(y).astype(np.float64)
+    # the added correction is 2 T B^T of the call's own T, summed in fp32 over r
+    assert R.rel_fro(got, 2.0 * (T @ b.astype(np.float64).T)) <= 1e-5
+    # against the oracle: T is within one bf16 ulp (2^-7 relative) plus the
+    # worst-case fp32 summation error K 2^-24 sum |x a| of its K products, so
+    # |dY| <= 2 (dT |B|^T) elementwise, plus the fp32 sum over r
+    T_ref = O.lora_intermediate(x, a).astype(np.float64)
+    dT = np.abs(T_ref) * 2.0 ** -7 + K * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(a.astype(np.float64)).T)
+    assert np.all(np.abs(T - T_ref) <= dT)
+    ref = O.lora_delta64(x, a, b, 2.0)
+    bound = np.linalg.norm(2.0 * (dT @ np.abs(b.astype(np.float64)).T)) / np.linalg.norm(ref) + 1e-5
+    assert R.rel_fro(got, ref) <= bound
     assert torch.all(buf[:, :8] == -3.0) and torch.all(buf[:, 8 + N:] == -3.0)
 
 

@@ -55,7 +55,7 @@ def test_pack_weight_w4_regular(cuda, G, K, N, dtype):
     p = cr.pack_weight_w4(wd, G)
     b_ref, s_ref, q_ref, wr = O.pack_weight_int4(w, G)
     q_gpu = O.unpack_nibbles(to_np(p.q))
-    rep = R.compare_codes(q_gpu, q_ref, O.code_values(wr, s_ref))
+    rep = R.compare_codes(q_gpu, q_ref, O.code_values(wr, s_ref), qmax=O.QMAX4)
     print(rep)
     assert rep.ok(), rep
     assert np.max(np.abs(q_gpu)) <= 7
@@ -71,7 +71,7 @@ def test_pack_weight_w4_randomized(cuda, G, K, N):
     sd = to_dev(signs, torch.int8)
     p = cr.pack_weight_w4(to_dev(w, torch.bfloat16), G, cr.RANDOMIZED, sd)
     _, s_ref, q_ref, wr = O.pack_weight_int4(w, G, O.RANDOMIZED, signs)
-    rep = R.compare_codes(O.unpack_nibbles(to_np(p.q)), q_ref, O.code_values(wr, s_ref))
+    rep = R.compare_codes(O.unpack_nibbles(to_np(p.q)), q_ref, O.code_values(wr, s_ref), qmax=O.QMAX4)
     assert rep.ok(), rep
     assert R.scale_rel_diff(to_np(p.scale), s_ref) <= R.SCALE_RTOL
 
@@ -159,7 +159,7 @@ def test_w4a8_decode_layer_full_size(cuda):
     qg, qu, qd = (O.unpack_nibbles(to_np(p.q)) for p in (pg, pu, pd))
     for W, p, q in ((Wg, pg, qg), (Wu, pu, qu), (Wd, pd, qd)):
         _, s_ref, q_ref, wr = O.pack_weight_int4(W, G)
-        assert R.compare_codes(q, q_ref, O.code_values(wr, s_ref)).ok()
+        assert R.compare_codes(q, q_ref, O.code_values(wr, s_ref), qmax=O.QMAX4).ok()
     g64 = O.epilogue64(O.int_gemm(qx, qg), to_np(a.scale), to_np(pg.scale))
     u64 = O.epilogue64(O.int_gemm(qx, qu), to_np(a.scale), to_np(pu.scale))
     h_ref = O.bf16_round((R.gelu64(g64, cr.GELU_TANH) * u64).astype(np.float32))

@@ -15,6 +15,7 @@ _epilogue64 = O.epilogue64
 _int_gemm = O.int_gemm
 _bf16_round = O.bf16_round
 _randomized_block = O.randomized_block
+_code_values = O.code_values
 
 
 def _h4_sign_flip():
@@ -232,6 +233,33 @@ def _lora_no_scale(X, A, B, scale):
     return _lora_delta64(X, A, B, 1.0)
 
 
+def _code_values_fp64(x, s):
+    # the quotient left in fp64 instead of rounded to fp32
+    x = np.asarray(x, np.float64)
+    s = np.asarray(s, np.float64)
+    v = np.zeros(x.shape)
+    nz = s > 0
+    v[nz] = x[nz] / s[nz][:, None]
+    return v
+
+
+def _code_values_reciprocal(x, s):
+    # x * (127 / amax) in fp32 instead of the division x / s
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    inv = np.zeros_like(amax)
+    nz = amax > 0
+    inv[nz] = (np.float32(127) / amax[nz]).astype(np.float32)
+    return (x * inv[:, None]).astype(np.float32)
+
+
+def _code_values_unmasked(x, s):
+    # zero rows divided by a zero scale (NaN codes) instead of v = 0
+    x = np.asarray(x, np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return (x / np.asarray(s, np.float32)[:, None]).astype(np.float32)
+
+
 MUTATIONS = {
     "h4_sign_flip": ("h4", _h4_sign_flip),
     "h4_unnormalised": ("h4", _h4_unnormalised),
@@ -244,6 +272,9 @@ MUTATIONS = {
     "quant_half_away": ("quantize_rows", _quant_half_away),
     "quant_truncates": ("quantize_rows", _quant_truncate),
     "quant_partial_row_scale": ("quantize_rows", _quant_first_group_scale),
+    "code_values_fp64": ("code_values", _code_values_fp64),
+    "code_values_reciprocal": ("code_values", _code_values_reciprocal),
+    "code_values_zero_rows_nan": ("code_values", _code_values_unmasked),
     "epilogue_drops_bias": ("epilogue64", _epi_no_bias),
     "epilogue_drops_weight_scale": ("epilogue64", _epi_no_sw),
     "epilogue_swaps_scales": ("epilogue64", _epi_swapped),

@@ -41,6 +41,15 @@ def test_window_widths():
     assert R.compare_codes(gpu, ref, v).outside_window == 1
 
 
+def test_window_scales_with_code_range():
+    # int4 codes (full scale 7): the window is 1e-6 * 7 = 7e-6 code units.
+    v = np.array([[2.5 + 6.9e-6, 2.5 + 7.2e-6, 2.5 + 1.2e-4]], dtype=np.float64)
+    ref = np.array([[3, 3, 3]], dtype=np.int8)
+    gpu = np.array([[2, 2, 2]], dtype=np.int8)
+    assert R.compare_codes(gpu, ref, v, qmax=7).outside_window == 2
+    assert R.compare_codes(gpu, ref, v).outside_window == 0
+
+
 def test_scale_and_rows():
     assert R.scale_rel_diff(np.array([1.0, 0.0]), np.array([1.0 + 1e-7, 0.0])) < 1e-6
     assert R.scale_rel_diff(np.array([1.0, 1e-9]), np.array([1.0, 0.0])) == float("inf")
