@@ -11,7 +11,10 @@ projection; gate and up as one gated launch); ``--unfused`` runs it as a
 separate torch op after plain linears instead.
 
 Workloads (``--workload``):
-  dit_attn_proj  (default) X bf16 [4096, 3072], 8 outlier channels; fused QKV
+  large_m_qkv    (default) X bf16 [32700, 6144], 0.1% of entries x100;
+                 W [18432, 6144]; plus the routed layer X' [32700, 2688] ->
+                 W' [6144, 2688] on the bf16 linear (2688 % 256 != 0).
+  dit_attn_proj  X bf16 [4096, 3072], 8 outlier channels; fused QKV
                  W [9216, 3072] and a second W [3072, 3072] share one pack.
                  Both run as one launch over the concatenated packed weight
                  (per-row packing makes it the concatenation of the two packed
@@ -22,8 +25,6 @@ Workloads (``--workload``):
                  QKV output (two launches after the linear).
   dit_mlp        X bf16 [8192, 3072]; W_up [12288, 3072], GELU, W_down
                  [3072, 12288].
-  large_m_qkv    X bf16 [32700, 6144]; W [18432, 6144]; plus the routed layer
-                 X' [32700, 2688] -> W' [6144, 2688] on the bf16 linear.
   decode_m{M}_g{G}[r]  gated FFN at M in {1, 4, 16}, K = 1152: W_gate, W_up
                  [6912, 1152] share one pack, h = gelu_tanh(gate) * up feeds
                  W_down [1152, 6912]; G in {16, 64, 1024}, "r" = randomized
@@ -36,12 +37,21 @@ Inputs live in HBM before timing starts.  To keep the 256 MB Infinity Cache
 from serving them, each step uses the next of several independent buffer sets
 (activations, packed weights, outputs) whose total exceeds 512 MB.
 
-The timed region is one replay of a HIP graph that holds exactly K steps (the
-launches a serving loop would capture).  Per-launch durations come from one
+The step is captured as HIP graphs of exactly K and of 2K steps (the launches
+a serving loop would capture).  Each graph is replayed three times, each
+replay bracketed by device synchronisation, and the median taken.  A replay
+carries a fixed cost (the graph launch and the ramp of its first kernel)
+besides its steps, so ``ms_per_step`` is the slope between the two lengths,
+(t_2K - t_K) / K, which does not depend on K; the K-step replay divided by K
+is reported as ``ms_per_step_k_graph``.  Per-launch durations come from one
 graph per launch of the step, holding that launch repeated over the buffer
 sets, timed with events on its stream and divided by the repeat count.
 ``--eager`` launches every kernel from Python instead, with an event between
 consecutive launches (at decode sizes that measures the host's launch cost).
+
+Besides the published peaks the line carries measured ceilings of the GPU it
+ran on: a device copy's GB/s, and the int8 MFMA rate and shader clock of an
+MFMA-only loop on random operands (libconvrot_probe.so).
 
 Prints one JSON line on stdout; per-kernel details go to stderr.
 """
@@ -255,10 +265,13 @@ class StepSet:
         """A packed (int8 or int4) weight, as opposed to a routed bf16 tensor."""
         return isinstance(w, (self.cr.Packed, self.cr.PackedW4))
 
-    def _workspace(self, nbytes, dev):
-        """Expanded-weight workspace of the int4 path above 16 rows."""
-        ws = self.torch.empty(nbytes, dtype=self.torch.int8, device=dev)
-        self.bufs.append(ws)
+    def _workspace(self, kind, M, N, K, dev):
+        """The workspace a linear call of ``kind`` uses (the small-M K split's
+        partial sums, the int4 path's expanded weight above 16 rows), owned
+        by this buffer set; None when the call needs none."""
+        ws = self.cr.linear_workspace(kind, M, N, K, dev)
+        if ws is not None:
+            self.bufs.append(ws)
         return ws
 
     # -- buffers -----------------------------------------------------------
@@ -294,13 +307,15 @@ class StepSet:
         cr, w, b = self.cr, self.W[name], self.b[name]
         ob = y.element_size()
         if isinstance(w, cr.Packed):
-            return Op(f"linear_{name}", lambda: cr.linear(src, w, b, out=y), "int8", M=src.rows, N=w.rows, K=w.K,
-                      out_b=ob)
+            ws = self._workspace("plain", src.rows, w.rows, w.K, y.device)
+            return Op(f"linear_{name}", lambda: cr.linear(src, w, b, out=y, workspace=ws), "int8", M=src.rows,
+                      N=w.rows, K=w.K, out_b=ob)
         if isinstance(w, cr.PackedW4):
-            ws = self._workspace(w.rows * w.K, y.device) if src.rows > SMALL_M else None
+            ws = self._workspace("w4", src.rows, w.rows, w.K, y.device)
             return Op(f"linear_{name}", lambda: cr.linear_w4(src, w, b, out=y, workspace=ws), "int4", M=src.rows,
                       N=w.rows, K=w.K, out_b=ob)
-        return Op(f"linear_{name}", lambda: cr.linear_bf16(src, w, b, out=y), "bf16", M=src.shape[0],
+        ws = self._workspace("bf16", src.shape[0], w.shape[0], w.shape[1], y.device)
+        return Op(f"linear_{name}", lambda: cr.linear_bf16(src, w, b, out=y, workspace=ws), "bf16", M=src.shape[0],
                   N=w.shape[0], K=w.shape[1], out_b=ob)
 
     def _plan(self, dev):
@@ -348,7 +363,9 @@ class StepSet:
                 # GELU in the up projection's epilogue
                 h = self._out("up", M, dev)
                 w, b = self.W["up"], self.b["up"]
-                ops.append(Op("linear_up_gelu", lambda: self.cr.linear_act(src0, w, b, self.cr.GELU_ERF, out=h),
+                wsa = self._workspace("plain", M, w.rows, w.K, dev)
+                ops.append(Op("linear_up_gelu", lambda: self.cr.linear_act(src0, w, b, self.cr.GELU_ERF, out=h,
+                                                                           workspace=wsa),
                               "int8", M=M, N=w.rows, K=w.K, out_b=h.element_size(), epilogue="act"))
             else:
                 y_up = self._out("up", M, dev)
@@ -369,7 +386,7 @@ class StepSet:
                 # int4 gate and up in one launch
                 h = self._out("gate", M, dev)
                 bg, bu = self.b["gate"], self.b["up"]
-                ws = self._workspace(2 * wg.rows * wg.K, dev) if M > SMALL_M else None
+                ws = self._workspace("w4_gated", M, wg.rows, wg.K, dev)
                 ops.append(Op("linear_gate_up", lambda: self.cr.linear_w4_gated(
                     src0, wg, wu, bg, bu, self.cr.GELU_TANH, out=h, workspace=ws),
                     "int4", M=M, N=wg.rows, K=wg.K, out_b=h.element_size(), epilogue="gated"))
@@ -377,8 +394,9 @@ class StepSet:
                 # gate and up in one launch, gelu_tanh(gate) * up in its epilogue
                 h = self._out("gate", M, dev)
                 bg, bu = self.b["gate"], self.b["up"]
+                wsg = self._workspace("gated", M, wg.rows, wg.K, dev)
                 ops.append(Op("linear_gate_up", lambda: self.cr.linear_gated(src0, wg, wu, bg, bu, self.cr.GELU_TANH,
-                                                                               out=h),
+                                                                               out=h, workspace=wsg),
                               "int8", M=M, N=wg.rows, K=wg.K, out_b=h.element_size(), epilogue="gated"))
             else:
                 g = self._out("gate", M, dev)
@@ -421,17 +439,26 @@ def _gelu_tanh(y):
 
 
 def cpu_baseline(wl, budget_s: float = 12.0):
-    """Time the oracle on a bounded row sample of the same step.
+    """Time the oracle on a bounded row sample of the same step, with the
+    pack (rotation + quantisation) and the quantised linears (exact integer
+    GEMM + epilogue) timed separately.
 
-    Weights are packed beforehand (untimed).  The harness activations between
-    chained layers (GELU) are computed with numpy inside the timed region.
+    The oracle runs on every host core this process may use
+    (``os.sched_getaffinity``), with the BLAS thread pool set to that count.
+    Weights are packed beforehand (untimed).  Routed layers (fp64 linear) and
+    the harness activations between chained layers (GELU in numpy) are timed
+    as "other".
     """
     import threadpoolctl
 
     import oracle.convrot_oracle as O
 
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        return _cpu_baseline(wl, budget_s, cores, O)
+
+
+def _cpu_baseline(wl, budget_s, cores, O):
     G, kind = wl.G, wl.kind
     signs = {wl.X.shape[1]: wl.signs}
     if wl.extra.get("signs_down") is not None:
@@ -451,24 +478,38 @@ def cpu_baseline(wl, budget_s: float = 12.0):
         if l is not routed and K % G == 0:
             if w4:
                 nib, s, _, _ = O.pack_weight_int4(l.W, G, kind, sg(K))
-                packed[n] = (nib, s)
+                packed[n] = (O.unpack_nibbles(nib), s)
             else:
                 q, s, _ = O.pack(l.W, G, kind, sg(K))
                 packed[n] = (q, s)
 
+    spent = {"pack": 0.0, "gemm": 0.0, "other": 0.0}
+    work = {"pack_bytes": 0.0, "gemm_ops": 0.0}
+
+    def timed(key, fn, *a):
+        t0 = time.perf_counter()
+        r = fn(*a)
+        spent[key] += time.perf_counter() - t0
+        return r
+
+    def pack(x):
+        work["pack_bytes"] += x.shape[0] * x.shape[1] * (2 if wl.xdtype == "bf16" else 4) + x.size + 4 * x.shape[0]
+        qx, sx, _ = timed("pack", O.pack, x, G, kind, sg(x.shape[1]))
+        return qx, sx
+
     def gemm(name, qx, sx):
-        q = O.unpack_nibbles(packed[name][0]) if w4 else packed[name][0]
-        return O.epilogue64(O.int_gemm(qx, q), sx, packed[name][1], lin[name].b).astype(np.float32)
+        q, s = packed[name]
+        work["gemm_ops"] += 2.0 * qx.shape[0] * q.shape[0] * q.shape[1]
+        return timed("gemm", lambda: O.epilogue64(O.int_gemm(qx, q), sx, s, lin[name].b).astype(np.float32))
 
     def layer(name, x):
         if name in packed:
-            qx, sx, _ = O.pack(x, G, kind, sg(x.shape[1]))
-            return gemm(name, qx, sx)
-        return O.linear_unquantized64(x, lin[name].W, lin[name].b).astype(np.float32)
+            return gemm(name, *pack(x))
+        return timed("other", lambda: O.linear_unquantized64(x, lin[name].W, lin[name].b).astype(np.float32))
 
     def shared(names, x):
         if all(n in packed for n in names):
-            qx, sx, _ = O.pack(x, G, kind, sg(x.shape[1]))
+            qx, sx = pack(x)
             return [gemm(n, qx, sx) for n in names]
         return [layer(n, x) for n in names]
 
@@ -484,15 +525,17 @@ def cpu_baseline(wl, budget_s: float = 12.0):
         if wl.cfg in (1, 2):
             ys = shared(list(l.name for l in wl.linears), x)
             if adapter is not None:
-                ys[0] = ys[0] + O.lora_delta64(x, adapter[0], adapter[1], 0.5).astype(np.float32)
+                ys[0] = ys[0] + timed("other", lambda: O.lora_delta64(x, adapter[0], adapter[1], 0.5)
+                                      .astype(np.float32))
         elif wl.cfg == 3:
-            layer("down", _gelu_erf(layer("up", x)).astype(np.float32))
+            h = timed("other", lambda y: _gelu_erf(y).astype(np.float32), layer("up", x))
+            layer("down", h)
         elif wl.cfg == 4:
             layer("qkv", x)
             layer(routed.name, wl.extra["X_routed"][:m])
         elif wl.cfg == 5:
             g, u = shared(["gate", "up"], x)
-            layer("down", (_gelu_tanh(g) * u).astype(np.float32))
+            layer("down", timed("other", lambda: (_gelu_tanh(g) * u).astype(np.float32)))
         return time.perf_counter() - t0
 
     ops_per_row = sum(2.0 * l.W.shape[0] * l.W.shape[1] for l in lin.values())
@@ -501,16 +544,26 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     t = run(m)
     while m < M and t < budget_s / 4:
         m = min(M, m * 4)
+        for k in spent:
+            spent[k] = 0.0
+        for k in work:
+            work[k] = 0.0
         t = run(m)
     reps, total = 1, t
     while total < budget_s and m == M:
         total += run(m)
         reps += 1
-    return {"value": round(ops_per_row * m * reps / total / 1e12, 6), "unit": "TOPS", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"first {m} of {M} activation rows of the same step, {reps} run(s) (pack + every linear's "
-                      f"exact int GEMM and epilogue, routed layers in fp64, GELU in numpy; weights packed "
-                      f"beforehand, untimed); {total:.2f} s"}
+    out = {"value": round(ops_per_row * m * reps / total / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"first {m} of {M} activation rows of the same step, {reps} run(s) (pack + every linear's "
+                     f"exact int GEMM and epilogue, routed layers in fp64, GELU in numpy; weights packed "
+                     f"beforehand, untimed); {total:.2f} s on {cores} cores (BLAS threads = cores)",
+           "seconds": {k: round(v, 3) for k, v in spent.items()}}
+    if spent["pack"] > 0:
+        out["pack_GBps"] = round(work["pack_bytes"] / spent["pack"] / 1e9, 4)
+    if spent["gemm"] > 0:
+        out["gemm_TOPS"] = round(work["gemm_ops"] / spent["gemm"] / 1e12, 6)
+    return out
 
 
 def main():
@@ -518,7 +571,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dit_attn_proj")
+    ap.add_argument("--workload", default="large_m_qkv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python in the timed region instead of replaying a captured graph")
@@ -530,6 +583,8 @@ def main():
                          "the concatenated weight")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy and MFMA-only ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is data parallel over "
@@ -581,20 +636,38 @@ def main():
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t_start
     else:
-        # The K steps (cycling through the buffer sets) are captured once as a
-        # HIP graph and replayed: the kernels run back to back, without the
-        # host's per-launch cost between them.  The graph is replayed once,
-        # untimed, before the timed replay.
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            for i in range(args.steps):
-                sets[i % len(sets)].step()
-        g_step.replay()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        g_step.replay()
-        torch.cuda.synchronize()
-        t_total = time.perf_counter() - t_start
+        # K steps and 2K steps (cycling through the buffer sets) are captured
+        # as HIP graphs and replayed: the kernels run back to back, without
+        # the host's per-launch cost between them.  Each graph is replayed
+        # once untimed, then three times timed (each replay bracketed by
+        # device synchronisation); the medians give the per-step slope.
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    sets[i % len(sets)].step()
+            g.replay()
+            torch.cuda.synchronize()
+            return g
+
+        def replay_s(g, n=3):
+            ts = []
+            for _ in range(n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                g.replay()
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+            return float(np.median(ts))
+
+        g_k = capture(args.steps)
+        t_k = replay_s(g_k)
+        g_2k = capture(2 * args.steps)
+        t_2k = replay_s(g_2k)
+        t_k = min(t_k, replay_s(g_k))  # again after the long graph: same clock state
+        del g_2k
+        t_total = t_2k - t_k     # K steps without the fixed per-replay cost
+        ms_k_graph = t_k * 1e3 / args.steps
         # Per-launch durations (events cannot be recorded inside a captured
         # graph here): launch j of the step, repeated over the buffer sets in
         # one graph, between two events on the stream it runs on.
@@ -665,6 +738,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "timing": "eager launches" if args.eager else
+                  "slope between graphs of K and 2K steps, (t_2K - t_K) / K, medians of 3 replays",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -689,6 +764,29 @@ def main():
                                    "achieved": round(kp["GB/s"], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(kp["frac_hbm"], 4),
                                    "traffic": measured_traffic("pack_rows", args.workload)}
+    if not args.eager:
+        result["ms_per_step_k_graph"] = round(ms_k_graph, 5)
+    if not args.no_ceilings:
+        from w8a8_int8_linear_amd import probe
+
+        mf = probe.mfma_i8(dev)
+        result["ceilings"] = {
+            "copy_GBps": probe.copy_gbps(dev),
+            "mfma_i8_TOPS": mf["TOPS"],
+            "mfma_i8_frac_of_peak": round(mf["TOPS"] / PEAK_I8_TOPS, 4),
+            "sclk_GHz_mfma_loop": mf["sclk_GHz"],
+            "sclk_GHz_range": [mf["sclk_GHz_min"], mf["sclk_GHz_max"]],
+            "note": "device copy (read + write bytes / s); MFMA-only v_mfma_i32_16x16x64_i8 loop, one workgroup "
+                    "per CU, two waves per SIMD, random normal codes; shader clock per CU from s_memtime against "
+                    "the 100 MHz s_memrealtime",
+        }
+        if roof["bound"] == "mfma":
+            roof["frac_of_measured_mfma"] = round(roof["achieved"] / mf["TOPS"], 4)
+        else:
+            roof["frac_of_copy"] = round(roof["achieved"] / result["ceilings"]["copy_GBps"], 4)
+        if "pack_roofline" in result:
+            result["pack_roofline"]["frac_of_copy"] = round(result["pack_roofline"]["achieved"] /
+                                                            result["ceilings"]["copy_GBps"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -41,18 +41,24 @@
  *   output of the pack and rotate entry points must have a 16-byte aligned
  *   base and a leading dimension whose size in bytes is a multiple of 16.
  *   The Y output of the linear entry points only needs element alignment.
- * - The caller owns every input and output buffer.  The only device memory
- *   the library allocates is one 8 MiB workspace per device, on the first
- *   linear call with M <= 16 that has fewer 16-feature output tiles than
- *   the GPU has CUs (it then splits K across workgroups, stores their
- *   partial sums there and adds them in a second launch).  That allocation
- *   is skipped while `stream` is being captured into a graph, and such a
- *   call then uses the unsplit kernel; an allocation failure likewise falls
- *   back, never errors.  The workspace is held until the process ends and
- *   needs no clearing, so captured graphs may replay calls that use it.  Two
- *   such small-M calls must not run at the same time on one device (on
- *   different streams); calls ordered on one stream, or by events, may.
- *   Beyond that the library keeps a thread-local error string.
+ * - The caller owns every buffer, inputs, outputs and workspaces alike.
+ *   The library allocates no device memory.  Its only state is a
+ *   thread-local error string and, per device, the CU count and the kernel
+ *   attributes it has set (written once, never reset).
+ * - Workspaces.  The linear entry points take `workspace` (a device pointer,
+ *   16-byte aligned, or NULL) and `workspace_bytes`.  With M <= 16 a
+ *   workspace of convrot_linear_workspace_bytes(...) bytes lets the
+ *   weight-streaming kernel split K across workgroups when the output has
+ *   fewer 16-feature tiles than the GPU has CUs: the partial sums go there
+ *   and a second launch adds them in K order.  NULL selects the unsplit
+ *   kernel.  int8 results are the same bits either way; bf16 results of
+ *   convrot_linear_bf16 may differ in the last place (fp32 summation
+ *   order).  A non-NULL workspace smaller than the query's size is
+ *   CONVROT_ERR_INVALID_ARG.  The int4 entry points with M > 16 need one
+ *   (the expanded weight).  A call fully rewrites what it uses, so a
+ *   workspace needs no clearing and captured graphs may replay such calls.
+ *   Calls that may run at the same time (different streams) need separate
+ *   workspaces.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the
  *   default stream).  Inputs must stay alive, and outputs untouched, until
  *   the stream has passed the call.  Outputs must not alias inputs.
@@ -75,7 +81,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 6
+#define CONVROT_ABI_VERSION 7
 
 typedef enum {
   CONVROT_OK = 0,
@@ -101,14 +107,31 @@ typedef enum {
 } convrot_rot_kind;
 
 /* Activation applied by a fused epilogue (convrot_linear_act,
- * convrot_linear_gated), with the erf and tanh of the device math library:
- *   GELU_ERF   gelu(y) = y/2 (1 + erf(y / sqrt 2))
- *   GELU_TANH  gelu(y) = y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))  */
+ * convrot_linear_gated):
+ *   GELU_ERF   gelu(y) = y Phi(y) = y/2 (1 + erf(y / sqrt 2)), with the
+ *              normal tail 1 - Phi(|y|) from the five-term erfc
+ *              approximation of Abramowitz & Stegun, formula 7.1.26
+ *              (absolute error <= 1.5e-7 on erfc, so |gelu error| <=
+ *              7.5e-8 |y| before fp32 rounding), evaluated with the
+ *              hardware reciprocal and exp2
+ *   GELU_TANH  gelu(y) = y/2 (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3),
+ *              evaluated as y / (1 + exp(-2u)) with the hardware exp2 and
+ *              reciprocal (a few fp32 ulp of y)  */
 typedef enum {
   CONVROT_ACT_NONE = 0, /* not accepted by the fused entry points (use convrot_linear) */
   CONVROT_ACT_GELU_ERF = 1,
   CONVROT_ACT_GELU_TANH = 2
 } convrot_act;
+
+/* Which linear entry point a workspace query is for
+ * (convrot_linear_workspace_bytes). */
+typedef enum {
+  CONVROT_LINEAR_PLAIN = 0,    /* convrot_linear, convrot_linear_act */
+  CONVROT_LINEAR_GATED = 1,    /* convrot_linear_gated */
+  CONVROT_LINEAR_BF16 = 2,     /* convrot_linear_bf16 */
+  CONVROT_LINEAR_W4 = 3,       /* convrot_linear_w4 */
+  CONVROT_LINEAR_W4_GATED = 4  /* convrot_linear_w4_gated */
+} convrot_linear_kind;
 
 /* Norm of the data-free smoothing scales (convrot_smooth_ffn). */
 typedef enum {
@@ -187,12 +210,27 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
  *   Y     [M, ldy] of `ydt`: CONVROT_F32, CONVROT_BF16 (round to nearest
  *         even) or CONVROT_I32 (the raw accumulator A; scales and bias are
  *         then not applied)
+ *   workspace, workspace_bytes
+ *         NULL / 0, or caller-owned device memory of at least
+ *         convrot_linear_workspace_bytes(CONVROT_LINEAR_PLAIN, M, N, K)
+ *         bytes (see "Workspaces" above)
  * Small M (<= 16) uses a weight-streaming kernel, larger M a tiled
  * matrix-core kernel; both produce bit-identical A (the small-M kernel's
  * split over K adds exact int32 partial sums). */
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w,
                               const float* bias, void* Y, convrot_dtype ydt, int64_t ldy,
-                              void* stream);
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace a linear call of `kind` uses for X [M, K] and N
+ * outputs on the current device:
+ *   M <= 16  the split-K partial sums (0 when the shape does not split K);
+ *            optional, NULL selects the unsplit kernel
+ *   M > 16   0, except CONVROT_LINEAR_W4 (N * K, required) and
+ *            CONVROT_LINEAR_W4_GATED (2 * N * K, required)
+ * The size depends on the device's CU count.  M, N >= 0 and K a positive
+ * multiple of 16, else CONVROT_ERR_INVALID_ARG. */
+convrot_status convrot_linear_workspace_bytes(convrot_linear_kind kind, int64_t M, int64_t N, int64_t K,
+                                              int64_t* bytes);
 
 /* The quantised linear with an activation fused into its epilogue (the
  * output of the linear is never written unactivated):
@@ -202,11 +240,13 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
  *         CONVROT_ERR_INVALID_ARG
  *   ydt   CONVROT_F32 or CONVROT_BF16 (CONVROT_I32 is rejected with
  *         CONVROT_ERR_DTYPE).
+ *   workspace, workspace_bytes  as convrot_linear (kind CONVROT_LINEAR_PLAIN)
  * A packed activation feeds the next layer's linear; this entry point is
  * for a layer followed by an activation, such as the first linear of an
  * MLP. */
 convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packed* w, const float* bias,
-                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* stream);
+                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
 
 /* A gated pair: two quantised linears that share one packed activation,
  * combined in the epilogue of a single launch,
@@ -221,18 +261,24 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
  *                 (CONVROT_ERR_MISMATCH otherwise)
  *   b_gate, b_up  [N] fp32 or NULL
  *   fn, ydt       as convrot_linear_act
- *   Y             [M, ldy]. */
+ *   Y             [M, ldy]
+ *   workspace, workspace_bytes  as convrot_linear (kind
+ *                 CONVROT_LINEAR_GATED). */
 convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_packed* w_gate, const float* b_gate,
                                     const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
-                                    convrot_dtype ydt, int64_t ldy, void* stream);
+                                    convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                                    void* stream);
 
 /* The unquantised path for layers the rotation cannot cover (K % G != 0):
  *   Y[r, o] = sum_i X[r, i] W[o, i] + bias[o]
  * bf16 operands, fp32 accumulation, output CONVROT_BF16 or CONVROT_F32.
- *   X [M, ldx] bf16, W [N, ldw] bf16, bias [N] fp32 or NULL, Y [M, ldy]. */
+ *   X [M, ldx] bf16, W [N, ldw] bf16, bias [N] fp32 or NULL, Y [M, ldy]
+ *   workspace, workspace_bytes  as convrot_linear (kind CONVROT_LINEAR_BF16);
+ *   with the split the fp32 partial sums are added in K order. */
 convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw,
                                    const float* bias, int64_t M, int64_t N, int64_t K,
-                                   void* Y, convrot_dtype ydt, int64_t ldy, void* stream);
+                                   void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
 
 /* The rotation alone, for checking: the same kernel as convrot_pack_act with
  * quantisation switched off, writing the fp32 rotated rows X R.
@@ -258,9 +304,10 @@ convrot_status convrot_pack_weight_w4(const void* W, convrot_dtype wdt, int64_t 
  *   fn         CONVROT_ACT_NONE (plain linear; ydt may then also be
  *              CONVROT_I32, the raw accumulator), CONVROT_ACT_GELU_ERF or
  *              CONVROT_ACT_GELU_TANH
- *   workspace  M <= 16: unused (may be NULL); the weight-streaming kernel
- *              reads the nibbles (half the bytes of an int8 weight) and
- *              expands them in registers.  M > 16: caller-owned device
+ *   workspace  M <= 16: optional split-K partial sums as for
+ *              convrot_linear (kind CONVROT_LINEAR_W4); the weight-streaming
+ *              kernel reads the nibbles (half the bytes of an int8 weight)
+ *              and expands them in registers.  M > 16: caller-owned device
  *              memory of at least workspace_bytes >= N * K bytes, 16-byte
  *              aligned, not shared with a concurrent call; the weight is
  *              expanded there to int8 codes and the tiled kernel runs.  Too
@@ -271,7 +318,9 @@ convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed
 
 /* Gated pair with int4 weights, Y = fn(G) * U as in convrot_linear_gated;
  * fn must be CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH.  For M > 16 the
- * workspace holds both expanded weights: workspace_bytes >= 2 * N * K. */
+ * workspace holds both expanded weights: workspace_bytes >= 2 * N * K; for
+ * M <= 16 it is optional, as for convrot_linear (kind
+ * CONVROT_LINEAR_W4_GATED). */
 convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_packed_w4* w_gate,
                                        const float* b_gate, const convrot_packed_w4* w_up, const float* b_up,
                                        convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,

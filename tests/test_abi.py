@@ -38,6 +38,21 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_header():
+    """libconvrot_probe.so (bench.py's hardware probes) exports exactly what
+    include/convrot_probe.h declares, and rejects bad arguments on the host."""
+    from w8a8_int8_linear_amd import probe
+
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "convrot_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(convrot_[a-z0-9_]+)\s*\(", src)))
+    assert names == sorted(probe.EXPORTED)
+    plib = probe.load()
+    f = plib.convrot_probe_mfma_i8
+    assert f(None, 256, 10, A16, A16B, 0, None) == 1
+    assert f(A16, 0, 10, A16, A16B, 0, None) == 1
+    assert f(MIS, 256, 10, A16, A16B, 0, None) == 1
+
+
 def test_abi_version_matches_header(lib):
     src = open(HEADER).read()
     v = int(re.search(r"#define CONVROT_ABI_VERSION (\d+)", src).group(1))
@@ -120,11 +135,11 @@ def test_pack_zero_rows_is_a_no_op(lib):
     assert pack_status(lib, out=packed(rows=-1)) == _lib.ERR_INVALID_ARG
 
 
-def linear_status(lib, act=None, w=None, bias=None, Y=A16C, ydt=_lib.BF16, ldy=None):
+def linear_status(lib, act=None, w=None, bias=None, Y=A16C, ydt=_lib.BF16, ldy=None, ws=None, ws_bytes=0):
     act = act if act is not None else packed(rows=32)
     w = w if w is not None else packed(rows=64, q=0x40000, scale=0x50000)
     return lib.convrot_linear(ctypes.byref(act), ctypes.byref(w), bias, Y, ydt,
-                              ldy if ldy is not None else w.rows, None)
+                              ldy if ldy is not None else w.rows, ws, ws_bytes, None)
 
 
 def test_linear_mismatch(lib):
@@ -145,7 +160,7 @@ def test_linear_output_checks(lib):
     assert linear_status(lib, Y=A16C + 2, ydt=_lib.F32) == _lib.ERR_ALIGN
     assert linear_status(lib, ldy=32) == _lib.ERR_INVALID_ARG     # ldy < N
     assert linear_status(lib, bias=A16 + 2) == _lib.ERR_ALIGN
-    assert lib.convrot_linear(None, None, None, A16C, _lib.BF16, 64, None) == _lib.ERR_INVALID_ARG
+    assert lib.convrot_linear(None, None, None, A16C, _lib.BF16, 64, None, 0, None) == _lib.ERR_INVALID_ARG
 
 
 def test_linear_empty_is_a_no_op(lib):
@@ -162,7 +177,7 @@ def test_linear_k_overflow_guard(lib):
 def act_status(lib, fn=_lib.ACT_GELU_ERF, ydt=_lib.BF16, act=None, w=None):
     act = act if act is not None else packed(rows=32)
     w = w if w is not None else packed(rows=64, q=0x40000, scale=0x50000)
-    return lib.convrot_linear_act(ctypes.byref(act), ctypes.byref(w), None, fn, A16C, ydt, w.rows, None)
+    return lib.convrot_linear_act(ctypes.byref(act), ctypes.byref(w), None, fn, A16C, ydt, w.rows, None, 0, None)
 
 
 def gated_status(lib, fn=_lib.ACT_GELU_TANH, ydt=_lib.BF16, up=None, gate=None):
@@ -170,7 +185,7 @@ def gated_status(lib, fn=_lib.ACT_GELU_TANH, ydt=_lib.BF16, up=None, gate=None):
     g = gate if gate is not None else packed(rows=64, q=0x40000, scale=0x50000)
     u = up if up is not None else packed(rows=64, q=0x80000, scale=0x90000)
     return lib.convrot_linear_gated(ctypes.byref(act), ctypes.byref(g), None, ctypes.byref(u), None, fn, A16C, ydt,
-                                    g.rows, None)
+                                    g.rows, None, 0, None)
 
 
 def test_linear_act_checks(lib):
@@ -188,16 +203,62 @@ def test_linear_gated_checks(lib):
     assert gated_status(lib, up=packed(rows=64, G=64, q=0x80000)) == _lib.ERR_MISMATCH  # rotation differs
     assert gated_status(lib, gate=packed(rows=64, K=512, q=0x40000)) == _lib.ERR_MISMATCH
     assert lib.convrot_linear_gated(None, None, None, None, None, _lib.ACT_GELU_TANH, A16C, _lib.BF16, 64,
-                                    None) == _lib.ERR_INVALID_ARG
+                                    None, 0, None) == _lib.ERR_INVALID_ARG
 
 
 def test_linear_bf16_checks(lib):
-    f = lib.convrot_linear_bf16
-    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2690, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
-    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.I32, 16, None) == _lib.ERR_DTYPE
-    assert f(None, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
-    assert f(A16, 2684, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.ERR_INVALID_ARG
-    assert f(A16, 2688, A16B, 2688, None, 0, 16, 2688, A16C, _lib.BF16, 16, None) == _lib.OK
+    def f(*a):
+        return lib.convrot_linear_bf16(*a, None, 0, None)
+    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2690, A16C, _lib.BF16, 16) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.I32, 16) == _lib.ERR_DTYPE
+    assert f(None, 2688, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2684, A16B, 2688, None, 8, 16, 2688, A16C, _lib.BF16, 16) == _lib.ERR_INVALID_ARG
+    assert f(A16, 2688, A16B, 2688, None, 0, 16, 2688, A16C, _lib.BF16, 16) == _lib.OK
+
+
+def ws_bytes(lib, kind, M, N, K):
+    out = ctypes.c_int64(-1)
+    st = lib.convrot_linear_workspace_bytes(kind, M, N, K, ctypes.byref(out))
+    return st, out.value
+
+
+def test_linear_workspace_query(lib):
+    """Small M: the split-K partials (the down projection's 72 tiles split,
+    the gated pair's 432 tiles do not); large M: nothing, except the int4
+    kinds' expanded weight.  The device's CU count enters the size (no GPU
+    here: the library assumes 256)."""
+    st, down = ws_bytes(lib, _lib.LINEAR_PLAIN, 16, 1152, 6912)
+    assert st == _lib.OK and down > 0 and down % 1024 == 0
+    assert ws_bytes(lib, _lib.LINEAR_GATED, 16, 6912, 1152) == (_lib.OK, 0)
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 17, 1152, 6912) == (_lib.OK, 0)
+    assert ws_bytes(lib, _lib.LINEAR_W4, 17, 1152, 6912) == (_lib.OK, 1152 * 6912)
+    assert ws_bytes(lib, _lib.LINEAR_W4_GATED, 64, 6912, 1152) == (_lib.OK, 2 * 6912 * 1152)
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 0, 1152, 6912) == (_lib.OK, 0)
+    assert ws_bytes(lib, _lib.LINEAR_GATED, 16, 1152, 6912)[1] == 2 * down   # two weights' partials
+    assert ws_bytes(lib, _lib.LINEAR_BF16, 16, 1152, 6912)[1] > 0
+    assert ws_bytes(lib, 9, 16, 1152, 6912)[0] == _lib.ERR_INVALID_ARG
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 16, 1152, 6913)[0] == _lib.ERR_INVALID_ARG
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, -1, 1152, 6912)[0] == _lib.ERR_INVALID_ARG
+    assert lib.convrot_linear_workspace_bytes(_lib.LINEAR_PLAIN, 16, 1152, 6912, None) == _lib.ERR_INVALID_ARG
+
+
+def test_linear_rejects_a_short_workspace(lib):
+    """A non-NULL workspace smaller than the split needs is an error before
+    any launch (NULL would select the unsplit kernel)."""
+    K, N = 6912, 1152
+    need = ws_bytes(lib, _lib.LINEAR_PLAIN, 16, N, K)[1]
+    act = packed(rows=16, K=K)
+    w = packed(rows=N, K=K, q=0x40000, scale=0x50000)
+    assert linear_status(lib, act=act, w=w, ws=0x100000, ws_bytes=need - 1) == _lib.ERR_INVALID_ARG
+    assert b"workspace" in lib.convrot_last_error()
+    assert linear_status(lib, act=act, w=w, ws=0x100008, ws_bytes=need) == _lib.ERR_ALIGN
+    f = lib.convrot_linear_act
+    assert f(ctypes.byref(act), ctypes.byref(w), None, _lib.ACT_GELU_ERF, A16C, _lib.BF16, N, 0x100000, need - 1,
+             None) == _lib.ERR_INVALID_ARG
+    assert lib.convrot_linear_bf16(A16, K, A16B, K, None, 16, N, K, A16C, _lib.BF16, N, 0x100000, 16,
+                                   None) == _lib.ERR_INVALID_ARG
+    w4 = packed_w4(rows=N, K=K)
+    assert w4_status(lib, act=act, w=w4, ws=0x100000, ws_bytes=16) == _lib.ERR_INVALID_ARG
 
 
 def test_rotate_checks(lib):

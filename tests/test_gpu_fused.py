@@ -64,6 +64,10 @@ def test_linear_act(cuda, M, N, K, act):
     assert R.rel_fro(ybf, O.bf16_round(ref.astype(np.float32))) <= R.Y_RTOL
     # bf16 outputs are the RNE rounding of the kernel's own fp32 outputs
     assert np.array_equal(ybf, O.bf16_round(y32))
+    # with a workspace small M may split K: the same result bits
+    ws = cr.linear_workspace("plain", M, N, K, cuda)
+    if ws is not None:
+        assert np.array_equal(to_np(cr.linear_act(a, w, bd, act, out_dtype=torch.float32, workspace=ws)), y32)
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -82,6 +86,10 @@ def test_linear_gated(cuda, M, N, K, act):
     ybf = to_np(cr.linear_gated(a, wg, wu, bgd, bud, act, out_dtype=torch.bfloat16))
     assert R.rel_fro(ybf, O.bf16_round(ref.astype(np.float32))) <= R.Y_RTOL
     assert np.array_equal(ybf, O.bf16_round(y32))
+    ws = cr.linear_workspace("gated", M, N, K, cuda)
+    if ws is not None:
+        y_split = cr.linear_gated(a, wg, wu, bgd, bud, act, out_dtype=torch.float32, workspace=ws)
+        assert np.array_equal(to_np(y_split), y32)
 
 
 def test_gated_without_bias_and_strided_output(cuda):

@@ -3,7 +3,8 @@ as the same launches made eagerly.
 
 Steps captured with torch.cuda.graph: a decode step of a gated
 feed-forward layer (pack the activation, gate and up in one gated launch,
-pack the product, down projection), the same step with int4 weights (also
+pack the product, down projection split over K in a caller-owned
+workspace), the same step with int4 weights (also
 at a width where the weights are staged through LDS), a DiT-sized step
 (one pack shared by two linears, 256-row tiles with ragged edges), and a
 linear followed by a LoRA correction.  Each graph is replayed three
@@ -41,28 +42,30 @@ def _x(M, K, seed, dev):
 
 def _decode_step(x, ws, bufs, G):
     (wg, bg), (wu, bu), (wd, bd) = ws
-    pa, h, pa2, y = bufs
+    pa, h, pa2, y, wsp = bufs
     cr.pack_act(x, G, out=pa)
     cr.linear_gated(pa, wg, wu, bg, bu, cr.GELU_TANH, out=h)
     cr.pack_act(h, G, out=pa2)
-    cr.linear(pa2, wd, bd, out=y)
+    cr.linear(pa2, wd, bd, out=y, workspace=wsp)   # down projection: K split in the caller's workspace
 
 
 def _decode_step_w4(x, ws, bufs, G):
     (wg, bg), (wu, bu), (wd, bd) = ws
-    pa, h, pa2, y = bufs
+    pa, h, pa2, y, wsp = bufs
     cr.pack_act(x, G, out=pa)
     cr.linear_w4_gated(pa, wg, wu, bg, bu, cr.GELU_TANH, out=h)
     cr.pack_act(h, G, out=pa2)
-    cr.linear_w4(pa2, wd, bd, out=y)
+    cr.linear_w4(pa2, wd, bd, out=y, workspace=wsp)
 
 
-def _decode_bufs(M, K, F, G, dev):
+def _decode_bufs(M, K, F, G, dev, kind="plain"):
     def packed(rows, k):
         return cr.Packed(torch.empty((rows, k), dtype=torch.int8, device=dev),
                          torch.empty(rows, dtype=torch.float32, device=dev), G)
+    wsp = cr.linear_workspace(kind, M, K, F, dev)
+    assert wsp is not None, "the decode down projection splits K"
     return (packed(M, K), torch.empty((M, F), dtype=torch.bfloat16, device=dev), packed(M, F),
-            torch.empty((M, K), dtype=torch.bfloat16, device=dev))
+            torch.empty((M, K), dtype=torch.bfloat16, device=dev), wsp)
 
 
 def _dit_step(x, ws, bufs, G):
@@ -81,8 +84,10 @@ def _dit_bufs(M, K, N1, N2, G, dev):
 
 
 def _outputs(bufs):
-    return [b.q if isinstance(b, cr.Packed) else b for b in bufs] + \
-           [b.scale for b in bufs if isinstance(b, cr.Packed)]
+    """Every output buffer of a step (workspaces are scratch, not outputs)."""
+    outs = [b for b in bufs if b is not None and (isinstance(b, cr.Packed) or b.dtype != torch.uint8)]
+    return [b.q if isinstance(b, cr.Packed) else b for b in outs] + \
+           [b.scale for b in outs if isinstance(b, cr.Packed)]
 
 
 def _replay_matches_eager(step, make_bufs, ws, M, K, G, seed, dev):
@@ -121,7 +126,8 @@ def test_dit_step_graph(cuda):
 def test_decode_step_w4_graph(cuda, M, K, F):
     G = 64
     ws = _weights([(F, K), (F, K), (K, F)], G, 9, cuda, bits=4)
-    _replay_matches_eager(_decode_step_w4, lambda: _decode_bufs(M, K, F, G, cuda), ws, M, K, G, 300 + M, cuda)
+    _replay_matches_eager(_decode_step_w4, lambda: _decode_bufs(M, K, F, G, cuda, "w4"), ws, M, K, G, 300 + M,
+                          cuda)
 
 
 def test_lora_step_graph(cuda):

@@ -35,10 +35,15 @@ def test_accumulator_bit_exact(cuda, M, N, K, G):
     qw = random_codes((N, K), seed=N + 5 * K)
     sx = np.ones(M, np.float32)
     sw = np.ones(N, np.float32)
-    A_gpu = to_np(cr.linear(_packed_from_codes(qx, sx, G, cuda), _packed_from_codes(qw, sw, G, cuda),
-                            out_dtype=torch.int32))
+    a, w = _packed_from_codes(qx, sx, G, cuda), _packed_from_codes(qw, sw, G, cuda)
+    A_gpu = to_np(cr.linear(a, w, out_dtype=torch.int32))
     A_ref = O.int_gemm(qx, qw)
     assert np.array_equal(A_gpu.astype(np.int64), A_ref)
+    # small M with a caller workspace: K split across workgroups, exact int32 partials
+    ws = cr.linear_workspace("plain", M, N, K, cuda)
+    if ws is not None:
+        A_split = to_np(cr.linear(a, w, out_dtype=torch.int32, workspace=ws))
+        assert np.array_equal(A_split.astype(np.int64), A_ref)
 
 
 def test_accumulator_extremes(cuda):
@@ -102,8 +107,25 @@ def test_small_m_kernel_matches_tiled_kernel(cuda):
     w = _packed_from_codes(qw, sw, 256, cuda)
     full = cr.linear(_packed_from_codes(qx, s48, 256, cuda), w, out_dtype=torch.int32)
     for m in (1, 5, 16):
-        small = cr.linear(_packed_from_codes(qx[:m], s48[:m], 256, cuda), w, out_dtype=torch.int32)
+        a = _packed_from_codes(qx[:m], s48[:m], 256, cuda)
+        small = cr.linear(a, w, out_dtype=torch.int32)
         assert torch.equal(small, full[:m])
+        split = cr.linear(a, w, out_dtype=torch.int32, workspace=cr.linear_workspace("plain", m, N, K, cuda))
+        assert torch.equal(split, full[:m])
+
+
+def test_small_m_workspace_is_reusable(cuda):
+    """One workspace serves consecutive calls of different shapes (each call
+    rewrites what it uses), and a larger one than needed is fine."""
+    K = 6912
+    big = torch.empty(cr.linear_workspace_bytes("plain", 16, 1152, K) * 2, dtype=torch.uint8, device=cuda)
+    for m, n in ((16, 1152), (3, 520), (16, 64)):
+        qx, qw = random_codes((m, K), 30 + m), random_codes((n, K), 31 + n)
+        a = _packed_from_codes(qx, np.ones(m, np.float32), 256, cuda)
+        w = _packed_from_codes(qw, np.ones(n, np.float32), 256, cuda)
+        assert cr.linear_workspace_bytes("plain", m, n, K) <= big.numel()
+        A = to_np(cr.linear(a, w, out_dtype=torch.int32, workspace=big))
+        assert np.array_equal(A.astype(np.int64), O.int_gemm(qx, qw))
 
 
 def test_row_split_bit_exact(cuda):

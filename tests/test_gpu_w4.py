@@ -202,6 +202,8 @@ def test_small_m_int8_staged_weights(cuda, M, N, K):
     wg = cr.Packed(to_dev(qg, torch.int8), to_dev(sw, torch.float32), 16)
     wu = cr.Packed(to_dev(qu, torch.int8), to_dev(sw, torch.float32), 16)
     assert np.array_equal(to_np(cr.linear(a, wg, out_dtype=torch.int32)), O.int_gemm(qx, qg))
+    ws = cr.linear_workspace("plain", M, N, K, cuda)   # split K where the shape allows
+    assert np.array_equal(to_np(cr.linear(a, wg, out_dtype=torch.int32, workspace=ws)), O.int_gemm(qx, qg))
     g64 = O.epilogue64(O.int_gemm(qx, qg), sx, sw)
     u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
     y = to_np(cr.linear_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))
@@ -219,6 +221,8 @@ def test_small_m_int4_staged_weights(cuda, M, N, K):
     a = cr.Packed(to_dev(qx, torch.int8), to_dev(sx, torch.float32), 16)
     wg, wu = _w4(qg, sw, 16), _w4(qu, sw, 16)
     assert np.array_equal(to_np(cr.linear_w4(a, wg, out_dtype=torch.int32)), O.int_gemm(qx, qg))
+    ws = cr.linear_workspace("w4", M, N, K, cuda)
+    assert np.array_equal(to_np(cr.linear_w4(a, wg, out_dtype=torch.int32, workspace=ws)), O.int_gemm(qx, qg))
     g64 = O.epilogue64(O.int_gemm(qx, qg), sx, sw)
     u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
     y = to_np(cr.linear_w4_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))

@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -24,11 +24,14 @@ ROT_REGULAR, ROT_RANDOMIZED = 0, 1
 ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
 # convrot_smooth_norm
 SMOOTH_L2, SMOOTH_MAX = 0, 1
+# convrot_linear_kind (workspace queries)
+LINEAR_PLAIN, LINEAR_GATED, LINEAR_BF16, LINEAR_W4, LINEAR_W4_GATED = range(5)
 
 EXPORTED = (
     "convrot_pack_act",
     "convrot_pack_weight",
     "convrot_linear",
+    "convrot_linear_workspace_bytes",
     "convrot_linear_act",
     "convrot_linear_gated",
     "convrot_linear_bf16",
@@ -89,13 +92,16 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_pack_act.restype = c_int
     lib.convrot_pack_weight.argtypes = [vp, c_int, c_i64, P, vp]
     lib.convrot_pack_weight.restype = c_int
-    lib.convrot_linear.argtypes = [P, P, vp, vp, c_int, c_i64, vp]
+    lib.convrot_linear.argtypes = [P, P, vp, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear.restype = c_int
-    lib.convrot_linear_act.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_workspace_bytes.argtypes = [c_int, c_i64, c_i64, c_i64, ctypes.POINTER(c_i64)]
+    lib.convrot_linear_workspace_bytes.restype = c_int
+    lib.convrot_linear_act.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear_act.restype = c_int
-    lib.convrot_linear_gated.argtypes = [P, P, vp, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_gated.argtypes = [P, P, vp, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear_gated.restype = c_int
-    lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp]
+    lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp, c_i64,
+                                        vp]
     lib.convrot_linear_bf16.restype = c_int
     lib.convrot_rotate.argtypes = [vp, c_int, c_i64, c_i64, c_i64, Rot, vp, c_i64, vp]
     lib.convrot_rotate.restype = c_int

@@ -2,7 +2,9 @@
 
 Every function marshals torch CUDA tensors (device memory) and the current
 torch stream into a call of libconvrot.so; all arithmetic happens in the HIP
-kernels.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
+kernels.  Shapes, dtypes, strides and devices of caller-supplied outputs are
+checked here before any call, since the library takes sizes from the
+operands.  Names follow the C entry points: ``pack_act``, ``pack_weight``,
 ``linear``, ``linear_act``, ``linear_gated``, ``linear_bf16``, ``rotate``,
 for int4 weights (W4A8) ``pack_weight_w4``, ``linear_w4``,
 ``linear_w4_gated``, ``unpack_w4``, the offline ``smooth_ffn`` and the
@@ -50,8 +52,17 @@ class Packed:
         return self.q.shape[1]
 
     def descriptor(self) -> _lib.Packed:
-        return _lib.Packed(self.q.data_ptr(), self.scale.data_ptr(), self.q.shape[0], self.q.shape[1],
-                           _ld(self.q), _rot(self.group, self.kind, self.signs))
+        q, s = self.q, self.scale
+        if q.dtype != torch.int8 or q.dim() != 2:
+            raise ValueError("packed codes must be a 2-D int8 tensor")
+        if q.shape[1] > 1 and q.stride(1) != 1:
+            raise ValueError("packed codes must have unit stride along K")
+        if s.dtype != torch.float32 or s.dim() != 1 or s.numel() != q.shape[0] or not s.is_contiguous():
+            raise ValueError("packed scales must be a contiguous float32 vector with one entry per row")
+        if not q.is_cuda or s.device != q.device:
+            raise ValueError("packed codes and scales must be device tensors on one device")
+        return _lib.Packed(q.data_ptr(), s.data_ptr(), q.shape[0], q.shape[1], _ld(q),
+                           _rot(self.group, self.kind, self.signs))
 
 
 def _rot(group: int, kind: str, signs: torch.Tensor | None) -> _lib.Rot:
@@ -73,6 +84,77 @@ def _need_cuda(t: torch.Tensor, name: str) -> None:
 
 def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _check_out(out: torch.Tensor, M: int, N: int, dtypes, device: torch.device) -> None:
+    """A caller's output must be exactly [M, N] with unit column stride on
+    the operands' device: the library takes M and N from the operands and
+    only the row pitch from ``out``, so anything smaller would be written
+    past its end."""
+    if out.dtype not in dtypes:
+        raise ValueError(f"output dtype must be one of {[str(d) for d in dtypes]}, got {out.dtype}")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"output must have shape [{M}, {N}], got {list(out.shape)}")
+    if N > 1 and out.stride(1) != 1:
+        raise ValueError("output must have unit stride along its columns")
+    if M > 1 and out.stride(0) < N:
+        raise ValueError("output rows overlap (row stride below N)")
+    if out.device != device:
+        raise ValueError(f"output is on {out.device}, the operands on {device}")
+
+
+def _check_bias(bias: torch.Tensor | None, N: int, device: torch.device, name: str = "bias") -> None:
+    if bias is None:
+        return
+    if bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 vector of length N")
+    if bias.device != device:
+        raise ValueError(f"{name} is on {bias.device}, the operands on {device}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return t.data_ptr() if t is not None else None
+
+
+# ---------------------------------------------------------------------------
+# Workspaces of the linear entry points
+# ---------------------------------------------------------------------------
+
+PLAIN, GATED, BF16, W4, W4_GATED = "plain", "gated", "bf16", "w4", "w4_gated"
+_LINEAR_KIND = {PLAIN: _lib.LINEAR_PLAIN, GATED: _lib.LINEAR_GATED, BF16: _lib.LINEAR_BF16, W4: _lib.LINEAR_W4,
+                W4_GATED: _lib.LINEAR_W4_GATED}
+
+
+def linear_workspace_bytes(kind: str, M: int, N: int, K: int) -> int:
+    """Bytes of workspace a linear call of ``kind`` ("plain" for linear and
+    linear_act, "gated", "bf16", "w4", "w4_gated") uses for X [M, K] and N
+    outputs on the current device (convrot_linear_workspace_bytes).  With
+    M <= 16 it is the optional split-K partial-sum buffer (0 when the shape
+    does not split); with M > 16 only the int4 kinds need one."""
+    if kind not in _LINEAR_KIND:
+        raise ValueError(f"kind must be one of {sorted(_LINEAR_KIND)}")
+    lib = _lib.load()
+    out = ctypes.c_int64(0)
+    _lib.check(lib.convrot_linear_workspace_bytes(_LINEAR_KIND[kind], M, N, K, ctypes.byref(out)))
+    return out.value
+
+
+def linear_workspace(kind: str, M: int, N: int, K: int, device: torch.device) -> torch.Tensor | None:
+    """A device buffer of ``linear_workspace_bytes(kind, M, N, K)`` bytes,
+    or None when that is 0 (a caller-side convenience: the buffer is an
+    ordinary torch allocation owned by the caller)."""
+    with torch.cuda.device(device):
+        n = linear_workspace_bytes(kind, M, N, K)
+    return torch.empty((n,), dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(workspace: torch.Tensor | None, device: torch.device):
+    """(pointer, bytes) of an optional workspace tensor."""
+    if workspace is None:
+        return None, 0
+    if not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError("workspace must be a contiguous tensor on the operands' device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _check_signs(signs, K, kind):
@@ -112,30 +194,34 @@ def pack_weight(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: t
 
 
 def linear(act: Packed, w: Packed, bias: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
-           out: torch.Tensor | None = None) -> torch.Tensor:
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = A * s_x * s_w + b from a packed activation and a packed weight
-    (convrot_linear).  ``out_dtype=torch.int32`` returns the raw accumulator."""
+    (convrot_linear).  ``out_dtype=torch.int32`` returns the raw accumulator.
+    ``workspace`` (see ``linear_workspace``) lets M <= 16 split K across
+    workgroups; without one the unsplit kernel runs (same result bits)."""
     M, N = act.rows, w.rows
+    dev = act.q.device
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=act.q.device)
-    if out.dtype not in _DT:
-        raise ValueError("output must be float32, bfloat16 or int32")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous float32 vector of length N")
+        if out_dtype not in _DT:
+            raise ValueError("output must be float32, bfloat16 or int32")
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _check_out(out, M, N, tuple(_DT), dev)
+    _check_bias(bias, N, dev)
     a, b = act.descriptor(), w.descriptor()
+    wp, wn = _ws(workspace, dev)
     lib = _lib.load()
-    _lib.check(lib.convrot_linear(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
-                                  out.data_ptr(), _DT[out.dtype], _ld(out), _stream(out.device)))
+    _lib.check(lib.convrot_linear(ctypes.byref(a), ctypes.byref(b), _ptr(bias), out.data_ptr(), _DT[out.dtype],
+                                  _ld(out), wp, wn, _stream(dev)))
     return out
 
 
 def _out_and_bias(M, N, device, out, out_dtype, bias):
     if out is None:
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("output must be float32 or bfloat16")
         out = torch.empty((M, N), dtype=out_dtype, device=device)
-    if out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("output must be float32 or bfloat16")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous float32 vector of length N")
+    _check_out(out, M, N, (torch.float32, torch.bfloat16), device)
+    _check_bias(bias, N, device)
     return out
 
 
@@ -146,53 +232,59 @@ def _act_code(act: str) -> int:
 
 
 def linear_act(act_in: Packed, w: Packed, bias: torch.Tensor | None = None, act: str = GELU_ERF,
-               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = act(A * s_x * s_w + b) with the activation in the epilogue
-    (convrot_linear_act)."""
-    out = _out_and_bias(act_in.rows, w.rows, act_in.q.device, out, out_dtype, bias)
+    (convrot_linear_act); ``workspace`` as in ``linear``."""
+    dev = act_in.q.device
+    out = _out_and_bias(act_in.rows, w.rows, dev, out, out_dtype, bias)
     a, b = act_in.descriptor(), w.descriptor()
+    wp, wn = _ws(workspace, dev)
     lib = _lib.load()
-    _lib.check(lib.convrot_linear_act(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
-                                      _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out), _stream(out.device)))
+    _lib.check(lib.convrot_linear_act(ctypes.byref(a), ctypes.byref(b), _ptr(bias), _act_code(act), out.data_ptr(),
+                                      _DT[out.dtype], _ld(out), wp, wn, _stream(dev)))
     return out
 
 
 def linear_gated(act_in: Packed, w_gate: Packed, w_up: Packed, b_gate: torch.Tensor | None = None,
                  b_up: torch.Tensor | None = None, act: str = GELU_TANH, out_dtype: torch.dtype = torch.bfloat16,
-                 out: torch.Tensor | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = act(gate) * up for two weights sharing one packed activation, in
-    one launch (convrot_linear_gated)."""
-    out = _out_and_bias(act_in.rows, w_gate.rows, act_in.q.device, out, out_dtype, b_gate)
-    if b_up is not None and (b_up.dtype != torch.float32 or b_up.numel() != w_up.rows or not b_up.is_contiguous()):
-        raise ValueError("b_up must be a contiguous float32 vector of length N")
+    one launch (convrot_linear_gated); ``workspace`` as in ``linear`` (kind
+    "gated")."""
+    dev = act_in.q.device
+    out = _out_and_bias(act_in.rows, w_gate.rows, dev, out, out_dtype, b_gate)
+    _check_bias(b_up, w_up.rows, dev, "b_up")
     a, g, u = act_in.descriptor(), w_gate.descriptor(), w_up.descriptor()
+    wp, wn = _ws(workspace, dev)
     lib = _lib.load()
     _lib.check(lib.convrot_linear_gated(
-        ctypes.byref(a), ctypes.byref(g), b_gate.data_ptr() if b_gate is not None else None, ctypes.byref(u),
-        b_up.data_ptr() if b_up is not None else None, _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out),
-        _stream(out.device)))
+        ctypes.byref(a), ctypes.byref(g), _ptr(b_gate), ctypes.byref(u), _ptr(b_up), _act_code(act),
+        out.data_ptr(), _DT[out.dtype], _ld(out), wp, wn, _stream(dev)))
     return out
 
 
 def linear_bf16(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
-                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Unquantised bf16 linear Y = X W^T + b for routed layers (convrot_linear_bf16)."""
-    _need_cuda(x, "x")
-    _need_cuda(w, "w")
+                out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Unquantised bf16 linear Y = X W^T + b for routed layers
+    (convrot_linear_bf16); ``workspace`` as in ``linear`` (kind "bf16")."""
+    if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise ValueError("x and w must be bfloat16")
     M, K = x.shape
     N = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("inner dimensions differ")
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous float32 vector of length N")
+    dev = x.device
+    out = _out_and_bias(M, N, dev, out, out_dtype, bias)
+    _need_cuda(x, "x")
+    _need_cuda(w, "w")
+    if w.device != dev:
+        raise ValueError("x and w must be on one device")
+    wp, wn = _ws(workspace, dev)
     lib = _lib.load()
-    _lib.check(lib.convrot_linear_bf16(x.data_ptr(), _ld(x), w.data_ptr(), _ld(w),
-                                       bias.data_ptr() if bias is not None else None, M, N, K,
-                                       out.data_ptr(), _DT[out.dtype], _ld(out), _stream(x.device)))
+    _lib.check(lib.convrot_linear_bf16(x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), _ptr(bias), M, N, K,
+                                       out.data_ptr(), _DT[out.dtype], _ld(out), wp, wn, _stream(dev)))
     return out
 
 
@@ -230,8 +322,15 @@ class PackedW4:
         return self.q.shape[0]
 
     def descriptor(self) -> _lib.PackedW4:
-        if self.q.dtype != torch.uint8 or self.q.shape[1] * 2 != self.K:
+        q, s = self.q, self.scale
+        if q.dtype != torch.uint8 or q.dim() != 2 or q.shape[1] * 2 != self.K:
             raise ValueError("q must be uint8 [rows, K / 2]")
+        if q.shape[1] > 1 and q.stride(1) != 1:
+            raise ValueError("q must have unit stride along its bytes")
+        if s.dtype != torch.float32 or s.dim() != 1 or s.numel() != q.shape[0] or not s.is_contiguous():
+            raise ValueError("scales must be a contiguous float32 vector with one entry per row")
+        if not q.is_cuda or s.device != q.device:
+            raise ValueError("q and scales must be device tensors on one device")
         return _lib.PackedW4(self.q.data_ptr(), self.scale.data_ptr(), self.q.shape[0], self.K, _ld(self.q),
                              _rot(self.group, self.kind, self.signs))
 
@@ -253,15 +352,12 @@ def pack_weight_w4(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs
     return out
 
 
-def _w4_workspace(M: int, N: int, K: int, sets: int, device, workspace):
-    if M <= 16:
+def _w4_workspace(kind: str, M: int, N: int, K: int, device, workspace):
+    """The workspace of an int4 call: required above 16 rows (allocated here
+    when not given), optional at or below."""
+    if M <= 16 or workspace is not None:
         return workspace
-    need = sets * N * K
-    if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.int8, device=device)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace needs {need} bytes")
-    return workspace
+    return linear_workspace(kind, M, N, K, device)
 
 
 def linear_w4(act_in: Packed, w: PackedW4, bias: torch.Tensor | None = None, act: str | None = None,
@@ -269,21 +365,23 @@ def linear_w4(act_in: Packed, w: PackedW4, bias: torch.Tensor | None = None, act
               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A8 linear Y = act(A * s_x * s_w + b), act None for the plain linear
     (convrot_linear_w4).  For more than 16 rows the expanded int8 weight goes
-    to ``workspace`` (allocated here when not given)."""
+    to ``workspace`` (allocated here when not given); at or below 16 rows a
+    workspace is optional and enables the K split, as in ``linear``."""
     M, N = act_in.rows, w.rows
+    dev = act_in.q.device
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=act_in.q.device)
-    if out.dtype not in _DT or (act is not None and out.dtype == torch.int32):
-        raise ValueError("output must be float32 or bfloat16 (or int32 without an activation)")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous float32 vector of length N")
-    ws = _w4_workspace(M, N, w.K, 1, out.device, workspace)
+        if out_dtype not in _DT:
+            raise ValueError("output must be float32, bfloat16 or int32")
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _check_out(out, M, N, tuple(_DT) if act is None else (torch.float32, torch.bfloat16), dev)
+    _check_bias(bias, N, dev)
+    ws = _w4_workspace(W4, M, N, w.K, dev, workspace)
     a, b = act_in.descriptor(), w.descriptor()
+    wp, wn = _ws(ws, dev)
     lib = _lib.load()
-    _lib.check(lib.convrot_linear_w4(ctypes.byref(a), ctypes.byref(b), bias.data_ptr() if bias is not None else None,
+    _lib.check(lib.convrot_linear_w4(ctypes.byref(a), ctypes.byref(b), _ptr(bias),
                                      _lib.ACT_NONE if act is None else _act_code(act), out.data_ptr(), _DT[out.dtype],
-                                     _ld(out), ws.data_ptr() if ws is not None else None,
-                                     ws.numel() * ws.element_size() if ws is not None else 0, _stream(out.device)))
+                                     _ld(out), wp, wn, _stream(dev)))
     return out
 
 
@@ -291,18 +389,17 @@ def linear_w4_gated(act_in: Packed, w_gate: PackedW4, w_up: PackedW4, b_gate: to
                     b_up: torch.Tensor | None = None, act: str = GELU_TANH, out_dtype: torch.dtype = torch.bfloat16,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = act(gate) * up with int4 weights sharing one packed activation
-    (convrot_linear_w4_gated)."""
-    out = _out_and_bias(act_in.rows, w_gate.rows, act_in.q.device, out, out_dtype, b_gate)
-    if b_up is not None and (b_up.dtype != torch.float32 or b_up.numel() != w_up.rows or not b_up.is_contiguous()):
-        raise ValueError("b_up must be a contiguous float32 vector of length N")
-    ws = _w4_workspace(act_in.rows, w_gate.rows, w_gate.K, 2, out.device, workspace)
+    (convrot_linear_w4_gated); ``workspace`` as in ``linear_w4``."""
+    dev = act_in.q.device
+    out = _out_and_bias(act_in.rows, w_gate.rows, dev, out, out_dtype, b_gate)
+    _check_bias(b_up, w_up.rows, dev, "b_up")
+    ws = _w4_workspace(W4_GATED, act_in.rows, w_gate.rows, w_gate.K, dev, workspace)
     a, g, u = act_in.descriptor(), w_gate.descriptor(), w_up.descriptor()
+    wp, wn = _ws(ws, dev)
     lib = _lib.load()
     _lib.check(lib.convrot_linear_w4_gated(
-        ctypes.byref(a), ctypes.byref(g), b_gate.data_ptr() if b_gate is not None else None, ctypes.byref(u),
-        b_up.data_ptr() if b_up is not None else None, _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out),
-        ws.data_ptr() if ws is not None else None, ws.numel() * ws.element_size() if ws is not None else 0,
-        _stream(out.device)))
+        ctypes.byref(a), ctypes.byref(g), _ptr(b_gate), ctypes.byref(u), _ptr(b_up), _act_code(act),
+        out.data_ptr(), _DT[out.dtype], _ld(out), wp, wn, _stream(dev)))
     return out
 
 

@@ -1,7 +1,9 @@
-"""Build the HIP library libconvrot.so in-tree for gfx950 with hipcc.
+"""Build the HIP libraries in-tree for gfx950 with hipcc: libconvrot.so (the
+linear layer, include/convrot.h) and libconvrot_probe.so (hardware
+measurement probes used by bench.py, include/convrot_probe.h).
 
 Usage: python -m w8a8_int8_linear_amd.build   (or call build()).
-Objects go to <repo>/_build/, the shared library next to this file.
+Objects go to <repo>/_build/, the shared libraries next to this file.
 """
 
 from __future__ import annotations
@@ -21,7 +23,11 @@ LIB_NAME = "libconvrot.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip", "w4.hip", "smooth.hip", "lora.hip"]
+SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip",
+           "w4.hip", "smooth.hip", "lora.hip"]
+PROBE_NAME = "libconvrot_probe.so"
+PROBE_PATH = os.path.join(PKG_DIR, PROBE_NAME)
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -48,13 +54,8 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libconvrot.so."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, os.cpu_count() or 2))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -64,10 +65,22 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
     missing = [l for l in r.stdout.splitlines() if "convrot" in l]
     if r.returncode != 0 or missing:
-        raise RuntimeError("libconvrot.so has undefined symbols:\n" + "\n".join(missing[:20]))
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"{os.path.basename(path)} has undefined symbols:\n" + "\n".join(missing[:20]))
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libconvrot.so and
+    libconvrot_probe.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, os.cpu_count() or 2))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_PATH}")
     return LIB_PATH
 
 

@@ -205,6 +205,24 @@ convrot_status check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
   return CONVROT_OK;
 }
 
+// Optional split-K workspace of a small-M call: NULL selects the unsplit
+// kernel; a non-NULL one must hold the split's partial sums.
+convrot_status check_split_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
+  if (ws == nullptr) return CONVROT_OK;
+  if (ws_bytes < need)
+    return fail(CONVROT_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld this call splits K into",
+                static_cast<long long>(ws_bytes), static_cast<long long>(need));
+  if (!aligned16(ws)) return fail(CONVROT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return CONVROT_OK;
+}
+
+// Workspace a small-M (M <= 16) call of `kind` splits K into.
+int64_t small_m_workspace(convrot_linear_kind kind, int64_t N, int64_t K) {
+  const bool gated = kind == CONVROT_LINEAR_GATED || kind == CONVROT_LINEAR_W4_GATED;
+  const bool w4 = kind == CONVROT_LINEAR_W4 || kind == CONVROT_LINEAR_W4_GATED;
+  return convrot::gemv_workspace_bytes(N, K, kind == CONVROT_LINEAR_BF16, w4, gated);
+}
+
 convrot_status check_act(convrot_act fn) {
   if (fn != CONVROT_ACT_GELU_ERF && fn != CONVROT_ACT_GELU_TANH)
     return fail(CONVROT_ERR_INVALID_ARG, "activation must be CONVROT_ACT_GELU_ERF or CONVROT_ACT_GELU_TANH");
@@ -226,8 +244,9 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
 }
 
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
-                              convrot_dtype ydt, int64_t ldy, void* stream) {
-  const convrot_status st = check_linear("convrot_linear", act, w, bias, Y, ydt, ldy, true);
+                              convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  convrot_status st = check_linear("convrot_linear", act, w, bias, Y, ydt, ldy, true);
   if (st != CONVROT_OK) return st;
   const int64_t M = act->rows, N = w->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
@@ -235,28 +254,55 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (M <= convrot::kGemvMaxRows) {
-    e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, N, K));
+    if (st != CONVROT_OK) return st;
+    e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy,
+                                workspace, s);
   } else {
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
   return from_hip(e, "convrot_linear");
 }
 
+convrot_status convrot_linear_workspace_bytes(convrot_linear_kind kind, int64_t M, int64_t N, int64_t K,
+                                              int64_t* bytes) {
+  const char* what = "convrot_linear_workspace_bytes";
+  if (bytes == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: bytes is NULL", what);
+  if (kind < CONVROT_LINEAR_PLAIN || kind > CONVROT_LINEAR_W4_GATED)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: unknown linear kind %d", what, static_cast<int>(kind));
+  const convrot_status st = check_k(K, kind == CONVROT_LINEAR_BF16 ? int64_t{1} << 30 : kMaxK);
+  if (st != CONVROT_OK) return st;
+  if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "%s: bad M or N", what);
+  if (M == 0 || N == 0) {
+    *bytes = 0;
+  } else if (M <= convrot::kGemvMaxRows) {
+    *bytes = small_m_workspace(kind, N, K);
+  } else {
+    *bytes = kind == CONVROT_LINEAR_W4 ? N * K : kind == CONVROT_LINEAR_W4_GATED ? 2 * N * K : 0;
+  }
+  return ok();
+}
+
 convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packed* w, const float* bias,
-                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* stream) {
+                                  convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
   convrot_status st = check_act(fn);
   if (st != CONVROT_OK) return st;
   st = check_linear("convrot_linear_act", act, w, bias, Y, ydt, ldy, false);
   if (st != CONVROT_OK) return st;
   const int64_t M = act->rows, N = w->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
+  if (M <= convrot::kGemvMaxRows) {
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, N, K));
+    if (st != CONVROT_OK) return st;
+  }
   const auto out = static_cast<convrot::Elt>(ydt);
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
-                                        out, ldy, s)
+                                        out, ldy, workspace, s)
           : convrot::launch_gemm_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
                                         out, ldy, s);
   return from_hip(e, "convrot_linear_act");
@@ -264,7 +310,8 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
 
 convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_packed* w_gate, const float* b_gate,
                                     const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
-                                    convrot_dtype ydt, int64_t ldy, void* stream) {
+                                    convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
   convrot_status st = check_act(fn);
   if (st != CONVROT_OK) return st;
   st = check_linear("convrot_linear_gated", act, w_gate, b_gate, Y, ydt, ldy, false);
@@ -276,13 +323,18 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
                 static_cast<long long>(w_gate->rows), static_cast<long long>(w_up->rows));
   const int64_t M = act->rows, N = w_gate->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
+  if (M <= convrot::kGemvMaxRows) {
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_GATED, N, K));
+    if (st != CONVROT_OK) return st;
+  }
   const auto out = static_cast<convrot::Elt>(ydt);
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
-                                          w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s)
+                                          w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy,
+                                          workspace, s)
           : convrot::launch_gemm_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_gated");
@@ -290,7 +342,7 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
 
 convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw, const float* bias,
                                    int64_t M, int64_t N, int64_t K, void* Y, convrot_dtype ydt, int64_t ldy,
-                                   void* stream) {
+                                   void* workspace, int64_t workspace_bytes, void* stream) {
   convrot_status st = check_k(K, int64_t{1} << 30);
   if (st != CONVROT_OK) return st;
   if (N < 0 || N > kMaxRows) return fail(CONVROT_ERR_INVALID_ARG, "bad N");
@@ -308,10 +360,14 @@ convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, in
     return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of X or W exceeds %lld bytes",
                 static_cast<long long>(kMaxLdBytes));
   if (M == 0 || N == 0) return ok();
+  if (M <= convrot::kGemvMaxRows) {
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_BF16, N, K));
+    if (st != CONVROT_OK) return st;
+  }
   const auto out = static_cast<convrot::Elt>(ydt);
   const auto s = static_cast<hipStream_t>(stream);
   const hipError_t e = M <= convrot::kGemvMaxRows
-                           ? convrot::launch_gemv_bf16(X, ldx, W, ldw, bias, M, N, K, Y, out, ldy, s)
+                           ? convrot::launch_gemv_bf16(X, ldx, W, ldw, bias, M, N, K, Y, out, ldy, workspace, s)
                            : convrot::launch_gemm_bf16(X, ldx, W, ldw, bias, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_bf16");
 }
@@ -376,8 +432,10 @@ convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= convrot::kGemvMaxRows) {
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4, N, K));
+    if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
-                                            out, ldy, s),
+                                            out, ldy, workspace, s),
                     what);
   }
   st = check_workspace(workspace, workspace_bytes, N * K);
@@ -419,9 +477,11 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= convrot::kGemvMaxRows) {
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4_GATED, N, K));
+    if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate,
                                                   w_up->q, w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y,
-                                                  out, ldy, s),
+                                                  out, ldy, workspace, s),
                     what);
   }
   st = check_workspace(workspace, workspace_bytes, 2 * N * K);

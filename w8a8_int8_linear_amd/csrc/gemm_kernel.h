@@ -50,6 +50,7 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "device.h"
 #include "epilogue.h"
 #include "launchers.h"
 
@@ -742,19 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   }
 }
 
-inline int num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-        prop.multiProcessorCount > 0)
-      cus = prop.multiProcessorCount;
-    else
-      cus = 256;
-  }
-  return cus;
-}
+inline int num_cus() { return device_cus(); }
 
 // Output-tile width: the candidate minimising (rounds of one tile per CU) x
 // (work per tile), i.e. the fewest idle CU-slots in the last round; ties go
@@ -789,13 +778,9 @@ hipError_t launch_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t
                         int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
   auto kern = gemm_nt_kernel<I8, OUT, KTAIL, TN, ACT, GATED>;
   constexpr int kSmem = smem_bytes<TN>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), kSmem, lds_set);
+  if (e != hipSuccess) return e;
   constexpr int kBNo = GATED ? 16 * TN : 32 * TN;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + kBNo - 1) / kBNo);

@@ -398,13 +398,9 @@ hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int6
                            int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
   auto kern = gemm_pp_kernel<I8, OUT, TN, ACT>;
   constexpr int kSmem = pp_smem_bytes<TN>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), kSmem, lds_set);
+  if (e != hipSuccess) return e;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + 64 * TN - 1) / (64 * TN));
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };

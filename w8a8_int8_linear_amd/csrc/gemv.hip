@@ -34,14 +34,14 @@
 //    the same 16 features of both weights against one set of activation
 //    loads.
 //  * When there are fewer 16-feature tiles than CUs (a down projection has
-//    N = 1152, i.e. 72 tiles), K is also split across workgroups: each
-//    (tile, K range) workgroup stores its partial sums (exact int32 in int8
-//    mode) in a per-device workspace, and a second launch of one wave per
-//    tile adds them in K order and applies the epilogue.  The launch
-//    boundary makes the partials visible; inside one launch that would take
-//    device-scope fences, which on this multi-XCD GPU write back and
-//    invalidate a whole L2 each.  Same result bits as the unsplit kernel in
-//    int8 mode.
+//    N = 1152, i.e. 72 tiles) and the caller supplies a workspace, K is also
+//    split across workgroups: each (tile, K range) workgroup stores its
+//    partial sums (exact int32 in int8 mode) in that workspace, and a second
+//    launch of one wave per tile adds them in K order and applies the
+//    epilogue.  The launch boundary makes the partials visible; inside one
+//    launch that would take device-scope fences, which on this multi-XCD GPU
+//    write back and invalidate a whole L2 each.  Same result bits as the
+//    unsplit kernel in int8 mode.
 //  * int4 weights (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
 //    per-channel int8 safetensors", sections "Solution" and "The rotation":
 //    codes in [-7, 7], one scale per output row, adjacent pairs in a byte):
@@ -53,9 +53,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <mutex>
 #include <type_traits>
 
+#include "device.h"
 #include "epilogue.h"
 #include "launchers.h"
 #include "w4_codec.h"
@@ -447,43 +447,7 @@ __global__ __launch_bounds__(64) void gemv_combine_kernel(EpiArgs epi, int M, in
   tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, static_cast<int>(blockIdx.x) * 16, epi, M, N, C, ldc);
 }
 
-// Per-device split-K workspace for the partial sums, allocated on the first
-// call that wants it (outside stream capture).  Calls that run at the same
-// time on one device (different streams) must not both take the split path.
-constexpr size_t kWsBytes = 8 << 20;
-
-bool split_workspace(hipStream_t stream, uint8_t** ws) {
-  static std::mutex mu;
-  static uint8_t* bufs[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  std::lock_guard<std::mutex> lock(mu);
-  if (bufs[dev] == nullptr) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
-    void* p = nullptr;
-    if (hipMalloc(&p, kWsBytes) != hipSuccess) {
-      (void)hipGetLastError();
-      return false;
-    }
-    bufs[dev] = static_cast<uint8_t*>(p);
-  }
-  *ws = bufs[dev];
-  return true;
-}
-
-inline int gemv_num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-           prop.multiProcessorCount > 0)
-              ? prop.multiProcessorCount
-              : 256;
-  }
-  return cus;
-}
+inline int gemv_num_cus() { return device_cus(); }
 
 template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1, bool DMA = false>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
@@ -508,12 +472,37 @@ void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uin
 constexpr int kMaxUnits = 32;
 inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 8; }
 
+// How a small-M launch splits K across workgroups: `splits` K ranges of
+// `units` K units per 16-feature tile (splits == 1: no split) and the bytes
+// of partial sums that needs (kSets x 64 lanes x 16 bytes per tile and
+// range).  K is split only when there are fewer tiles than CUs: aim at two
+// workgroups per CU and keep at least 8 MFMA steps per range.
+struct SplitPlan {
+  int64_t splits;
+  int64_t units;
+  int64_t bytes;
+};
+
+SplitPlan split_plan(int64_t N, int64_t kbytes, int sets, bool w4) {
+  const int64_t unit = w4 ? 128 : kStepBytes;
+  const int64_t nunits = (kbytes + unit - 1) / unit;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t cus = gemv_num_cus();
+  const SplitPlan none{1, nunits, 0};
+  if (tiles >= cus) return none;
+  int64_t splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nunits * (unit / kStepBytes) / 8);
+  if (splits <= 1) return none;
+  const int64_t units = (nunits + splits - 1) / splits;
+  splits = (nunits + units - 1) / units;  // no empty range
+  if (splits <= 1) return none;
+  return SplitPlan{splits, units, tiles * splits * sets * 1024};
+}
+
 template <bool I8, int OUT, int ACT = 0, bool GATED = false, bool W4 = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
-                      int64_t N, int64_t kbytes, void* C, int64_t ldc, hipStream_t stream) {
+                      int64_t N, int64_t kbytes, void* C, int64_t ldc, void* ws, hipStream_t stream) {
   constexpr int kSets = GATED ? 2 : 1;
   constexpr int kUnit = W4 ? 128 : kStepBytes;
-  constexpr int kStepsPerUnit = kUnit / kStepBytes;
   // Weights go through LDS in whole lines when a wave streams enough units
   // for the staging to pay (a round is two units); int4 rows also need
   // K % 32 == 0 so that no 16-byte chunk straddles K.
@@ -522,23 +511,15 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   const bool stage_ok = !W4 || kbytes % 32 == 0;
   const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
+  const int64_t cus = gemv_num_cus();
   const auto* a = static_cast<const uint8_t*>(A);
   const auto* b = static_cast<const uint8_t*>(B);
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
 
-  // Split K when there are fewer tiles than CUs: aim at two workgroups per
-  // CU, keep at least 8 MFMA steps per split, stay inside the workspace.
-  int64_t splits = 1;
-  const int64_t cus = gemv_num_cus();
-  if (tiles < cus) {
-    splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nunits * kStepsPerUnit / 8);
-    const int64_t cap = static_cast<int64_t>(kWsBytes / (static_cast<size_t>(kSets) * 1024));
-    splits = std::min<int64_t>(splits, cap / tiles);
-  }
-  uint8_t* ws = nullptr;
-  if (splits > 1 && split_workspace(stream, &ws)) {
-    const int64_t units = (nunits + splits - 1) / splits;
-    splits = (nunits + units - 1) / units;  // no empty split
+  // The caller's workspace (validated to hold plan.bytes) enables the split.
+  const SplitPlan plan = split_plan(N, kbytes, kSets, W4);
+  if (plan.splits > 1 && ws != nullptr) {
+    const int64_t units = plan.units, splits = plan.splits;
     const int waves = waves_for(units);
     const int per = static_cast<int>((units + waves - 1) / waves);
     const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(units)};
@@ -584,86 +565,91 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
 
 }  // namespace
 
+int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gated) {
+  if (N <= 0 || K <= 0) return 0;
+  return split_plan(N, bf16 ? 2 * K : K, gated ? 2 : 1, w4).bytes;
+}
+
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, int64_t M, int64_t N, int64_t K, void* C, Elt out,
-                          int64_t ldc, hipStream_t stream) {
+                          int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   switch (out) {
-    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
   }
 }
 
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                               const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                              Elt out, int64_t ldc, hipStream_t stream) {
+                              Elt out, int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
-               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
-             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
+               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
+             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
 }
 
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const int8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, hipStream_t stream) {
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sbg, biasg, reinterpret_cast<const uint8_t*>(Bu), ldbu, sbu, biasu};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
-               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
-  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
-             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
+    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
+               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
+  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
+             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
 }
 
 hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                          Elt out, int64_t ldc, hipStream_t stream) {
+                          Elt out, int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   if (act == Act::None) {
     switch (out) {
-      case Elt::F32: return launch_out<true, 0, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-      case Elt::BF16: return launch_out<true, 1, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-      default: return launch_out<true, 2, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+      case Elt::F32: return launch_out<true, 0, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+      case Elt::BF16: return launch_out<true, 1, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+      default: return launch_out<true, 2, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
     }
   }
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
-               : launch_out<true, 1, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
-  return f32 ? launch_out<true, 0, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream)
-             : launch_out<true, 1, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, stream);
+    return f32 ? launch_out<true, 0, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
+               : launch_out<true, 1, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+  return f32 ? launch_out<true, 0, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
+             : launch_out<true, 1, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
 }
 
 hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, hipStream_t stream) {
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sbg, biasg, Bu, ldbu, sbu, biasu};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
-               : launch_out<true, 1, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
-  return f32 ? launch_out<true, 0, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream)
-             : launch_out<true, 1, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, stream);
+    return f32 ? launch_out<true, 0, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
+               : launch_out<true, 1, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
+  return f32 ? launch_out<true, 0, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
+             : launch_out<true, 1, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
 }
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,
-                            int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream) {
+                            int64_t N, int64_t K, void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{nullptr, nullptr, bias, nullptr, 0, nullptr, nullptr};
   // Row strides and K in bytes.
-  if (out == Elt::F32) return launch_out<false, 0>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, stream);
-  return launch_out<false, 1>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, stream);
+  if (out == Elt::F32) return launch_out<false, 0>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, ws, stream);
+  return launch_out<false, 1>(A, 2 * lda, B, 2 * ldb, epi, M, N, 2 * K, C, ldc, ws, stream);
 }
 
 }  // namespace convrot

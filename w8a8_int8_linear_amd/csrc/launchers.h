@@ -64,25 +64,31 @@ hipError_t launch_gemm_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, 
 
 // Weight-streaming kernels for small M (M <= kGemvMaxRows).  The int8 one
 // gives the same result bits as launch_gemm_i8; the bf16 one computes the
-// same as launch_gemm_bf16 up to fp32 summation order.
+// same as launch_gemm_bf16 up to fp32 summation order.  `ws` is NULL (no
+// split over K) or a 16-byte aligned buffer of at least
+// gemv_workspace_bytes(...) bytes for the split's partial sums.
 constexpr int64_t kGemvMaxRows = 16;
+// Partial-sum bytes a small-M launch over N outputs and K inputs splits
+// into on the current device (0: that shape does not split).  bf16: the
+// unquantised mode; w4: int4 weights; gated: two weights per launch.
+int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gated);
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                           const float* sa, const float* sb, const float* bias,
                           int64_t M, int64_t N, int64_t K,
-                          void* C, Elt out, int64_t ldc, hipStream_t stream);
+                          void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
                             const float* bias, int64_t M, int64_t N, int64_t K,
-                            void* C, Elt out, int64_t ldc, hipStream_t stream);
+                            void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                               const float* sa, const float* sb, const float* bias, Act act,
                               int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                              hipStream_t stream);
+                              void* ws, hipStream_t stream);
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg,
                                 const float* sbg, const float* biasg, const int8_t* Bu, int64_t ldbu,
                                 const float* sbu, const float* biasu, const float* sa, Act act,
                                 int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                                hipStream_t stream);
+                                void* ws, hipStream_t stream);
 
 // Data-free smoothing of an FFN's intermediate channels (offline): s [F]
 // and, where the outputs are non-null, the scaled fp32 weights
@@ -109,10 +115,10 @@ hipError_t launch_lora_up(const void* T, int64_t ldt, const void* B, int64_t ldb
 // None (then `out` may be I32) for the plain linear.
 hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                          Elt out, int64_t ldc, hipStream_t stream);
+                          Elt out, int64_t ldc, void* ws, hipStream_t stream);
 hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, hipStream_t stream);
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);
 
 }  // namespace convrot

@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "device.h"
 #include "launchers.h"
 
 namespace convrot {
@@ -232,10 +233,7 @@ int lora_down_blocks(int64_t M, int64_t K, int64_t r) {
   // launch costs more than the split saves (16 rows, K = 1152: 7.5 us
   // unsplit, 8.2 us split in two).
   if (M < 128 || K <= 0) return 1;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus();
   const int64_t rows = 16 * lora_row_tiles(r);
   const int64_t row_blocks = (M + rows - 1) / rows;
   const int64_t steps = (K + 31) / 32;

@@ -1,0 +1,79 @@
+// Hardware probes (libconvrot_probe.so; interface in convrot_probe.h): the
+// int8 matrix-core rate on random operands with no memory traffic in the
+// loop, and the shader clock under that load, read from the s_memtime
+// (shader clock) and s_memrealtime (constant 100 MHz) counters.  The loop
+// uses the MFMA form of the layer's GEMM (v_mfma_i32_16x16x64_i8) with two
+// wavefronts per SIMD, so it shows the rate the GEMM's main loop could reach
+// were it never waiting for data.
+#include <hip/hip_runtime.h>
+
+#include "convrot_probe.h"
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChains = CONVROT_PROBE_CHAINS;
+
+// Both counters, read in one asm block that also waits for them (they are
+// scalar memory reads).  Volatile asm keeps program order with the other
+// volatile asm below; `dep` orders the read after the value it names.
+__device__ __forceinline__ void read_counters(uint64_t& clk, uint64_t& real, int dep) {
+  asm volatile(
+      "s_memtime %0\n\t"
+      "s_memrealtime %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(clk), "=s"(real)
+      : "v"(dep));
+}
+
+__global__ __launch_bounds__(CONVROT_PROBE_THREADS, 1) void mfma_i8_probe(const i32x4* __restrict__ operands,
+                                                                            int iters, uint64_t* __restrict__ stamps,
+                                                                            int32_t* __restrict__ sink, int flag) {
+  const int tid = threadIdx.x;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * CONVROT_PROBE_THREADS + tid;
+  // two operand sets per lane: the row and column fragments of one MFMA each
+  const i32x4 a0_in = operands[4 * g], b0_in = operands[4 * g + 1];
+  const i32x4 a1_in = operands[4 * g + 2], b1_in = operands[4 * g + 3];
+  i32x4 acc[kChains];
+#pragma unroll
+  for (int j = 0; j < kChains; ++j) acc[j] = i32x4{0, 0, 0, 0};
+  uint64_t t0, r0, t1, r1;
+  read_counters(t0, r0, 0);
+  // the operands pass through volatile asm after the first read, so no MFMA
+  // can be placed before it
+  i32x4 a0 = a0_in, b0 = b0_in, a1 = a1_in, b1 = b1_in;
+  asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1));
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+      acc[j] = (j & 1) ? __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[j], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[j], 0, 0, 0);
+  }
+  // the counters are read after the last MFMA result is available
+  int32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  read_counters(t1, r1, s);
+  if (tid == 0) {
+    uint64_t* o = stamps + 4 * static_cast<int64_t>(blockIdx.x);
+    o[0] = t0;
+    o[1] = t1;
+    o[2] = r0;
+    o[3] = r1;
+  }
+  if (flag == 0x5eed) sink[g] = s;
+}
+
+}  // namespace
+
+extern "C" int convrot_probe_mfma_i8(const void* operands, int grid, int iters, uint64_t* stamps, int32_t* sink,
+                                     int flag, void* stream) {
+  if (operands == nullptr || stamps == nullptr || sink == nullptr || grid <= 0 || iters <= 0 ||
+      (reinterpret_cast<uintptr_t>(operands) & 15u) != 0 || (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
+    return 1;
+  hipLaunchKernelGGL(mfma_i8_probe, dim3(static_cast<unsigned>(grid)), dim3(CONVROT_PROBE_THREADS), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const i32x4*>(operands), iters, stamps, sink,
+                     flag);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}

@@ -2,8 +2,9 @@
 
 Routing follows the sglang kitchen_int8 integration (PR 34581 summary page,
 implementation section): a layer whose input width K is not a multiple of
-the group size stays on the unquantised bf16 linear, and the decision is
-logged so that a fallback is never silent.  Non-2-D inputs are flattened to
+the group size stays on the unquantised bf16 linear.  ``RoutingLog`` keeps
+one record per layer (path and reason) and logs every fallback, so that one
+is never silent.  Non-2-D inputs are flattened to
 rows and restored afterwards.
 
 Weights are int8 codes, or int4 codes with ``weight_bits=4`` (W4A8, the
@@ -24,6 +25,7 @@ output (``split``).
 from __future__ import annotations
 
 import logging
+from dataclasses import dataclass
 
 import torch
 
@@ -32,23 +34,42 @@ from . import api
 log = logging.getLogger("w8a8_int8_linear_amd")
 
 
+@dataclass(frozen=True)
+class Route:
+    """The path one layer takes and why."""
+    layer: str
+    K: int
+    group: int
+    path: str     # "int8" or "int4" (quantised ConvRot linear) or "bf16" (unquantised)
+    reason: str
+
+
 class RoutingLog:
-    """Summary of which layers run quantised and which stay in bf16."""
+    """One ``Route`` per layer built with it.  A layer routed to the
+    unquantised bf16 linear is also logged at WARNING level when it is
+    recorded, so that a fallback never passes unnoticed."""
 
     def __init__(self) -> None:
-        self.quantized: list[str] = []
-        self.fallback: list[str] = []
+        self.routes: list[Route] = []
 
-    def note(self, name: str, quantized: bool, K: int, G: int) -> None:
-        if quantized:
-            self.quantized.append(name)
+    def record(self, layer: str, K: int, group: int, weight_bits: int) -> Route:
+        if K % group == 0:
+            r = Route(layer, K, group, f"int{weight_bits}", f"G = {group} divides K = {K}")
         else:
-            self.fallback.append(f"{name}(in={K})")
-            log.info("convrot: %s keeps the bf16 linear (K=%d not divisible by G=%d)", name, K, G)
+            r = Route(layer, K, group, "bf16", f"K = {K} is not a multiple of G = {group}")
+            log.warning("convrot: layer %s runs the unquantised bf16 linear (%s)", layer, r.reason)
+        self.routes.append(r)
+        return r
 
-    def summary(self) -> str:
-        return (f"convrot: {len(self.quantized)} linear layers int8, {len(self.fallback)} left in bf16"
-                + (f": {', '.join(self.fallback)}" if self.fallback else ""))
+    def by_path(self, path: str) -> list[Route]:
+        return [r for r in self.routes if r.path == path]
+
+    def report(self) -> str:
+        """One line per layer: name, input width, path, reason."""
+        w = max([len(r.layer) for r in self.routes] + [5])
+        lines = [f"{'layer':<{w}}  {'K':>6}  path  reason"]
+        lines += [f"{r.layer:<{w}}  {r.K:>6}  {r.path:<4}  {r.reason}" for r in self.routes]
+        return "\n".join(lines)
 
 
 class ConvRotLinear:
@@ -81,7 +102,7 @@ class ConvRotLinear:
         b = bias.to(torch.float32).contiguous() if bias is not None else None
         quant = K % group == 0
         if routing is not None:
-            routing.note(name, quant, K, group)
+            routing.record(name, K, group, weight_bits)
         if quant:
             pack = api.pack_weight if weight_bits == 8 else api.pack_weight_w4
             packed = pack(w.contiguous(), group, kind, signs)
@@ -137,10 +158,17 @@ class ConvRotLinear:
             raise ValueError(f"adapter shapes must be a [r, {self.K}] and b [{self.N}, r]")
         self.adapters.append((a.to(torch.bfloat16).contiguous(), b.to(torch.bfloat16).contiguous(), float(scale)))
 
+    def _workspace(self, kind: str, M: int, device: torch.device) -> torch.Tensor | None:
+        """The split-K workspace of a small-M call (a torch allocation of the
+        caller's; None when the shape does not split).  Above 16 rows the
+        int4 binding allocates its expanded-weight workspace itself."""
+        return api.linear_workspace(kind, M, self.N, self.K, device) if M <= 16 else None
+
     def _linear(self, x: api.Packed, dt: torch.dtype) -> torch.Tensor:
         if isinstance(self.packed, api.PackedW4):
-            return api.linear_w4(x, self.packed, self.bias, out_dtype=dt)
-        return api.linear(x, self.packed, self.bias, dt)
+            return api.linear_w4(x, self.packed, self.bias, out_dtype=dt,
+                                 workspace=self._workspace(api.W4, x.rows, x.q.device))
+        return api.linear(x, self.packed, self.bias, dt, workspace=self._workspace(api.PLAIN, x.rows, x.q.device))
 
     def pack_input(self, x: torch.Tensor) -> api.Packed:
         """Pack rows of x once; reuse the result for every layer with the same
@@ -161,7 +189,8 @@ class ConvRotLinear:
         if self.quantized:
             y = self._linear(self.pack_input(rows), dt)
         else:
-            y = api.linear_bf16(rows.to(torch.bfloat16), self.w_bf16, self.bias, dt)
+            y = api.linear_bf16(rows.to(torch.bfloat16), self.w_bf16, self.bias, dt,
+                                workspace=self._workspace(api.BF16, rows.shape[0], rows.device))
         if self.adapters:
             xb = rows.to(torch.bfloat16).contiguous()
             for a, b, scale in self.adapters:

@@ -1,0 +1,92 @@
+"""Hardware measurement probes (libconvrot_probe.so, include/convrot_probe.h).
+
+``mfma_i8(device)`` runs the MFMA-only int8 loop on random codes (normal,
+sigma 32 code units) with one workgroup per CU and returns the rate it reached and the shader clock each
+CU ran at during it (from the s_memtime / s_memrealtime counters the kernel
+stamps).  ``copy_gbps(device)`` times a plain device-to-device copy.  These
+are the measured ceilings next to which bench.py reports the published peaks;
+they are not part of the linear layer.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+PROBE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot_probe.so")
+THREADS = 512
+CHAINS = 8
+OPS_PER_MFMA = 32768
+REALTIME_HZ = 100e6   # s_memrealtime counts at a constant 100 MHz
+EXPORTED = ("convrot_probe_mfma_i8",)
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(PROBE_PATH):
+            raise ImportError(f"{PROBE_PATH} is missing: build it with `python -m w8a8_int8_linear_amd.build`")
+        lib = ctypes.CDLL(PROBE_PATH)
+        vp = ctypes.c_void_p
+        lib.convrot_probe_mfma_i8.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp]
+        lib.convrot_probe_mfma_i8.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def mfma_i8(device: torch.device, iters: int = 20000, seed: int = 7) -> dict:
+    """int8 MFMA-only throughput (TOPS) over one workgroup per CU, and the
+    per-CU shader clock (GHz: median, min, max) during the loop."""
+    lib = load()
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    # codes like those of a quantised normal row (row max about 4 sigma, so
+    # sigma is about 32 code units), as the layer's GEMM multiplies
+    z = torch.randn(cus * THREADS * 64, generator=g) * 32.0
+    ops_bytes = z.round().clamp(-127, 127).to(torch.int8).to(device)
+    stamps = torch.zeros(cus * 4, dtype=torch.int64, device=device)
+    sink = torch.empty(cus * THREADS, dtype=torch.int32, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def run(n):
+        st = lib.convrot_probe_mfma_i8(ops_bytes.data_ptr(), cus, n, stamps.data_ptr(), sink.data_ptr(), 0,
+                                       stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"convrot_probe_mfma_i8 failed ({st})")
+
+    run(max(1, iters // 10))  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(iters)
+    e1.record(stream)
+    torch.cuda.synchronize(device)
+    ms = e0.elapsed_time(e1)
+    s = stamps.view(cus, 4).cpu().numpy().astype(np.float64)
+    ghz = (s[:, 1] - s[:, 0]) / ((s[:, 3] - s[:, 2]) / REALTIME_HZ) / 1e9
+    ops = cus * (THREADS // 64) * iters * CHAINS * OPS_PER_MFMA
+    return {"TOPS": round(ops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3), "cus": cus,
+            "sclk_GHz": round(float(np.median(ghz)), 3), "sclk_GHz_min": round(float(ghz.min()), 3),
+            "sclk_GHz_max": round(float(ghz.max()), 3)}
+
+
+def copy_gbps(device: torch.device, mib: int = 1024, reps: int = 5) -> float:
+    """Device-to-device copy of ``mib`` MiB (read + write bytes per second,
+    median over ``reps``): the bandwidth a plain streaming kernel reaches."""
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize(device)
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    return round(2 * (mib << 20) / (float(np.median(ts)) * 1e-3) / 1e9, 1)
