@@ -770,13 +770,17 @@ def main():
         from w8a8_int8_linear_amd import probe
 
         mf = probe.mfma_i8(dev)
+        cp = probe.copy_gbps(dev)
         result["ceilings"] = {
-            "copy_GBps": probe.copy_gbps(dev),
+            "copy_GBps": cp["GBps"],
+            "copy_by_grid": cp["by_grid_per_cu"],
+            "torch_copy_GBps": cp["torch_copy_GBps"],
             "mfma_i8_TOPS": mf["TOPS"],
             "mfma_i8_frac_of_peak": round(mf["TOPS"] / PEAK_I8_TOPS, 4),
             "sclk_GHz_mfma_loop": mf["sclk_GHz"],
             "sclk_GHz_range": [mf["sclk_GHz_min"], mf["sclk_GHz_max"]],
-            "note": "device copy (read + write bytes / s); MFMA-only v_mfma_i32_16x16x64_i8 loop, one workgroup "
+            "note": "streaming copy of 1 GiB (read + write bytes / s, best of three grid sizes); MFMA-only "
+                    "v_mfma_i32_16x16x64_i8 loop, one workgroup "
                     "per CU, two waves per SIMD, random normal codes; shader clock per CU from s_memtime against "
                     "the 100 MHz s_memrealtime",
         }

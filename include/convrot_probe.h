@@ -4,7 +4,8 @@
  * These are not part of the linear layer's interface (include/convrot.h).
  * They measure what the roofline fractions of the layer's kernels are
  * compared against on the running GPU: the int8 matrix-core rate on random
- * operands with no memory traffic, and the shader clock under that load.
+ * operands with no memory traffic, the shader clock under that load, and
+ * the bandwidth of a plain streaming copy.
  * Same conventions as convrot.h: device pointers, asynchronous on `stream`,
  * host-side validation before any launch, 0 on success.
  */
@@ -41,6 +42,14 @@ extern "C" {
  * when the launch fails. */
 int convrot_probe_mfma_i8(const void* operands, int grid, int iters, uint64_t* stamps, int32_t* sink, int flag,
                           void* stream);
+
+/* Streaming device copy of `bytes` bytes (a multiple of 16; src and dst
+ * 16-byte aligned, not overlapping) by `grid` workgroups of 256 threads,
+ * each thread moving four 16-byte chunks per round with nontemporal loads
+ * and stores: the bandwidth a plain streaming kernel reaches (read + write
+ * bytes per second).  Returns 0, 1 on a bad argument, 2 when the launch
+ * fails. */
+int convrot_probe_copy(const void* src, void* dst, int64_t bytes, int grid, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,7 +65,37 @@ __global__ __launch_bounds__(CONVROT_PROBE_THREADS, 1) void mfma_i8_probe(const 
   if (flag == 0x5eed) sink[g] = s;
 }
 
+// Streaming copy: each thread moves kCopyUnroll 16-byte chunks per round,
+// all loads of a round issued before its stores (nontemporal both ways), over
+// a grid that covers the GPU several times.  `n16` counts 16-byte chunks.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_probe(const i32x4* __restrict__ src, i32x4* __restrict__ dst,
+                                                           int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  for (; i + (kCopyUnroll - 1) * stride < n16; i += kCopyUnroll * stride) {
+    i32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
+
+extern "C" int convrot_probe_copy(const void* src, void* dst, int64_t bytes, int grid, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes <= 0 || bytes % 16 != 0 || grid <= 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15u) != 0)
+    return 1;
+  hipLaunchKernelGGL(copy_probe, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const i32x4*>(src), static_cast<i32x4*>(dst),
+                     bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int convrot_probe_mfma_i8(const void* operands, int grid, int iters, uint64_t* stamps, int32_t* sink,
                                      int flag, void* stream) {

@@ -21,7 +21,7 @@ THREADS = 512
 CHAINS = 8
 OPS_PER_MFMA = 32768
 REALTIME_HZ = 100e6   # s_memrealtime counts at a constant 100 MHz
-EXPORTED = ("convrot_probe_mfma_i8",)
+EXPORTED = ("convrot_probe_copy", "convrot_probe_mfma_i8")
 
 _lib = None
 
@@ -35,6 +35,8 @@ def load() -> ctypes.CDLL:
         vp = ctypes.c_void_p
         lib.convrot_probe_mfma_i8.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp]
         lib.convrot_probe_mfma_i8.restype = ctypes.c_int
+        lib.convrot_probe_copy.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
+        lib.convrot_probe_copy.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -74,19 +76,36 @@ def mfma_i8(device: torch.device, iters: int = 20000, seed: int = 7) -> dict:
             "sclk_GHz_max": round(float(ghz.max()), 3)}
 
 
-def copy_gbps(device: torch.device, mib: int = 1024, reps: int = 5) -> float:
-    """Device-to-device copy of ``mib`` MiB (read + write bytes per second,
-    median over ``reps``): the bandwidth a plain streaming kernel reaches."""
-    src = torch.ones(mib << 20, dtype=torch.uint8, device=device)
+def copy_gbps(device: torch.device, mib: int = 1024, reps: int = 5) -> dict:
+    """A device-to-device copy of ``mib`` MiB, read + write bytes per second
+    (median over ``reps``): the streaming probe kernel at several grid sizes
+    (the best is the measured streaming ceiling) and torch's own copy."""
+    lib = load()
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    nbytes = mib << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device=device)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize(device)
-        ts.append(e0.elapsed_time(e1))
+    stream = torch.cuda.current_stream(device)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize(device)
+            ts.append(e0.elapsed_time(e1))
+        return round(2 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+
+    def probe(grid):
+        def run():
+            if lib.convrot_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid, stream.cuda_stream) != 0:
+                raise RuntimeError("convrot_probe_copy failed")
+        return run
+
+    by_grid = {f"{k}x": timed(probe(k * cus)) for k in (4, 8, 16)}
+    out = {"GBps": max(by_grid.values()), "by_grid_per_cu": by_grid, "torch_copy_GBps": timed(lambda: dst.copy_(src))}
     del src, dst
-    return round(2 * (mib << 20) / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    return out
