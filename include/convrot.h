@@ -221,6 +221,30 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
                               const float* bias, void* Y, convrot_dtype ydt, int64_t ldy,
                               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Size of the static scratch of convrot_linear_noalloc (bytes). */
+#define CONVROT_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/* convrot_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks, kernels and result bits as
+ * convrot_linear with a workspace, but the small-M split's partial sums go
+ * to a static device array of CONVROT_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends.  Nothing is
+ * allocated, by the library or on its behalf.
+ *   - A shape whose split needs more than that scratch is rejected with
+ *     CONVROT_ERR_INVALID_ARG before anything is enqueued (on a 256-CU GPU
+ *     the largest split of this entry point needs 0.75 MiB, so every shape
+ *     fits there).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's partial sums; each call fully rewrites what it reads, so
+ *     nothing needs clearing.  Calls that overlap in time on one GPU
+ *     (different streams, or graphs replayed concurrently) race on it and
+ *     give wrong results; calls ordered on one stream or by events do not.
+ *   - The scratch's device address is resolved on the first call on each
+ *     device (hipGetSymbolAddress); a failure there is CONVROT_ERR_HIP. */
+convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
+                                      convrot_dtype ydt, int64_t ldy, void* stream);
+
 /* Bytes of workspace a linear call of `kind` uses for X [M, K] and N
  * outputs on the current device:
  *   M <= 16  the split-K partial sums (0 when the shape does not split K);

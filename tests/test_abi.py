@@ -242,6 +242,22 @@ def test_linear_workspace_query(lib):
     assert lib.convrot_linear_workspace_bytes(_lib.LINEAR_PLAIN, 16, 1152, 6912, None) == _lib.ERR_INVALID_ARG
 
 
+def test_linear_noalloc_checks(lib):
+    """The no-allocation variant validates like convrot_linear before it
+    touches its scratch."""
+    f = lib.convrot_linear_noalloc
+    act, w = packed(rows=16, K=6912), packed(rows=1152, K=6912, q=0x40000, scale=0x50000)
+    assert f(None, None, None, A16C, _lib.BF16, 64, None) == _lib.ERR_INVALID_ARG
+    assert f(ctypes.byref(act), ctypes.byref(packed(rows=1152, K=3072, q=0x40000)), None, A16C, _lib.BF16, 1152,
+             None) == _lib.ERR_MISMATCH
+    assert f(ctypes.byref(act), ctypes.byref(w), None, A16C, 9, 1152, None) == _lib.ERR_DTYPE
+    assert f(ctypes.byref(act), ctypes.byref(w), None, A16C, _lib.BF16, 1000, None) == _lib.ERR_INVALID_ARG
+    assert f(ctypes.byref(packed(rows=0, K=6912)), ctypes.byref(w), None, A16C, _lib.BF16, 1152, None) == _lib.OK
+    # the largest split of this entry point fits its static scratch on a 256-CU GPU
+    worst = max(ws_bytes(lib, _lib.LINEAR_PLAIN, 16, n, 12288)[1] for n in range(16, 4096, 16))
+    assert 0 < worst <= _lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_linear_rejects_a_short_workspace(lib):
     """A non-NULL workspace smaller than the split needs is an error before
     any launch (NULL would select the unsplit kernel)."""

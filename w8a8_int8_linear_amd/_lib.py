@@ -13,6 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
 ABI_VERSION = 7
+NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # convrot_status
 OK, ERR_INVALID_ARG, ERR_GROUP, ERR_DTYPE, ERR_ALIGN, ERR_MISMATCH, ERR_HIP = range(7)
@@ -32,6 +33,7 @@ EXPORTED = (
     "convrot_pack_weight",
     "convrot_linear",
     "convrot_linear_workspace_bytes",
+    "convrot_linear_noalloc",
     "convrot_linear_act",
     "convrot_linear_gated",
     "convrot_linear_bf16",
@@ -94,6 +96,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_pack_weight.restype = c_int
     lib.convrot_linear.argtypes = [P, P, vp, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear.restype = c_int
+    lib.convrot_linear_noalloc.argtypes = [P, P, vp, vp, c_int, c_i64, vp]
+    lib.convrot_linear_noalloc.restype = c_int
     lib.convrot_linear_workspace_bytes.argtypes = [c_int, c_i64, c_i64, c_i64, ctypes.POINTER(c_i64)]
     lib.convrot_linear_workspace_bytes.restype = c_int
     lib.convrot_linear_act.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]

@@ -215,6 +215,22 @@ def linear(act: Packed, w: Packed, bias: torch.Tensor | None = None, out_dtype: 
     return out
 
 
+def linear_noalloc(act: Packed, w: Packed, out: torch.Tensor, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """``linear`` for callers that cannot allocate (convrot_linear_noalloc):
+    the caller passes ``out`` [M, N] (float32, bfloat16 or int32); the
+    small-M split's partial sums go to the library's static per-GPU scratch.
+    Calls that overlap in time on one GPU race on that scratch."""
+    M, N = act.rows, w.rows
+    dev = act.q.device
+    _check_out(out, M, N, tuple(_DT), dev)
+    _check_bias(bias, N, dev)
+    a, b = act.descriptor(), w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_noalloc(ctypes.byref(a), ctypes.byref(b), _ptr(bias), out.data_ptr(),
+                                          _DT[out.dtype], _ld(out), _stream(dev)))
+    return out
+
+
 def _out_and_bias(M, N, device, out, out_dtype, bias):
     if out is None:
         if out_dtype not in (torch.float32, torch.bfloat16):

@@ -3,11 +3,13 @@
 // The declarations and the contract of every entry point are in convrot.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
 #include "convrot.h"
+#include "device.h"
 #include "launchers.h"
 
 namespace {
@@ -262,6 +264,70 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
   return from_hip(e, "convrot_linear");
+}
+
+}  // extern "C"
+
+namespace {
+// Scratch of convrot_linear_noalloc: file-scope device memory for the
+// small-M K split's partial sums.  Every GPU the library runs on holds its
+// own copy until the process ends.  On the host `scratch` names a host-side
+// stand-in, not a device address: host code only ever uses the address
+// hipGetSymbolAddress returns for the current device, resolved once per
+// device on that device's first call and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[convrot::kMaxDevices];
+
+convrot_status scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "convrot_linear_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= convrot::kMaxDevices)
+    return fail(CONVROT_ERR_INVALID_ARG, "convrot_linear_noalloc: device %d beyond the %d supported", dev,
+                convrot::kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CONVROT_ERR_HIP, "convrot_linear_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return CONVROT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
+                                      convrot_dtype ydt, int64_t ldy, void* stream) {
+  const char* what = "convrot_linear_noalloc";
+  convrot_status st = check_linear(what, act, w, bias, Y, ydt, ldy, true);
+  if (st != CONVROT_OK) return st;
+  const int64_t M = act->rows, N = w->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  const auto out = static_cast<convrot::Elt>(ydt);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (M <= convrot::kGemvMaxRows) {
+    const int64_t need = small_m_workspace(CONVROT_LINEAR_PLAIN, N, K);
+    if (need > CONVROT_NOALLOC_SCRATCH_BYTES)
+      return fail(CONVROT_ERR_INVALID_ARG,
+                  "%s: this shape splits K into %lld bytes of partial sums, beyond the %d-byte static scratch "
+                  "(use convrot_linear with a workspace)",
+                  what, static_cast<long long>(need), CONVROT_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+      st = scratch_address(&ws);
+      if (st != CONVROT_OK) return st;
+    }
+    e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, ws,
+                                s);
+  } else {
+    e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
+  }
+  return from_hip(e, what);
 }
 
 convrot_status convrot_linear_workspace_bytes(convrot_linear_kind kind, int64_t M, int64_t N, int64_t K,
