@@ -246,6 +246,27 @@ def code_values(Xr32: np.ndarray, s: np.ndarray) -> np.ndarray:
     return v
 
 
+def group_absmax(Xr32: np.ndarray, G: int) -> np.ndarray:
+    """Largest magnitude of every contiguous G-group of fp32 rotated rows,
+    [rows, K / G].
+
+    Producer fusion of the next layer's rotation and row maximum (the
+    "Backend support" section of "INT8 Convrot Safetensors" names the
+    rotation, the row-wise maximum reduction and the quantisation as the
+    fused activation-side work): a producing layer can emit these per-group
+    maxima of its rotated output, and the whole-row maximum that sets the
+    scale in "Runtime activation quantization" is their maximum, because the
+    groups partition the row.  Zero groups give 0.
+    """
+    x = np.asarray(Xr32)
+    if x.dtype != np.float32:
+        raise TypeError("group_absmax expects the fp32 rotated rows")
+    rows, K = x.shape
+    if K % G:
+        raise ValueError("K must be a multiple of G")
+    return np.max(np.abs(x).reshape(rows, K // G, G), axis=2) if K else np.zeros((rows, 0), np.float32)
+
+
 def pack(X: np.ndarray, G: int, kind: str = REGULAR,
          signs: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Rotate then quantise rows (activations at run time, weights offline).

@@ -239,6 +239,31 @@ def check_code_values(seed: int = 18):
     assert np.all(v4[2] == 0)
 
 
+def check_group_absmax(seed: int = 19):
+    """The per-group maxima of a rotated row: their maximum is the row
+    maximum that sets the scale (fp32(max / 127) equals quantize_rows' s);
+    a one-hot row spreads over its own group only (|c| / sqrt(G) there, 0
+    in every other group); brute force over the groups by a Python loop on
+    a small case; zero rows give zeros."""
+    g = np.random.default_rng(seed)
+    for G in (4, 16, 64, 256):
+        x = (g.standard_normal((6, 4 * G)) * g.uniform(0.1, 30, (6, 1))).astype(np.float32)
+        x[4] = 0.0
+        xr = O.rotate(x, G)
+        pm = O.group_absmax(xr, G)
+        assert pm.shape == (6, 4) and pm.dtype == np.float32
+        _, s = O.quantize_rows(xr)
+        assert np.array_equal((np.max(pm, axis=1) / np.float32(127)).astype(np.float32), s)
+        assert np.all(pm[4] == 0)
+        for r in (0, 5):
+            for b in range(4):
+                assert pm[r, b] == max(abs(float(v)) for v in xr[r, b * G:(b + 1) * G])
+        one = np.zeros((1, 4 * G), np.float32)
+        one[0, 2 * G + G - 1] = -3.0
+        pm1 = O.group_absmax(O.rotate(one, G), G)
+        assert pm1[0, 2] == np.float32(3.0 / np.sqrt(G)) and np.all(pm1[0, [0, 1, 3]] == 0)
+
+
 def check_qmax_from_pages():
     consts = page_constants()
     assert O.QMAX == consts["qmax"]
@@ -566,6 +591,7 @@ ALL_CHECKS = [
     ("quant_ties_half_even", check_quant_ties_half_even, ()),
     ("qmax_from_pages", check_qmax_from_pages, ()),
     ("code_values", check_code_values, ()),
+    ("group_absmax", check_group_absmax, ()),
     ("int_gemm_bruteforce", check_int_gemm_bruteforce, ()),
     ("int_gemm_extremes", check_int_gemm_extremes, ()),
     ("int_gemm_large_random", check_int_gemm_large_random, ()),

@@ -16,6 +16,7 @@ _int_gemm = O.int_gemm
 _bf16_round = O.bf16_round
 _randomized_block = O.randomized_block
 _code_values = O.code_values
+_group_absmax = O.group_absmax
 
 
 def _h4_sign_flip():
@@ -260,6 +261,20 @@ def _code_values_unmasked(x, s):
         return (x / np.asarray(s, np.float32)[:, None]).astype(np.float32)
 
 
+def _group_absmax_strided(x, G):
+    # groups taken as strided columns instead of contiguous blocks
+    x = np.asarray(x, np.float32)
+    rows, K = x.shape
+    return np.max(np.abs(x).reshape(rows, G, K // G), axis=1)
+
+
+def _group_absmax_signed(x, G):
+    # the largest value instead of the largest magnitude
+    x = np.asarray(x, np.float32)
+    rows, K = x.shape
+    return np.max(x.reshape(rows, K // G, G), axis=2)
+
+
 MUTATIONS = {
     "h4_sign_flip": ("h4", _h4_sign_flip),
     "h4_unnormalised": ("h4", _h4_unnormalised),
@@ -275,6 +290,8 @@ MUTATIONS = {
     "code_values_fp64": ("code_values", _code_values_fp64),
     "code_values_reciprocal": ("code_values", _code_values_reciprocal),
     "code_values_zero_rows_nan": ("code_values", _code_values_unmasked),
+    "group_absmax_strided_groups": ("group_absmax", _group_absmax_strided),
+    "group_absmax_signed": ("group_absmax", _group_absmax_signed),
     "epilogue_drops_bias": ("epilogue64", _epi_no_bias),
     "epilogue_drops_weight_scale": ("epilogue64", _epi_no_sw),
     "epilogue_swaps_scales": ("epilogue64", _epi_swapped),
