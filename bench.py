@@ -80,13 +80,13 @@ SMALL_M = 16             # up to this many rows a linear runs on the weight-stre
 METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
 # the sources each kernel is compiled from; a traffic summary is valid only for these exact bytes
 KERNEL_SOURCE = {
-    "gemm_i8": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_i8.hip"),
-    "gemm_i8_act": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_act.hip"),
+    "gemm_i8": ("gemm_kernel.h", "gemm_pp.h", "lanes.h", "epilogue.h", "gemm_i8.hip"),
+    "gemm_i8_act": ("gemm_kernel.h", "gemm_pp.h", "lanes.h", "epilogue.h", "gemm_act.hip"),
     "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
-    "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "epilogue.h", "gemm_bf16.hip"),
+    "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "lanes.h", "epilogue.h", "gemm_bf16.hip"),
     "gemv_i8": ("gemv.hip", "epilogue.h", "w4_codec.h"),
     "gemv_w4": ("gemv.hip", "epilogue.h", "w4_codec.h"),
-    "pack_rows": ("pack_rows.hip",),
+    "pack_rows": ("pack_rows.hip", "lanes.h"),
 }
 
 
@@ -199,8 +199,9 @@ class Op:
 class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
-    def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True):
+    def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
+        self.producer_fusion = producer_fusion and fused and wl.cfg == 3
         # linears that share the packed activation run as one launch over the
         # concatenated weight (configs whose linears all read the same input)
         self.merge = merge and wl.cfg == 2 and all(l.W.shape[1] % wl.G == 0 for l in wl.linears)
@@ -358,6 +359,21 @@ class StepSet:
                             "lora", M=M, N=y.shape[1], K=K, out_b=y.element_size())
                     op.epilogue_rank = r
                     ops.append(op)
+        elif wl.cfg == 3 and self.producer_fusion:
+            # GELU in the up projection's epilogue, which also emits the group
+            # maxima of its rotated output; the down layer's pack takes its row
+            # maxima from them
+            h = self._out("up", M, dev)
+            w, b = self.W["up"], self.b["up"]
+            pm = torch.empty((M, w.rows // wl.G), dtype=torch.float32, device=dev)
+            self.bufs.append(pm)
+            ops.append(Op("linear_up_gelu_rowmax", lambda: self.cr.linear_act_rowmax(
+                src0, w, wl.G, b, self.cr.GELU_ERF, out=h, rowmax=pm), "int8", M=M, N=w.rows, K=w.K,
+                out_b=h.element_size(), epilogue="act"))
+            pa2 = self._packed(M, h.shape[1], dev)
+            ops.append(Op("pack_act2_rowmax", lambda: self.cr.pack_act_rowmax(h, pm, wl.G, out=pa2), "pack", M=M,
+                          K=h.shape[1], in_b=h.element_size()))
+            ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
         elif wl.cfg == 3:
             if self.fused:
                 # GELU in the up projection's epilogue
@@ -578,6 +594,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run the activation between chained layers as a separate torch op instead of in the "
                          "linear's epilogue")
+    ap.add_argument("--producer-fusion", action="store_true",
+                    help="MLP: the up projection's epilogue emits the rotated group maxima of its output and the "
+                         "down layer's pack takes its row maxima from them")
     ap.add_argument("--separate-linears", action="store_true",
                     help="launch linears that share one packed activation one by one instead of as one launch over "
                          "the concatenated weight")
@@ -606,9 +625,10 @@ def main():
 
     fused = not args.unfused
     merge = not args.separate_linears
-    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge)]
+    pf = args.producer_fusion
+    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
-        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge))
+        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -748,6 +768,7 @@ def main():
         "config": {"workload": wl.name, "M": wl.X.shape[0], "K": wl.X.shape[1],
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
                    "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
+                   "producer_fusion": bool(sets[0].producer_fusion),
                    "shared_pack_linears": "one launch" if sets[0].merge else "one launch each",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "weights": "int4" if wl.extra.get("wbits") == 4 else "int8",

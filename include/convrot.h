@@ -272,6 +272,43 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
                                   convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, void* workspace,
                                   int64_t workspace_bytes, void* stream);
 
+/* Producer fusion of the next layer's pack.  The activation side of the
+ * method is a rotation, a whole-row maximum and a quantisation ("INT8
+ * Convrot Safetensors", "Backend support" and "Runtime activation
+ * quantization": the row's scale is its largest rotated magnitude over 127).
+ * This is convrot_linear_act that, in the same launch, also computes the
+ * row maximum's parts for the layer that reads Y: for every row r of Y and
+ * every contiguous group j of group_next output features,
+ *   rowmax[r, j] = max over the group of |(Y[r, group j] R)_i|
+ * with R the regular rotation of size group_next, applied to Y as stored
+ * (a bf16 Y is rounded first).  convrot_pack_act_rowmax then packs Y with
+ * these maxima and skips its own row reduction; the codes and scales are
+ * those of convrot_pack_act on Y, bit for bit (both evaluate the rotation
+ * with the same operations in the same order).
+ *   group_next  4, 16, 64 or 256, else CONVROT_ERR_GROUP
+ *   rowmax      [M, ldm] fp32, caller-owned, 4-byte aligned,
+ *               ldm >= N / group_next
+ * Needs M > 16 (the tiled kernel), N % 256 == 0, K % 128 == 0 and Y rows
+ * aligned for 4-element stores (Y aligned to 4 elements, ldy % 4 == 0);
+ * otherwise CONVROT_ERR_INVALID_ARG.  Other arguments, checks and errors as
+ * convrot_linear_act. */
+convrot_status convrot_linear_act_rowmax(const convrot_packed* act, const convrot_packed* w, const float* bias,
+                                         convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, int32_t group_next,
+                                         float* rowmax, int64_t ldm, void* stream);
+
+/* The pack of activation rows whose rotated group maxima are given (as
+ * convrot_linear_act_rowmax writes them): the codes and scales of
+ * convrot_pack_act, with the row maximum taken from `rowmax` instead of a
+ * reduction over the row.
+ *   X       [out->rows, ldx] of `xdt` (CONVROT_F32 or CONVROT_BF16)
+ *   rowmax  [out->rows, ldm] fp32, ldm >= K / G, the maxima for
+ *           G = out->rot.group
+ *   out     as convrot_pack_act; the rotation must be the regular kind with
+ *           G in {4, 16, 64, 256} (else CONVROT_ERR_GROUP)
+ * Maxima that do not belong to X give a wrong scale; nothing checks them. */
+convrot_status convrot_pack_act_rowmax(const void* X, convrot_dtype xdt, int64_t ldx, const float* rowmax,
+                                       int64_t ldm, const convrot_packed* out, void* stream);
+
 /* A gated pair: two quantised linears that share one packed activation,
  * combined in the epilogue of a single launch,
  *   G[r, o] = A_gate[r, o] * act->scale[r] * w_gate->scale[o] + b_gate[o]

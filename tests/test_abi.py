@@ -258,6 +258,33 @@ def test_linear_noalloc_checks(lib):
     assert 0 < worst <= _lib.NOALLOC_SCRATCH_BYTES
 
 
+def test_rowmax_entry_point_checks(lib):
+    """Producer-fusion entry points validate on the host before any launch."""
+    f = lib.convrot_linear_act_rowmax
+
+    def st(group=256, N=512, M=64, Y=A16C, ldy=512, ldm=2, rowmax=0x60000, fn=_lib.ACT_GELU_ERF):
+        a = packed(rows=M, K=1024)
+        ww = packed(rows=N, K=1024, q=0x40000, scale=0x50000)
+        return f(ctypes.byref(a), ctypes.byref(ww), None, fn, Y, _lib.BF16, ldy, group, rowmax, ldm, None)
+    assert st(group=128) == _lib.ERR_GROUP
+    assert st(group=1024, ldm=1) == _lib.ERR_GROUP
+    assert st(N=320, ldy=320) == _lib.ERR_INVALID_ARG      # N % 256
+    assert st(M=16) == _lib.ERR_INVALID_ARG                 # small M
+    assert st(ldm=1) == _lib.ERR_INVALID_ARG                # ldm < N / G
+    assert st(Y=A16C + 2) == _lib.ERR_ALIGN                 # rows not aligned for 4-element stores
+    assert st(rowmax=None) == _lib.ERR_INVALID_ARG
+    assert st(fn=_lib.ACT_NONE) == _lib.ERR_INVALID_ARG
+    assert st(M=0) == _lib.OK
+    g = lib.convrot_pack_act_rowmax
+    out = packed(rows=8, K=1024, G=256)
+    assert g(A16C, _lib.BF16, 1024, 0x60000, 3, ctypes.byref(out), None) == _lib.ERR_INVALID_ARG   # ldm < K / G
+    big = packed(rows=8, K=2048, G=1024)
+    assert g(A16C, _lib.BF16, 2048, 0x60000, 2, ctypes.byref(big), None) == _lib.ERR_GROUP
+    rnd = packed(rows=8, K=1024, G=256, kind=_lib.ROT_RANDOMIZED, signs=0x70000)
+    assert g(A16C, _lib.BF16, 1024, 0x60000, 4, ctypes.byref(rnd), None) == _lib.ERR_GROUP
+    assert g(A16C, _lib.BF16, 1024, 0x60000, 4, ctypes.byref(packed(rows=0, K=1024)), None) == _lib.OK
+
+
 def test_linear_rejects_a_short_workspace(lib):
     """A non-NULL workspace smaller than the split needs is an error before
     any launch (NULL would select the unsplit kernel)."""

@@ -213,6 +213,23 @@ def test_dit_mlp_full(cuda):
     err = R.rel_fro(g_fused, ref)
     say(f"  fused up+GELU: Y rel Frobenius {err:.3e}")
     assert err <= R.Y_RTOL
+    # Producer fusion of the down layer's pack, as the benchmark's
+    # --producer-fusion step runs it: the same Y, group maxima of its
+    # rotation, and a pack from those maxima equal to the pack of Y.
+    g_full = cr.linear_act(pa, pw_up, to_dev(up.b, torch.float32), cr.GELU_ERF)
+    g_f2, pm = cr.linear_act_rowmax(pa, pw_up, G, to_dev(up.b, torch.float32), cr.GELU_ERF)
+    assert torch.equal(g_f2, g_full)
+    del g_full
+    pm_rows = to_np(pm.index_select(0, St0))
+    pm_ref = O.group_absmax(O.rotate(to_np(g_f2.index_select(0, St0)), G), G)
+    row = np.max(pm_ref, axis=1, keepdims=True)
+    assert np.all(np.abs(pm_rows - pm_ref) <= R.ROT_RTOL * row)
+    p_f2 = cr.pack_act_rowmax(g_f2, pm, G)
+    p_un = cr.pack_act(g_f2, G)
+    assert torch.equal(p_f2.q, p_un.q) and torch.equal(p_f2.scale, p_un.scale)
+    say(f"  producer fusion: group maxima on {len(S)} rows within {R.ROT_RTOL} of the oracle, pack from them "
+        f"equal to the pack of Y")
+    del g_f2, pm, p_f2, p_un
     h = torch.nn.functional.gelu(y_up)
     del y_up
     St = torch.from_numpy(S).to(cuda)

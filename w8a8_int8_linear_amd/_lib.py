@@ -35,6 +35,8 @@ EXPORTED = (
     "convrot_linear_workspace_bytes",
     "convrot_linear_noalloc",
     "convrot_linear_act",
+    "convrot_linear_act_rowmax",
+    "convrot_pack_act_rowmax",
     "convrot_linear_gated",
     "convrot_linear_bf16",
     "convrot_rotate",
@@ -102,6 +104,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_linear_workspace_bytes.restype = c_int
     lib.convrot_linear_act.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear_act.restype = c_int
+    lib.convrot_linear_act_rowmax.argtypes = [P, P, vp, c_int, vp, c_int, c_i64, ctypes.c_int32, vp, c_i64, vp]
+    lib.convrot_linear_act_rowmax.restype = c_int
+    lib.convrot_pack_act_rowmax.argtypes = [vp, c_int, c_i64, vp, c_i64, P, vp]
+    lib.convrot_pack_act_rowmax.restype = c_int
     lib.convrot_linear_gated.argtypes = [P, P, vp, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear_gated.restype = c_int
     lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp, c_i64,

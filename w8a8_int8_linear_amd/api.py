@@ -262,6 +262,55 @@ def linear_act(act_in: Packed, w: Packed, bias: torch.Tensor | None = None, act:
     return out
 
 
+def linear_act_rowmax(act_in: Packed, w: Packed, group_next: int = 256, bias: torch.Tensor | None = None,
+                      act: str = GELU_ERF, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      rowmax: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """``linear_act`` that also returns, for the layer reading its output,
+    the largest magnitude of every group of ``group_next`` output features
+    after the regular rotation (convrot_linear_act_rowmax): (Y, rowmax
+    [M, N / group_next]).  ``pack_act_rowmax(Y, rowmax, group_next)`` then
+    equals ``pack_act(Y, group_next)`` bit for bit."""
+    dev = act_in.q.device
+    M, N = act_in.rows, w.rows
+    out = _out_and_bias(M, N, dev, out, out_dtype, bias)
+    if group_next <= 0 or N % group_next:
+        raise ValueError("group_next must divide N")
+    if rowmax is None:
+        rowmax = torch.empty((M, N // group_next), dtype=torch.float32, device=dev)
+    if rowmax.dtype != torch.float32 or tuple(rowmax.shape) != (M, N // group_next) or rowmax.device != dev or \
+            (rowmax.shape[1] > 1 and rowmax.stride(1) != 1):
+        raise ValueError(f"rowmax must be float32 [{M}, {N // group_next}] on the operands' device")
+    a, b = act_in.descriptor(), w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_act_rowmax(ctypes.byref(a), ctypes.byref(b), _ptr(bias), _act_code(act),
+                                             out.data_ptr(), _DT[out.dtype], _ld(out), int(group_next),
+                                             rowmax.data_ptr(), _ld(rowmax), _stream(dev)))
+    return out, rowmax
+
+
+def pack_act_rowmax(x: torch.Tensor, rowmax: torch.Tensor, group: int = 256, out: Packed | None = None) -> Packed:
+    """Pack rows of x whose rotated group maxima are given (from
+    ``linear_act_rowmax``) without reducing the rows again
+    (convrot_pack_act_rowmax); regular rotation only."""
+    _need_cuda(x, "input")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("input must be float32 or bfloat16")
+    rows, K = x.shape
+    if group <= 0 or K % group:
+        raise ValueError("group must divide K")
+    if rowmax.dtype != torch.float32 or tuple(rowmax.shape) != (rows, K // group) or rowmax.device != x.device or \
+            (rowmax.shape[1] > 1 and rowmax.stride(1) != 1):
+        raise ValueError(f"rowmax must be float32 [{rows}, {K // group}] on the input's device")
+    if out is None:
+        out = Packed(torch.empty((rows, K), dtype=torch.int8, device=x.device),
+                     torch.empty((rows,), dtype=torch.float32, device=x.device), group)
+    desc = out.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_pack_act_rowmax(x.data_ptr(), _DT[x.dtype], _ld(x), rowmax.data_ptr(), _ld(rowmax),
+                                           ctypes.byref(desc), _stream(x.device)))
+    return out
+
+
 def linear_gated(act_in: Packed, w_gate: Packed, w_up: Packed, b_gate: torch.Tensor | None = None,
                  b_up: torch.Tensor | None = None, act: str = GELU_TANH, out_dtype: torch.dtype = torch.bfloat16,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:

@@ -374,6 +374,59 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
   return from_hip(e, "convrot_linear_act");
 }
 
+convrot_status convrot_linear_act_rowmax(const convrot_packed* act, const convrot_packed* w, const float* bias,
+                                         convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy, int32_t group_next,
+                                         float* rowmax, int64_t ldm, void* stream) {
+  const char* what = "convrot_linear_act_rowmax";
+  convrot_status st = check_act(fn);
+  if (st != CONVROT_OK) return st;
+  st = check_linear(what, act, w, bias, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  const int lg = log2_exact(group_next);
+  if (lg < 2 || lg > 8 || (lg & 1))
+    return fail(CONVROT_ERR_GROUP, "%s: group_next must be 4, 16, 64 or 256, got %d", what, group_next);
+  const int64_t M = act->rows, N = w->rows, K = act->K;
+  if (M == 0 || N == 0) return ok();
+  if (M <= convrot::kGemvMaxRows)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: needs M > %lld (the tiled kernel); use convrot_linear_act and "
+                "convrot_pack_act", what, static_cast<long long>(convrot::kGemvMaxRows));
+  if (N % 256 != 0 || K % 128 != 0)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: needs N %% 256 == 0 and K %% 128 == 0 (N = %lld, K = %lld)", what,
+                static_cast<long long>(N), static_cast<long long>(K));
+  if (reinterpret_cast<uintptr_t>(Y) % (4 * elt_size(ydt)) != 0 || ldy % 4 != 0)
+    return fail(CONVROT_ERR_ALIGN, "%s: Y rows must be aligned for 4-element stores", what);
+  st = check_matrix("rowmax", rowmax, M, N / group_next, ldm, 4, false);
+  if (st != CONVROT_OK) return st;
+  const hipError_t e = convrot::launch_gemm_i8_act_rowmax(
+      act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, static_cast<convrot::Act>(fn), M, N, K, Y,
+      static_cast<convrot::Elt>(ydt), ldy, rowmax, ldm, lg, static_cast<hipStream_t>(stream));
+  return from_hip(e, what);
+}
+
+convrot_status convrot_pack_act_rowmax(const void* X, convrot_dtype xdt, int64_t ldx, const float* rowmax,
+                                       int64_t ldm, const convrot_packed* out, void* stream) {
+  const char* what = "convrot_pack_act_rowmax";
+  int log2G = 0;
+  if (out == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: output descriptor is NULL", what);
+  convrot_status st = check_k(out->K, kMaxPackK);
+  if (st != CONVROT_OK) return st;
+  st = check_packed("packed output", out, &log2G);
+  if (st != CONVROT_OK) return st;
+  if (out->rot.kind != CONVROT_ROT_REGULAR || log2G > 8)
+    return fail(CONVROT_ERR_GROUP, "%s: given maxima need the regular rotation with G in {4, 16, 64, 256}", what);
+  if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
+  st = check_matrix("input", X, out->rows, out->K, ldx, elt_size(xdt));
+  if (st != CONVROT_OK) return st;
+  st = check_matrix("rowmax", rowmax, out->rows, out->K >> log2G, ldm, 4, false);
+  if (st != CONVROT_OK) return st;
+  if (out->rows == 0) return ok();
+  const hipError_t e = convrot::launch_pack_rows_prescaled(X, static_cast<convrot::Elt>(xdt), out->rows, out->K, ldx,
+                                                           log2G, rowmax, ldm, out->q, out->ld, out->scale,
+                                                           static_cast<hipStream_t>(stream));
+  return from_hip(e, what);
+}
+
 convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_packed* w_gate, const float* b_gate,
                                     const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
                                     convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,

@@ -18,6 +18,16 @@ struct EpiArgs {
   const float* bias2;
 };
 
+// Producer fusion of the next layer's pack: per-group maxima of the rotated
+// output.  out [M, ld] fp32 receives, for every row and every contiguous
+// group of G = 2^log2g output features, the largest magnitude of that group
+// of the output (as stored) multiplied by the regular rotation R_G.
+struct RowmaxArgs {
+  float* out;
+  int64_t ld;
+  int log2g;
+};
+
 // GELU in its erf form, y Phi(y), branch-free.  With a = |y| and
 // h = erfc(a / sqrt 2) / 2 (the normal tail beyond a), y Phi(y) equals
 // max(y, 0) - a h for either sign of y, one fused multiply-add that never

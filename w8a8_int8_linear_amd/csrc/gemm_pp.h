@@ -42,8 +42,22 @@
 // private LDS area per wave and read back so that each lane finishes fixed
 // 4-feature segments (conversion, both scales, bias, activation) and stores
 // whole row pieces.
+//
+// Producer fusion (ROWMAX, 256-wide tiles): the epilogue also computes, for
+// the next layer's pack, the largest magnitude of every G-group (G <= 256)
+// of each output row after the regular rotation R_G, from the output as
+// stored.  The two waves that share 64 tokens (w and w + 4) stage their
+// halves of the tile into one area, so that each finishes 16 whole
+// 256-feature rows per 32 tokens, four features per lane.  The group's
+// base-4 digits are the element (digit 0), lane bits 0-1 (digit 1) and the
+// Gray codes of lane bits 2-3 and 4-5 (digits 2 and 3), so that every lane
+// exchange of the rotation is the one the pack kernel uses (quad and row
+// DPP, the 16- and 32-lane swizzles); the rotation takes the pack kernel's
+// operations in the pack kernel's order (lanes.h), so the maxima equal the
+// pack's own bit for bit.
 #pragma once
 #include "gemm_kernel.h"
+#include "lanes.h"
 
 namespace convrot {
 namespace {
@@ -58,15 +72,25 @@ constexpr int pp_smem_bytes() {
   return 3 * kATileBytes + 2 * (64 * TN) * kBK;
 }
 
+// First of the four features lane l finishes in the ROWMAX epilogue: digit
+// 1 of the feature index is lane bits 0-1, digits 2 and 3 the Gray codes of
+// lane bits 2-3 and 4-5.
+__device__ __forceinline__ int rowmax_col(int lane) {
+  const int m2 = (lane >> 2) & 3, m3 = lane >> 4;
+  return 4 * ((lane & 3) + 4 * (m2 ^ (m2 >> 1)) + 16 * (m3 ^ (m3 >> 1)));
+}
+
 // OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator (int8 mode only).
 // ACT: epilogue activation (see activation() in epilogue.h).
-template <bool I8, int OUT, int TN, int ACT>
+template <bool I8, int OUT, int TN, int ACT, bool ROWMAX = false>
 __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool vec_out) {
+    int N, int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool vec_out,
+    RowmaxArgs rm) {
   static_assert(TN >= 2 && TN <= 4, "tile width");
   static_assert(I8 || OUT != 2, "raw accumulators are an int8 feature");
   static_assert(ACT == 0 || OUT != 2, "activations need a float output");
+  static_assert(!ROWMAX || (TN == 4 && OUT != 2), "group maxima need 256-wide tiles and a float output");
   constexpr int kBN = 64 * TN;          // B-tile rows (output features)
   constexpr int kWN = 32 * TN;          // B rows per wave
   constexpr int kBTileBytes = kBN * kBK;
@@ -193,7 +217,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kLaneSegs; ++j) {
-      const int n = n_blk + wn + 4 * ((64 * j + lane) % kSegs);
+      // (ROWMAX: the lane finishes 4 features of the whole tile, see rowmax_col)
+      const int n = ROWMAX ? n_blk + rowmax_col(lane) : n_blk + wn + 4 * ((64 * j + lane) % kSegs);
       const bool vec = vec_cols && n_blk + kBN <= N;
       auto load4 = [&](const float* v, float dflt) -> f32x4 {
         if (v == nullptr) return f32x4{dflt, dflt, dflt, dflt};
@@ -273,6 +298,122 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
           for (int r = 0; r < 4 && n + r < N; ++r) out[r] = a[r];
         }
       }
+    }
+  } else if constexpr (ROWMAX) {
+    using namespace lanes;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int kRowPitch = kBN * 4 + 16;  // a staged row of the whole tile + its scale, padded across banks
+    static_assert(4 * 32 * kRowPitch <= pp_smem_bytes<TN>(), "pair staging area");
+    uint8_t* pst = smem + (wid & 3) * 32 * kRowPitch;  // shared by waves w and w + 4
+    const int lg = rm.log2g;
+    const float norm = __builtin_ldexpf(1.0f, -(lg / 2));
+    const int col = rowmax_col(lane);
+    const int n_seg = n_blk + col;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // Stage tokens 32 u .. 32 u + 31 of the pair: this wave's 128
+      // features of each row, at column wn (every slice read of every wave
+      // finished before the loop's last barrier; the previous pass over
+      // this area finished before the barrier that ends it).
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 2 * u + h;
+        uint8_t* row_ptr = pst + (16 * h + frow) * kRowPitch;
+#pragma unroll
+        for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (wn + 16 * f + n_lane) * 4) = acc[t][f];
+        if (grp == 0 && fk == 0) *reinterpret_cast<float*>(row_ptr + kBN * 4) = s_row[t];
+      }
+      wait_lds();
+      barrier();  // both halves of every staged row are in place
+      // This wave finishes rows 16 grp .. 16 grp + 15 of the 32.
+#pragma unroll 2
+      for (int pr = 0; pr < 16; ++pr) {
+        const int r = 16 * grp + pr;
+        const acc_t a = *reinterpret_cast<const acc_t*>(pst + r * kRowPitch + col * 4);
+        const float sr = *reinterpret_cast<const float*>(pst + r * kRowPitch + kBN * 4);
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = static_cast<float>(a[q]);
+          const float z = I8 ? fmaf(v, sr * s_col[0][q], b_col[0][q]) : v + b_col[0][q];
+          y[q] = activation<ACT>(z);
+        }
+        const int m = m_blk + wm + 32 * u + r;
+        // the output as stored, the values the next pack reads
+        float hv[4];
+        if constexpr (OUT == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = y[q];
+          if (m < M)
+            *reinterpret_cast<f32x4*>(static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
+                f32x4{y[0], y[1], y[2], y[3]};
+        } else {
+          const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+          hv[0] = static_cast<float>(lo[0]);
+          hv[1] = static_cast<float>(lo[1]);
+          hv[2] = static_cast<float>(hi[0]);
+          hv[3] = static_cast<float>(hi[1]);
+          if (m < M)
+            *reinterpret_cast<u32x2*>(static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+        // Unnormalised rotation, the pack kernel's stages in its order:
+        // digit 0 in registers; digit 1 (lane bits 0-1) as the in-register
+        // butterfly's sum and fused multiply-add over the quad; digits 2
+        // and 3 (Gray-coded lane bits 2-3 and 4-5) as
+        // (a_d - a_{3-d}) + (other pair's sum), the partner a row rotation
+        // by 8 / lane ^ 32 away and the other pair a row rotation by 4 /
+        // lane ^ 16 away.
+        bfly4(hv[0], hv[1], hv[2], hv[3]);
+        if (lg >= 4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = hv[q];
+            const float pq = x + dpp<kQuadXor1>(x);
+            const float s4 = pq + dpp<kQuadXor2>(pq);
+            hv[q] = fmaf(-2.f, dpp<kQuadXor3>(x), s4);
+          }
+        }
+        if (lg >= 6) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = hv[q];
+            const float us = x + dpp<kRowRor8>(x);
+            hv[q] = (x - dpp<kRowRor8>(x)) + dpp<kRowRor4>(us);
+          }
+        }
+        if (lg >= 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = hv[q];
+            const float xp = xor32(x);
+            const float us = x + xp;
+            hv[q] = (x - xp) + swz<kSwzXor16>(us);
+          }
+        }
+        // Largest magnitude over the group's G / 4 lanes (a quad, a row of
+        // 16, or the wavefront; bit patterns of non-negative values order
+        // like unsigned integers).
+        uint32_t bits = as_u(fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3]))));
+        if (lg >= 8) {
+          bits = wave_max_bits(bits);
+        } else {
+          if (lg >= 4) {
+            bits = max(bits, dpp_u<kQuadXor1>(bits));
+            bits = max(bits, dpp_u<kQuadXor2>(bits));
+          }
+          if (lg >= 6) {
+            bits = max(bits, dpp_u<kRowRor4>(bits));
+            bits = max(bits, dpp_u<kRowRor8>(bits));
+          }
+        }
+        if (m < M && (lane & ((1 << (lg - 2)) - 1)) == 0)
+          rm.out[static_cast<int64_t>(m) * rm.ld + (n_seg >> lg)] = as_f(bits) * norm;
+      }
+      barrier();  // every read of this area is done before it is staged again
     }
   } else {
     // Per 32 tokens (two 16-token tiles): the raw accumulators go to a
@@ -393,10 +534,11 @@ inline int choose_tn_pp(int64_t M, int64_t cols) {
   return best;
 }
 
-template <bool I8, int OUT, int TN, int ACT>
+template <bool I8, int OUT, int TN, int ACT, bool ROWMAX = false>
 hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi,
-                           int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream) {
-  auto kern = gemm_pp_kernel<I8, OUT, TN, ACT>;
+                           int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream,
+                           const RowmaxArgs& rm = RowmaxArgs{nullptr, 0, 0}) {
+  auto kern = gemm_pp_kernel<I8, OUT, TN, ACT, ROWMAX>;
   constexpr int kSmem = pp_smem_bytes<TN>();
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), kSmem, lds_set);
@@ -410,7 +552,7 @@ hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int6
   const bool vec_out = (reinterpret_cast<uintptr_t>(C) % (4 * out_elt)) == 0 && ldc % 4 == 0;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(kPPThreads), kSmem, stream, A, lda, B,
                      ldb, epi, static_cast<int>(M), static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m,
-                     tiles_n, vec_cols, vec_out);
+                     tiles_n, vec_cols, vec_out, rm);
   return hipGetLastError();
 }
 
@@ -425,6 +567,17 @@ hipError_t launch_gemm_pp(const uint8_t* A, int64_t lda, const uint8_t* B, int64
     case 3: return launch_pp_typed<I8, OUT, 3, ACT>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
     default: return launch_pp_typed<I8, OUT, 4, ACT>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream);
   }
+}
+
+// The linear with an activation and the next layer's per-group maxima
+// (ROWMAX): always 256-wide tiles; the caller guarantees N % 256 == 0,
+// G = 2^log2g with log2g in {2, 4, 6, 8}, whole 128-byte K slices and
+// output rows aligned for 4-element stores.
+template <int OUT, int ACT>
+hipError_t launch_gemm_pp_rowmax(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi,
+                                 int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, const RowmaxArgs& rm,
+                                 hipStream_t stream) {
+  return launch_pp_typed<true, OUT, 4, ACT, true>(A, lda, B, ldb, epi, M, N, Kb, C, ldc, stream, rm);
 }
 
 }  // namespace

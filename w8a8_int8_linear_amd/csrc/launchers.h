@@ -53,6 +53,24 @@ hipError_t launch_gemm_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int
                               int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
                               hipStream_t stream);
 
+// launch_gemm_i8_act that also writes, for the next layer's pack, the
+// largest magnitude of every G-group (G = 2^log2g, log2g in {2, 4, 6, 8}) of
+// each output row (as stored) after the regular rotation R_G:
+// rowmax [M, ldm] fp32.  Needs N % 256 == 0, K % 128 == 0, C aligned for
+// 4-element stores (ldc % 4 == 0).
+hipError_t launch_gemm_i8_act_rowmax(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
+                                     const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K,
+                                     void* C, Elt out, int64_t ldc, float* rowmax, int64_t ldm, int log2g,
+                                     hipStream_t stream);
+
+// The pack of rows of X whose per-group maxima of the rotated values are
+// given (pmax [rows, ldp], as launch_gemm_i8_act_rowmax writes them): int8
+// codes and scales, regular kind, log2G in {2, 4, 6, 8}.  The same bits as
+// launch_pack_rows for maxima computed with the same operations.
+hipError_t launch_pack_rows_prescaled(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
+                                      const float* pmax, int64_t ldp, int8_t* q, int64_t ldq, float* scale,
+                                      hipStream_t stream);
+
 // Gated pair sharing the packed activation A:
 //   Y = act(A Bg^T sa sbg + biasg) * (A Bu^T sa sbu + biasu)
 // `act` is GeluErf or GeluTanh and `out` F32 or BF16.

@@ -43,6 +43,7 @@
 
 #include <type_traits>
 
+#include "lanes.h"
 #include "launchers.h"
 
 namespace convrot {
@@ -51,52 +52,10 @@ namespace {
 constexpr int kChunk = 16;
 constexpr int kMaxThreads = 1024;
 
-// DPP control words.
-constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kQuadXor3 = 0x1B;  // quad_perm [3,2,1,0]
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;  // lane ^ 8 within a row of 16
-// ds_swizzle bit-mask mode: lane' = lane ^ xor_mask within 32 lanes.
-constexpr int kSwzXor4 = 0x1F | (4 << 10);
-constexpr int kSwzXor16 = 0x1F | (16 << 10);
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
-__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-template <int PATTERN>
-__device__ __forceinline__ float swz(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), PATTERN));
-}
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
-// Value held by lane ^ MASK (MASK a power of two below 64).
-template <int MASK>
-__device__ __forceinline__ float lane_xor(float x) {
-  if constexpr (MASK == 1) return dpp<kQuadXor1>(x);
-  else if constexpr (MASK == 2) return dpp<kQuadXor2>(x);
-  else if constexpr (MASK == 4) return swz<kSwzXor4>(x);
-  else if constexpr (MASK == 8) return dpp<kRowRor8>(x);
-  else if constexpr (MASK == 16) return swz<kSwzXor16>(x);
-  else return xor32(x);
-}
-
-// Unnormalised radix-4 butterfly (2 H4) on four registers.
-__device__ __forceinline__ void bfly4(float& a0, float& a1, float& a2, float& a3) {
-  const float s = (a0 + a1) + (a2 + a3);
-  const float b0 = fmaf(-2.f, a3, s);
-  const float b1 = fmaf(-2.f, a2, s);
-  const float b2 = fmaf(-2.f, a1, s);
-  const float b3 = fmaf(-2.f, a0, s);
-  a0 = b0; a1 = b1; a2 = b2; a3 = b3;
-}
+using namespace lanes;
 
 // Radix-4 butterfly whose digit lives in lane bits (2k, 2k+1).
 // k = 0: identity digit order within a quad, partner at lane ^ 3.
@@ -209,31 +168,19 @@ __device__ __forceinline__ uint32_t quant8_nibbles(const float* v, float inv) {
   return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
 }
 
-// Maximum over the wavefront of non-negative values.  For those the IEEE
-// bit patterns order like unsigned integers, so the reduction runs on the
-// bits (an unsigned max takes its lane exchange as a DPP operand and needs
-// none of the NaN canonicalisation a float max would add at every step).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ uint32_t wave_max_bits(uint32_t m) {
-  m = max(m, dpp_u<kQuadXor1>(m));
-  m = max(m, dpp_u<kQuadXor2>(m));
-  m = max(m, dpp_u<kRowRor4>(m));
-  m = max(m, dpp_u<kRowRor8>(m));
-  m = max(m, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(m), kSwzXor16)));
-  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
-  return m;
-}
-
 // QMODE: 0 rotation only (fp32 rows to xrot), 1 int8 codes, 2 int4 codes
 // (nibble pairs, K / 2 bytes per row, scale = max / 7).
-template <typename InT, int LOG2G, bool RAND, int QMODE, int CPT>
+// PRE (int8 codes, regular kind): the row maximum comes from `pmax`
+// [rows, ldp], the largest magnitude of every G-group of the row's rotated
+// values as a producing layer's epilogue computed it with the same
+// operations (lanes.h); every wavefront takes the maximum of those K / G
+// values itself, so the row needs no exchange between wavefronts.
+template <typename InT, int LOG2G, bool RAND, int QMODE, int CPT, bool PRE = false>
 __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     const InT* __restrict__ X, int64_t ldx, int K, const int8_t* __restrict__ signs,
     int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
-    float* __restrict__ xrot, int64_t ldr) {
+    float* __restrict__ xrot, int64_t ldr, const float* __restrict__ pmax, int64_t ldp) {
+  static_assert(!PRE || (QMODE == 1 && !RAND), "given group maxima: int8 codes of the regular kind");
   constexpr int G = 1 << LOG2G;
   constexpr int L = G >= kChunk ? G / kChunk : 1;  // lanes per group
   static_assert(L <= 64, "a group must fit in one wavefront");
@@ -246,6 +193,18 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
   const int T = blockDim.x;
   const int lane = tid & 63;
   const InT* xrow = X + static_cast<int64_t>(row) * ldx;
+
+  // Given group maxima: the row's maximum of them, requested before the
+  // row itself so that the two loads overlap (one value live, not the row).
+  uint32_t pre_bits = 0;
+  if constexpr (PRE) {
+    // through a buffer resource sized to the row's K / G maxima: reads past
+    // the end return 0, so the loop is uniform and needs no lane test
+    const int ngroups = K >> LOG2G;
+    const __amdgpu_buffer_rsrc_t pr = row_rsrc(pmax + static_cast<int64_t>(row) * ldp, 4 * ngroups);
+    for (int g0 = 0; g0 < ngroups; g0 += 64)
+      pre_bits = max(pre_bits, static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(pr, 4 * (g0 + lane), 0, 0)));
+  }
 
   const __amdgpu_buffer_rsrc_t xr = row_rsrc(xrow, K * static_cast<int>(sizeof(InT)));
   float v[CPT][kChunk];
@@ -347,24 +306,43 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     }
     return;
   } else {
-    float m = 0.f;
+    float amax_u;
+    if constexpr (PRE) {
+      // The given maxima are of the normalised values; norm is a power of
+      // two, so dividing it out again is exact.  The lane's own maximum is
+      // still formed (and kept by an empty asm use): without a use of every
+      // rotated value right after the rotation, the compiler interleaves
+      // the rotation with the quantisation and four chunks per thread no
+      // longer fit the registers of a 1024-thread workgroup (measured: 75
+      // spilled registers and a 4x slower launch).
+      float m = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+      for (int c = 0; c < CPT; ++c) {
 #pragma unroll
-      for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+        for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+      }
+      asm volatile("" ::"v"(m));
+      amax_u = as_f(wave_max_bits(pre_bits)) / norm;
+    } else {
+      float m = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+        for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+      }
+      // Every lane ends with its wavefront's maximum; rows of several
+      // wavefronts combine theirs through LDS (uniform branch: T is the
+      // workgroup size).
+      uint32_t amax_bits = wave_max_bits(as_u(m));
+      const int nwaves = T >> 6;
+      if (nwaves > 1) {
+        if (lane == 0) wave_amax[tid >> 6] = amax_bits;
+        __syncthreads();
+        amax_bits = wave_amax[0];
+        for (int w = 1; w < nwaves; ++w) amax_bits = max(amax_bits, wave_amax[w]);
+      }
+      amax_u = as_f(amax_bits);
     }
-    // Every lane ends with its wavefront's maximum; rows of several
-    // wavefronts combine theirs through LDS (uniform branch: T is the
-    // workgroup size).
-    uint32_t amax_bits = wave_max_bits(as_u(m));
-    const int nwaves = T >> 6;
-    if (nwaves > 1) {
-      if (lane == 0) wave_amax[tid >> 6] = amax_bits;
-      __syncthreads();
-      amax_bits = wave_amax[0];
-      for (int w = 1; w < nwaves; ++w) amax_bits = max(amax_bits, wave_amax[w]);
-    }
-    const float amax_u = as_f(amax_bits);
 
     // Unnormalised codes: y_u * (qmax / amax_u) == y / s exactly up to the
     // rounding of the reciprocal; all-zero rows give inv = 0 and codes 0.
@@ -395,10 +373,10 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
   }
 }
 
-template <typename InT, int LOG2G, bool RAND, int QMODE>
+template <typename InT, int LOG2G, bool RAND, int QMODE, bool PRE = false>
 hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, const int8_t* signs,
                         int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
-                        hipStream_t stream) {
+                        hipStream_t stream, const float* pmax = nullptr, int64_t ldp = 0) {
   const int64_t nvt = K / kChunk;  // chunks in a row
   // Chunks per thread: more of them spread the per-wavefront fixed work (the
   // reductions, the scale division, addressing) over more elements; take 2
@@ -414,16 +392,16 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
   const InT* x = static_cast<const InT*>(X);
   switch (cpt) {
     case 1:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 1>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 1, PRE>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
       break;
     case 2:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 2>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 2, PRE>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
       break;
     case 4:
-      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 4>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr);
+      hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 4, PRE>), grid, block, 0, stream, x, ldx,
+                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
       break;
     default:
       return hipErrorInvalidValue;  // K above 64 * 1024 is rejected by the caller
@@ -481,7 +459,33 @@ hipError_t dispatch_input(Elt xdt, int log2G, RotKind kind, const void* X, int64
   return dispatch_kind<float, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
 }
 
+template <typename InT>
+hipError_t dispatch_prescaled(int log2G, const void* X, int64_t rows, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                              float* scale, const float* pmax, int64_t ldp, hipStream_t stream) {
+#define CONVROT_PRE_CASE(LG)                                                                                 \
+  case LG:                                                                                                   \
+    return dispatch_cpt<InT, LG, false, 1, true>(X, rows, K, ldx, nullptr, q, ldq, scale, nullptr, 0, stream, \
+                                                 pmax, ldp);
+  switch (log2G) {
+    CONVROT_PRE_CASE(2)
+    CONVROT_PRE_CASE(4)
+    CONVROT_PRE_CASE(6)
+    CONVROT_PRE_CASE(8)
+    default: return hipErrorInvalidValue;  // G = 1024 cannot come from a 256-wide producing tile
+  }
+#undef CONVROT_PRE_CASE
+}
+
 }  // namespace
+
+hipError_t launch_pack_rows_prescaled(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
+                                      const float* pmax, int64_t ldp, int8_t* q, int64_t ldq, float* scale,
+                                      hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (xdt == Elt::BF16)
+    return dispatch_prescaled<uint16_t>(log2G, X, rows, K, ldx, q, ldq, scale, pmax, ldp, stream);
+  return dispatch_prescaled<float>(log2G, X, rows, K, ldx, q, ldq, scale, pmax, ldp, stream);
+}
 
 hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
                             RotKind kind, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
