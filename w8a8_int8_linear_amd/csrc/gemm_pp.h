@@ -102,11 +102,6 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
   using Op = Mfma<I8>;
   using acc_t = typename Op::acc_t;
 
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m_blk = tm * kBM;
-  const int n_blk = tn * kBN;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -115,35 +110,50 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
   const int wn = grp * kWN;            // features of the wave within the tile
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);
   const int grp_u = wid_u >> 2;
+  const int total = tiles_m * tiles_n;
+  const int nk = Kb / kBK;
 
   // Transfers: instruction i of wave w fills 1 KiB block w + 8 i of a slice
   // (8 rows; lane l writes physical chunk l % 8 of row l / 8, which holds
   // logical chunk (l % 8) ^ (l / 8)).  Rows past the matrix edge re-read
   // the last row; their results are never stored.
   const int dma_ch = (lane & 7) ^ (lane >> 3);
-  uint32_t off_a[kDmaA], off_b[kDmaB];
-#pragma unroll
-  for (int i = 0; i < kDmaA; ++i) {
-    const int row = 8 * (wid + 8 * i) + (lane >> 3);
-    off_a[i] = static_cast<uint32_t>(min(row, M - m_blk - 1)) * static_cast<uint32_t>(lda) + dma_ch * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < kDmaB; ++i) {
-    const int row = 8 * (wid + 8 * i) + (lane >> 3);
-    off_b[i] = static_cast<uint32_t>(min(row, N - n_blk - 1)) * static_cast<uint32_t>(ldb) + dma_ch * 16;
-  }
-  const uint8_t* a_tile = A + static_cast<int64_t>(m_blk) * lda;
-  const uint8_t* b_tile = B + static_cast<int64_t>(n_blk) * ldb;
-  auto dma_a = [&](int slice, int buf) {
-    const uint8_t* g = a_tile + slice * kBK;
-#pragma unroll
-    for (int i = 0; i < kDmaA; ++i) dma16(g + off_a[i], smem + buf * kATileBytes + (wid_u + 8 * i) * 1024);
+  // Per-tile state: the tile's corner, the operand panels and each lane's
+  // transfer offsets within them.
+  struct Tile {
+    int m_blk, n_blk;
+    const uint8_t* a;
+    const uint8_t* b;
+    uint32_t off_a[kDmaA], off_b[kDmaB];
   };
-  auto dma_b = [&](int slice, int buf) {
-    const uint8_t* g = b_tile + slice * kBK;
+  auto tile_at = [&](int id, Tile& T) {
+    int tm, tn;
+    tile_coords(id, tiles_m, tiles_n, tm, tn);
+    T.m_blk = tm * kBM;
+    T.n_blk = tn * kBN;
+    T.a = A + static_cast<int64_t>(T.m_blk) * lda;
+    T.b = B + static_cast<int64_t>(T.n_blk) * ldb;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) {
+      const int row = 8 * (wid + 8 * i) + (lane >> 3);
+      T.off_a[i] = static_cast<uint32_t>(min(row, M - T.m_blk - 1)) * static_cast<uint32_t>(lda) + dma_ch * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+      const int row = 8 * (wid + 8 * i) + (lane >> 3);
+      T.off_b[i] = static_cast<uint32_t>(min(row, N - T.n_blk - 1)) * static_cast<uint32_t>(ldb) + dma_ch * 16;
+    }
+  };
+  auto dma_a = [&](const Tile& T, int slice, int buf) {
+    const uint8_t* g = T.a + slice * kBK;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) dma16(g + T.off_a[i], smem + buf * kATileBytes + (wid_u + 8 * i) * 1024);
+  };
+  auto dma_b = [&](const Tile& T, int slice, int buf) {
+    const uint8_t* g = T.b + slice * kBK;
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
-      dma16(g + off_b[i], smem + kBBase + buf * kBTileBytes + (wid_u + 8 * i) * 1024);
+      dma16(g + T.off_b[i], smem + kBBase + buf * kBTileBytes + (wid_u + 8 * i) * 1024);
   };
 
   // Fragment reads: lane l takes row l % 16 of a 16-row tile and 16-byte
@@ -164,11 +174,13 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
 
   constexpr int kTF = 2 * TN;  // 16-feature tiles per wave
   acc_t acc[4][kTF];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int f = 0; f < kTF; ++f) acc[t][f] = acc_t{};
-  pad<5>();  // the zeroing is VALU work read by the first MFMAs
+      for (int f = 0; f < kTF; ++f) acc[t][f] = acc_t{};
+    pad<5>();  // the zeroing is VALU work read by the first MFMAs
+  };
 
   // One fragment set: a wave reads it in a memory phase and consumes it in
   // the next phase; the overlap comes from the other wave on the SIMD.
@@ -201,311 +213,372 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     keep_live(fb);
   };
 
-  // Epilogue operands, requested before the main loop so that their latency
-  // hides behind it.  Per lane: the row scale of its four tokens (MFMA
-  // layout, token = l % 16 of each 16-token tile), and the column scales and
-  // biases of the 4-feature output segments it finishes (row layout, see
-  // the epilogue).
+  // Epilogue operands of a tile, requested well before its epilogue (the
+  // first tile's before its main loop, every later tile's before the
+  // previous tile's epilogue).  Per lane: the row scale of its four tokens
+  // (MFMA layout, token = l % 16 of each 16-token tile), and the column
+  // scales and biases of the 4-feature output segments it finishes (row
+  // layout, see the epilogue).
   constexpr int kSegs = kWN / 4;                       // 4-feature segments per wave row
   constexpr int kLaneSegs = kSegs / gcd_pow2_64(kSegs);  // distinct segments per lane
-  float s_row[4] = {1.f, 1.f, 1.f, 1.f};
-  f32x4 s_col[kLaneSegs], b_col[kLaneSegs];
-  if constexpr (OUT != 2) {
-    if constexpr (I8) {
+  struct Scales {
+    float row[4];
+    f32x4 col[kLaneSegs], bias[kLaneSegs];
+  };
+  auto load_scales = [&](const Tile& T, Scales& S) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s_row[t] = epi.sa[min(m_blk + wm + 16 * t + frow, M - 1)];
+    for (int t = 0; t < 4; ++t) S.row[t] = 1.f;
+    if constexpr (OUT != 2) {
+      if constexpr (I8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S.row[t] = epi.sa[min(T.m_blk + wm + 16 * t + frow, M - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kLaneSegs; ++j) {
+        // (ROWMAX: the lane finishes 4 features of the whole tile, see rowmax_col)
+        const int n = ROWMAX ? T.n_blk + rowmax_col(lane) : T.n_blk + wn + 4 * ((64 * j + lane) % kSegs);
+        const bool vec = vec_cols && T.n_blk + kBN <= N;
+        auto load4 = [&](const float* v, float dflt) -> f32x4 {
+          if (v == nullptr) return f32x4{dflt, dflt, dflt, dflt};
+          if (vec) return *reinterpret_cast<const f32x4*>(v + n);
+          f32x4 r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = v[min(n + i, N - 1)];
+          return r;
+        };
+        S.col[j] = I8 ? load4(epi.sb, 1.f) : f32x4{1.f, 1.f, 1.f, 1.f};
+        S.bias[j] = load4(epi.bias, 0.f);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < kLaneSegs; ++j) {
-      // (ROWMAX: the lane finishes 4 features of the whole tile, see rowmax_col)
-      const int n = ROWMAX ? n_blk + rowmax_col(lane) : n_blk + wn + 4 * ((64 * j + lane) % kSegs);
-      const bool vec = vec_cols && n_blk + kBN <= N;
-      auto load4 = [&](const float* v, float dflt) -> f32x4 {
-        if (v == nullptr) return f32x4{dflt, dflt, dflt, dflt};
-        if (vec) return *reinterpret_cast<const f32x4*>(v + n);
-        f32x4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = v[min(n + i, N - 1)];
-        return r;
-      };
-      s_col[j] = I8 ? load4(epi.sb, 1.f) : f32x4{1.f, 1.f, 1.f, 1.f};
-      b_col[j] = load4(epi.bias, 0.f);
-    }
-  }
+  };
 
-  const int nk = Kb / kBK;
-  dma_a(0, 0);
-  dma_b(0, 0);
-  if (nk > 1) dma_a(1, 1);
+  // Persistent walk: this workgroup takes tiles blockIdx.x, + gridDim.x, ...
+  // of the XCD-ordered list (a grid of one workgroup per tile runs the body
+  // once).  Before a tile's epilogue the next tile's scales and first three
+  // slices (A 0, A 1 and B 0, buffers no wave reads any more once the main
+  // loop has passed its last barrier) are requested, so their latency hides
+  // behind the epilogue, whose staging uses A buffer 2 and B buffer 1 only.
+  // The ROWMAX epilogue stages through most of LDS, and the raw int32
+  // output (a checking mode) would spill registers holding the next tile's
+  // state; both take one tile per workgroup.
+  constexpr bool kPrefetch = !ROWMAX && OUT != 2;
+  int tile = blockIdx.x;
+  Tile cur;
+  tile_at(tile, cur);
+  Scales sc;
+  load_scales(cur, sc);
+  zero_acc();
+  dma_a(cur, 0, 0);
+  dma_b(cur, 0, 0);
+  if (nk > 1) dma_a(cur, 1, 1);
   if (nk > 1) wait_vm<kDmaA>(); else wait_vm<0>();
   barrier();
   if (grp_u == 1) barrier();  // the second group runs one phase behind
 
-  int p = 0;
-  int a_cur = 0;  // p % 3
-  do {
-    const int b_cur = p & 1;
-    const int a_next = a_cur == 2 ? 0 : a_cur + 1;
-    const int a_after = a_next == 2 ? 0 : a_next + 1;  // (p + 2) % 3
-    // memory phase: fragments of step 0 of slice p, then the B part of slice
-    // p + 1 (LDS reads queued behind transfers wait for them; in this order
-    // the transfers issue while the reads are in flight)
-    read_step(0, a_cur, b_cur);
-    if (p + 1 < nk) dma_b(p + 1, b_cur ^ 1);
-    wait_lds();
-    barrier();
-    compute_step();
-    barrier();
-    // memory phase: fragments of step 1 of slice p, then the A part of slice
-    // p + 2; every transfer but that A part must have landed before the
-    // barrier
-    read_step(1, a_cur, b_cur);
-    if (p + 2 < nk) dma_a(p + 2, a_after);
-    if (p + 2 < nk) wait_vm<kDmaA>(); else wait_vm<0>();
-    wait_lds();
-    barrier();
-    compute_step();
-    if (grp_u == 0 || p + 1 < nk) barrier();
-    a_cur = a_next;
-    ++p;
-  } while (p < nk);
-
-  // MFMA results are read below by ordinary instructions: wait out the
-  // longest MFMA write latency, then redefine every accumulator so no copy
-  // of one can be placed before the padding.
-  pad<24>();
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int f = 0; f < kTF; ++f) touch_acc(acc[t][f]);
-
-  // Epilogue.  Lane l holds, for tile (t, f), token m = m0 + 16 t + l % 16
-  // and features n = n0 + 16 f + 4 (l / 16) + r, r = 0..3.
-  const int n_lane = 4 * fk;
-  if constexpr (OUT == 2) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int m = m_blk + wm + 16 * t + frow;
-      if (m >= M) continue;
-#pragma unroll
-      for (int f = 0; f < kTF; ++f) {
-        const int n = n_blk + wn + 16 * f + n_lane;
-        int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
-        const i32x4 a = acc[t][f];
-        if (n + 3 < N && vec_ok(out)) {
-          *reinterpret_cast<i32x4*>(out) = a;
-        } else {
-          for (int r = 0; r < 4 && n + r < N; ++r) out[r] = a[r];
-        }
-      }
-    }
-  } else if constexpr (ROWMAX) {
-    using namespace lanes;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    constexpr int kRowPitch = kBN * 4 + 16;  // a staged row of the whole tile + its scale, padded across banks
-    static_assert(4 * 32 * kRowPitch <= pp_smem_bytes<TN>(), "pair staging area");
-    uint8_t* pst = smem + (wid & 3) * 32 * kRowPitch;  // shared by waves w and w + 4
-    const int lg = rm.log2g;
-    const float norm = __builtin_ldexpf(1.0f, -(lg / 2));
-    const int col = rowmax_col(lane);
-    const int n_seg = n_blk + col;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // Stage tokens 32 u .. 32 u + 31 of the pair: this wave's 128
-      // features of each row, at column wn (every slice read of every wave
-      // finished before the loop's last barrier; the previous pass over
-      // this area finished before the barrier that ends it).
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 2 * u + h;
-        uint8_t* row_ptr = pst + (16 * h + frow) * kRowPitch;
-#pragma unroll
-        for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (wn + 16 * f + n_lane) * 4) = acc[t][f];
-        if (grp == 0 && fk == 0) *reinterpret_cast<float*>(row_ptr + kBN * 4) = s_row[t];
-      }
+  while (true) {
+    int p = 0;
+    int a_cur = 0;  // p % 3
+    do {
+      const int b_cur = p & 1;
+      const int a_next = a_cur == 2 ? 0 : a_cur + 1;
+      const int a_after = a_next == 2 ? 0 : a_next + 1;  // (p + 2) % 3
+      // memory phase: fragments of step 0 of slice p, then the B part of
+      // slice p + 1 (LDS reads queued behind transfers wait for them; in
+      // this order the transfers issue while the reads are in flight)
+      read_step(0, a_cur, b_cur);
+      if (p + 1 < nk) dma_b(cur, p + 1, b_cur ^ 1);
       wait_lds();
-      barrier();  // both halves of every staged row are in place
-      // This wave finishes rows 16 grp .. 16 grp + 15 of the 32.
-#pragma unroll 2
-      for (int pr = 0; pr < 16; ++pr) {
-        const int r = 16 * grp + pr;
-        const acc_t a = *reinterpret_cast<const acc_t*>(pst + r * kRowPitch + col * 4);
-        const float sr = *reinterpret_cast<const float*>(pst + r * kRowPitch + kBN * 4);
-        float y[4];
+      barrier();
+      compute_step();
+      barrier();
+      // memory phase: fragments of step 1 of slice p, then the A part of
+      // slice p + 2; every transfer but that A part must have landed before
+      // the barrier
+      read_step(1, a_cur, b_cur);
+      if (p + 2 < nk) dma_a(cur, p + 2, a_after);
+      if (p + 2 < nk) wait_vm<kDmaA>(); else wait_vm<0>();
+      wait_lds();
+      barrier();
+      compute_step();
+      if (grp_u == 0 || p + 1 < nk) barrier();
+      a_cur = a_next;
+      ++p;
+    } while (p < nk);
+
+    // MFMA results are read below by ordinary instructions: wait out the
+    // longest MFMA write latency, then redefine every accumulator so no copy
+    // of one can be placed before the padding.
+    pad<24>();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = static_cast<float>(a[q]);
-          const float z = I8 ? fmaf(v, sr * s_col[0][q], b_col[0][q]) : v + b_col[0][q];
-          y[q] = activation<ACT>(z);
-        }
-        const int m = m_blk + wm + 32 * u + r;
-        // the output as stored, the values the next pack reads
-        float hv[4];
-        if constexpr (OUT == 0) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = y[q];
-          if (m < M)
-            *reinterpret_cast<f32x4*>(static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
-                f32x4{y[0], y[1], y[2], y[3]};
-        } else {
-          const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
-          const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
-          hv[0] = static_cast<float>(lo[0]);
-          hv[1] = static_cast<float>(lo[1]);
-          hv[2] = static_cast<float>(hi[0]);
-          hv[3] = static_cast<float>(hi[1]);
-          if (m < M)
-            *reinterpret_cast<u32x2*>(static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
-                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        }
-        // Unnormalised rotation, the pack kernel's stages in its order:
-        // digit 0 in registers; digit 1 (lane bits 0-1) as the in-register
-        // butterfly's sum and fused multiply-add over the quad; digits 2
-        // and 3 (Gray-coded lane bits 2-3 and 4-5) as
-        // (a_d - a_{3-d}) + (other pair's sum), the partner a row rotation
-        // by 8 / lane ^ 32 away and the other pair a row rotation by 4 /
-        // lane ^ 16 away.
-        bfly4(hv[0], hv[1], hv[2], hv[3]);
-        if (lg >= 4) {
+      for (int f = 0; f < kTF; ++f) touch_acc(acc[t][f]);
+
+    const int next = tile + static_cast<int>(gridDim.x);
+    const bool more = kPrefetch && next < total;  // uniform
+    Tile nxt = cur;
+    Scales sc_next = sc;
+    if (more) {
+      tile_at(next, nxt);
+      load_scales(nxt, sc_next);
+      dma_a(nxt, 0, 0);
+      dma_b(nxt, 0, 0);
+      if (nk > 1) dma_a(nxt, 1, 1);
+    }
+
+    const int m_blk = cur.m_blk, n_blk = cur.n_blk;
+    const float* s_row = sc.row;
+    const f32x4* s_col = sc.col;
+    const f32x4* b_col = sc.bias;
+    // Epilogue.  Lane l holds, for tile (t, f), token m = m0 + 16 t + l % 16
+    // and features n = n0 + 16 f + 4 (l / 16) + r, r = 0..3.
+    const int n_lane = 4 * fk;
+    if constexpr (OUT == 2) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x = hv[q];
-            const float pq = x + dpp<kQuadXor1>(x);
-            const float s4 = pq + dpp<kQuadXor2>(pq);
-            hv[q] = fmaf(-2.f, dpp<kQuadXor3>(x), s4);
+      for (int t = 0; t < 4; ++t) {
+        const int m = m_blk + wm + 16 * t + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int f = 0; f < kTF; ++f) {
+          const int n = n_blk + wn + 16 * f + n_lane;
+          int32_t* out = static_cast<int32_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+          const i32x4 a = acc[t][f];
+          if (n + 3 < N && vec_ok(out)) {
+            *reinterpret_cast<i32x4*>(out) = a;
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) out[r] = a[r];
           }
         }
-        if (lg >= 6) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x = hv[q];
-            const float us = x + dpp<kRowRor8>(x);
-            hv[q] = (x - dpp<kRowRor8>(x)) + dpp<kRowRor4>(us);
-          }
+      }
+    } else if constexpr (ROWMAX) {
+      using namespace lanes;
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      constexpr int kRowPitch = kBN * 4 + 16;  // a staged row of the whole tile + its scale, padded across banks
+      static_assert(4 * 32 * kRowPitch <= pp_smem_bytes<TN>(), "pair staging area");
+      uint8_t* pst = smem + (wid & 3) * 32 * kRowPitch;  // shared by waves w and w + 4
+      const int lg = rm.log2g;
+      const float norm = __builtin_ldexpf(1.0f, -(lg / 2));
+      const int col = rowmax_col(lane);
+      const int n_seg = n_blk + col;
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // Stage tokens 32 u .. 32 u + 31 of the pair: this wave's 128
+        // features of each row, at column wn (every slice read of every wave
+        // finished before the loop's last barrier; the previous pass over
+        // this area finished before the barrier that ends it).
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 2 * u + h;
+          uint8_t* row_ptr = pst + (16 * h + frow) * kRowPitch;
+  #pragma unroll
+          for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (wn + 16 * f + n_lane) * 4) = acc[t][f];
+          if (grp == 0 && fk == 0) *reinterpret_cast<float*>(row_ptr + kBN * 4) = s_row[t];
         }
-        if (lg >= 8) {
-#pragma unroll
+        wait_lds();
+        barrier();  // both halves of every staged row are in place
+        // This wave finishes rows 16 grp .. 16 grp + 15 of the 32.
+  #pragma unroll 2
+        for (int pr = 0; pr < 16; ++pr) {
+          const int r = 16 * grp + pr;
+          const acc_t a = *reinterpret_cast<const acc_t*>(pst + r * kRowPitch + col * 4);
+          const float sr = *reinterpret_cast<const float*>(pst + r * kRowPitch + kBN * 4);
+          float y[4];
+  #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float x = hv[q];
-            const float xp = xor32(x);
-            const float us = x + xp;
-            hv[q] = (x - xp) + swz<kSwzXor16>(us);
+            const float v = static_cast<float>(a[q]);
+            const float z = I8 ? fmaf(v, sr * s_col[0][q], b_col[0][q]) : v + b_col[0][q];
+            y[q] = activation<ACT>(z);
           }
-        }
-        // Largest magnitude over the group's G / 4 lanes (a quad, a row of
-        // 16, or the wavefront; bit patterns of non-negative values order
-        // like unsigned integers).
-        uint32_t bits = as_u(fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3]))));
-        if (lg >= 8) {
-          bits = wave_max_bits(bits);
-        } else {
+          const int m = m_blk + wm + 32 * u + r;
+          // the output as stored, the values the next pack reads
+          float hv[4];
+          if constexpr (OUT == 0) {
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) hv[q] = y[q];
+            if (m < M)
+              *reinterpret_cast<f32x4*>(static_cast<float*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
+                  f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+            hv[0] = static_cast<float>(lo[0]);
+            hv[1] = static_cast<float>(lo[1]);
+            hv[2] = static_cast<float>(hi[0]);
+            hv[3] = static_cast<float>(hi[1]);
+            if (m < M)
+              *reinterpret_cast<u32x2*>(static_cast<__bf16*>(C) + static_cast<int64_t>(m) * ldc + n_seg) =
+                  u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+          // Unnormalised rotation, the pack kernel's stages in its order:
+          // digit 0 in registers; digit 1 (lane bits 0-1) as the in-register
+          // butterfly's sum and fused multiply-add over the quad; digits 2
+          // and 3 (Gray-coded lane bits 2-3 and 4-5) as
+          // (a_d - a_{3-d}) + (other pair's sum), the partner a row rotation
+          // by 8 / lane ^ 32 away and the other pair a row rotation by 4 /
+          // lane ^ 16 away.
+          bfly4(hv[0], hv[1], hv[2], hv[3]);
           if (lg >= 4) {
-            bits = max(bits, dpp_u<kQuadXor1>(bits));
-            bits = max(bits, dpp_u<kQuadXor2>(bits));
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x = hv[q];
+              const float pq = x + dpp<kQuadXor1>(x);
+              const float s4 = pq + dpp<kQuadXor2>(pq);
+              hv[q] = fmaf(-2.f, dpp<kQuadXor3>(x), s4);
+            }
           }
           if (lg >= 6) {
-            bits = max(bits, dpp_u<kRowRor4>(bits));
-            bits = max(bits, dpp_u<kRowRor8>(bits));
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x = hv[q];
+              const float us = x + dpp<kRowRor8>(x);
+              hv[q] = (x - dpp<kRowRor8>(x)) + dpp<kRowRor4>(us);
+            }
           }
+          if (lg >= 8) {
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x = hv[q];
+              const float xp = xor32(x);
+              const float us = x + xp;
+              hv[q] = (x - xp) + swz<kSwzXor16>(us);
+            }
+          }
+          // Largest magnitude over the group's G / 4 lanes (a quad, a row of
+          // 16, or the wavefront; bit patterns of non-negative values order
+          // like unsigned integers).
+          uint32_t bits = as_u(fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3]))));
+          if (lg >= 8) {
+            bits = wave_max_bits(bits);
+          } else {
+            if (lg >= 4) {
+              bits = max(bits, dpp_u<kQuadXor1>(bits));
+              bits = max(bits, dpp_u<kQuadXor2>(bits));
+            }
+            if (lg >= 6) {
+              bits = max(bits, dpp_u<kRowRor4>(bits));
+              bits = max(bits, dpp_u<kRowRor8>(bits));
+            }
+          }
+          if (m < M && (lane & ((1 << (lg - 2)) - 1)) == 0)
+            rm.out[static_cast<int64_t>(m) * rm.ld + (n_seg >> lg)] = as_f(bits) * norm;
         }
-        if (m < M && (lane & ((1 << (lg - 2)) - 1)) == 0)
-          rm.out[static_cast<int64_t>(m) * rm.ld + (n_seg >> lg)] = as_f(bits) * norm;
+        barrier();  // every read of this area is done before it is staged again
       }
-      barrier();  // every read of this area is done before it is staged again
-    }
-  } else {
-    // Per 32 tokens (two 16-token tiles): the raw accumulators go to a
-    // private LDS area of the wave as rows, with each row's scale in the
-    // row's padding (every slice read finished before the last barrier);
-    // each lane then takes 4-feature segments of those rows, whose column
-    // scale and bias it already holds, converts, finishes them and stores
-    // whole row pieces.  The value is fma(acc, s_x s_w, b), the same
-    // expression in the same precision as the other linear kernels, so the
-    // result bits do not depend on which kernel a shape runs on.
-    using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
-    constexpr int kPitch = kWN * 4 + 16;  // one row of the wave + its scale, padded across banks
-    constexpr int kPasses = 32 * kSegs / 64;
-    static_assert(8 * 32 * kPitch <= pp_smem_bytes<TN>(), "staging area");
-    uint8_t* stage = smem + wid * 32 * kPitch;
-    // Tiles wholly inside the output take a branch-free pass loop (so the
-    // LDS reads of later passes can issue ahead of earlier stores): lane l's
-    // segment and row in pass p repeat with period kLaneSegs, the row
-    // advancing by kRowStep, so a few per-lane bases and uniform strides
-    // give every address.
-    const bool full = vec_out && m_blk + kBM <= M && n_blk + kBN <= N;  // uniform
-    constexpr int kRowStep = 64 * kLaneSegs / kSegs;
-    out_t* lane_base[kLaneSegs];
+    } else {
+      // Per 8 tokens (half a 16-token tile): the raw accumulators go to a
+      // private LDS area of the wave as rows, with each row's scale in the
+      // row's padding (the lanes holding those 8 tokens write, the others
+      // wait); each lane then takes 4-feature segments of those rows, whose
+      // column scale and bias it already holds, converts, finishes them and
+      // stores whole row pieces.  The areas lie in A buffer 2 (waves 0-3)
+      // and B buffer 1 (waves 4-7), which the next tile's first slices do
+      // not use; every slice read finished before the main loop's last
+      // barrier.  The value is fma(acc, s_x s_w, b), the same expression in
+      // the same precision as the other linear kernels, so the result bits
+      // do not depend on which kernel a shape runs on.
+      using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
+      constexpr int kPitch = kWN * 4 + 16;  // one row of the wave + its scale, padded across banks
+      constexpr int kPasses = 8 * kSegs / 64;
+      static_assert((8 * kSegs) % 64 == 0, "whole passes per 8 rows");
+      static_assert(4 * 8 * kPitch <= kATileBytes && 4 * 8 * kPitch <= kBTileBytes, "staging areas");
+      uint8_t* stage = wid_u < 4 ? smem + 2 * kATileBytes + wid_u * 8 * kPitch
+                                 : smem + kBBase + kBTileBytes + (wid_u - 4) * 8 * kPitch;
+      // Tiles wholly inside the output take a branch-free pass loop (so the
+      // LDS reads of later passes can issue ahead of earlier stores): lane
+      // l's segment and row in pass p repeat with period kLaneSegs, the row
+      // advancing by kRowStep, so a few per-lane bases and uniform strides
+      // give every address.
+      const bool full = vec_out && m_blk + kBM <= M && n_blk + kBN <= N;  // uniform
+      constexpr int kRowStep = 64 * kLaneSegs / kSegs;
+      out_t* lane_base[kLaneSegs];
 #pragma unroll
-    for (int j = 0; j < kLaneSegs; ++j) {
-      const int c = 64 * j + lane;
-      lane_base[j] = static_cast<out_t*>(C) + static_cast<int64_t>(m_blk + wm + c / kSegs) * ldc + n_blk + wn +
-                     4 * (c % kSegs);
-    }
-    // Segment of pass p: converted, scaled, biased and activated outputs.
-    auto finish = [&](int p, float y[4]) {
-      const int c = 64 * p + lane;
-      const int row = c / kSegs, seg = c % kSegs;
-      const int j = p % kLaneSegs;
-      const acc_t a = *reinterpret_cast<const acc_t*>(stage + row * kPitch + seg * 16);
-      const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = static_cast<float>(a[r]);
-        const float z = I8 ? fmaf(v, sr * s_col[j][r], b_col[j][r]) : v + b_col[j][r];
-        y[r] = activation<ACT>(z);
+      for (int j = 0; j < kLaneSegs; ++j) {
+        const int c = 64 * j + lane;
+        lane_base[j] = static_cast<out_t*>(C) + static_cast<int64_t>(m_blk + wm + c / kSegs) * ldc + n_blk + wn +
+                       4 * (c % kSegs);
       }
-    };
-    auto store4 = [](out_t* out, const float y[4]) {
-      if constexpr (OUT == 0) {
-        *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
-      } else {
-        // Two pairs, each one packed round-to-nearest-even conversion.
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
-        *reinterpret_cast<u32x2*>(out) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
-    };
+      // Segment of pass p: converted, scaled, biased and activated outputs.
+      auto finish = [&](int p, float y[4]) {
+        const int c = 64 * p + lane;
+        const int row = c / kSegs, seg = c % kSegs;
+        const int j = p % kLaneSegs;
+        const acc_t a = *reinterpret_cast<const acc_t*>(stage + row * kPitch + seg * 16);
+        const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 2 * u + h;
-        uint8_t* row_ptr = stage + (16 * h + frow) * kPitch;
-#pragma unroll
-        for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (16 * f + n_lane) * 4) = acc[t][f];
-        if (fk == 0) *reinterpret_cast<float*>(row_ptr + kWN * 4) = s_row[t];
-      }
-      if (full) {
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-          float y[4];
-          finish(p, y);
-          store4(lane_base[p % kLaneSegs] + static_cast<int64_t>(32 * u + (p / kLaneSegs) * kRowStep) * ldc, y);
+        for (int r = 0; r < 4; ++r) {
+          const float v = static_cast<float>(a[r]);
+          const float z = I8 ? fmaf(v, sr * s_col[j][r], b_col[j][r]) : v + b_col[j][r];
+          y[r] = activation<ACT>(z);
         }
-      } else {
+      };
+      auto store4 = [](out_t* out, const float y[4]) {
+        if constexpr (OUT == 0) {
+          *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+        } else {
+          // Two pairs, each one packed round-to-nearest-even conversion.
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+          *reinterpret_cast<u32x2*>(out) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      };
 #pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-          float y[4];
-          finish(p, y);
-          const int c = 64 * p + lane;
-          const int m = m_blk + wm + 32 * u + c / kSegs;
-          const int n = n_blk + wn + 4 * (c % kSegs);
-          if (m < M) {
-            out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
-            if (vec_out && n + 3 < N) {
-              store4(out, y);
-            } else {
-              for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r0 = 16 * t + 8 * h;  // first token of the 8 within the wave's 64
+          if ((frow >> 3) == h) {
+            uint8_t* row_ptr = stage + (frow & 7) * kPitch;
+#pragma unroll
+            for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (16 * f + n_lane) * 4) = acc[t][f];
+            if (fk == 0) *reinterpret_cast<float*>(row_ptr + kWN * 4) = s_row[t];
+          }
+          if (full) {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+              float y[4];
+              finish(p, y);
+              store4(lane_base[p % kLaneSegs] + static_cast<int64_t>(r0 + (p / kLaneSegs) * kRowStep) * ldc, y);
+            }
+          } else {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+              float y[4];
+              finish(p, y);
+              const int c = 64 * p + lane;
+              const int m = m_blk + wm + r0 + c / kSegs;
+              const int n = n_blk + wn + 4 * (c % kSegs);
+              if (m < M) {
+                out_t* out = static_cast<out_t*>(C) + static_cast<int64_t>(m) * ldc + n;
+                if (vec_out && n + 3 < N) {
+                  store4(out, y);
+                } else {
+                  for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
+                }
+              }
             }
           }
         }
       }
     }
+
+    if (!more) break;
+    // The next tile: its state, zeroed accumulators, and its first slices
+    // landed (each wave waits for its own transfers, which the barrier then
+    // publishes; the wait also covers this tile's stores).  The barrier also
+    // ends every wave's epilogue before the next main loop writes A buffer 2
+    // and B buffer 1 again.
+    tile = next;
+    cur = nxt;
+    sc = sc_next;
+    zero_acc();
+    wait_vm<0>();
+    barrier();
+    if (grp_u == 1) barrier();  // the second group runs one phase behind
   }
 }
 
@@ -545,12 +618,22 @@ hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int6
   if (e != hipSuccess) return e;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + 64 * TN - 1) / (64 * TN));
+  // One workgroup per CU walking the tile list (one workgroup fits a CU);
+  // the ROWMAX epilogue and the raw int32 output take one tile per
+  // workgroup (the kernel does not walk for them).  CONVROT_GEMM_GRID=tiles
+  // launches one workgroup per tile (same-box comparisons only).
+  static const bool one_per_tile = [] {
+    const char* e = std::getenv("CONVROT_GEMM_GRID");
+    return e != nullptr && std::strcmp(e, "tiles") == 0;
+  }();
+  const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
+  const int64_t grid = (ROWMAX || OUT == 2 || one_per_tile) ? tiles : std::min<int64_t>(tiles, num_cus());
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec_cols = al16(epi.sb) && al16(epi.bias);
   // Four consecutive outputs go out as one store when rows keep them aligned.
   const int out_elt = OUT == 1 ? 2 : 4;
   const bool vec_out = (reinterpret_cast<uintptr_t>(C) % (4 * out_elt)) == 0 && ldc % 4 == 0;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(kPPThreads), kSmem, stream, A, lda, B,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kPPThreads), kSmem, stream, A, lda, B,
                      ldb, epi, static_cast<int>(M), static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m,
                      tiles_n, vec_cols, vec_out, rm);
   return hipGetLastError();
