@@ -792,10 +792,12 @@ def main():
 
         mf = probe.mfma_i8(dev)
         cp = probe.copy_gbps(dev)
+        sw = probe.copy_sweep(dev)
         result["ceilings"] = {
             "copy_GBps": cp["GBps"],
             "copy_by_grid": cp["by_grid_per_cu"],
             "torch_copy_GBps": cp["torch_copy_GBps"],
+            "copy_fit": sw,
             "mfma_i8_TOPS": mf["TOPS"],
             "mfma_i8_frac_of_peak": round(mf["TOPS"] / PEAK_I8_TOPS, 4),
             "sclk_GHz_mfma_loop": mf["sclk_GHz"],
@@ -809,9 +811,19 @@ def main():
             roof["frac_of_measured_mfma"] = round(roof["achieved"] / mf["TOPS"], 4)
         else:
             roof["frac_of_copy"] = round(roof["achieved"] / result["ceilings"]["copy_GBps"], 4)
+        def copy_floor_frac(op):
+            # the op's measured time against a streaming copy of its bytes
+            # (fixed cost plus bytes at the fitted bandwidth)
+            best_us = sw["t0_us"] + op.bytes() / (sw["GBps"] * 1e3)
+            return round(best_us / kernels[op.name]["us"], 4)
+
         if "pack_roofline" in result:
             result["pack_roofline"]["frac_of_copy"] = round(result["pack_roofline"]["achieved"] /
                                                             result["ceilings"]["copy_GBps"], 4)
+            pk_op = [op for op in ops if op.name == result["pack_roofline"]["launch"]][0]
+            result["pack_roofline"]["frac_of_sized_copy"] = copy_floor_frac(pk_op)
+        if roof["bound"] == "hbm":
+            roof["frac_of_sized_copy"] = copy_floor_frac(dom)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

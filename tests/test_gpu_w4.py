@@ -213,7 +213,8 @@ def test_small_m_int8_staged_weights(cuda, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(16, 3200, 8192), (5, 6912, 4096), (12, 9000, 5152), (3, 17000, 2080)])
 def test_small_m_int4_staged_weights(cuda, M, N, K):
     """int4 weights staged through LDS in whole lines (waves streaming five
-    or more 128-code units, K % 32 == 0): split K (3200 x 8192), a K tail
+    or more 128-code units, K % 32 == 0): a long K (3200 x 8192; int4 never
+    splits K, so the workspace query returns none), a K tail
     inside a unit with ragged N (9000 x 5152), two tiles per workgroup
     (17000); plain and gated, against the exact accumulator."""
     qx, sx, qg, sw, _ = _operands(M, N, K, 11 * N + K)
@@ -221,8 +222,7 @@ def test_small_m_int4_staged_weights(cuda, M, N, K):
     a = cr.Packed(to_dev(qx, torch.int8), to_dev(sx, torch.float32), 16)
     wg, wu = _w4(qg, sw, 16), _w4(qu, sw, 16)
     assert np.array_equal(to_np(cr.linear_w4(a, wg, out_dtype=torch.int32)), O.int_gemm(qx, qg))
-    ws = cr.linear_workspace("w4", M, N, K, cuda)
-    assert np.array_equal(to_np(cr.linear_w4(a, wg, out_dtype=torch.int32, workspace=ws)), O.int_gemm(qx, qg))
+    assert cr.linear_workspace("w4", M, N, K, cuda) is None
     g64 = O.epilogue64(O.int_gemm(qx, qg), sx, sw)
     u64 = O.epilogue64(O.int_gemm(qx, qu), sx, sw)
     y = to_np(cr.linear_w4_gated(a, wg, wu, act=cr.GELU_TANH, out_dtype=torch.float32))

@@ -489,7 +489,11 @@ SplitPlan split_plan(int64_t N, int64_t kbytes, int sets, bool w4) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = gemv_num_cus();
   const SplitPlan none{1, nunits, 0};
-  if (tiles >= cus) return none;
+  // int4 weights stream half the bytes per K unit, and the second launch
+  // costs more than the split saves (decode down projection, 1152 x 6912,
+  // M = 16, same box: 7.4 us unsplit against 8.6 us split with its
+  // combining launch; int8: 10.1 against 9.3 us).
+  if (w4 || tiles >= cus) return none;
   int64_t splits = std::min<int64_t>((2 * cus + tiles - 1) / tiles, nunits * (unit / kStepBytes) / 8);
   if (splits <= 1) return none;
   const int64_t units = (nunits + splits - 1) / splits;

@@ -109,3 +109,47 @@ def copy_gbps(device: torch.device, mib: int = 1024, reps: int = 5) -> dict:
     out = {"GBps": max(by_grid.values()), "by_grid_per_cu": by_grid, "torch_copy_GBps": timed(lambda: dst.copy_(src))}
     del src, dst
     return out
+
+
+def copy_sweep(device: torch.device, sizes_mib=(4, 16, 64, 256), span_mib: int = 1024, reps: int = 16) -> dict:
+    """Streaming-copy time against size, each size copied ``reps`` times in
+    one HIP graph over consecutive slices of a ``span_mib`` buffer (so the
+    256 MB Infinity Cache cannot serve repeats) and timed with events: the
+    per-launch fixed cost t0 and the streaming bandwidth of the least-squares
+    fit t = t0 + (read + write bytes) / BW.  A kernel moving B bytes cannot
+    beat t0 + B / BW on this GPU."""
+    lib = load()
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    span = span_mib << 20
+    src = torch.ones(span, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(device)
+    pts = []
+    for mib in sizes_mib:
+        nb = mib << 20
+        slots = max(1, span // nb)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                off = (r % slots) * nb
+                if lib.convrot_probe_copy(src.data_ptr() + off, dst.data_ptr() + off, nb, 8 * cus,
+                                          torch.cuda.current_stream(device).cuda_stream) != 0:
+                    raise RuntimeError("convrot_probe_copy failed")
+        g.replay()
+        torch.cuda.synchronize(device)
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize(device)
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        pts.append((2.0 * nb, float(np.median(ts))))
+        del g
+    x = np.array([p[0] for p in pts])
+    y = np.array([p[1] for p in pts])
+    slope, t0 = np.polyfit(x, y, 1)
+    del src, dst
+    return {"t0_us": round(float(t0), 3), "GBps": round(1e-3 / float(slope), 1),
+            "points_us": {f"{int(b / 2 / 2**20)}MiB": round(t, 2) for b, t in pts}}
