@@ -50,8 +50,9 @@ sets, timed with events on its stream and divided by the repeat count.
 consecutive launches (at decode sizes that measures the host's launch cost).
 
 Besides the published peaks the line carries measured ceilings of the GPU it
-ran on: a device copy's GB/s, and the int8 MFMA rate and shader clock of an
-MFMA-only loop on random operands (libconvrot_probe.so).
+ran on: a device copy's GB/s, the fixed cost and bandwidth of streaming
+copies and reads fitted over sizes, and the int8 MFMA rate and shader clock
+of an MFMA-only loop on random operands (libconvrot_probe.so).
 
 Prints one JSON line on stdout; per-kernel details go to stderr.
 """
@@ -793,16 +794,20 @@ def main():
         mf = probe.mfma_i8(dev)
         cp = probe.copy_gbps(dev)
         sw = probe.copy_sweep(dev)
+        rd = probe.read_sweep(dev)
         result["ceilings"] = {
             "copy_GBps": cp["GBps"],
             "copy_by_grid": cp["by_grid_per_cu"],
             "torch_copy_GBps": cp["torch_copy_GBps"],
             "copy_fit": sw,
+            "read_fit": rd,
             "mfma_i8_TOPS": mf["TOPS"],
             "mfma_i8_frac_of_peak": round(mf["TOPS"] / PEAK_I8_TOPS, 4),
             "sclk_GHz_mfma_loop": mf["sclk_GHz"],
             "sclk_GHz_range": [mf["sclk_GHz_min"], mf["sclk_GHz_max"]],
-            "note": "streaming copy of 1 GiB (read + write bytes / s, best of three grid sizes); MFMA-only "
+            "note": "streaming copy of 1 GiB (read + write bytes / s, best of three grid sizes); copy_fit and "
+                    "read_fit: time = t0 + bytes / GBps fitted over graph-replayed copies and reads of 4-256 MiB; "
+                    "MFMA-only "
                     "v_mfma_i32_16x16x64_i8 loop, one workgroup "
                     "per CU, two waves per SIMD, random normal codes; shader clock per CU from s_memtime against "
                     "the 100 MHz s_memrealtime",
@@ -824,6 +829,10 @@ def main():
             result["pack_roofline"]["frac_of_sized_copy"] = copy_floor_frac(pk_op)
         if roof["bound"] == "hbm":
             roof["frac_of_sized_copy"] = copy_floor_frac(dom)
+            # weight streaming is nearly all reads: its floor is a read of
+            # its bytes
+            roof["frac_of_sized_read"] = round((rd["t0_us"] + dom.bytes() / (rd["GBps"] * 1e3)) /
+                                               kernels[dom.name]["us"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

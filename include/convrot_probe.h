@@ -5,7 +5,7 @@
  * They measure what the roofline fractions of the layer's kernels are
  * compared against on the running GPU: the int8 matrix-core rate on random
  * operands with no memory traffic, the shader clock under that load, and
- * the bandwidth of a plain streaming copy.
+ * the bandwidth of a plain streaming copy and of a plain streaming read.
  * Same conventions as convrot.h: device pointers, asynchronous on `stream`,
  * host-side validation before any launch, 0 on success.
  */
@@ -50,6 +50,14 @@ int convrot_probe_mfma_i8(const void* operands, int grid, int iters, uint64_t* s
  * bytes per second).  Returns 0, 1 on a bad argument, 2 when the launch
  * fails. */
 int convrot_probe_copy(const void* src, void* dst, int64_t bytes, int grid, void* stream);
+
+/* Streaming read of `bytes` bytes (a multiple of 16; src 16-byte aligned)
+ * by `grid` workgroups of 256 threads, with the copy's access pattern and no
+ * stores: the bandwidth and per-launch fixed cost a read-dominated kernel
+ * (weight streaming at small M) is bounded by.  `sink` (grid * 256 int32)
+ * is written only when `flag` == 0x5eed (never in use; it keeps the loads
+ * live).  Returns 0, 1 on a bad argument, 2 when the launch fails. */
+int convrot_probe_read(const void* src, int64_t bytes, int grid, int32_t* sink, int flag, void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,14 @@ def test_probe_library_exports_its_header():
     assert f(None, 256, 10, A16, A16B, 0, None) == 1
     assert f(A16, 0, 10, A16, A16B, 0, None) == 1
     assert f(MIS, 256, 10, A16, A16B, 0, None) == 1
+    r = plib.convrot_probe_read
+    assert r(None, 1024, 8, A16, 0, None) == 1
+    assert r(A16, 1000, 8, A16, 0, None) == 1
+    assert r(MIS, 1024, 8, A16, 0, None) == 1
+    assert r(A16, 1024, 0, A16, 0, None) == 1
+    c = plib.convrot_probe_copy
+    assert c(A16, A16, 1000, 8, None) == 1
+    assert c(MIS, A16, 1024, 8, None) == 1
 
 
 def test_abi_version_matches_header(lib):

@@ -117,11 +117,44 @@ struct SplitArgs {
   int steps;
 };
 
+// The epilogue's per-row and per-feature operands of one lane (row
+// m = lane & 15, features n0 + 4 (lane >> 4) + r), loaded by the epilogue
+// wave before its main loop so that they arrive with the first weights
+// instead of after the last MFMA (indexes clamped into the operands; lanes
+// past M or N store nothing).
+template <bool GATED>
+struct EpiIn {
+  float s_row;
+  float sb[4], b[4];
+  float sb2[GATED ? 4 : 1], b2[GATED ? 4 : 1];
+};
+
+template <bool I8, int OUT, bool GATED>
+__device__ __forceinline__ EpiIn<GATED> load_epi(int lane, int n0, const EpiArgs& epi, int M, int N) {
+  EpiIn<GATED> in{};
+  if constexpr (OUT != 2) {
+    const int m = min(lane & 15, M - 1);
+    const int n = n0 + 4 * (lane >> 4);
+    in.s_row = I8 ? epi.sa[m] : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nn = min(n + r, N - 1);
+      in.sb[r] = I8 ? epi.sb[nn] : 1.f;
+      in.b[r] = epi.bias ? epi.bias[nn] : 0.f;
+      if constexpr (GATED) {
+        in.sb2[r] = epi.sb2[nn];
+        in.b2[r] = epi.bias2 ? epi.bias2[nn] : 0.f;
+      }
+    }
+  }
+  return in;
+}
+
 // Epilogue of one 16-feature tile: lane holds output row m = lane & 15 and
 // features n0 + 4 (lane >> 4) + r of the accumulators acc[set].
 template <bool I8, int OUT, int ACT, bool GATED, typename Acc>
-__device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, const EpiArgs& epi, int M, int N,
-                                              void* __restrict__ C, int64_t ldc) {
+__device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, const EpiIn<GATED>& in, int M,
+                                              int N, void* __restrict__ C, int64_t ldc) {
   constexpr int kSets = GATED ? 2 : 1;
   const int m = lane & 15;
   const int n = n0 + 4 * (lane >> 4);
@@ -134,16 +167,13 @@ __device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, 
       for (int r = 0; r < 4 && n + r < N; ++r) out[r] = acc[0][r];
     }
   } else {
-    const float s_row = I8 ? epi.sa[m] : 1.f;
     float y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int nn = min(n + r, N - 1);
-      const float b = epi.bias ? epi.bias[nn] : 0.f;
-      y[r] = I8 ? fmaf(static_cast<float>(acc[0][r]), s_row * epi.sb[nn], b) : static_cast<float>(acc[0][r]) + b;
+      const float b = in.b[r];
+      y[r] = I8 ? fmaf(static_cast<float>(acc[0][r]), in.s_row * in.sb[r], b) : static_cast<float>(acc[0][r]) + b;
       if constexpr (GATED) {
-        const float b2 = epi.bias2 ? epi.bias2[nn] : 0.f;
-        const float u = fmaf(static_cast<float>(acc[kSets - 1][r]), s_row * epi.sb2[nn], b2);
+        const float u = fmaf(static_cast<float>(acc[kSets - 1][r]), in.s_row * in.sb2[r], in.b2[r]);
         y[r] = activation<ACT>(y[r]) * u;
       } else {
         y[r] = activation<ACT>(y[r]);
@@ -220,6 +250,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int u_hi = SPLIT ? min(nunits, u_lo + sp.steps) : nunits;
   const int u_begin = u_lo + wid * per;
   const int u_end = min(u_hi, u_begin + per);
+
+  EpiIn<GATED> epi_in[SPLIT ? 1 : TILES];
+  if (!SPLIT && wid == 0) {
+#pragma unroll
+    for (int i = 0; i < (SPLIT ? 1 : TILES); ++i) epi_in[i] = load_epi<I8, OUT, GATED>(lane, n0 + 16 * i, epi, M, N);
+  }
 
   Acc acc[kSets][TILES];
 #pragma unroll
@@ -423,7 +459,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
       Acc tile[kSets];
 #pragma unroll
       for (int t = 0; t < kSets; ++t) tile[t] = acc[t][i];
-      tile_epilogue<I8, OUT, ACT, GATED>(tile, lane, n0 + 16 * i, epi, M, N, C, ldc);
+      tile_epilogue<I8, OUT, ACT, GATED>(tile, lane, n0 + 16 * i, epi_in[i], M, N, C, ldc);
     }
   }
 }
@@ -437,6 +473,7 @@ __global__ __launch_bounds__(64) void gemv_combine_kernel(EpiArgs epi, int M, in
   constexpr int kSets = GATED ? 2 : 1;
   const int lane = threadIdx.x;
   const i32x4* all = sp.part + static_cast<int64_t>(blockIdx.x) * sp.splits * kSets * 64;
+  const EpiIn<GATED> in = load_epi<I8, OUT, GATED>(lane, static_cast<int>(blockIdx.x) * 16, epi, M, N);
   Acc acc[kSets];
 #pragma unroll
   for (int t = 0; t < kSets; ++t) {
@@ -444,7 +481,7 @@ __global__ __launch_bounds__(64) void gemv_combine_kernel(EpiArgs epi, int M, in
     for (int q = 1; q < sp.splits; ++q) sum += __builtin_bit_cast(Acc, all[(q * kSets + t) * 64 + lane]);
     acc[t] = sum;
   }
-  tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, static_cast<int>(blockIdx.x) * 16, epi, M, N, C, ldc);
+  tile_epilogue<I8, OUT, ACT, GATED>(acc, lane, static_cast<int>(blockIdx.x) * 16, in, M, N, C, ldc);
 }
 
 inline int gemv_num_cus() { return device_cus(); }

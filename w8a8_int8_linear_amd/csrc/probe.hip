@@ -85,7 +85,36 @@ __global__ __launch_bounds__(kCopyThreads) void copy_probe(const i32x4* __restri
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Streaming read: the same access pattern as the copy with no stores; each
+// thread folds its chunks into one word (xor), stored only when `flag` is
+// 0x5eed (never in use), which keeps every load live.
+__global__ __launch_bounds__(kCopyThreads) void read_probe(const i32x4* __restrict__ src, int64_t n16,
+                                                           int32_t* __restrict__ sink, int flag) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  int64_t i = g;
+  i32x4 f = {0, 0, 0, 0};
+  for (; i + (kCopyUnroll - 1) * stride < n16; i += kCopyUnroll * stride) {
+    i32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) f ^= v[u];
+  }
+  for (; i < n16; i += stride) f ^= __builtin_nontemporal_load(src + i);
+  if (flag == 0x5eed) sink[g] = f[0] ^ f[1] ^ f[2] ^ f[3];
+}
+
 }  // namespace
+
+extern "C" int convrot_probe_read(const void* src, int64_t bytes, int grid, int32_t* sink, int flag, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes <= 0 || bytes % 16 != 0 || grid <= 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) != 0)
+    return 1;
+  hipLaunchKernelGGL(read_probe, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const i32x4*>(src), bytes / 16, sink, flag);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int convrot_probe_copy(const void* src, void* dst, int64_t bytes, int grid, void* stream) {
   if (src == nullptr || dst == nullptr || bytes <= 0 || bytes % 16 != 0 || grid <= 0 ||

@@ -21,7 +21,7 @@ THREADS = 512
 CHAINS = 8
 OPS_PER_MFMA = 32768
 REALTIME_HZ = 100e6   # s_memrealtime counts at a constant 100 MHz
-EXPORTED = ("convrot_probe_copy", "convrot_probe_mfma_i8")
+EXPORTED = ("convrot_probe_copy", "convrot_probe_mfma_i8", "convrot_probe_read")
 
 _lib = None
 
@@ -37,6 +37,8 @@ def load() -> ctypes.CDLL:
         lib.convrot_probe_mfma_i8.restype = ctypes.c_int
         lib.convrot_probe_copy.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
         lib.convrot_probe_copy.restype = ctypes.c_int
+        lib.convrot_probe_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, ctypes.c_int, vp]
+        lib.convrot_probe_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -111,18 +113,13 @@ def copy_gbps(device: torch.device, mib: int = 1024, reps: int = 5) -> dict:
     return out
 
 
-def copy_sweep(device: torch.device, sizes_mib=(4, 16, 64, 256), span_mib: int = 1024, reps: int = 16) -> dict:
-    """Streaming-copy time against size, each size copied ``reps`` times in
-    one HIP graph over consecutive slices of a ``span_mib`` buffer (so the
-    256 MB Infinity Cache cannot serve repeats) and timed with events: the
-    per-launch fixed cost t0 and the streaming bandwidth of the least-squares
-    fit t = t0 + (read + write bytes) / BW.  A kernel moving B bytes cannot
-    beat t0 + B / BW on this GPU."""
+def _sweep(device, sizes_mib, span_mib, reps, reads_only):
     lib = load()
     cus = torch.cuda.get_device_properties(device).multi_processor_count
     span = span_mib << 20
     src = torch.ones(span, dtype=torch.uint8, device=device)
-    dst = torch.empty_like(src)
+    dst = None if reads_only else torch.empty_like(src)
+    sink = torch.empty(8 * cus * 256, dtype=torch.int32, device=device)
     stream = torch.cuda.current_stream(device)
     pts = []
     for mib in sizes_mib:
@@ -130,11 +127,15 @@ def copy_sweep(device: torch.device, sizes_mib=(4, 16, 64, 256), span_mib: int =
         slots = max(1, span // nb)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(device).cuda_stream
             for r in range(reps):
                 off = (r % slots) * nb
-                if lib.convrot_probe_copy(src.data_ptr() + off, dst.data_ptr() + off, nb, 8 * cus,
-                                          torch.cuda.current_stream(device).cuda_stream) != 0:
-                    raise RuntimeError("convrot_probe_copy failed")
+                if reads_only:
+                    st = lib.convrot_probe_read(src.data_ptr() + off, nb, 8 * cus, sink.data_ptr(), 0, cs)
+                else:
+                    st = lib.convrot_probe_copy(src.data_ptr() + off, dst.data_ptr() + off, nb, 8 * cus, cs)
+                if st != 0:
+                    raise RuntimeError("probe launch failed")
         g.replay()
         torch.cuda.synchronize(device)
         ts = []
@@ -145,11 +146,27 @@ def copy_sweep(device: torch.device, sizes_mib=(4, 16, 64, 256), span_mib: int =
             e1.record(stream)
             torch.cuda.synchronize(device)
             ts.append(e0.elapsed_time(e1) * 1e3 / reps)
-        pts.append((2.0 * nb, float(np.median(ts))))
+        pts.append(((1.0 if reads_only else 2.0) * nb, float(np.median(ts))))
         del g
     x = np.array([p[0] for p in pts])
     y = np.array([p[1] for p in pts])
     slope, t0 = np.polyfit(x, y, 1)
     del src, dst
     return {"t0_us": round(float(t0), 3), "GBps": round(1e-3 / float(slope), 1),
-            "points_us": {f"{int(b / 2 / 2**20)}MiB": round(t, 2) for b, t in pts}}
+            "points_us": {f"{mib}MiB": round(t, 2) for mib, (_, t) in zip(sizes_mib, pts)}}
+
+
+def copy_sweep(device: torch.device, sizes_mib=(4, 16, 64, 256), span_mib: int = 1024, reps: int = 16) -> dict:
+    """Streaming-copy time against size, each size copied ``reps`` times in
+    one HIP graph over consecutive slices of a ``span_mib`` buffer (so the
+    256 MB Infinity Cache cannot serve repeats) and timed with events: the
+    per-launch fixed cost t0 and the streaming bandwidth of the least-squares
+    fit t = t0 + (read + write bytes) / BW.  A kernel moving B bytes cannot
+    beat t0 + B / BW on this GPU."""
+    return _sweep(device, sizes_mib, span_mib, reps, reads_only=False)
+
+
+def read_sweep(device: torch.device, sizes_mib=(4, 8, 16, 64, 256), span_mib: int = 1024, reps: int = 16) -> dict:
+    """The same fit for a streaming read with no stores, t = t0 + bytes / BW:
+    the floor of a read-dominated launch such as small-M weight streaming."""
+    return _sweep(device, sizes_mib, span_mib, reps, reads_only=True)
