@@ -467,24 +467,32 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
         barrier();  // every read of this area is done before it is staged again
       }
     } else {
-      // Per 8 tokens (half a 16-token tile): the raw accumulators go to a
-      // private LDS area of the wave as rows, with each row's scale in the
-      // row's padding (the lanes holding those 8 tokens write, the others
-      // wait); each lane then takes 4-feature segments of those rows, whose
-      // column scale and bias it already holds, converts, finishes them and
-      // stores whole row pieces.  The areas lie in A buffer 2 (waves 0-3)
-      // and B buffer 1 (waves 4-7), which the next tile's first slices do
-      // not use; every slice read finished before the main loop's last
-      // barrier.  The value is fma(acc, s_x s_w, b), the same expression in
-      // the same precision as the other linear kernels, so the result bits
-      // do not depend on which kernel a shape runs on.
+      // Per 16-token tile: the raw accumulators go to a private LDS area of
+      // the wave as rows (16-byte chunks XOR-swizzled by row, so that the
+      // 16 rows a column of lanes writes, and the chunks of a row a pass
+      // reads, fall in distinct banks); each lane then takes 4-feature
+      // segments of those rows, whose column scale and bias it already
+      // holds, fetches the row's scale from the lane that holds it
+      // (ds_bpermute), converts, finishes them and stores whole row pieces.
+      // The areas lie in A buffer 2 (waves 0-3) and B buffer 1 (waves 4-7),
+      // which the next tile's first slices do not use; every slice read
+      // finished before the main loop's last barrier.  The value is
+      // fma(acc, s_x s_w, b), the same expression in the same precision as
+      // the other linear kernels, so the result bits do not depend on which
+      // kernel a shape runs on.
       using out_t = typename std::conditional<OUT == 0, float, __bf16>::type;
-      constexpr int kPitch = kWN * 4 + 16;  // one row of the wave + its scale, padded across banks
-      constexpr int kPasses = 8 * kSegs / 64;
-      static_assert((8 * kSegs) % 64 == 0, "whole passes per 8 rows");
-      static_assert(4 * 8 * kPitch <= kATileBytes && 4 * 8 * kPitch <= kBTileBytes, "staging areas");
-      uint8_t* stage = wid_u < 4 ? smem + 2 * kATileBytes + wid_u * 8 * kPitch
-                                 : smem + kBBase + kBTileBytes + (wid_u - 4) * 8 * kPitch;
+      constexpr int kPitch = kWN * 4;                  // one row of the wave's features
+      constexpr int kSwz = kSegs % 16 == 0 ? 15 : 7;  // chunk swizzle: row bits within the row's chunk count
+      constexpr int kPasses = 16 * kSegs / 64;
+      static_assert((16 * kSegs) % 64 == 0, "whole passes per 16 rows");
+      // Passes run in kRuns straight runs (see below); the erf GELU's
+      // temporaries take quarter runs at the widest tile.
+      constexpr int kRuns = (ACT == 1 && TN == 4) ? 4 : 2;
+      constexpr int kRunPasses = kPasses / kRuns;
+      static_assert(kPasses % kRuns == 0 && kRunPasses % kLaneSegs == 0, "runs repeat the segment pattern");
+      static_assert(4 * 16 * kPitch <= kATileBytes && 4 * 16 * kPitch <= kBTileBytes, "staging areas");
+      uint8_t* stage = wid_u < 4 ? smem + 2 * kATileBytes + wid_u * 16 * kPitch
+                                 : smem + kBBase + kBTileBytes + (wid_u - 4) * 16 * kPitch;
       // Tiles wholly inside the output take a branch-free pass loop (so the
       // LDS reads of later passes can issue ahead of earlier stores): lane
       // l's segment and row in pass p repeat with period kLaneSegs, the row
@@ -499,13 +507,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
         lane_base[j] = static_cast<out_t*>(C) + static_cast<int64_t>(m_blk + wm + c / kSegs) * ldc + n_blk + wn +
                        4 * (c % kSegs);
       }
-      // Segment of pass p: converted, scaled, biased and activated outputs.
-      auto finish = [&](int p, float y[4]) {
+      // Segment of pass p: converted, scaled, biased and activated outputs
+      // (row scale of token `row` of the tile: s_row of lane `row`).
+      auto finish = [&](int p, int j, float s_tile, float y[4]) {
         const int c = 64 * p + lane;
         const int row = c / kSegs, seg = c % kSegs;
-        const int j = p % kLaneSegs;
-        const acc_t a = *reinterpret_cast<const acc_t*>(stage + row * kPitch + seg * 16);
-        const float sr = *reinterpret_cast<const float*>(stage + row * kPitch + kWN * 4);
+        const acc_t a = *reinterpret_cast<const acc_t*>(stage + row * kPitch + ((seg ^ (row & kSwz)) << 4));
+        const float sr = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(row << 2, __builtin_bit_cast(int, s_tile)));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = static_cast<float>(a[r]);
@@ -528,27 +537,37 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
       };
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
+        {
+          const int r0 = 16 * t;  // first token of the tile within the wave's 64
+          {
+            // chunk 4 f + fk of row frow: features 16 f + 4 fk .. + 3
+            uint8_t* row_ptr = stage + frow * kPitch;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r0 = 16 * t + 8 * h;  // first token of the 8 within the wave's 64
-          if ((frow >> 3) == h) {
-            uint8_t* row_ptr = stage + (frow & 7) * kPitch;
-#pragma unroll
-            for (int f = 0; f < kTF; ++f) *reinterpret_cast<acc_t*>(row_ptr + (16 * f + n_lane) * 4) = acc[t][f];
-            if (fk == 0) *reinterpret_cast<float*>(row_ptr + kWN * 4) = s_row[t];
+            for (int f = 0; f < kTF; ++f)
+              *reinterpret_cast<acc_t*>(row_ptr + (((4 * f + fk) ^ (frow & kSwz)) << 4)) = acc[t][f];
           }
+          // The passes run in kRuns straight runs (the column scales' index
+          // p % kLaneSegs stays a constant); fewer reads in flight keep the
+          // registers within the budget of two waves per SIMD.
           if (full) {
+#pragma unroll 1
+            for (int hp = 0; hp < kRuns; ++hp) {
 #pragma unroll
-            for (int p = 0; p < kPasses; ++p) {
-              float y[4];
-              finish(p, y);
-              store4(lane_base[p % kLaneSegs] + static_cast<int64_t>(r0 + (p / kLaneSegs) * kRowStep) * ldc, y);
+              for (int q = 0; q < kRunPasses; ++q) {
+                const int p = hp * kRunPasses + q;
+                float y[4];
+                finish(p, q % kLaneSegs, s_row[t], y);
+                store4(lane_base[q % kLaneSegs] + static_cast<int64_t>(r0 + (p / kLaneSegs) * kRowStep) * ldc, y);
+              }
             }
           } else {
+#pragma unroll 1
+            for (int hp = 0; hp < kRuns; ++hp) {
 #pragma unroll
-            for (int p = 0; p < kPasses; ++p) {
+            for (int q = 0; q < kRunPasses; ++q) {
+              const int p = hp * kRunPasses + q;
               float y[4];
-              finish(p, y);
+              finish(p, q % kLaneSegs, s_row[t], y);
               const int c = 64 * p + lane;
               const int m = m_blk + wm + r0 + c / kSegs;
               const int n = n_blk + wn + 4 * (c % kSegs);
@@ -560,6 +579,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
                   for (int r = 0; r < 4 && n + r < N; ++r) out[r] = static_cast<out_t>(y[r]);
                 }
               }
+            }
             }
           }
         }
