@@ -559,7 +559,7 @@ def _cpu_baseline(wl, budget_s, cores, O):
     M = wl.X.shape[0]
     m = min(M, 64)
     t = run(m)
-    while m < M and t < budget_s / 4:
+    while m < M and t < budget_s / 2:
         m = min(M, m * 4)
         for k in spent:
             spent[k] = 0.0
