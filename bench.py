@@ -91,11 +91,22 @@ KERNEL_SOURCE = {
 }
 
 
+def _code_only(text: str) -> str:
+    """A source file's code without its comments and blank space, so that an
+    edit of the prose alone does not invalidate counters taken on the same
+    kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+
+
 def source_digest(kernel: str) -> str:
+    """sha256 of the code (comments and blank space removed) of the sources a
+    kernel is built from."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCE[kernel]:
-        with open(os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "w8a8_int8_linear_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -38,10 +38,15 @@
 // Epilogue.  Weights are the MFMA "row" operand, so each lane's four
 // accumulators of a tile hold four consecutive output features of one
 // token.  Scales and biases are loaded before the main loop.  The raw
-// accumulators are staged as rows (each row's scale in its padding) in a
-// private LDS area per wave and read back so that each lane finishes fixed
-// 4-feature segments (conversion, both scales, bias, activation) and stores
-// whole row pieces.
+// accumulators of each 16-token tile are staged as rows (16-byte chunks
+// XOR-swizzled by row) in a private LDS area per wave and read back so
+// that each lane finishes fixed 4-feature segments (conversion, both
+// scales, bias, activation; the row scale taken from the lane that holds
+// it) and stores whole row pieces.
+//
+// Walk.  The grid is one workgroup per CU; each takes every gridDim.x-th
+// tile of an XCD-ordered tile list, and requests the next tile's scales
+// and first slices before its current tile's epilogue.
 //
 // Producer fusion (ROWMAX, 256-wide tiles): the epilogue also computes, for
 // the next layer's pack, the largest magnitude of every G-group (G <= 256)
