@@ -211,9 +211,12 @@ class Op:
 class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
-    def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False):
+    def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False,
+                 tiled=False):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
         self.producer_fusion = producer_fusion and fused and wl.cfg == 3
+        # weights in the TILE16 layout, which only the M <= 16 path reads
+        self.tiled = tiled and wl.X.shape[0] <= 16
         # linears that share the packed activation run as one launch over the
         # concatenated weight (configs whose linears all read the same input)
         self.merge = merge and wl.cfg == 2 and all(l.W.shape[1] % wl.G == 0 for l in wl.linears)
@@ -250,8 +253,12 @@ class StepSet:
                     self.W[lin.name] = wd.to(bf16)
                 elif wl.extra.get("wbits") == 4:
                     self.W[lin.name] = cr.pack_weight_w4(wd, G, kind, self.signs.get(K))
+                    if self.tiled and lin.W.shape[0] % 16 == 0 and K % 128 == 0:
+                        self.W[lin.name] = cr.tile_weight_w4(self.W[lin.name])
                 else:
                     self.W[lin.name] = cr.pack_weight(wd, G, kind, self.signs.get(K))
+                    if self.tiled and lin.W.shape[0] % 16 == 0 and K % 64 == 0:
+                        self.W[lin.name] = cr.tile_weight(self.W[lin.name])
                     del wd
                 self.b[lin.name] = up(lin.b, f32) if lin.b is not None else None
             self.X2 = up(wl.extra["X_routed"], bf16) if "X_routed" in wl.extra else None
@@ -265,9 +272,9 @@ class StepSet:
             self.lora = template.lora
             self.signs = template.signs
             self.X = template.X.clone()
-            self.W = {k: (cr.Packed(v.q.clone(), v.scale.clone(), v.group, v.kind, v.signs)
+            self.W = {k: (cr.Packed(v.q.clone(), v.scale.clone(), v.group, v.kind, v.signs, v.layout)
                           if isinstance(v, cr.Packed) else
-                          cr.PackedW4(v.q.clone(), v.scale.clone(), v.K, v.group, v.kind, v.signs)
+                          cr.PackedW4(v.q.clone(), v.scale.clone(), v.K, v.group, v.kind, v.signs, v.layout)
                           if isinstance(v, cr.PackedW4) else v.clone()) for k, v in template.W.items()}
             self.b = template.b
             self.X2 = template.X2.clone() if template.X2 is not None else None
@@ -614,6 +621,9 @@ def main():
                          "the concatenated weight")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (calibrates HBM byte counters)")
+    ap.add_argument("--row-weights", action="store_true",
+                    help="decode (M <= 16): keep the packed weights in the row layout instead of the TILE16 layout "
+                         "the weight-streaming kernel reads fastest")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy and MFMA-only ceilings")
     args = ap.parse_args()
@@ -638,9 +648,11 @@ def main():
     fused = not args.unfused
     merge = not args.separate_linears
     pf = args.producer_fusion
-    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf)]
+    tl = not args.row_weights
+    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
-        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf))
+        sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf,
+                            tiled=tl))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -781,6 +793,8 @@ def main():
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
                    "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
                    "producer_fusion": bool(sets[0].producer_fusion),
+                   "weight_layout": "tile16" if any(getattr(v, "layout", "rows") == "tile16"
+                                                    for v in sets[0].W.values()) else "rows",
                    "shared_pack_linears": "one launch" if sets[0].merge else "one launch each",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "weights": "int4" if wl.extra.get("wbits") == 4 else "int8",

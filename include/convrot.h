@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 7
+#define CONVROT_ABI_VERSION 8
 
 typedef enum {
   CONVROT_OK = 0,
@@ -148,10 +148,35 @@ typedef struct {
   const int8_t* signs;  /* [K] +-1, randomized kind only */
 } convrot_rot;
 
+/* Where a packed weight's codes lie in memory (the `layout` field of
+ * convrot_packed and convrot_packed_w4).
+ *   ROWS    row-major [rows, ld], as described with each struct (the
+ *           checkpoint layout; every entry point reads it).  Packed
+ *           activations are always ROWS.
+ *   TILE16  rows grouped in tiles of 16 consecutive rows and, within a
+ *           tile, K cut into units of 64 bytes (64 int8 codes or 128 int4
+ *           codes); with ld equal to the bytes of one row (K, or K / 2 for
+ *           int4), byte b of row r is at
+ *             q + (r / 16) * 16 * ld + (b / 64) * 1024 + (r % 16) * 64 + b % 64
+ *           so the 16 rows' bytes of one unit are 1 KiB of consecutive
+ *           memory, which the weight-streaming kernel (M <= 16) reads
+ *           faster than 16 row pieces 1 row apart.  Only that path reads
+ *           it: a linear call with a TILE16 weight and M > 16 is
+ *           CONVROT_ERR_INVALID_ARG.  It needs rows % 16 == 0, ld == the row
+ *           bytes, and K % 64 == 0 (int4: K % 128 == 0).
+ *           convrot_tile_weight and convrot_tile_weight_w4 convert a ROWS
+ *           weight; the pack entry points write ROWS only. */
+typedef enum {
+  CONVROT_LAYOUT_ROWS = 0,
+  CONVROT_LAYOUT_TILE16 = 1
+} convrot_layout;
+
 /* A packed operand: int8 rows and one fp32 scale per row, both caller-owned
  * device buffers, plus the rotation that produced them.
- *   q      [rows, ld] int8, row-major, ld >= K, ld % 16 == 0
+ *   q      [rows, ld] int8, row-major, ld >= K, ld % 16 == 0 (or the TILE16
+ *          layout above)
  *   scale  [rows] fp32
+ *   layout convrot_layout (CONVROT_LAYOUT_ROWS for activations)
  * The same struct describes a packed activation (rows = M) and a packed
  * weight (rows = N; the canonical checkpoint layout, one int8 row per output
  * feature, "INT8 Convrot Safetensors", "Checkpoint format"). */
@@ -162,6 +187,7 @@ typedef struct {
   int64_t K;
   int64_t ld;
   convrot_rot rot;
+  int32_t layout;
 } convrot_packed;
 
 /* A packed int4 weight (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
@@ -181,6 +207,7 @@ typedef struct {
   int64_t K;
   int64_t ld;
   convrot_rot rot;
+  int32_t layout;  /* convrot_layout */
 } convrot_packed_w4;
 
 /* Rotate and quantise activation rows ("Runtime activation quantization").
@@ -205,7 +232,8 @@ convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw
  *   act   packed activation [M = act->rows, K]
  *   w     packed weight [N = w->rows, K]; act->K == w->K and the two
  *         rotation descriptors must be equal (same G, kind and signs
- *         pointer), otherwise CONVROT_ERR_MISMATCH
+ *         pointer), otherwise CONVROT_ERR_MISMATCH; ROWS layout, or TILE16
+ *         when M <= 16 (CONVROT_ERR_INVALID_ARG otherwise)
  *   bias  [N] fp32 or NULL
  *   Y     [M, ldy] of `ydt`: CONVROT_F32, CONVROT_BF16 (round to nearest
  *         even) or CONVROT_I32 (the raw accumulator A; scales and bias are
@@ -320,7 +348,8 @@ convrot_status convrot_pack_act_rowmax(const void* X, convrot_dtype xdt, int64_t
  * every linear that shares the input).
  *   w_gate, w_up  packed weights [N, K], each checked against `act` as in
  *                 convrot_linear; they must have the same N
- *                 (CONVROT_ERR_MISMATCH otherwise)
+ *                 (CONVROT_ERR_MISMATCH otherwise) and the same layout
+ *                 (CONVROT_ERR_INVALID_ARG otherwise)
  *   b_gate, b_up  [N] fp32 or NULL
  *   fn, ydt       as convrot_linear_act
  *   Y             [M, ldy]
@@ -362,7 +391,8 @@ convrot_status convrot_pack_weight_w4(const void* W, convrot_dtype wdt, int64_t 
  * convrot_linear_act).
  *   act        packed activation [M, K]; act->K == w->K and equal rotation
  *              descriptors, else CONVROT_ERR_MISMATCH
- *   w          packed int4 weight [N, K]
+ *   w          packed int4 weight [N, K]; ROWS layout, or TILE16 when
+ *              M <= 16 (CONVROT_ERR_INVALID_ARG otherwise)
  *   fn         CONVROT_ACT_NONE (plain linear; ydt may then also be
  *              CONVROT_I32, the raw accumulator), CONVROT_ACT_GELU_ERF or
  *              CONVROT_ACT_GELU_TANH
@@ -389,8 +419,22 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
                                        int64_t workspace_bytes, void* stream);
 
 /* Expand int4 codes to int8 codes (for checking, or to keep an int8 copy):
+ *   w   ROWS layout
  *   dst [w->rows, ldd] int8, ldd >= w->K, ldd % 16 == 0, 16-byte aligned. */
 convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_t ldd, void* stream);
+
+/* Copy a packed weight into the TILE16 layout (offline; see convrot_layout).
+ *   in   packed weight in the ROWS layout (any valid ld)
+ *   out  destination: layout CONVROT_LAYOUT_TILE16, the same rows, K and
+ *        rotation as `in`, ld == K; out->q receives the rows * K code bytes
+ *        in the tiled order and out->scale a copy of the scales.
+ * Errors: CONVROT_ERR_INVALID_ARG for a wrong layout, rows % 16 != 0,
+ * K % 64 != 0 or out->ld != K; CONVROT_ERR_MISMATCH when rows, K or the
+ * rotation differ.  `in` and `out` must not overlap. */
+convrot_status convrot_tile_weight(const convrot_packed* in, const convrot_packed* out, void* stream);
+
+/* The same for int4 weights: out->ld == K / 2 and K % 128 == 0. */
+convrot_status convrot_tile_weight_w4(const convrot_packed_w4* in, const convrot_packed_w4* out, void* stream);
 
 /* Data-free smoothing of an FFN's intermediate channels, offline, before
  * the weights are packed (gemma.cpp issue "Add experimental W8A8 MatMul with

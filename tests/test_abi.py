@@ -75,12 +75,14 @@ def test_status_strings(lib):
 
 def test_struct_layout():
     assert ctypes.sizeof(_lib.Rot) == 16
-    assert ctypes.sizeof(_lib.Packed) == 56
+    assert ctypes.sizeof(_lib.Packed) == 64
     assert _lib.Packed.rot.offset == 40
+    assert _lib.Packed.layout.offset == 56
 
 
-def packed(rows=4, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=A16, scale=A16B):
-    return _lib.Packed(q, scale, rows, K, ld if ld is not None else K, _lib.Rot(G, kind, signs))
+def packed(rows=4, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=A16, scale=A16B,
+           layout=_lib.LAYOUT_ROWS):
+    return _lib.Packed(q, scale, rows, K, ld if ld is not None else K, _lib.Rot(G, kind, signs), layout)
 
 
 def pack_status(lib, X=A16C, xdt=_lib.BF16, ldx=None, out=None):
@@ -340,13 +342,15 @@ def test_missing_library_fails_loudly(tmp_path):
 
 # -- int4 weights (W4A8) -------------------------------------------------------
 
-def packed_w4(rows=64, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=0x40000, scale=0x50000):
-    return _lib.PackedW4(q, scale, rows, K, ld if ld is not None else K // 2, _lib.Rot(G, kind, signs))
+def packed_w4(rows=64, K=256, ld=None, G=256, kind=_lib.ROT_REGULAR, signs=None, q=0x40000, scale=0x50000,
+              layout=_lib.LAYOUT_ROWS):
+    return _lib.PackedW4(q, scale, rows, K, ld if ld is not None else K // 2, _lib.Rot(G, kind, signs), layout)
 
 
 def test_w4_struct_layout():
-    assert ctypes.sizeof(_lib.PackedW4) == ctypes.sizeof(_lib.Packed) == 56
+    assert ctypes.sizeof(_lib.PackedW4) == ctypes.sizeof(_lib.Packed) == 64
     assert _lib.PackedW4.rot.offset == 40
+    assert _lib.PackedW4.layout.offset == 56
 
 
 def w4_status(lib, act=None, w=None, fn=_lib.ACT_NONE, ydt=_lib.BF16, ws=None, ws_bytes=0):
@@ -465,3 +469,79 @@ def test_lora_workspace_query(lib):
     # the call itself rejects a workspace one byte short of the query
     assert lora_status(lib, M=4096, ldx=3072, K=3072, lda=3072, r=32, ldb=32, N=48, ldy=48, ws_bytes=n - 1) \
         == _lib.ERR_INVALID_ARG
+
+
+# -- TILE16 weight layout -------------------------------------------------------
+# Every case below is rejected on the host before any launch.
+
+T16 = _lib.LAYOUT_TILE16
+
+
+def tile_status(lib, src=None, dst=None):
+    src = src if src is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    dst = dst if dst is not None else packed(rows=64, q=0x80000, scale=0x90000, layout=T16)
+    return lib.convrot_tile_weight(ctypes.byref(src), ctypes.byref(dst), None)
+
+
+def test_tile_weight_checks(lib):
+    assert lib.convrot_tile_weight(None, None, None) == _lib.ERR_INVALID_ARG
+    assert tile_status(lib, dst=packed(rows=64, q=0x80000, scale=0x90000)) == _lib.ERR_INVALID_ARG  # ROWS output
+    assert b"TILE16" in lib.convrot_last_error()
+    assert tile_status(lib, src=packed(rows=64, q=0x40000, layout=T16)) == _lib.ERR_INVALID_ARG     # tiled input
+    assert tile_status(lib, dst=packed(rows=60, q=0x80000, layout=T16)) == _lib.ERR_INVALID_ARG     # rows % 16
+    assert tile_status(lib, dst=packed(rows=64, ld=512, q=0x80000, layout=T16)) == _lib.ERR_INVALID_ARG  # padded
+    assert tile_status(lib, src=packed(rows=64, K=96, G=16, q=0x40000),
+                       dst=packed(rows=64, K=96, G=16, q=0x80000, layout=T16)) == _lib.ERR_INVALID_ARG  # K % 64
+    assert tile_status(lib, dst=packed(rows=64, q=0x80000, layout=2)) == _lib.ERR_INVALID_ARG       # unknown layout
+    assert b"unknown layout" in lib.convrot_last_error()
+    assert tile_status(lib, src=packed(rows=48, q=0x40000)) == _lib.ERR_MISMATCH
+    assert tile_status(lib, src=packed(rows=64, K=512, q=0x40000),
+                       dst=packed(rows=64, K=512, q=0x80000, layout=T16, G=64)) == _lib.ERR_MISMATCH
+    # the tiled copy cannot be written over its own source
+    assert tile_status(lib, dst=packed(rows=64, q=0x40000 + 64 * 256 - 16, layout=T16)) == _lib.ERR_INVALID_ARG
+    assert b"overlap" in lib.convrot_last_error()
+    assert tile_status(lib, src=packed(rows=0, q=0x40000), dst=packed(rows=0, q=0x80000, layout=T16)) == _lib.OK
+
+
+def test_tile_weight_w4_checks(lib):
+    def st(src=None, dst=None):
+        src = src if src is not None else packed_w4()
+        dst = dst if dst is not None else packed_w4(q=0x80000, scale=0x90000, layout=T16)
+        return lib.convrot_tile_weight_w4(ctypes.byref(src), ctypes.byref(dst), None)
+    assert st(dst=packed_w4(q=0x80000, scale=0x90000)) == _lib.ERR_INVALID_ARG
+    assert st(dst=packed_w4(rows=56, q=0x80000, layout=T16)) == _lib.ERR_INVALID_ARG
+    assert st(dst=packed_w4(ld=256, q=0x80000, layout=T16)) == _lib.ERR_INVALID_ARG
+    assert st(src=packed_w4(rows=32)) == _lib.ERR_MISMATCH
+    assert st(src=packed_w4(rows=0), dst=packed_w4(rows=0, q=0x80000, layout=T16)) == _lib.OK
+
+
+def test_tiled_weight_serves_small_m_only(lib):
+    tiled = packed(rows=64, q=0x40000, scale=0x50000, layout=T16)
+    assert linear_status(lib, act=packed(rows=17), w=tiled) == _lib.ERR_INVALID_ARG
+    assert b"M <= 16" in lib.convrot_last_error()
+    assert act_status(lib, act=packed(rows=32), w=tiled) == _lib.ERR_INVALID_ARG
+    assert w4_status(lib, w=packed_w4(layout=T16), ws=0x80000, ws_bytes=1 << 20) == _lib.ERR_INVALID_ARG
+    assert b"M <= 16" in lib.convrot_last_error()
+    # an activation is never tiled
+    assert linear_status(lib, act=packed(rows=16, layout=T16), w=packed(rows=64, q=0x40000)) == _lib.ERR_INVALID_ARG
+    assert b"activation" in lib.convrot_last_error()
+
+
+def test_gated_pairs_share_a_layout(lib):
+    tiled = packed(rows=64, q=0x40000, scale=0x50000, layout=T16)
+    assert gated_status(lib, gate=tiled) == _lib.ERR_INVALID_ARG
+    assert b"same layout" in lib.convrot_last_error()
+    g = packed_w4(layout=T16)
+    u = packed_w4(q=0x90000, scale=0xA0000)
+    act = packed(rows=8)
+    assert lib.convrot_linear_w4_gated(ctypes.byref(act), ctypes.byref(g), None, ctypes.byref(u), None,
+                                       _lib.ACT_GELU_TANH, A16C, _lib.BF16, 64, None, 0, None) == _lib.ERR_INVALID_ARG
+    assert b"same layout" in lib.convrot_last_error()
+
+
+def test_packing_and_unpacking_stay_in_rows(lib):
+    assert pack_status(lib, out=packed(rows=16, layout=T16)) == _lib.ERR_INVALID_ARG
+    out = packed_w4(layout=T16)
+    assert lib.convrot_pack_weight_w4(A16C, _lib.BF16, 256, ctypes.byref(out), None) == _lib.ERR_INVALID_ARG
+    assert lib.convrot_unpack_w4(ctypes.byref(out), A16C, 256, None) == _lib.ERR_INVALID_ARG
+    assert b"ROWS" in lib.convrot_last_error()

@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # convrot_status
@@ -27,6 +27,7 @@ ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
 SMOOTH_L2, SMOOTH_MAX = 0, 1
 # convrot_linear_kind (workspace queries)
 LINEAR_PLAIN, LINEAR_GATED, LINEAR_BF16, LINEAR_W4, LINEAR_W4_GATED = range(5)
+LAYOUT_ROWS, LAYOUT_TILE16 = 0, 1
 
 EXPORTED = (
     "convrot_pack_act",
@@ -44,6 +45,8 @@ EXPORTED = (
     "convrot_linear_w4",
     "convrot_linear_w4_gated",
     "convrot_unpack_w4",
+    "convrot_tile_weight",
+    "convrot_tile_weight_w4",
     "convrot_smooth_ffn",
     "convrot_lora_workspace_bytes",
     "convrot_lora_add",
@@ -65,6 +68,7 @@ class Packed(ctypes.Structure):
         ("K", ctypes.c_int64),
         ("ld", ctypes.c_int64),
         ("rot", Rot),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -76,6 +80,7 @@ class PackedW4(ctypes.Structure):
         ("K", ctypes.c_int64),
         ("ld", ctypes.c_int64),
         ("rot", Rot),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -124,6 +129,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_linear_w4_gated.restype = c_int
     lib.convrot_unpack_w4.argtypes = [P4, vp, c_i64, vp]
     lib.convrot_unpack_w4.restype = c_int
+    lib.convrot_tile_weight.argtypes = [ctypes.POINTER(Packed), ctypes.POINTER(Packed), vp]
+    lib.convrot_tile_weight.restype = c_int
+    lib.convrot_tile_weight_w4.argtypes = [P4, P4, vp]
+    lib.convrot_tile_weight_w4.restype = c_int
     lib.convrot_smooth_ffn.argtypes = [vp, c_int, c_i64, vp, c_int, c_i64, c_i64, c_i64, c_i64, c_int, vp, vp, c_i64,
                                        vp, c_i64, vp]
     lib.convrot_smooth_ffn.restype = c_int

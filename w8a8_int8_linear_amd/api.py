@@ -24,6 +24,9 @@ REGULAR = "regular"
 RANDOMIZED = "randomized"
 _KIND = {REGULAR: _lib.ROT_REGULAR, RANDOMIZED: _lib.ROT_RANDOMIZED}
 _DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.int32: _lib.I32}
+ROWS = "rows"
+TILE16 = "tile16"
+_LAYOUT = {ROWS: _lib.LAYOUT_ROWS, TILE16: _lib.LAYOUT_TILE16}
 GELU_ERF = "gelu_erf"
 GELU_TANH = "gelu_tanh"
 _ACT = {GELU_ERF: _lib.ACT_GELU_ERF, GELU_TANH: _lib.ACT_GELU_TANH}
@@ -42,6 +45,7 @@ class Packed:
     group: int
     kind: str = REGULAR
     signs: torch.Tensor | None = None
+    layout: str = ROWS       # ROWS, or TILE16 for a weight read only at M <= 16 (tile_weight)
 
     @property
     def rows(self) -> int:
@@ -62,7 +66,13 @@ class Packed:
         if not q.is_cuda or s.device != q.device:
             raise ValueError("packed codes and scales must be device tensors on one device")
         return _lib.Packed(q.data_ptr(), s.data_ptr(), q.shape[0], q.shape[1], _ld(q),
-                           _rot(self.group, self.kind, self.signs))
+                           _rot(self.group, self.kind, self.signs), _layout(self.layout))
+
+
+def _layout(layout: str) -> int:
+    if layout not in _LAYOUT:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUT)}, got {layout!r}")
+    return _LAYOUT[layout]
 
 
 def _rot(group: int, kind: str, signs: torch.Tensor | None) -> _lib.Rot:
@@ -381,6 +391,7 @@ class PackedW4:
     group: int
     kind: str = REGULAR
     signs: torch.Tensor | None = None
+    layout: str = ROWS       # ROWS, or TILE16 (tile_weight_w4)
 
     @property
     def rows(self) -> int:
@@ -397,7 +408,7 @@ class PackedW4:
         if not q.is_cuda or s.device != q.device:
             raise ValueError("q and scales must be device tensors on one device")
         return _lib.PackedW4(self.q.data_ptr(), self.scale.data_ptr(), self.q.shape[0], self.K, _ld(self.q),
-                             _rot(self.group, self.kind, self.signs))
+                             _rot(self.group, self.kind, self.signs), _layout(self.layout))
 
 
 def pack_weight_w4(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
@@ -484,6 +495,35 @@ def unpack_w4(w: PackedW4, out: torch.Tensor | None = None) -> torch.Tensor:
 
 _SMOOTH = {"l2": _lib.SMOOTH_L2, "max": _lib.SMOOTH_MAX}
 
+
+
+def tile_weight(w: Packed) -> Packed:
+    """A copy of a packed weight in the TILE16 layout (convrot_tile_weight):
+    16-row tiles whose 64-byte K units are each 1 KiB of consecutive memory,
+    which the small-M path (M <= 16) streams faster.  Only M <= 16 calls
+    accept it; keep the ROWS weight for larger M.  Needs N % 16 == 0 and
+    K % 64 == 0."""
+    if w.layout != ROWS:
+        raise ValueError("tile_weight takes a ROWS weight")
+    dev = w.q.device
+    out = Packed(torch.empty((w.rows, w.K), dtype=torch.int8, device=dev), torch.empty_like(w.scale), w.group, w.kind,
+                 w.signs, TILE16)
+    lib = _lib.load()
+    _lib.check(lib.convrot_tile_weight(ctypes.byref(w.descriptor()), ctypes.byref(out.descriptor()), _stream(dev)))
+    return out
+
+
+def tile_weight_w4(w: PackedW4) -> PackedW4:
+    """tile_weight for int4 weights (convrot_tile_weight_w4; K % 128 == 0)."""
+    if w.layout != ROWS:
+        raise ValueError("tile_weight_w4 takes a ROWS weight")
+    dev = w.q.device
+    out = PackedW4(torch.empty((w.rows, w.K // 2), dtype=torch.uint8, device=dev), torch.empty_like(w.scale), w.K,
+                   w.group, w.kind, w.signs, TILE16)
+    lib = _lib.load()
+    _lib.check(lib.convrot_tile_weight_w4(ctypes.byref(w.descriptor()), ctypes.byref(out.descriptor()),
+                                          _stream(dev)))
+    return out
 
 def smooth_ffn(w_up: torch.Tensor, w_down: torch.Tensor, norm: str = "l2", scaled: bool = True):
     """s [F] = sqrt(n_up / n_down) per intermediate channel and, with

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "pack_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "gemm_act.hip", "gemm_gated.hip", "gemv.hip",
-           "w4.hip", "smooth.hip", "lora.hip"]
+           "w4.hip", "smooth.hip", "lora.hip", "tile.hip"]
 PROBE_NAME = "libconvrot_probe.so"
 PROBE_PATH = os.path.join(PKG_DIR, PROBE_NAME)
 PROBE_SOURCES = ["probe.hip"]

@@ -104,6 +104,22 @@ convrot_status check_matrix(const char* name, const void* p, int64_t rows, int64
   return CONVROT_OK;
 }
 
+// The layout field of a packed weight: ROWS, or TILE16 with whole tiles of
+// 16 rows, dense rows (ld == the row's bytes) and whole 64-byte units.
+convrot_status check_layout(const char* name, int32_t layout, int64_t rows, int64_t ld, int64_t row_bytes,
+                            int64_t unit_codes, int64_t K) {
+  if (layout == CONVROT_LAYOUT_ROWS) return CONVROT_OK;
+  if (layout != CONVROT_LAYOUT_TILE16)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: unknown layout %d", name, static_cast<int>(layout));
+  if (rows % 16 != 0 || ld != row_bytes || K % unit_codes != 0)
+    return fail(CONVROT_ERR_INVALID_ARG,
+                "%s: the TILE16 layout needs rows %% 16 == 0 (got %lld), ld == %lld bytes (got %lld) and "
+                "K %% %lld == 0 (got %lld)",
+                name, static_cast<long long>(rows), static_cast<long long>(row_bytes), static_cast<long long>(ld),
+                static_cast<long long>(unit_codes), static_cast<long long>(K));
+  return CONVROT_OK;
+}
+
 convrot_status check_packed(const char* name, const convrot_packed* p, int* log2G) {
   if (p == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s descriptor is NULL", name);
   convrot_status st = check_k(p->K, kMaxK);
@@ -115,6 +131,22 @@ convrot_status check_packed(const char* name, const convrot_packed* p, int* log2
   if (p->rows > 0 && p->scale == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s scale is NULL", name);
   if ((reinterpret_cast<uintptr_t>(p->scale) & 3u) != 0)
     return fail(CONVROT_ERR_ALIGN, "%s scale must be 4-byte aligned", name);
+  return check_layout(name, p->layout, p->rows, p->ld, p->K, 64, p->K);
+}
+
+// Only weights may be tiled, and only the weight-streaming path (M <= 16)
+// reads the tiled layout.
+convrot_status check_rows_layout(const char* name, int32_t layout) {
+  if (layout != CONVROT_LAYOUT_ROWS)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s must be in the ROWS layout", name);
+  return CONVROT_OK;
+}
+
+convrot_status check_weight_layout_for_m(const char* fn, int32_t layout, int64_t M) {
+  if (layout == CONVROT_LAYOUT_TILE16 && M > convrot::kGemvMaxRows)
+    return fail(CONVROT_ERR_INVALID_ARG,
+                "%s: a TILE16 weight serves M <= %d only (M = %lld); use the ROWS layout for larger M", fn,
+                convrot::kGemvMaxRows, static_cast<long long>(M));
   return CONVROT_OK;
 }
 
@@ -125,6 +157,8 @@ convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int
   convrot_status st = check_k(out->K, kMaxPackK);
   if (st != CONVROT_OK) return st;
   st = check_packed("packed output", out, &log2G);
+  if (st != CONVROT_OK) return st;
+  st = check_rows_layout("packed output", out->layout);
   if (st != CONVROT_OK) return st;
   if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
     return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
@@ -146,6 +180,10 @@ convrot_status check_linear(const char* fn, const convrot_packed* act, const con
   convrot_status st = check_packed("activation", act, &lga);
   if (st != CONVROT_OK) return st;
   st = check_packed("weight", w, &lgw);
+  if (st != CONVROT_OK) return st;
+  st = check_rows_layout("activation", act->layout);
+  if (st != CONVROT_OK) return st;
+  st = check_weight_layout_for_m(fn, w->layout, act->rows);
   if (st != CONVROT_OK) return st;
   if (act->K != w->K)
     return fail(CONVROT_ERR_MISMATCH, "activation K = %lld but weight K = %lld", static_cast<long long>(act->K),
@@ -189,13 +227,14 @@ convrot_status check_packed_w4(const char* name, const convrot_packed_w4* p, int
   if (p->ld > kMaxLdBytes)
     return fail(CONVROT_ERR_INVALID_ARG, "%s: leading dimension exceeds %lld bytes", name,
                 static_cast<long long>(kMaxLdBytes));
-  return CONVROT_OK;
+  return check_layout(name, p->layout, p->rows, p->ld, p->K / 2, 128, p->K);
 }
 
 // An int4 weight seen through the int8 descriptor checks of check_linear:
-// the same K, rotation and row count (the code pointer is only compared).
+// the same K, rotation, row count and layout (the code pointer is only
+// compared; a tiled view passes the int8 tile checks since K % 128 == 0).
 convrot_packed as_int8_view(const convrot_packed_w4& w) {
-  return convrot_packed{reinterpret_cast<int8_t*>(w.q), w.scale, w.rows, w.K, w.K, w.rot};
+  return convrot_packed{reinterpret_cast<int8_t*>(w.q), w.scale, w.rows, w.K, w.K, w.rot, w.layout};
 }
 
 // M > 16 with int4 weights: the expanded codes go to the caller's workspace.
@@ -205,6 +244,33 @@ convrot_status check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
                 static_cast<long long>(need), static_cast<long long>(ws == nullptr ? 0 : ws_bytes));
   if (!aligned16(ws)) return fail(CONVROT_ERR_ALIGN, "workspace must be 16-byte aligned");
   return CONVROT_OK;
+}
+
+// Copy of a ROWS weight into the TILE16 layout (row_bytes per row: K for
+// int8 codes, K / 2 for int4 nibble pairs).
+template <typename D>
+convrot_status tile_impl(const char* what, const D* in, const D* out, int64_t row_bytes, void* stream,
+                         convrot_status (*check)(const char*, const D*, int*)) {
+  int lgi = 0, lgo = 0;
+  convrot_status st = check("input", in, &lgi);
+  if (st != CONVROT_OK) return st;
+  st = check("output", out, &lgo);
+  if (st != CONVROT_OK) return st;
+  st = check_rows_layout("input", in->layout);
+  if (st != CONVROT_OK) return st;
+  if (out->layout != CONVROT_LAYOUT_TILE16)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: the output descriptor must have the TILE16 layout", what);
+  if (in->rows != out->rows || in->K != out->K || in->rot.group != out->rot.group || in->rot.kind != out->rot.kind ||
+      in->rot.signs != out->rot.signs)
+    return fail(CONVROT_ERR_MISMATCH, "%s: input and output differ in rows, K or rotation", what);
+  if (in->rows == 0) return ok();
+  const auto* src = reinterpret_cast<const uint8_t*>(in->q);
+  auto* dst = reinterpret_cast<uint8_t*>(out->q);
+  if (src < dst + out->rows * row_bytes && dst < src + (in->rows - 1) * in->ld + row_bytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: input and output overlap", what);
+  return from_hip(convrot::launch_tile_rows(src, in->ld, dst, in->rows, row_bytes, in->scale, out->scale,
+                                            static_cast<hipStream_t>(stream)),
+                  what);
 }
 
 // Optional split-K workspace of a small-M call: NULL selects the unsplit
@@ -259,7 +325,7 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
     st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, N, K));
     if (st != CONVROT_OK) return st;
     e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy,
-                                workspace, s);
+                                workspace, s, w->layout == CONVROT_LAYOUT_TILE16);
   } else {
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
@@ -323,7 +389,7 @@ convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_p
       if (st != CONVROT_OK) return st;
     }
     e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, ws,
-                                s);
+                                s, w->layout == CONVROT_LAYOUT_TILE16);
   } else {
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
@@ -368,7 +434,7 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
   const hipError_t e =
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
-                                        out, ldy, workspace, s)
+                                        out, ldy, workspace, s, w->layout == CONVROT_LAYOUT_TILE16)
           : convrot::launch_gemm_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
                                         out, ldy, s);
   return from_hip(e, "convrot_linear_act");
@@ -412,6 +478,8 @@ convrot_status convrot_pack_act_rowmax(const void* X, convrot_dtype xdt, int64_t
   if (st != CONVROT_OK) return st;
   st = check_packed("packed output", out, &log2G);
   if (st != CONVROT_OK) return st;
+  st = check_rows_layout("packed output", out->layout);
+  if (st != CONVROT_OK) return st;
   if (out->rot.kind != CONVROT_ROT_REGULAR || log2G > 8)
     return fail(CONVROT_ERR_GROUP, "%s: given maxima need the regular rotation with G in {4, 16, 64, 256}", what);
   if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
@@ -440,6 +508,8 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
   if (w_gate->rows != w_up->rows)
     return fail(CONVROT_ERR_MISMATCH, "gate has %lld output rows but up has %lld",
                 static_cast<long long>(w_gate->rows), static_cast<long long>(w_up->rows));
+  if (w_gate->layout != w_up->layout)
+    return fail(CONVROT_ERR_INVALID_ARG, "convrot_linear_gated: gate and up weights must have the same layout");
   const int64_t M = act->rows, N = w_gate->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
   if (M <= convrot::kGemvMaxRows) {
@@ -453,7 +523,7 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy,
-                                          workspace, s)
+                                          workspace, s, w_gate->layout == CONVROT_LAYOUT_TILE16)
           : convrot::launch_gemm_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_gated");
@@ -520,6 +590,8 @@ convrot_status convrot_pack_weight_w4(const void* W, convrot_dtype wdt, int64_t 
   if (st != CONVROT_OK) return st;
   st = check_packed_w4("packed output", out, &log2G);
   if (st != CONVROT_OK) return st;
+  st = check_rows_layout("packed output", out->layout);
+  if (st != CONVROT_OK) return st;
   if (wdt != CONVROT_F32 && wdt != CONVROT_BF16)
     return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
   st = check_matrix("input", W, out->rows, out->K, ldw, elt_size(wdt));
@@ -554,7 +626,7 @@ convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed
     st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4, N, K));
     if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
-                                            out, ldy, workspace, s),
+                                            out, ldy, workspace, s, w->layout == CONVROT_LAYOUT_TILE16),
                     what);
   }
   st = check_workspace(workspace, workspace_bytes, N * K);
@@ -590,6 +662,8 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
   if (w_gate->rows != w_up->rows)
     return fail(CONVROT_ERR_MISMATCH, "gate has %lld output rows but up has %lld",
                 static_cast<long long>(w_gate->rows), static_cast<long long>(w_up->rows));
+  if (w_gate->layout != w_up->layout)
+    return fail(CONVROT_ERR_INVALID_ARG, "convrot_linear_w4_gated: gate and up weights must have the same layout");
   const int64_t M = act->rows, N = w_gate->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
   const auto out = static_cast<convrot::Elt>(ydt);
@@ -600,7 +674,7 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
     if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate,
                                                   w_up->q, w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y,
-                                                  out, ldy, workspace, s),
+                                                  out, ldy, workspace, s, w_gate->layout == CONVROT_LAYOUT_TILE16),
                     what);
   }
   st = check_workspace(workspace, workspace_bytes, 2 * N * K);
@@ -619,11 +693,24 @@ convrot_status convrot_unpack_w4(const convrot_packed_w4* w, int8_t* dst, int64_
   int lg = 0;
   convrot_status st = check_packed_w4("weight", w, &lg);
   if (st != CONVROT_OK) return st;
+  st = check_rows_layout("weight", w->layout);
+  if (st != CONVROT_OK) return st;
   st = check_matrix("dst", dst, w->rows, w->K, ldd, 1);
   if (st != CONVROT_OK) return st;
   if (w->rows == 0) return ok();
   return from_hip(convrot::launch_unpack_w4(w->q, w->ld, w->rows, w->K, dst, ldd, static_cast<hipStream_t>(stream)),
                   "convrot_unpack_w4");
+}
+
+convrot_status convrot_tile_weight(const convrot_packed* in, const convrot_packed* out, void* stream) {
+  if (in == nullptr || out == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "convrot_tile_weight: NULL descriptor");
+  return tile_impl<convrot_packed>("convrot_tile_weight", in, out, in->K, stream, check_packed);
+}
+
+convrot_status convrot_tile_weight_w4(const convrot_packed_w4* in, const convrot_packed_w4* out, void* stream) {
+  if (in == nullptr || out == nullptr)
+    return fail(CONVROT_ERR_INVALID_ARG, "convrot_tile_weight_w4: NULL descriptor");
+  return tile_impl<convrot_packed_w4>("convrot_tile_weight_w4", in, out, in->K / 2, stream, check_packed_w4);
 }
 
 convrot_status convrot_smooth_ffn(const void* W_up, convrot_dtype up_dt, int64_t ldu, const void* W_down,

@@ -214,7 +214,7 @@ template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPL
           int TILES = 1, bool DMA = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp) {
+    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   static_assert(!W4 || I8, "int4 weights pair with int8 activations");
   static_assert(TILES == 1 || (!GATED && !SPLIT), "several tiles per workgroup only on the plain unsplit path");
@@ -234,13 +234,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int ch = lane >> 4;
 
   // Weight rows: TILES tiles of each set; in int4 mode 16 nibble bytes per
-  // lane and unit, else 16 weight bytes per lane and step.
+  // lane and unit, else 16 weight bytes per lane and step.  A 64-byte unit
+  // of a row lies unit_stride bytes after the previous one, and row r of a
+  // tile row_pitch bytes after its first row: 64 and ldb in the row layout,
+  // 1024 and 64 in the TILE16 layout (whose tiles start where the row
+  // layout's 16-row blocks do, ldb being the bytes of one row).
+  const int unit_stride = tiled ? 1024 : 64;
+  const int64_t pitch1 = tiled ? 64 : ldb;
+  const int64_t pitch2 = tiled ? 64 : epi.ldb2;
   const uint8_t* wrow[kSets][TILES];
 #pragma unroll
   for (int i = 0; i < TILES; ++i) {
-    const int64_t n = min(n0 + 16 * i + row, N - 1);
-    wrow[0][i] = B + n * ldb + ch * 16;
-    if constexpr (GATED) wrow[kSets - 1][i] = epi.B2 + n * epi.ldb2 + ch * 16;
+    const int64_t nt = n0 + 16 * i;
+    const int64_t r = min(nt + row, static_cast<int64_t>(N) - 1) - nt;
+    wrow[0][i] = B + nt * ldb + r * pitch1 + ch * 16;
+    if constexpr (GATED) wrow[kSets - 1][i] = epi.B2 + nt * epi.ldb2 + r * pitch2 + ch * 16;
   }
   const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * (W4 ? 32 : 16);
 
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
           for (int t = 0; t < kSets; ++t)
 #pragma unroll
             for (int i = 0; i < TILES; ++i) {
-              const uint8_t* p = wrow[t][i] + byte / 2;
+              const uint8_t* p = wrow[t][i] + (byte >> 7) * unit_stride;  // byte / 2 in the row layout
               if (hi) {
                 r.w[t][i][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
               } else {
@@ -305,7 +313,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
         for (int t = 0; t < kSets; ++t)
 #pragma unroll
           for (int i = 0; i < TILES; ++i)
-            r.w[t][i][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t][i] + byte));
+            r.w[t][i][u] =
+                __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t][i] + (byte >> 6) * unit_stride));
         r.x[u][0] = *reinterpret_cast<const i32x4*>(xrow + byte);
       }
     }
@@ -351,12 +360,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
       for (int i = 0; i < TILES; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int64_t n = min(n0 + 16 * i + 8 * h + drow, N - 1);
-          dbase[t][i][h] = (t == 0 ? B + n * ldb : epi.B2 + n * epi.ldb2);
+          const int64_t nt = n0 + 16 * i;
+          const int64_t r = min(nt + 8 * h + drow, static_cast<int64_t>(N) - 1) - nt;
+          dbase[t][i][h] = (t == 0 ? B + nt * ldb + r * pitch1 : epi.B2 + nt * epi.ldb2 + r * pitch2);
         }
     auto issue = [&](int u0, int buf, i32x4 (&x)[2][kXH], bool (&xv)[2][kXH]) {
       const int wb = u0 * 64;  // weight byte of the round's line
-      const int off = wb + dchunk * 16 + 16 <= wbytes ? wb + dchunk * 16 : 0;
+      // chunk dchunk of the line: unit u0 + dchunk / 4, 16-byte piece dchunk % 4
+      const int off = wb + dchunk * 16 + 16 <= wbytes ? (u0 + (dchunk >> 2)) * unit_stride + (dchunk & 3) * 16 : 0;
 #pragma unroll
       for (int t = 0; t < kSets; ++t)
 #pragma unroll
@@ -489,15 +500,15 @@ inline int gemv_num_cus() { return device_cus(); }
 template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1, bool DMA = false>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
                   const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
-                  hipStream_t stream) {
+                  bool tiled, hipStream_t stream) {
   switch (waves) {
     case 4:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(256), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled);
       break;
     default:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(512), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp);
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled);
       break;
   }
 }
@@ -541,7 +552,8 @@ SplitPlan split_plan(int64_t N, int64_t kbytes, int sets, bool w4) {
 
 template <bool I8, int OUT, int ACT = 0, bool GATED = false, bool W4 = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
-                      int64_t N, int64_t kbytes, void* C, int64_t ldc, void* ws, hipStream_t stream) {
+                      int64_t N, int64_t kbytes, void* C, int64_t ldc, void* ws, hipStream_t stream,
+                      bool tiled = false) {
   constexpr int kSets = GATED ? 2 : 1;
   constexpr int kUnit = W4 ? 128 : kStepBytes;
   // Weights go through LDS in whole lines when a wave streams enough units
@@ -567,10 +579,10 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splits));
     if (kStageable && stage_ok && per >= kStageMinUnits)
       launch_waves<I8, OUT, ACT, GATED, true, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                 ldc, sp, stream);
+                                                                 ldc, sp, tiled, stream);
     else
       launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp,
-                                                  stream);
+                                                  tiled, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_combine_kernel<I8, OUT, ACT, GATED>), dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
@@ -588,19 +600,19 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const dim3 grid(static_cast<unsigned>((tiles + 1) / 2));
     if (stage)
       launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n,
-                                                                              kb, per, C, ldc, none, stream);
+                                                                              kb, per, C, ldc, none, tiled, stream);
     else
       launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                  ldc, none, stream);
+                                                                  ldc, none, tiled, stream);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(tiles));
   if (stage)
     launch_waves<I8, OUT, ACT, GATED, false, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                ldc, none, stream);
+                                                                ldc, none, tiled, stream);
   else
     launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none,
-                                                 stream);
+                                                 tiled, stream);
   return hipGetLastError();
 }
 
@@ -613,75 +625,75 @@ int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gate
 
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, int64_t M, int64_t N, int64_t K, void* C, Elt out,
-                          int64_t ldc, void* ws, hipStream_t stream) {
+                          int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   switch (out) {
-    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
   }
 }
 
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                               const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                              Elt out, int64_t ldc, void* ws, hipStream_t stream) {
+                              Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
-               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
-             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
+               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
+             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
 }
 
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const int8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream) {
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sbg, biasg, reinterpret_cast<const uint8_t*>(Bu), ldbu, sbu, biasu};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
-               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
-  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
-             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
+    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
+               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
+  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
+             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
 }
 
 hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                          Elt out, int64_t ldc, void* ws, hipStream_t stream) {
+                          Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   if (act == Act::None) {
     switch (out) {
-      case Elt::F32: return launch_out<true, 0, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-      case Elt::BF16: return launch_out<true, 1, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-      default: return launch_out<true, 2, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+      case Elt::F32: return launch_out<true, 0, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+      case Elt::BF16: return launch_out<true, 1, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+      default: return launch_out<true, 2, 0, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
     }
   }
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
-               : launch_out<true, 1, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
-  return f32 ? launch_out<true, 0, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream)
-             : launch_out<true, 1, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream);
+    return f32 ? launch_out<true, 0, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
+               : launch_out<true, 1, 1, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+  return f32 ? launch_out<true, 0, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
+             : launch_out<true, 1, 2, false, true>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
 }
 
 hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream) {
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sbg, biasg, Bu, ldbu, sbu, biasu};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
-               : launch_out<true, 1, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
-  return f32 ? launch_out<true, 0, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream)
-             : launch_out<true, 1, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream);
+    return f32 ? launch_out<true, 0, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
+               : launch_out<true, 1, 1, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
+  return f32 ? launch_out<true, 0, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
+             : launch_out<true, 1, 2, true, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
 }
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const float* bias, int64_t M,

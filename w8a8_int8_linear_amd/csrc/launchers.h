@@ -93,7 +93,7 @@ int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gate
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                           const float* sa, const float* sb, const float* bias,
                           int64_t M, int64_t N, int64_t K,
-                          void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);
+                          void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false);
 
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
                             const float* bias, int64_t M, int64_t N, int64_t K,
@@ -101,12 +101,21 @@ hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t l
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                               const float* sa, const float* sb, const float* bias, Act act,
                               int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                              void* ws, hipStream_t stream);
+                              void* ws, hipStream_t stream, bool tiled = false);
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg,
                                 const float* sbg, const float* biasg, const int8_t* Bu, int64_t ldbu,
                                 const float* sbu, const float* biasu, const float* sa, Act act,
                                 int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                                void* ws, hipStream_t stream);
+                                void* ws, hipStream_t stream, bool tiled = false);
+
+// The weight of a small-M launch in the TILE16 layout (`tiled`): tiles of
+// 16 rows, each 64-byte K unit of a tile 1 KiB of consecutive memory; ldb is
+// then the bytes of one row.  Needs N % 16 == 0 and whole units.
+//
+// TILE16 copy of rows of row_bytes bytes (row_bytes % 64 == 0, rows % 16 ==
+// 0): dst receives rows * row_bytes bytes, s_out a copy of s_in [rows].
+hipError_t launch_tile_rows(const uint8_t* src, int64_t lds, uint8_t* dst, int64_t rows, int64_t row_bytes,
+                            const float* s_in, float* s_out, hipStream_t stream);
 
 // Data-free smoothing of an FFN's intermediate channels (offline): s [F]
 // and, where the outputs are non-null, the scaled fp32 weights
@@ -133,10 +142,10 @@ hipError_t launch_lora_up(const void* T, int64_t ldt, const void* B, int64_t ldb
 // None (then `out` may be I32) for the plain linear.
 hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                          Elt out, int64_t ldc, void* ws, hipStream_t stream);
+                          Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false);
 hipError_t launch_gemv_w4_gated(const int8_t* A, int64_t lda, const uint8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const uint8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false);
 
 }  // namespace convrot

@@ -130,13 +130,16 @@ class ConvRotLinear:
                 raise ValueError(f"{l.name} and {first.name} use different sign vectors")
             if l.packed.q.shape[1] != first.packed.q.shape[1]:
                 raise ValueError(f"{l.name} and {first.name} have different packed row pitches")
+            if l.packed.layout != first.packed.layout:
+                raise ValueError(f"{l.name} and {first.name} have different weight layouts")
         q = torch.cat([l.packed.q for l in layers])
         scale = torch.cat([l.packed.scale for l in layers])
         p0 = first.packed
+        # (TILE16 weights stack too: each layer's rows are whole 16-row tiles)
         if isinstance(p0, api.PackedW4):
-            packed = api.PackedW4(q, scale, p0.K, p0.group, p0.kind, p0.signs)
+            packed = api.PackedW4(q, scale, p0.K, p0.group, p0.kind, p0.signs, p0.layout)
         else:
-            packed = api.Packed(q, scale, p0.group, p0.kind, p0.signs)
+            packed = api.Packed(q, scale, p0.group, p0.kind, p0.signs, p0.layout)
         bias = None
         if any(l.bias is not None for l in layers):
             bias = torch.cat([l.bias if l.bias is not None else torch.zeros(l.N, dtype=torch.float32,
@@ -145,6 +148,15 @@ class ConvRotLinear:
                      first.kind, packed, None, bias)
         merged.splits = [n for l in layers for n in l.splits]
         return merged
+
+    def tile_for_decode(self) -> None:
+        """Keep the packed weight in the TILE16 layout (``api.tile_weight``),
+        which the small-M path streams faster; the layer then serves inputs of
+        at most 16 rows.  Needs N % 16 == 0 and K % 64 == 0 (int4: K % 128)."""
+        if not self.quantized:
+            raise ValueError(f"{self.name} is routed to bf16; only packed weights are tiled")
+        tile = api.tile_weight_w4 if isinstance(self.packed, api.PackedW4) else api.tile_weight
+        self.packed = tile(self.packed)
 
     def split(self, y: torch.Tensor) -> tuple[torch.Tensor, ...]:
         """The outputs of the layers a merged layer was made from, as column
