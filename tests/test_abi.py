@@ -247,6 +247,16 @@ def test_linear_workspace_query(lib):
     assert ws_bytes(lib, _lib.LINEAR_PLAIN, 0, 1152, 6912) == (_lib.OK, 0)
     assert ws_bytes(lib, _lib.LINEAR_GATED, 16, 1152, 6912)[1] == 2 * down   # two weights' partials
     assert ws_bytes(lib, _lib.LINEAR_BF16, 16, 1152, 6912)[1] > 0
+    # up to 12 rows, a plain int8 launch with fewer tiles than CUs and at
+    # least 32 K units takes one 16-wave workgroup per tile and no split
+    for m in (1, 4, 12):
+        assert ws_bytes(lib, _lib.LINEAR_PLAIN, m, 1152, 6912) == (_lib.OK, 0)
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 13, 1152, 6912) == (_lib.OK, down)
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 4, 1152, 1984)[1] > 0          # 31 K units: split
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 4, 1152, 2048) == (_lib.OK, 0)
+    assert ws_bytes(lib, _lib.LINEAR_PLAIN, 4, 4096, 6912) == (_lib.OK, 0)  # 256 tiles: no split either way
+    assert ws_bytes(lib, _lib.LINEAR_GATED, 1, 1152, 6912)[1] == 2 * down   # gated and bf16 keep the split
+    assert ws_bytes(lib, _lib.LINEAR_BF16, 1, 1152, 6912)[1] > 0
     assert ws_bytes(lib, 9, 16, 1152, 6912)[0] == _lib.ERR_INVALID_ARG
     assert ws_bytes(lib, _lib.LINEAR_PLAIN, 16, 1152, 6913)[0] == _lib.ERR_INVALID_ARG
     assert ws_bytes(lib, _lib.LINEAR_PLAIN, -1, 1152, 6912)[0] == _lib.ERR_INVALID_ARG

@@ -192,3 +192,39 @@ def test_mismatch_is_an_error(cuda):
     w = cr.pack_weight(to_dev(random_rows((16, 1024), 14, dtype="bf16"), torch.bfloat16), 256)
     with pytest.raises(cr.ConvrotError):
         cr.linear(cr.pack_act(x, 64), w)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1152, 6912), (4, 1152, 6912), (12, 1152, 6912), (7, 1000, 4112),
+                                   (3, 72, 2048), (12, 4080, 16400), (2, 16, 40960)])
+def test_small_m_wide_workgroups(cuda, M, N, K):
+    """Up to 12 rows with fewer tiles than CUs: one 16-wave workgroup per tile
+    over all of K (staged and register paths, K tails, ragged N); no
+    workspace is asked for, and one passed is not used.  Plain, GELU and
+    TILE16 weights against the oracle's accumulator; 13 rows take the split."""
+    seed = 3 * M + N + K
+    qx, qw = random_codes((M, K), seed), random_codes((N, K), seed + 1)
+    g = np.random.default_rng(seed)
+    sx = g.uniform(0.5, 1.5, M).astype(np.float32) / np.float32(127.0)
+    sw = g.uniform(0.5, 1.5, N).astype(np.float32) / np.float32(127.0)
+    b = (g.standard_normal(N) * 0.5).astype(np.float32)
+    a, w = _packed_from_codes(qx, sx, 16, cuda), _packed_from_codes(qw, sw, 16, cuda)
+    assert cr.linear_workspace_bytes("plain", M, N, K) == 0
+    A_ref = O.int_gemm(qx, qw)
+    assert np.array_equal(to_np(cr.linear(a, w, out_dtype=torch.int32)).astype(np.int64), A_ref)
+    spare = torch.empty(1 << 20, dtype=torch.uint8, device=cuda)
+    assert np.array_equal(to_np(cr.linear(a, w, out_dtype=torch.int32, workspace=spare)).astype(np.int64), A_ref)
+    y64 = O.epilogue64(A_ref, sx, sw, b)
+    bd = to_dev(b, torch.float32)
+    assert R.rel_fro(to_np(cr.linear(a, w, bd, out_dtype=torch.float32)), y64) <= 1e-5
+    y = to_np(cr.linear_act(a, w, bd, cr.GELU_ERF, out_dtype=torch.float32))
+    assert R.rel_fro(y, R.gelu64(y64, "gelu_erf")) <= 1e-5
+    if N % 16 == 0 and K % 64 == 0:
+        t = cr.tile_weight(w)
+        assert np.array_equal(to_np(cr.linear(a, t, out_dtype=torch.int32)).astype(np.int64), A_ref)
+    # one more row: the K split with its combining launch, the same bits
+    qx13 = random_codes((13, K), seed + 2)
+    a13 = _packed_from_codes(qx13, np.ones(13, np.float32), 16, cuda)
+    ws = cr.linear_workspace("plain", 13, N, K, cuda)
+    assert ws is not None or (N + 15) // 16 >= 256 or K < 1024
+    A13 = to_np(cr.linear(a13, w, out_dtype=torch.int32, workspace=ws)).astype(np.int64)
+    assert np.array_equal(A13, O.int_gemm(qx13, qw))

@@ -29,9 +29,10 @@ def _operands(M, N, K, seed, cuda):
 
 
 # (M, N, K): the decode down projection (72 tiles, K split 8 ways), then a
-# smaller input on the same scratch; then a shape that does not split, and
-# one on the tiled kernel (no scratch at all).
-CALLS = [(16, 1152, 6912), (3, 520, 3072), (1, 6912, 1152), (40, 300, 1024)]
+# smaller split on the same scratch; then shapes that do not split (432
+# tiles; four rows on one 16-wave workgroup per tile), and one on the tiled
+# kernel (no scratch at all).
+CALLS = [(16, 1152, 6912), (16, 520, 3072), (1, 6912, 1152), (4, 1152, 6912), (40, 300, 1024)]
 
 
 def test_noalloc_matches_linear_on_consecutive_calls(cuda):
@@ -57,7 +58,7 @@ def test_noalloc_repeated_call_same_bits(cuda):
     M, N, K = 16, 1152, 6912
     _, _, a, w, b = _operands(M, N, K, 7, cuda)
     first = cr.linear_noalloc(a, w, torch.empty((M, N), dtype=torch.bfloat16, device=cuda), b)
-    _, _, a2, w2, b2 = _operands(8, 900, 4096, 8, cuda)
-    cr.linear_noalloc(a2, w2, torch.empty((8, 900), dtype=torch.bfloat16, device=cuda), b2)
+    _, _, a2, w2, b2 = _operands(16, 900, 4096, 8, cuda)
+    cr.linear_noalloc(a2, w2, torch.empty((16, 900), dtype=torch.bfloat16, device=cuda), b2)
     again = cr.linear_noalloc(a, w, torch.empty((M, N), dtype=torch.bfloat16, device=cuda), b)
     assert torch.equal(first, again)

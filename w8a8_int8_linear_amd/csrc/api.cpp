@@ -285,10 +285,10 @@ convrot_status check_split_workspace(const void* ws, int64_t ws_bytes, int64_t n
 }
 
 // Workspace a small-M (M <= 16) call of `kind` splits K into.
-int64_t small_m_workspace(convrot_linear_kind kind, int64_t N, int64_t K) {
+int64_t small_m_workspace(convrot_linear_kind kind, int64_t M, int64_t N, int64_t K) {
   const bool gated = kind == CONVROT_LINEAR_GATED || kind == CONVROT_LINEAR_W4_GATED;
   const bool w4 = kind == CONVROT_LINEAR_W4 || kind == CONVROT_LINEAR_W4_GATED;
-  return convrot::gemv_workspace_bytes(N, K, kind == CONVROT_LINEAR_BF16, w4, gated);
+  return convrot::gemv_workspace_bytes(M, N, K, kind == CONVROT_LINEAR_BF16, w4, gated);
 }
 
 convrot_status check_act(convrot_act fn) {
@@ -322,7 +322,7 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, M, N, K));
     if (st != CONVROT_OK) return st;
     e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy,
                                 workspace, s, w->layout == CONVROT_LAYOUT_TILE16);
@@ -377,7 +377,7 @@ convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_p
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (M <= convrot::kGemvMaxRows) {
-    const int64_t need = small_m_workspace(CONVROT_LINEAR_PLAIN, N, K);
+    const int64_t need = small_m_workspace(CONVROT_LINEAR_PLAIN, M, N, K);
     if (need > CONVROT_NOALLOC_SCRATCH_BYTES)
       return fail(CONVROT_ERR_INVALID_ARG,
                   "%s: this shape splits K into %lld bytes of partial sums, beyond the %d-byte static scratch "
@@ -408,7 +408,7 @@ convrot_status convrot_linear_workspace_bytes(convrot_linear_kind kind, int64_t 
   if (M == 0 || N == 0) {
     *bytes = 0;
   } else if (M <= convrot::kGemvMaxRows) {
-    *bytes = small_m_workspace(kind, N, K);
+    *bytes = small_m_workspace(kind, M, N, K);
   } else {
     *bytes = kind == CONVROT_LINEAR_W4 ? N * K : kind == CONVROT_LINEAR_W4_GATED ? 2 * N * K : 0;
   }
@@ -425,7 +425,7 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
   const int64_t M = act->rows, N = w->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, M, N, K));
     if (st != CONVROT_OK) return st;
   }
   const auto out = static_cast<convrot::Elt>(ydt);
@@ -513,7 +513,7 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
   const int64_t M = act->rows, N = w_gate->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_GATED, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_GATED, M, N, K));
     if (st != CONVROT_OK) return st;
   }
   const auto out = static_cast<convrot::Elt>(ydt);
@@ -550,7 +550,7 @@ convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, in
                 static_cast<long long>(kMaxLdBytes));
   if (M == 0 || N == 0) return ok();
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_BF16, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_BF16, M, N, K));
     if (st != CONVROT_OK) return st;
   }
   const auto out = static_cast<convrot::Elt>(ydt);
@@ -623,7 +623,7 @@ convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4, M, N, K));
     if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
                                             out, ldy, workspace, s, w->layout == CONVROT_LAYOUT_TILE16),
@@ -670,7 +670,7 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
   const auto a = static_cast<convrot::Act>(fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= convrot::kGemvMaxRows) {
-    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4_GATED, N, K));
+    st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_W4_GATED, M, N, K));
     if (st != CONVROT_OK) return st;
     return from_hip(convrot::launch_gemv_w4_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate,
                                                   w_up->q, w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y,

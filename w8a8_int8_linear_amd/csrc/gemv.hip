@@ -42,6 +42,13 @@
 //    launch that would take device-scope fences, which on this multi-XCD GPU
 //    write back and invalidate a whole L2 each.  Same result bits as the
 //    unsplit kernel in int8 mode.
+//  * Plain int8 launches with at most 12 activation rows and fewer tiles
+//    than CUs take neither: one workgroup of 16 waves per tile splits all
+//    of K among its waves and adds through LDS, one launch (see
+//    wide_tiles).
+//  * TILE16 weights (convrot_tile_weight): the 16 rows of a tile store each
+//    64-byte K unit as 1 KiB of consecutive memory; only the addresses of
+//    the weight loads change.
 //  * int4 weights (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
 //    per-channel int8 safetensors", sections "Solution" and "The rotation":
 //    codes in [-7, 7], one scale per output row, adjacent pairs in a byte):
@@ -520,23 +527,41 @@ void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uin
 constexpr int kMaxUnits = 32;
 inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 8; }
 
+// Few activation rows, few tiles: one workgroup of kWideWaves waves per
+// 16-feature tile streams all of K (its waves split K and add through LDS),
+// with no split across workgroups and so no combining launch.  For plain
+// int8 launches with at most kWideMaxRows rows, fewer tiles than CUs and at
+// least two K units per wave.  Measured on the decode down projection
+// (1152 x 6912, TILE16 weights), against the split with its combining
+// launch: the step 8.7% faster at M = 1, 8% at M = 2, 6% at M = 4, 5% at
+// M = 8, 4.5% at M = 12, but 6.6% slower at M = 16, where the sixteen
+// activation rows double what each of the few CUs reads.
+constexpr int kWideWaves = 16;
+constexpr int64_t kWideMaxRows = 12;
+bool wide_tiles(int64_t M, int64_t N, int64_t nunits, bool i8, bool w4, int sets) {
+  return i8 && !w4 && sets == 1 && M <= kWideMaxRows && (N + 15) / 16 < gemv_num_cus() &&
+         nunits >= 2 * kWideWaves;
+}
+
 // How a small-M launch splits K across workgroups: `splits` K ranges of
 // `units` K units per 16-feature tile (splits == 1: no split) and the bytes
 // of partial sums that needs (kSets x 64 lanes x 16 bytes per tile and
-// range).  K is split only when there are fewer tiles than CUs: aim at two
-// workgroups per CU and keep at least 8 MFMA steps per range.
+// range).  K is split only when there are fewer tiles than CUs and the
+// launch does not take one wide workgroup per tile: aim at two workgroups
+// per CU and keep at least 8 MFMA steps per range.
 struct SplitPlan {
   int64_t splits;
   int64_t units;
   int64_t bytes;
 };
 
-SplitPlan split_plan(int64_t N, int64_t kbytes, int sets, bool w4) {
+SplitPlan split_plan(int64_t M, int64_t N, int64_t kbytes, int sets, bool w4, bool i8) {
   const int64_t unit = w4 ? 128 : kStepBytes;
   const int64_t nunits = (kbytes + unit - 1) / unit;
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = gemv_num_cus();
   const SplitPlan none{1, nunits, 0};
+  if (wide_tiles(M, N, nunits, i8, w4, sets)) return none;
   // int4 weights stream half the bytes per K unit, and the second launch
   // costs more than the split saves (decode down projection, 1152 x 6912,
   // M = 16, same box: 7.4 us unsplit against 8.6 us split with its
@@ -570,7 +595,21 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(kbytes);
 
   // The caller's workspace (validated to hold plan.bytes) enables the split.
-  const SplitPlan plan = split_plan(N, kbytes, kSets, W4);
+  if constexpr (I8 && !W4 && !GATED) {
+    if (wide_tiles(M, N, nunits, I8, W4, kSets)) {
+      const int per = static_cast<int>((nunits + kWideWaves - 1) / kWideWaves);
+      const dim3 grid(static_cast<unsigned>(tiles));
+      const SplitArgs none{nullptr, 1, 0};
+      if (per >= kStageMinUnits)
+        hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, true>), grid,
+                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled);
+      else
+        hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, false>), grid,
+                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled);
+      return hipGetLastError();
+    }
+  }
+  const SplitPlan plan = split_plan(M, N, kbytes, kSets, W4, I8);
   if (plan.splits > 1 && ws != nullptr) {
     const int64_t units = plan.units, splits = plan.splits;
     const int waves = waves_for(units);
@@ -618,9 +657,9 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
 
 }  // namespace
 
-int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gated) {
+int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, bool bf16, bool w4, bool gated) {
   if (N <= 0 || K <= 0) return 0;
-  return split_plan(N, bf16 ? 2 * K : K, gated ? 2 : 1, w4).bytes;
+  return split_plan(M, N, bf16 ? 2 * K : K, gated ? 2 : 1, w4, !bf16).bytes;
 }
 
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,

@@ -86,10 +86,10 @@ hipError_t launch_gemm_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, 
 // split over K) or a 16-byte aligned buffer of at least
 // gemv_workspace_bytes(...) bytes for the split's partial sums.
 constexpr int64_t kGemvMaxRows = 16;
-// Partial-sum bytes a small-M launch over N outputs and K inputs splits
-// into on the current device (0: that shape does not split).  bf16: the
-// unquantised mode; w4: int4 weights; gated: two weights per launch.
-int64_t gemv_workspace_bytes(int64_t N, int64_t K, bool bf16, bool w4, bool gated);
+// Partial-sum bytes a small-M launch over M rows, N outputs and K inputs
+// splits into on the current device (0: that shape does not split).  bf16:
+// the unquantised mode; w4: int4 weights; gated: two weights per launch.
+int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, bool bf16, bool w4, bool gated);
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                           const float* sa, const float* sb, const float* bias,
                           int64_t M, int64_t N, int64_t K,
