@@ -78,6 +78,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0    # 8 TB/s HBM3E
 COLD_BYTES = 512 << 20
 SMALL_M = 16             # up to this many rows a linear runs on the weight-streaming kernel
+PACKIN_GATED_ROWS = 3    # up to this many decode rows the gated launch packs its own input
 METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
 # the sources each kernel is compiled from; a traffic summary is valid only for these exact bytes
 KERNEL_SOURCE = {
@@ -85,9 +86,9 @@ KERNEL_SOURCE = {
     "gemm_i8_act": ("gemm_kernel.h", "gemm_pp.h", "lanes.h", "epilogue.h", "gemm_act.hip"),
     "gemm_i8_gated": ("gemm_kernel.h", "epilogue.h", "gemm_gated.hip"),
     "gemm_bf16": ("gemm_kernel.h", "gemm_pp.h", "lanes.h", "epilogue.h", "gemm_bf16.hip"),
-    "gemv_i8": ("gemv.hip", "epilogue.h", "w4_codec.h"),
-    "gemv_w4": ("gemv.hip", "epilogue.h", "w4_codec.h"),
-    "pack_rows": ("pack_rows.hip", "lanes.h"),
+    "gemv_i8": ("gemv.hip", "epilogue.h", "w4_codec.h", "pack_core.h", "lanes.h"),
+    "gemv_w4": ("gemv.hip", "epilogue.h", "w4_codec.h", "pack_core.h", "lanes.h"),
+    "pack_rows": ("pack_rows.hip", "pack_core.h", "lanes.h"),
 }
 
 
@@ -161,9 +162,12 @@ def make_workload(name: str):
 class Op:
     """One timed launch of the step and what it moves or computes."""
 
-    def __init__(self, name, fn, kind, M=0, N=0, K=0, in_b=0, out_b=0, epilogue=""):
+    def __init__(self, name, fn, kind, M=0, N=0, K=0, in_b=0, out_b=0, epilogue="", packin=False):
         self.name, self.fn, self.kind = name, fn, kind
         self.M, self.N, self.K, self.in_b, self.out_b = M, N, K, in_b, out_b
+        # a linear that packs its own activation rows: reads X (in_b bytes per
+        # element) instead of the int8 codes and scales
+        self.packin = packin
         # "" plain, "act" activation in the epilogue, "gated" act(gate) * up:
         # N output columns from 2N weight rows
         self.epilogue = epilogue
@@ -198,7 +202,8 @@ class Op:
         if self.kind in ("int8", "int4"):
             R = self.rows
             wb = R * K if self.kind == "int8" else R * K // 2  # int4: two codes per byte
-            return M * K + 4 * M + wb + 8 * R + M * N * self.out_b
+            xb = M * K * self.in_b if self.packin else M * K + 4 * M
+            return xb + wb + 8 * R + M * N * self.out_b
         if self.kind == "bf16":
             return 2 * M * K + 2 * N * K + 4 * N + M * N * self.out_b
         if self.kind == "lora":
@@ -212,8 +217,15 @@ class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
     def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False,
-                 tiled=False):
+                 tiled=False, packin=False):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
+        # decode with at most PACKIN_GATED_ROWS rows and int8 weights: the
+        # gated launch packs its own bf16 input rows (the down projection,
+        # whose 16-wave workgroups would each pack a 6912-wide row, keeps the
+        # separate pack, which measured faster there)
+        self.packin = (packin and fused and wl.cfg == 5 and wl.X.shape[0] <= PACKIN_GATED_ROWS
+                       and wl.xdtype == "bf16" and wl.extra.get("wbits") != 4
+                       and all(l.W.shape[1] % wl.G == 0 for l in wl.linears))
         self.producer_fusion = producer_fusion and fused and wl.cfg == 3
         # weights in the TILE16 layout, which only the M <= 16 path reads
         self.tiled = tiled and wl.X.shape[0] <= 16
@@ -345,6 +357,8 @@ class StepSet:
         ops = []
         names = [l.name for l in wl.linears]
         first = "_".join(names) if self.merge else names[0]
+        if self.packin:
+            return self._plan_packin(dev)
         if self._quant(self.W[first]):
             src0 = self._packed(M, K, dev)
             ops.append(self._pack_op("pack_act", self.X, src0))
@@ -450,6 +464,22 @@ class StepSet:
                 ops.append(self._linear_op("down", h, self._out("down", M, dev)))
         else:
             raise SystemExit(f"no step plan for config {wl.cfg}")
+        return ops
+
+    def _plan_packin(self, dev):
+        """Decode step in three launches: gate and up with the pack of X in
+        one, then the pack of h and the down projection."""
+        cr = self.cr
+        M = self.X.shape[0]
+        wg, wu = self.W["gate"], self.W["up"]
+        bg, bu = self.b["gate"], self.b["up"]
+        h = self._out("gate", M, dev)
+        ops = [Op("linear_gate_up", lambda: cr.linear_gated_packin(self.X, wg, wu, bg, bu, cr.GELU_TANH, out=h),
+                  "int8", M=M, N=wg.rows, K=wg.K, in_b=self.X.element_size(), out_b=h.element_size(),
+                  epilogue="gated", packin=True)]
+        pa2 = self._packed(M, h.shape[1], dev)
+        ops.append(self._pack_op("pack_act2", h, pa2))
+        ops.append(self._linear_op("down", pa2, self._out("down", M, dev)))
         return ops
 
     def step(self, ev=None):
@@ -624,6 +654,9 @@ def main():
     ap.add_argument("--row-weights", action="store_true",
                     help="decode (M <= 16): keep the packed weights in the row layout instead of the TILE16 layout "
                          "the weight-streaming kernel reads fastest")
+    ap.add_argument("--no-packin", action="store_true",
+                    help="decode with at most 3 rows: pack the gated launch's input in a launch of its own instead "
+                         "of inside the gated launch")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy and MFMA-only ceilings")
     args = ap.parse_args()
@@ -649,10 +682,11 @@ def main():
     merge = not args.separate_linears
     pf = args.producer_fusion
     tl = not args.row_weights
-    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl)]
+    pin = not args.no_packin
+    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl, packin=pin)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
         sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf,
-                            tiled=tl))
+                            tiled=tl, packin=pin))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -793,6 +827,7 @@ def main():
                    "N": [l.W.shape[0] for l in wl.linears], "G": wl.G, "rotation": wl.kind, "in": wl.xdtype,
                    "epilogue": "fused" if fused else "separate", "launch": "eager" if args.eager else "graph",
                    "producer_fusion": bool(sets[0].producer_fusion),
+                   "activation_pack": "in the gated launch" if sets[0].packin else "own launch",
                    "weight_layout": "tile16" if any(getattr(v, "layout", "rows") == "tile16"
                                                     for v in sets[0].W.values()) else "rows",
                    "shared_pack_linears": "one launch" if sets[0].merge else "one launch each",

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 8
+#define CONVROT_ABI_VERSION 9
 
 typedef enum {
   CONVROT_OK = 0,
@@ -361,6 +361,40 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
                                     const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
                                     convrot_dtype ydt, int64_t ldy, void* workspace, int64_t workspace_bytes,
                                     void* stream);
+
+/* Few-row linears that pack their own activation rows: the rotation, row
+ * maximum and quantisation of convrot_pack_act ("INT8 Convrot Safetensors",
+ * "Runtime activation quantization"; "Backend support" on fusing the three)
+ * done inside the weight-streaming launch, every workgroup packing the rows
+ * into on-chip memory with the pack kernel's operations, then the linear of
+ * convrot_linear_act (plain) or convrot_linear_gated on those codes, all in
+ * one launch.  The result bits equal packing with convrot_pack_act and then
+ * calling convrot_linear / convrot_linear_act / convrot_linear_gated; the
+ * packed rows are not written out.  For decoding, where the two launches'
+ * fixed costs dominate.
+ *   X       [M, ldx] bf16, rows 16-byte aligned (ldx * 2 a multiple of 16);
+ *           other dtypes are CONVROT_ERR_DTYPE (pack them with
+ *           convrot_pack_act)
+ *   M       0 to 4 rows (more: CONVROT_ERR_INVALID_ARG)
+ *   w       packed weight [N, K] (either layout); its rotation (G, kind,
+ *           signs) is the one applied to X.  K at most 16384 for
+ *           convrot_linear_packin and 4096 for convrot_linear_gated_packin
+ *           (CONVROT_ERR_INVALID_ARG above)
+ *   bias    [N] fp32 or NULL
+ *   fn      CONVROT_ACT_NONE, _GELU_ERF or _GELU_TANH (plain); a GELU form
+ *           (gated)
+ *   Y       [M, ldy] of ydt: CONVROT_F32 or CONVROT_BF16, or CONVROT_I32
+ *           (the raw accumulator) for the plain form without activation
+ * The gated form takes w_gate and w_up as convrot_linear_gated does (same N,
+ * K, rotation and layout: CONVROT_ERR_MISMATCH / CONVROT_ERR_INVALID_ARG).
+ * Needs no workspace.  M = 0 or N = 0 launches nothing. */
+convrot_status convrot_linear_packin(const void* X, convrot_dtype xdt, int64_t ldx, int64_t M, const convrot_packed* w,
+                                     const float* bias, convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy,
+                                     void* stream);
+convrot_status convrot_linear_gated_packin(const void* X, convrot_dtype xdt, int64_t ldx, int64_t M,
+                                           const convrot_packed* w_gate, const float* b_gate,
+                                           const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
+                                           convrot_dtype ydt, int64_t ldy, void* stream);
 
 /* The unquantised path for layers the rotation cannot cover (K % G != 0):
  *   Y[r, o] = sum_i X[r, i] W[o, i] + bias[o]

@@ -555,3 +555,60 @@ def test_packing_and_unpacking_stay_in_rows(lib):
     assert lib.convrot_pack_weight_w4(A16C, _lib.BF16, 256, ctypes.byref(out), None) == _lib.ERR_INVALID_ARG
     assert lib.convrot_unpack_w4(ctypes.byref(out), A16C, 256, None) == _lib.ERR_INVALID_ARG
     assert b"ROWS" in lib.convrot_last_error()
+
+
+# -- linears that pack their own activation rows ----------------------------------
+
+def packin_status(lib, X=A16C, xdt=_lib.BF16, ldx=256, M=1, w=None, fn=_lib.ACT_NONE, ydt=_lib.BF16, Y=0x90000,
+                  ldy=None):
+    w = w if w is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    return lib.convrot_linear_packin(X, xdt, ldx, M, ctypes.byref(w), None, fn, Y, ydt,
+                                     ldy if ldy is not None else w.rows, None)
+
+
+def gated_packin_status(lib, M=1, gate=None, up=None, fn=_lib.ACT_GELU_TANH, ydt=_lib.BF16, xdt=_lib.BF16, ldx=None):
+    g = gate if gate is not None else packed(rows=64, q=0x40000, scale=0x50000)
+    u = up if up is not None else packed(rows=64, q=0x80000, scale=0x90000)
+    return lib.convrot_linear_gated_packin(A16C, xdt, ldx if ldx is not None else g.K, M, ctypes.byref(g), None,
+                                           ctypes.byref(u), None, fn, 0xA0000, ydt, g.rows, None)
+
+
+def test_packin_checks(lib):
+    """Every rule is checked on the host before any launch."""
+    assert packin_status(lib, M=5) == _lib.ERR_INVALID_ARG
+    assert b"0 to 4 rows" in lib.convrot_last_error()
+    assert packin_status(lib, M=-1) == _lib.ERR_INVALID_ARG
+    assert packin_status(lib, xdt=_lib.F32) == _lib.ERR_DTYPE
+    assert packin_status(lib, X=A16C + 8) == _lib.ERR_ALIGN            # rows read in 16-byte chunks
+    assert packin_status(lib, ldx=252) == _lib.ERR_INVALID_ARG          # ldx < K
+    assert packin_status(lib, ldx=260) == _lib.ERR_ALIGN                # 520-byte row pitch
+    assert packin_status(lib, X=None) == _lib.ERR_INVALID_ARG
+    assert packin_status(lib, fn=7) == _lib.ERR_INVALID_ARG
+    assert packin_status(lib, fn=_lib.ACT_GELU_ERF, ydt=_lib.I32) == _lib.ERR_DTYPE
+    assert packin_status(lib, ydt=9) == _lib.ERR_DTYPE
+    assert packin_status(lib, Y=None) == _lib.ERR_INVALID_ARG
+    assert packin_status(lib, ldy=32) == _lib.ERR_INVALID_ARG           # ldy < N
+    big = packed(rows=64, K=16400, G=16, q=0x40000, scale=0x50000)
+    assert packin_status(lib, w=big, ldx=16400) == _lib.ERR_INVALID_ARG
+    assert b"16384" in lib.convrot_last_error()
+    assert packin_status(lib, w=packed(rows=64, G=64, kind=9, q=0x40000)) == _lib.ERR_INVALID_ARG
+    assert packin_status(lib, M=0) == _lib.OK
+    assert packin_status(lib, w=packed(rows=0, q=0x40000)) == _lib.OK
+    assert lib.convrot_linear_packin(A16C, _lib.BF16, 256, 1, None, None, 0, 0x90000, _lib.BF16, 64,
+                                     None) == _lib.ERR_INVALID_ARG
+
+
+def test_gated_packin_checks(lib):
+    assert gated_packin_status(lib, fn=_lib.ACT_NONE) == _lib.ERR_INVALID_ARG
+    assert gated_packin_status(lib, ydt=_lib.I32) == _lib.ERR_DTYPE
+    assert gated_packin_status(lib, xdt=_lib.F32) == _lib.ERR_DTYPE
+    assert gated_packin_status(lib, M=5) == _lib.ERR_INVALID_ARG
+    k4112 = dict(K=4112, G=16)
+    assert gated_packin_status(lib, gate=packed(rows=64, q=0x40000, **k4112),
+                               up=packed(rows=64, q=0x80000, **k4112)) == _lib.ERR_INVALID_ARG
+    assert gated_packin_status(lib, up=packed(rows=48, q=0x80000)) == _lib.ERR_MISMATCH
+    assert gated_packin_status(lib, up=packed(rows=64, G=64, q=0x80000)) == _lib.ERR_MISMATCH
+    tiled = packed(rows=64, q=0x80000, layout=_lib.LAYOUT_TILE16)
+    assert gated_packin_status(lib, up=tiled) == _lib.ERR_INVALID_ARG
+    assert b"same layout" in lib.convrot_last_error()
+    assert gated_packin_status(lib, M=0) == _lib.OK

@@ -7,8 +7,9 @@ library has not been built.
 """
 
 from .api import (  # noqa: F401
-    GELU_ERF, GELU_TANH, RANDOMIZED, REGULAR, ROWS, TILE16, Packed, PackedW4, linear, linear_act, linear_act_rowmax,
-    linear_bf16, linear_gated, linear_noalloc, linear_w4, linear_w4_gated, linear_workspace, linear_workspace_bytes,
+    GELU_ERF, GELU_TANH, PACKIN_MAX_ROWS, RANDOMIZED, REGULAR, ROWS, TILE16, Packed, PackedW4, linear, linear_act,
+    linear_act_rowmax, linear_bf16, linear_gated, linear_gated_packin, linear_noalloc, linear_packin, linear_w4,
+    linear_w4_gated, linear_workspace, linear_workspace_bytes,
     lora_add, lora_workspace_bytes, pack_act, pack_act_rowmax, pack_weight, pack_weight_w4, rotate, smooth_ffn,
     tile_weight, tile_weight_w4, unpack_w4,
 )

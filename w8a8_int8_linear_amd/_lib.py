@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # convrot_status
@@ -39,6 +39,8 @@ EXPORTED = (
     "convrot_linear_act_rowmax",
     "convrot_pack_act_rowmax",
     "convrot_linear_gated",
+    "convrot_linear_packin",
+    "convrot_linear_gated_packin",
     "convrot_linear_bf16",
     "convrot_rotate",
     "convrot_pack_weight_w4",
@@ -115,6 +117,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.convrot_pack_act_rowmax.restype = c_int
     lib.convrot_linear_gated.argtypes = [P, P, vp, P, vp, c_int, vp, c_int, c_i64, vp, c_i64, vp]
     lib.convrot_linear_gated.restype = c_int
+    lib.convrot_linear_packin.argtypes = [vp, c_int, c_i64, c_i64, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_packin.restype = c_int
+    lib.convrot_linear_gated_packin.argtypes = [vp, c_int, c_i64, c_i64, P, vp, P, vp, c_int, vp, c_int, c_i64, vp]
+    lib.convrot_linear_gated_packin.restype = c_int
     lib.convrot_linear_bf16.argtypes = [vp, c_i64, vp, c_i64, vp, c_i64, c_i64, c_i64, vp, c_int, c_i64, vp, c_i64,
                                         vp]
     lib.convrot_linear_bf16.restype = c_int

@@ -339,6 +339,64 @@ def linear_gated(act_in: Packed, w_gate: Packed, w_up: Packed, b_gate: torch.Ten
     return out
 
 
+PACKIN_MAX_ROWS = 4
+
+
+def _packin_input(x: torch.Tensor, w: Packed) -> None:
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be a bfloat16 [M, {w.K}] tensor")
+    if x.shape[1] > 1 and x.stride(1) != 1:
+        raise ValueError("x must have unit stride along K")
+    if x.device != w.q.device:
+        raise ValueError("x and the packed weight must be on one device")
+
+
+def linear_packin(x: torch.Tensor, w: Packed, bias: torch.Tensor | None = None, act: str | None = None,
+                  out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``linear`` (or ``linear_act`` with ``act``) of bf16 rows x [M, K],
+    M <= PACKIN_MAX_ROWS, packed inside the same launch with the weight's
+    rotation (convrot_linear_packin): the result bits of
+    ``linear(pack_act(x, ...), w)`` in one launch instead of two."""
+    _packin_input(x, w)
+    M, N = x.shape[0], w.rows
+    dev = x.device
+    if act is None:
+        if out is None:
+            if out_dtype not in _DT:
+                raise ValueError("output must be float32, bfloat16 or int32")
+            out = torch.empty((M, N), dtype=out_dtype, device=dev)
+        _check_out(out, M, N, tuple(_DT), dev)
+        _check_bias(bias, N, dev)
+        code = _lib.ACT_NONE
+    else:
+        out = _out_and_bias(M, N, dev, out, out_dtype, bias)
+        code = _act_code(act)
+    b = w.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_packin(x.data_ptr(), _lib.BF16, _ld(x), M, ctypes.byref(b), _ptr(bias), code,
+                                         out.data_ptr(), _DT[out.dtype], _ld(out), _stream(dev)))
+    return out
+
+
+def linear_gated_packin(x: torch.Tensor, w_gate: Packed, w_up: Packed, b_gate: torch.Tensor | None = None,
+                        b_up: torch.Tensor | None = None, act: str = GELU_TANH,
+                        out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``linear_gated`` of bf16 rows x [M, K], M <= PACKIN_MAX_ROWS, packed
+    inside the same launch (convrot_linear_gated_packin)."""
+    _packin_input(x, w_gate)
+    M = x.shape[0]
+    dev = x.device
+    out = _out_and_bias(M, w_gate.rows, dev, out, out_dtype, b_gate)
+    _check_bias(b_up, w_up.rows, dev, "b_up")
+    g, u = w_gate.descriptor(), w_up.descriptor()
+    lib = _lib.load()
+    _lib.check(lib.convrot_linear_gated_packin(
+        x.data_ptr(), _lib.BF16, _ld(x), M, ctypes.byref(g), _ptr(b_gate), ctypes.byref(u), _ptr(b_up),
+        _act_code(act), out.data_ptr(), _DT[out.dtype], _ld(out), _stream(dev)))
+    return out
+
+
 def linear_bf16(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
                 out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:

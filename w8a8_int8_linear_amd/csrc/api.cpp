@@ -297,6 +297,38 @@ convrot_status check_act(convrot_act fn) {
   return CONVROT_OK;
 }
 
+// Checks of a linear that packs its own activation rows: bf16 X [M, ldx]
+// with 16-byte aligned rows, at most kPackinMaxRows rows, a weight whose K
+// the launch covers with one 16-feature chunk per thread, and Y [M, N].
+convrot_status check_packin(const char* fn, const void* X, convrot_dtype xdt, int64_t ldx, int64_t M,
+                            const convrot_packed* w, const float* bias, const void* Y, convrot_dtype ydt, int64_t ldy,
+                            bool gated, bool i32_ok, int* log2G) {
+  if (w == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: weight descriptor is NULL", fn);
+  convrot_status st = check_packed("weight", w, log2G);
+  if (st != CONVROT_OK) return st;
+  if (xdt != CONVROT_BF16)
+    return fail(CONVROT_ERR_DTYPE, "%s: X must be CONVROT_BF16 (pack other inputs with convrot_pack_act)", fn);
+  if (M < 0 || M > convrot::kPackinMaxRows)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: M = %lld; a packing linear takes 0 to %lld rows", fn,
+                static_cast<long long>(M), static_cast<long long>(convrot::kPackinMaxRows));
+  if (w->K > convrot::packin_max_k(gated))
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: K = %lld exceeds the %lld a packing launch covers", fn,
+                static_cast<long long>(w->K), static_cast<long long>(convrot::packin_max_k(gated)));
+  st = check_matrix("X", X, M, w->K, ldx, 2);
+  if (st != CONVROT_OK) return st;
+  if (ydt != CONVROT_F32 && ydt != CONVROT_BF16 && !(i32_ok && ydt == CONVROT_I32))
+    return fail(CONVROT_ERR_DTYPE, "%s: output must be CONVROT_F32 or CONVROT_BF16%s", fn,
+                i32_ok ? " or CONVROT_I32" : "");
+  st = check_matrix("Y", Y, M, w->rows, ldy, elt_size(ydt), false);
+  if (st != CONVROT_OK) return st;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)
+    return fail(CONVROT_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (w->ld > kMaxLdBytes)
+    return fail(CONVROT_ERR_INVALID_ARG, "leading dimension of the packed weight exceeds %lld bytes",
+                static_cast<long long>(kMaxLdBytes));
+  return CONVROT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -527,6 +559,53 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
           : convrot::launch_gemm_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_gated");
+}
+
+convrot_status convrot_linear_packin(const void* X, convrot_dtype xdt, int64_t ldx, int64_t M, const convrot_packed* w,
+                                     const float* bias, convrot_act fn, void* Y, convrot_dtype ydt, int64_t ldy,
+                                     void* stream) {
+  const char* what = "convrot_linear_packin";
+  if (fn != CONVROT_ACT_NONE && fn != CONVROT_ACT_GELU_ERF && fn != CONVROT_ACT_GELU_TANH)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(fn));
+  int log2G = 0;
+  convrot_status st = check_packin(what, X, xdt, ldx, M, w, bias, Y, ydt, ldy, false, fn == CONVROT_ACT_NONE, &log2G);
+  if (st != CONVROT_OK) return st;
+  if (M == 0 || w->rows == 0) return ok();
+  const hipError_t e = convrot::launch_gemv_i8_packin(
+      X, ldx, log2G, static_cast<convrot::RotKind>(w->rot.kind), w->rot.signs, w->q, w->ld, w->scale, bias,
+      static_cast<convrot::Act>(fn), M, w->rows, w->K, Y, static_cast<convrot::Elt>(ydt), ldy,
+      static_cast<hipStream_t>(stream), w->layout == CONVROT_LAYOUT_TILE16);
+  return from_hip(e, what);
+}
+
+convrot_status convrot_linear_gated_packin(const void* X, convrot_dtype xdt, int64_t ldx, int64_t M,
+                                           const convrot_packed* w_gate, const float* b_gate,
+                                           const convrot_packed* w_up, const float* b_up, convrot_act fn, void* Y,
+                                           convrot_dtype ydt, int64_t ldy, void* stream) {
+  const char* what = "convrot_linear_gated_packin";
+  convrot_status st = check_act(fn);
+  if (st != CONVROT_OK) return st;
+  int lg = 0, lu = 0;
+  st = check_packin(what, X, xdt, ldx, M, w_gate, b_gate, Y, ydt, ldy, true, false, &lg);
+  if (st != CONVROT_OK) return st;
+  st = check_packin(what, X, xdt, ldx, M, w_up, b_up, Y, ydt, ldy, true, false, &lu);
+  if (st != CONVROT_OK) return st;
+  if (w_gate->rows != w_up->rows || w_gate->K != w_up->K)
+    return fail(CONVROT_ERR_MISMATCH, "%s: gate is [%lld, %lld] but up is [%lld, %lld]", what,
+                static_cast<long long>(w_gate->rows), static_cast<long long>(w_gate->K),
+                static_cast<long long>(w_up->rows), static_cast<long long>(w_up->K));
+  if (w_gate->rot.group != w_up->rot.group || w_gate->rot.kind != w_up->rot.kind ||
+      w_gate->rot.signs != w_up->rot.signs)
+    return fail(CONVROT_ERR_MISMATCH, "%s: gate and up were packed with different rotations", what);
+  if (w_gate->layout != w_up->layout)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: gate and up weights must have the same layout", what);
+  if (M == 0 || w_gate->rows == 0) return ok();
+  const hipError_t e = convrot::launch_gemv_i8_gated_packin(
+      X, ldx, lg, static_cast<convrot::RotKind>(w_gate->rot.kind), w_gate->rot.signs, w_gate->q, w_gate->ld,
+      w_gate->scale, b_gate, w_up->q, w_up->ld, w_up->scale, b_up, static_cast<convrot::Act>(fn), M, w_gate->rows,
+      w_gate->K, Y, static_cast<convrot::Elt>(ydt), ldy, static_cast<hipStream_t>(stream),
+      w_gate->layout == CONVROT_LAYOUT_TILE16);
+  return from_hip(e, what);
 }
 
 convrot_status convrot_linear_bf16(const void* X, int64_t ldx, const void* W, int64_t ldw, const float* bias,

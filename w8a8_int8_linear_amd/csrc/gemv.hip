@@ -65,6 +65,7 @@
 #include "device.h"
 #include "epilogue.h"
 #include "launchers.h"
+#include "pack_core.h"
 #include "w4_codec.h"
 
 namespace convrot {
@@ -123,6 +124,76 @@ struct SplitArgs {
   int splits;
   int steps;
 };
+
+// Activation rows a launch packs itself (XP): bf16 X [M, ldx elements],
+// rotated with G = 2^log2g of the regular or randomized kind (K signs for
+// the latter) and quantised with the pack kernel's steps (pack_core.h).
+struct XPackArgs {
+  const void* X;
+  int64_t ldx;
+  int log2g;
+  int rand;
+  const int8_t* signs;
+};
+
+// The XP prologue: every thread of the workgroup (T >= K / 16 of them)
+// takes one 16-feature chunk of each row, in the pack kernel's lane order
+// (G / 16 lanes per group, chunk_in_group): the loads of all M rows (and
+// of the chunk's signs) are issued first, then each row is rotated and its
+// wavefront maximum posted; after one barrier every row's maximum gives its
+// scale s_x[r] and the 16 codes of the chunk go to `codes` (row pitch
+// `pitch` bytes).  Chunks past K read zeros and write nothing.  Ends with a
+// barrier.
+template <bool RAND, int WAVES>
+__device__ __forceinline__ void xpack_rows(const XPackArgs& xp, int M, int K, uint8_t* codes, int pitch, float* s_x,
+                                           uint32_t* wmax) {
+  static_assert(WAVES % 4 == 0, "wavefront maxima are read four at a time");
+  using namespace pack;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int L = xp.log2g >= 4 ? 1 << (xp.log2g - 4) : 1;  // lanes per group
+  const int off = ((tid / L) * L + chunk_in_group<RAND>(tid % L)) * kChunk;
+  // Every load first, unconditionally (rows past M re-read row M - 1), so
+  // that all of them are in flight together.
+  u32x4 raw[kPackinMaxRows][2];
+#pragma unroll
+  for (int r = 0; r < kPackinMaxRows; ++r) {
+    const __amdgpu_buffer_rsrc_t xr =
+        row_rsrc(static_cast<const uint16_t*>(xp.X) + static_cast<int64_t>(min(r, M - 1)) * xp.ldx, 2 * K);
+    raw[r][0] = __builtin_amdgcn_raw_buffer_load_b128(xr, 2 * off, 0, kNonTemporal);
+    raw[r][1] = __builtin_amdgcn_raw_buffer_load_b128(xr, 2 * off + 16, 0, kNonTemporal);
+  }
+  u32x4 sv = {0, 0, 0, 0};
+  if constexpr (RAND) sv = load_signs(row_rsrc(xp.signs, K), off);
+  float v[kPackinMaxRows][kChunk];
+#pragma unroll
+  for (int r = 0; r < kPackinMaxRows; ++r) {
+    if (r < M) {
+      bf16_words_to_chunk(raw[r][0], raw[r][1], v[r]);
+      rotate_chunk<RAND>(v[r], lane, xp.log2g, sv);
+      const uint32_t bits = wave_max_bits(as_u(chunk_absmax(v[r], 0.f)));
+      if (lane == 0) wmax[r * WAVES + wid] = bits;
+    }
+  }
+  __syncthreads();
+  const float norm = rot_norm_rt(xp.log2g, RAND);
+#pragma unroll
+  for (int r = 0; r < kPackinMaxRows; ++r) {
+    if (r < M) {
+      // the row's WAVES wavefront maxima, read as 16-byte vectors
+      uint32_t amax_bits = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; w += 4) {
+        const u32x4 m4 = *reinterpret_cast<const u32x4*>(wmax + r * WAVES + w);
+        amax_bits = max(amax_bits, max(max(m4.x, m4.y), max(m4.z, m4.w)));
+      }
+      const float amax_u = as_f(amax_bits);
+      if (tid == 0) s_x[r] = row_scale(amax_u, norm, 127.f);
+      if (off < K)
+        *reinterpret_cast<u32x4*>(codes + r * pitch + off) = quant_chunk(v[r], quant_factor(amax_u, 127.f));
+    }
+  }
+  __syncthreads();
+}
 
 // The epilogue's per-row and per-feature operands of one lane (row
 // m = lane & 15, features n0 + 4 (lane >> 4) + r), loaded by the epilogue
@@ -218,13 +289,14 @@ __device__ __forceinline__ void tile_epilogue(const Acc* acc, int lane, int n0, 
 // the same assignment of k to (MFMA, lane), so every product pairs matching
 // k; the int32 sum does not depend on the order.
 template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPLIT = false, bool W4 = false,
-          int TILES = 1, bool DMA = false>
+          int TILES = 1, bool DMA = false, bool XP = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled) {
+    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled, XPackArgs xp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   static_assert(!W4 || I8, "int4 weights pair with int8 activations");
   static_assert(TILES == 1 || (!GATED && !SPLIT), "several tiles per workgroup only on the plain unsplit path");
+  static_assert(!XP || (I8 && !W4 && !SPLIT && TILES == 1), "a packing launch: int8 weights, one tile, no split");
   using Acc = typename Mma<I8>::Acc;
   constexpr int kSets = GATED ? 2 : 1;         // weight row sets streamed (gate, up)
   constexpr int kUnit = W4 ? 128 : kStepBytes;  // activation bytes per K unit
@@ -257,7 +329,40 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     wrow[0][i] = B + nt * ldb + r * pitch1 + ch * 16;
     if constexpr (GATED) wrow[kSets - 1][i] = epi.B2 + nt * epi.ldb2 + r * pitch2 + ch * 16;
   }
-  const uint8_t* xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * (W4 ? 32 : 16);
+  // XP: the workgroup packs the M activation rows into LDS (codes at a
+  // pitch of K + 16 bytes, then the row scales and the wavefront maxima;
+  // the first round of weight transfers is issued before, so it lands
+  // meanwhile), and every activation fragment is read from there.
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  typedef const __attribute__((address_space(3))) uint8_t* lds_bytes_t;
+  typedef const __attribute__((address_space(3))) i32x4* lds_i32x4_t;
+  const uint8_t* xrow = nullptr;
+  lds_bytes_t xlds = nullptr;
+  if constexpr (XP) {
+    xlds = (lds_bytes_t)(xs + min(row, M - 1) * (kbytes + 16) + ch * 16);
+  } else {
+    xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * (W4 ? 32 : 16);
+  }
+  auto xp_prologue = [&]() {
+    if constexpr (XP) {
+      const int pitch = kbytes + 16;
+      float* s_x = reinterpret_cast<float*>(xs + M * pitch);
+      uint32_t* wmax = reinterpret_cast<uint32_t*>(s_x + 4);
+      if (xp.rand)
+        xpack_rows<true, WAVES>(xp, M, kbytes, xs, pitch, s_x, wmax);
+      else
+        xpack_rows<false, WAVES>(xp, M, kbytes, xs, pitch, s_x, wmax);
+      epi.sa = s_x;
+    }
+  };
+  // 16 activation bytes of this lane at `byte` (LDS reads in XP launches,
+  // so they never count against the vector-memory counter).
+  auto xload = [&](int byte) -> i32x4 {
+    if constexpr (XP)
+      return *(lds_i32x4_t)(xlds + byte);
+    else
+      return *reinterpret_cast<const i32x4*>(xrow + byte);
+  };
 
   const int nunits = (kbytes + kUnit - 1) / kUnit;
   // K units [u_lo, u_hi) of this workgroup, `per` of them per wave.
@@ -267,10 +372,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int u_end = min(u_hi, u_begin + per);
 
   EpiIn<GATED> epi_in[SPLIT ? 1 : TILES];
-  if (!SPLIT && wid == 0) {
+  auto load_epi_in = [&]() {
+    if (!SPLIT && wid == 0) {
 #pragma unroll
-    for (int i = 0; i < (SPLIT ? 1 : TILES); ++i) epi_in[i] = load_epi<I8, OUT, GATED>(lane, n0 + 16 * i, epi, M, N);
-  }
+      for (int i = 0; i < (SPLIT ? 1 : TILES); ++i)
+        epi_in[i] = load_epi<I8, OUT, GATED>(lane, n0 + 16 * i, epi, M, N);
+    }
+  };
+  if constexpr (!XP) load_epi_in();  // XP: once the prologue has the row scales
 
   Acc acc[kSets][TILES];
 #pragma unroll
@@ -322,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
           for (int i = 0; i < TILES; ++i)
             r.w[t][i][u] =
                 __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[t][i] + (byte >> 6) * unit_stride));
-        r.x[u][0] = *reinterpret_cast<const i32x4*>(xrow + byte);
+        r.x[u][0] = xload(byte);
       }
     }
   };
@@ -355,7 +464,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     // activations (int4: K % 32 == 0, so a chunk is wholly in or out).
     constexpr int kSlots = kSets * TILES;
     constexpr int kXH = W4 ? 2 : 1;                    // activation loads per unit
-    constexpr int kOpsPerRound = 2 * kSlots + 2 * kXH;  // transfers + activation loads
+    constexpr int kOpsPerRound = 2 * kSlots + (XP ? 0 : 2 * kXH);  // transfers + global activation loads
     const int wbytes = W4 ? kbytes / 2 : kbytes;        // weight bytes of a row
     uint8_t* ring = &wring[wid][0][0][0];
     const int drow = lane >> 3;
@@ -371,7 +480,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
           const int64_t r = min(nt + 8 * h + drow, static_cast<int64_t>(N) - 1) - nt;
           dbase[t][i][h] = (t == 0 ? B + nt * ldb + r * pitch1 : epi.B2 + nt * epi.ldb2 + r * pitch2);
         }
-    auto issue = [&](int u0, int buf, i32x4 (&x)[2][kXH], bool (&xv)[2][kXH]) {
+    auto issue_w = [&](int u0, int buf) {
       const int wb = u0 * 64;  // weight byte of the round's line
       // chunk dchunk of the line: unit u0 + dchunk / 4, 16-byte piece dchunk % 4
       const int off = wb + dchunk * 16 + 16 <= wbytes ? (u0 + (dchunk >> 2)) * unit_stride + (dchunk & 3) * 16 : 0;
@@ -382,14 +491,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             gemv_dma16(dbase[t][i][h] + off, ring + (buf * kSlots + t * TILES + i) * 2048 + h * 1024);
+    };
+    auto issue_x = [&](int u0, i32x4 (&x)[2][kXH], bool (&xv)[2][kXH]) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int hh = 0; hh < kXH; ++hh) {
           const int b = (u0 + q) * kUnit + 16 * hh;  // from this lane's activation base
           xv[q][hh] = u0 + q < u_end && (u0 + q) * kUnit + ch * 16 * kXH + 16 * (hh + 1) <= kbytes;
-          x[q][hh] = *reinterpret_cast<const i32x4*>(xrow + (xv[q][hh] ? b : 0));
+          x[q][hh] = xload(xv[q][hh] ? b : 0);
         }
+    };
+    auto issue = [&](int u0, int buf, i32x4 (&x)[2][kXH], bool (&xv)[2][kXH]) {
+      issue_w(u0, buf);
+      issue_x(u0, x, xv);
     };
     auto consume = [&](int buf, const i32x4 (&x)[2][kXH], const bool (&xv)[2][kXH]) {
 #pragma unroll
@@ -414,7 +529,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     };
     i32x4 xa[2][kXH], xb[2][kXH];
     bool va[2][kXH], vb[2][kXH];
-    if (u_begin < u_end) issue(u_begin, 0, xa, va);
+    if (u_begin < u_end) issue_w(u_begin, 0);
+    if constexpr (XP) {
+      xp_prologue();
+      load_epi_in();
+    }
+    if (u_begin < u_end) issue_x(u_begin, xa, va);
     int buf = 0;
     for (int u0 = u_begin; u0 < u_end; u0 += 4) {
       const bool more = u0 + 2 < u_end;
@@ -439,9 +559,45 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     }
   } else {
   Round ra, rb;
-  if (u_begin < u_end) load(u_begin, ra);
+  bool rb_ready = false;
+  if constexpr (XP) {
+    // Both rounds of weights (up to 2 kRound units per wave) are requested
+    // before the prologue packs the activation rows, so that they stream in
+    // meanwhile; the activation fragments follow from LDS.
+    auto load_w = [&](int u0, Round& r) {
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int byte = (u0 + u) * kUnit;
+        const bool ok = u0 + u < u_end && byte + ch * 16 < kbytes;
+#pragma unroll
+        for (int t = 0; t < kSets; ++t)
+#pragma unroll
+          for (int i = 0; i < TILES; ++i)
+            r.w[t][i][u] = ok ? __builtin_nontemporal_load(
+                                    reinterpret_cast<const i32x4*>(wrow[t][i] + (byte >> 6) * unit_stride))
+                              : i32x4{0, 0, 0, 0};
+      }
+    };
+    auto load_x = [&](int u0, Round& r) {
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int byte = (u0 + u) * kUnit;
+        r.x[u][0] = u0 + u < u_end && byte + ch * 16 < kbytes ? xload(byte) : i32x4{0, 0, 0, 0};
+      }
+    };
+    if (u_begin < u_end) load_w(u_begin, ra);
+    rb_ready = u_begin + kRound < u_end;
+    if (rb_ready) load_w(u_begin + kRound, rb);
+    xp_prologue();
+    load_epi_in();
+    if (u_begin < u_end) load_x(u_begin, ra);
+    if (rb_ready) load_x(u_begin + kRound, rb);
+  } else {
+    if (u_begin < u_end) load(u_begin, ra);
+  }
   for (int u0 = u_begin; u0 < u_end; u0 += 2 * kRound) {
-    if (u0 + kRound < u_end) load(u0 + kRound, rb);
+    if (!rb_ready && u0 + kRound < u_end) load(u0 + kRound, rb);
+    rb_ready = false;
     mma(ra);
     if (u0 + kRound >= u_end) break;
     if (u0 + 2 * kRound < u_end) load(u0 + 2 * kRound, ra);
@@ -511,11 +667,11 @@ void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uin
   switch (waves) {
     case 4:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(256), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled);
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, XPackArgs{});
       break;
     default:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(512), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled);
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, XPackArgs{});
       break;
   }
 }
@@ -537,6 +693,9 @@ inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 
 // M = 8, 4.5% at M = 12, but 6.6% slower at M = 16, where the sixteen
 // activation rows double what each of the few CUs reads.
 constexpr int kWideWaves = 16;
+// A wave stages its weights through LDS when it streams at least this many
+// K units (a round is two units).
+constexpr int kStageMinUnits = 5;
 constexpr int64_t kWideMaxRows = 12;
 bool wide_tiles(int64_t M, int64_t N, int64_t nunits, bool i8, bool w4, int sets) {
   return i8 && !w4 && sets == 1 && M <= kWideMaxRows && (N + 15) / 16 < gemv_num_cus() &&
@@ -585,7 +744,6 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   // for the staging to pay (a round is two units); int4 rows also need
   // K % 32 == 0 so that no 16-byte chunk straddles K.
   constexpr bool kStageable = I8;
-  constexpr int kStageMinUnits = 5;
   const bool stage_ok = !W4 || kbytes % 32 == 0;
   const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
@@ -602,10 +760,12 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
       const SplitArgs none{nullptr, 1, 0};
       if (per >= kStageMinUnits)
         hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, true>), grid,
-                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled);
+                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled,
+                           XPackArgs{});
       else
         hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, false>), grid,
-                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled);
+                           dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled,
+                           XPackArgs{});
       return hipGetLastError();
     }
   }
@@ -655,7 +815,86 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   return hipGetLastError();
 }
 
+// Launch that packs its own bf16 activation rows (M <= kPackinMaxRows):
+// one workgroup per 16-feature tile over all of K, 16 waves for a plain
+// linear, 4 for the gated pair (its two weight sets per lane fit four
+// waves' registers), one thread per 16-feature chunk of a row in the
+// prologue (the caller keeps K <= packin_max_k).  Dynamic LDS: the codes at
+// a pitch of K + 16 bytes, four row scales, four rows of wavefront maxima.
+template <int OUT, int ACT, bool GATED>
+hipError_t launch_out_packin(const XPackArgs& xp, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
+                             int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t stream, bool tiled) {
+  constexpr int kWaves = GATED ? 4 : kWideWaves;
+  constexpr int kDynMax = static_cast<int>(kPackinMaxRows) * (16 * 64 * kWaves + 16) + 16 + 16 * kWaves;
+  const int64_t nunits = (K + kStepBytes - 1) / kStepBytes;
+  const int64_t tiles = (N + 15) / 16;
+  const int per = static_cast<int>((nunits + kWaves - 1) / kWaves);
+  const int dyn = static_cast<int>(M * (K + 16)) + 16 + 16 * kWaves;
+  auto kdma = gemv_kernel<true, OUT, kWaves, ACT, GATED, false, false, 1, true, true>;
+  auto kreg = gemv_kernel<true, OUT, kWaves, ACT, GATED, false, false, 1, false, true>;
+  // Gated: the register path, where each wave requests its first two rounds
+  // of weights before the prologue (the staged path holds one round in LDS;
+  // decode gate/up, M = 1: 7.6 against 8.2 us).  Plain: the staged path as
+  // in launch_out (its first round issued before the prologue), which
+  // measured faster for the 16-wave launch (down projection, M = 1: 8.6
+  // against 9.3 us).
+  const bool stage = !GATED && per >= kStageMinUnits;
+  static std::atomic<uint64_t> lds_dma{0}, lds_reg{0};
+  const hipError_t e = stage ? set_lds_limit(reinterpret_cast<const void*>(kdma), kDynMax, lds_dma)
+                             : set_lds_limit(reinterpret_cast<const void*>(kreg), kDynMax, lds_reg);
+  if (e != hipSuccess) return e;
+  const SplitArgs none{nullptr, 1, 0};
+  const auto* b = static_cast<const uint8_t*>(B);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(K);
+  if (stage)
+    hipLaunchKernelGGL(kdma, dim3(static_cast<unsigned>(tiles)), dim3(64 * kWaves), dyn, stream, nullptr, 0, b, ldb,
+                       epi, m, n, kb, per, C, ldc, none, tiled, xp);
+  else
+    hipLaunchKernelGGL(kreg, dim3(static_cast<unsigned>(tiles)), dim3(64 * kWaves), dyn, stream, nullptr, 0, b, ldb,
+                       epi, m, n, kb, per, C, ldc, none, tiled, xp);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int64_t packin_max_k(bool gated) { return 16 * 64 * (gated ? 4 : kWideWaves); }
+
+hipError_t launch_gemv_i8_packin(const void* X, int64_t ldx, int log2g, RotKind kind, const int8_t* signs,
+                                 const int8_t* B, int64_t ldb, const float* sb, const float* bias, Act act, int64_t M,
+                                 int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream, bool tiled) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const XPackArgs xp{X, ldx, log2g, kind == RotKind::Randomized ? 1 : 0, signs};
+  const EpiArgs epi{nullptr, sb, bias, nullptr, 0, nullptr, nullptr};
+  if (act == Act::None) {
+    switch (out) {
+      case Elt::F32: return launch_out_packin<0, 0, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled);
+      case Elt::BF16: return launch_out_packin<1, 0, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled);
+      default: return launch_out_packin<2, 0, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled);
+    }
+  }
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out_packin<0, 1, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled)
+               : launch_out_packin<1, 1, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled);
+  return f32 ? launch_out_packin<0, 2, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled)
+             : launch_out_packin<1, 2, false>(xp, B, ldb, epi, M, N, K, C, ldc, stream, tiled);
+}
+
+hipError_t launch_gemv_i8_gated_packin(const void* X, int64_t ldx, int log2g, RotKind kind, const int8_t* signs,
+                                       const int8_t* Bg, int64_t ldbg, const float* sbg, const float* biasg,
+                                       const int8_t* Bu, int64_t ldbu, const float* sbu, const float* biasu, Act act,
+                                       int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                                       hipStream_t stream, bool tiled) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const XPackArgs xp{X, ldx, log2g, kind == RotKind::Randomized ? 1 : 0, signs};
+  const EpiArgs epi{nullptr, sbg, biasg, reinterpret_cast<const uint8_t*>(Bu), ldbu, sbu, biasu};
+  const bool f32 = out == Elt::F32;
+  if (act == Act::GeluErf)
+    return f32 ? launch_out_packin<0, 1, true>(xp, Bg, ldbg, epi, M, N, K, C, ldc, stream, tiled)
+               : launch_out_packin<1, 1, true>(xp, Bg, ldbg, epi, M, N, K, C, ldc, stream, tiled);
+  return f32 ? launch_out_packin<0, 2, true>(xp, Bg, ldbg, epi, M, N, K, C, ldc, stream, tiled)
+             : launch_out_packin<1, 2, true>(xp, Bg, ldbg, epi, M, N, K, C, ldc, stream, tiled);
+}
 
 int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, bool bf16, bool w4, bool gated) {
   if (N <= 0 || K <= 0) return 0;

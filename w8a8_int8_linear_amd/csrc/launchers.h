@@ -95,6 +95,22 @@ hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t
                           int64_t M, int64_t N, int64_t K,
                           void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false);
 
+// Small-M linears that pack their own activation rows: bf16 X [M, ldx
+// elements], M <= kPackinMaxRows, K <= packin_max_k(gated), rotated with
+// G = 2^log2g of `kind` and quantised exactly as launch_pack_rows does, then
+// the same products and epilogue as launch_gemv_i8 / _i8_gated on those
+// codes (the same result bits as packing first).
+constexpr int64_t kPackinMaxRows = 4;
+int64_t packin_max_k(bool gated);
+hipError_t launch_gemv_i8_packin(const void* X, int64_t ldx, int log2g, RotKind kind, const int8_t* signs,
+                                 const int8_t* B, int64_t ldb, const float* sb, const float* bias, Act act, int64_t M,
+                                 int64_t N, int64_t K, void* C, Elt out, int64_t ldc, hipStream_t stream, bool tiled);
+hipError_t launch_gemv_i8_gated_packin(const void* X, int64_t ldx, int log2g, RotKind kind, const int8_t* signs,
+                                       const int8_t* Bg, int64_t ldbg, const float* sbg, const float* biasg,
+                                       const int8_t* Bu, int64_t ldbu, const float* sbu, const float* biasu, Act act,
+                                       int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
+                                       hipStream_t stream, bool tiled);
+
 hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
                             const float* bias, int64_t M, int64_t N, int64_t K,
                             void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream);

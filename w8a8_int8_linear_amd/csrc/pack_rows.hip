@@ -43,130 +43,15 @@
 
 #include <type_traits>
 
-#include "lanes.h"
 #include "launchers.h"
+#include "pack_core.h"
 
 namespace convrot {
 namespace {
 
-constexpr int kChunk = 16;
 constexpr int kMaxThreads = 1024;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-using namespace lanes;
-
-// Radix-4 butterfly whose digit lives in lane bits (2k, 2k+1).
-// k = 0: identity digit order within a quad, partner at lane ^ 3.
-// k = 1: Gray-coded digit in lane bits 2-3, partner at lane ^ 8.
-// k = 2: Gray-coded digit in lane bits 4-5, partner at lane ^ 32.
-// With the digit d of this lane and 3 - d held by the partner, the output
-// s - 2 a_{3-d} equals (a_d - a_{3-d}) + (sum of the other pair), and the
-// other pair's sum is held by the lanes one exchange away (lane ^ 1 in a
-// quad, a rotation by 4 within 16 lanes for the Gray-coded digit 1, lane ^ 16
-// for digit 2).  That is three two-operand instructions per element, each
-// taking its lane exchange as a DPP source operand.
-template <int K>
-__device__ __forceinline__ float bfly4_lanes(float x) {
-  if constexpr (K == 0) {
-    const float u = x + dpp<kQuadXor3>(x);
-    const float w = x - dpp<kQuadXor3>(x);
-    return w + dpp<kQuadXor1>(u);
-  } else if constexpr (K == 1) {
-    const float u = x + dpp<kRowRor8>(x);
-    const float w = x - dpp<kRowRor8>(x);
-    return w + dpp<kRowRor4>(u);
-  } else {
-    const float p = xor32(x);
-    const float u = x + p;
-    const float w = x - p;
-    return w + swz<kSwzXor16>(u);
-  }
-}
-
-// Radix-2 (Sylvester) butterfly across lane bit b: the lane with the bit
-// clear keeps a + c, the other keeps a - c (a = low lane's value).
-template <int MASK>
-__device__ __forceinline__ float bfly2_lanes(float x, int lane) {
-  const float p = lane_xor<MASK>(x);
-  return (lane & MASK) ? (p - x) : (x + p);
-}
-
-__device__ __forceinline__ int gray2(int m) { return m ^ (m >> 1); }
-
-// Position of a lane's chunk inside its group.  Regular kind: base-4 digit
-// 0 of the lane position as is, digits 1 and 2 Gray-coded.  Randomized kind:
-// identity (radix-2 exchanges need no reordering).
-template <bool RAND>
-__device__ __forceinline__ int chunk_in_group(int pos) {
-  if constexpr (RAND) {
-    return pos;
-  } else {
-    return (pos & 3) + 4 * gray2((pos >> 2) & 3) + 16 * gray2((pos >> 4) & 3);
-  }
-}
-
-// Rows are accessed through buffer resources whose size is the row's valid
-// bytes: a load past the end returns zeros and a store past the end is
-// dropped, so chunks beyond K (threads rounded up to whole wavefronts) need
-// no test, no zero fill and no store guard.  Word 3 is the raw-buffer
-// default (32-bit data format).  Cache policy: non-temporal, the row is
-// touched once.
-constexpr int kBufWord3 = 0x00020000;
-constexpr int kNonTemporal = 2;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
-}
-
-template <typename InT>
-__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]);
-
-template <>
-__device__ __forceinline__ void load_chunk<uint16_t>(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]) {
-  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * elem_off, 0, kNonTemporal);
-  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * elem_off + 16, 0, kNonTemporal);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = as_f(w[i] << 16);
-    v[2 * i + 1] = as_f(w[i] & 0xFFFF0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load_chunk<float>(__amdgpu_buffer_rsrc_t r, int elem_off, float v[kChunk]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, 4 * elem_off + 16 * i, 0, kNonTemporal);
-    v[4 * i] = as_f(a.x); v[4 * i + 1] = as_f(a.y); v[4 * i + 2] = as_f(a.z); v[4 * i + 3] = as_f(a.w);
-  }
-}
-
-// Round-to-nearest-even int8 codes of a*inv..d*inv (|.| <= 127 + tiny),
-// packed little-endian into one dword.
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
-  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: ulp 1, low byte = two's complement code
-  const uint32_t qa = as_u(fmaf(a, inv, kMagic));
-  const uint32_t qb = as_u(fmaf(b, inv, kMagic));
-  const uint32_t qc = as_u(fmaf(c, inv, kMagic));
-  const uint32_t qd = as_u(fmaf(d, inv, kMagic));
-  const uint32_t ab = __builtin_amdgcn_perm(qb, qa, 0x0c0c0400u);
-  const uint32_t cd = __builtin_amdgcn_perm(qd, qc, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// Sixteen codes of one chunk as int4 nibble pairs (element 2j in the low,
-// 2j + 1 in the high nibble of byte j): the even and the odd codes are each
-// gathered into a dword of bytes by quant4, and one bit-field insert merges
-// their low nibbles.  |code| <= 7, so the low nibble of a code's byte is its
-// 4-bit two's complement.
-__device__ __forceinline__ uint32_t quant8_nibbles(const float* v, float inv) {
-  const uint32_t even = quant4(v[0], v[2], v[4], v[6], inv);
-  const uint32_t odd = quant4(v[1], v[3], v[5], v[7], inv);
-  return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
-}
+using namespace pack;
 
 // QMODE: 0 rotation only (fp32 rows to xrot), 1 int8 codes, 2 int4 codes
 // (nibble pairs, K / 2 bytes per row, scale = max / 7).
@@ -218,61 +103,24 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     load_chunk<InT>(xr, off[c], v[c]);
   }
 
+  // The steps of pack_core.h, each over all of the thread's chunks.
   if constexpr (RAND) {
     const __amdgpu_buffer_rsrc_t sr = row_rsrc(signs, K);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(sr, off[c], 0, 0);
-      const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+    for (int c = 0; c < CPT; ++c) apply_signs(sr, off[c], v[c]);
 #pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
-        const int8_t sgn = static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
-        v[c][e] = sgn < 0 ? -v[c][e] : v[c][e];
-      }
-    }
-    // In-register radix-2 stages over element bits 0..3.
+    for (int c = 0; c < CPT; ++c) rand_stages_in_chunk(v[c]);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-#pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          if ((e >> b) & 1) continue;
-          const float a = v[c][e], d = v[c][e | (1 << b)];
-          v[c][e] = a + d;
-          v[c][e | (1 << b)] = a - d;
-        }
-      }
-    }
-    // Lane bits 0..LOG2G-5.
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
-        float x = v[c][e];
-        if constexpr (LOG2G >= 5) x = bfly2_lanes<1>(x, lane);
-        if constexpr (LOG2G >= 6) x = bfly2_lanes<2>(x, lane);
-        if constexpr (LOG2G >= 7) x = bfly2_lanes<4>(x, lane);
-        if constexpr (LOG2G >= 8) x = bfly2_lanes<8>(x, lane);
-        if constexpr (LOG2G >= 9) x = bfly2_lanes<16>(x, lane);
-        if constexpr (LOG2G >= 10) x = bfly2_lanes<32>(x, lane);
-        v[c][e] = x;
-      }
+      for (int e = 0; e < kChunk; ++e) v[c][e] = rand_stages_across_lanes<LOG2G>(v[c][e], lane);
     }
   } else {
-    // Base-4 digit 0 (element bits 0-1), in registers.
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) bfly4(v[c][4 * a], v[c][4 * a + 1], v[c][4 * a + 2], v[c][4 * a + 3]);
-    }
-    // Digit 1 (element bits 2-3), in registers.
+    for (int c = 0; c < CPT; ++c) regular_digit0(v[c]);
     if constexpr (LOG2G >= 4) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bfly4(v[c][b], v[c][4 + b], v[c][8 + b], v[c][12 + b]);
-      }
+      for (int c = 0; c < CPT; ++c) regular_digit1(v[c]);
     }
     // Digits 2.. across lanes, one digit at a time over all elements (the
     // independent elements fill the wait states a DPP read needs after the
@@ -288,11 +136,7 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     if constexpr (LOG2G >= 10) lane_stage(std::integral_constant<int, 2>{});
   }
 
-  // Scale that turns the unnormalised transform into the orthonormal one:
-  // 2^-(LOG2G/2) for the regular kind (one factor 1/2 per radix-4 stage),
-  // 1/sqrt(G) for the randomized kind.
-  const float norm = RAND ? (1.0f / __builtin_sqrtf(static_cast<float>(G)))
-                          : __builtin_ldexpf(1.0f, -(LOG2G / 2));
+  const float norm = rot_norm<LOG2G, RAND>();
 
   if constexpr (QMODE == 0) {
     const __amdgpu_buffer_rsrc_t rr = row_rsrc(xrot + static_cast<int64_t>(row) * ldr, 4 * K);
@@ -317,19 +161,13 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
       // spilled registers and a 4x slower launch).
       float m = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-        for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
-      }
+      for (int c = 0; c < CPT; ++c) m = chunk_absmax(v[c], m);
       asm volatile("" ::"v"(m));
       amax_u = as_f(wave_max_bits(pre_bits)) / norm;
     } else {
       float m = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-        for (int e = 0; e < kChunk; e += 2) m = fmaxf(m, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
-      }
+      for (int c = 0; c < CPT; ++c) m = chunk_absmax(v[c], m);
       // Every lane ends with its wavefront's maximum; rows of several
       // wavefronts combine theirs through LDS (uniform branch: T is the
       // workgroup size).
@@ -347,19 +185,14 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     // Unnormalised codes: y_u * (qmax / amax_u) == y / s exactly up to the
     // rounding of the reciprocal; all-zero rows give inv = 0 and codes 0.
     constexpr float kQMax = QMODE == 2 ? 7.0f : 127.0f;
-    const float inv = amax_u > 0.f ? kQMax / amax_u : 0.f;
-    if (tid == 0) scale[row] = (amax_u * norm) / kQMax;
+    const float inv = quant_factor(amax_u, kQMax);
+    if (tid == 0) scale[row] = row_scale(amax_u, norm, kQMax);
 
     if constexpr (QMODE == 1) {
       const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        u32x4 o;
-        o.x = quant4(v[c][0], v[c][1], v[c][2], v[c][3], inv);
-        o.y = quant4(v[c][4], v[c][5], v[c][6], v[c][7], inv);
-        o.z = quant4(v[c][8], v[c][9], v[c][10], v[c][11], inv);
-        o.w = quant4(v[c][12], v[c][13], v[c][14], v[c][15], inv);
-        __builtin_amdgcn_raw_buffer_store_b128(o, qr, off[c], 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(quant_chunk(v[c], inv), qr, off[c], 0, kNonTemporal);
       }
     } else {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
