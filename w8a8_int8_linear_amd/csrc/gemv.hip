@@ -49,6 +49,11 @@
 //  * TILE16 weights (convrot_tile_weight): the 16 rows of a tile store each
 //    64-byte K unit as 1 KiB of consecutive memory; only the addresses of
 //    the weight loads change.
+//  * Launches that pack their own input (XP; convrot_linear_packin and
+//    _gated_packin, up to 4 bf16 rows): each workgroup first packs the rows
+//    into LDS with the pack kernel's steps (pack_core.h) while its first
+//    weight rounds are in flight, then reads every activation fragment from
+//    LDS.  Same codes, scales and result bits as packing first.
 //  * int4 weights (W4A8; stable-diffusion.cpp PR "load ConvRot int4 and
 //    per-channel int8 safetensors", sections "Solution" and "The rotation":
 //    codes in [-7, 7], one scale per output row, adjacent pairs in a byte):
