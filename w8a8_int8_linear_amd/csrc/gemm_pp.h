@@ -42,7 +42,8 @@
 // XOR-swizzled by row) in a private LDS area per wave and read back so
 // that each lane finishes fixed 4-feature segments (conversion, both
 // scales, bias, activation; the row scale taken from the lane that holds
-// it) and stores whole row pieces.
+// it) and stores whole row pieces (with the non-temporal hint when the
+// output is larger than the 256 MB Infinity Cache).
 //
 // Walk.  The grid is one workgroup per CU; each takes every gridDim.x-th
 // tile of an XCD-ordered tile list, and requests the next tile's scales
@@ -87,7 +88,8 @@ __device__ __forceinline__ int rowmax_col(int lane) {
 
 // OUT: 0 = fp32, 1 = bf16, 2 = raw int32 accumulator (int8 mode only).
 // ACT: epilogue activation (see activation() in epilogue.h).
-template <bool I8, int OUT, int TN, int ACT, bool ROWMAX = false>
+// STREAM: output stores with the non-temporal hint (see launch_pp_typed).
+template <bool I8, int OUT, int TN, int ACT, bool ROWMAX = false, bool STREAM = false>
 __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
     int N, int Kb, void* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, bool vec_cols, bool vec_out,
@@ -527,9 +529,18 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
           y[r] = activation<ACT>(z);
         }
       };
+      // STREAM (outputs larger than the 256 MB Infinity Cache): stores with
+      // the non-temporal hint, which leave the L2 to the operand panels;
+      // smaller outputs stay cached for the launch that reads them next.  (A
+      // run-time choice between the two stores is merged into one plain
+      // store by the compiler, hence the template parameter.)
       auto store4 = [](out_t* out, const float y[4]) {
         if constexpr (OUT == 0) {
-          *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+          const f32x4 v = {y[0], y[1], y[2], y[3]};
+          if constexpr (STREAM)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out));
+          else
+            *reinterpret_cast<f32x4*>(out) = v;
         } else {
           // Two pairs, each one packed round-to-nearest-even conversion.
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -537,7 +548,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
           const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
           const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
-          *reinterpret_cast<u32x2*>(out) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          if constexpr (STREAM)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(out));
+          else
+            *reinterpret_cast<u32x2*>(out) = v;
         }
       };
 #pragma unroll
@@ -636,10 +651,21 @@ template <bool I8, int OUT, int TN, int ACT, bool ROWMAX = false>
 hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const EpiArgs& epi,
                            int64_t M, int64_t N, int64_t Kb, void* C, int64_t ldc, hipStream_t stream,
                            const RowmaxArgs& rm = RowmaxArgs{nullptr, 0, 0}) {
-  auto kern = gemm_pp_kernel<I8, OUT, TN, ACT, ROWMAX>;
+  // Outputs that cannot stay in the 256 MB Infinity Cache for their reader
+  // are streamed out (large-M QKV 1.0-2.2% and its routed bf16 layer
+  // 2.9-3.6% faster per launch, two boxes).  A smaller output keeps plain
+  // stores: the DiT launch was 7% faster streaming its 100 MB, but the LoRA
+  // correction that adds into that output in place made that step 4.7%
+  // slower.
+  constexpr bool kCanStream = !ROWMAX && OUT != 2;
+  const int out_elt = OUT == 1 ? 2 : 4;
+  const bool stream_out = kCanStream && M * N * out_elt > (int64_t{256} << 20);
+  auto kern = stream_out ? gemm_pp_kernel<I8, OUT, TN, ACT, ROWMAX, kCanStream>
+                         : gemm_pp_kernel<I8, OUT, TN, ACT, ROWMAX, false>;
   constexpr int kSmem = pp_smem_bytes<TN>();
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), kSmem, lds_set);
+  static std::atomic<uint64_t> lds_set{0}, lds_set_stream{0};
+  const hipError_t e =
+      set_lds_limit(reinterpret_cast<const void*>(kern), kSmem, stream_out ? lds_set_stream : lds_set);
   if (e != hipSuccess) return e;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + 64 * TN - 1) / (64 * TN));
@@ -656,7 +682,6 @@ hipError_t launch_pp_typed(const uint8_t* A, int64_t lda, const uint8_t* B, int6
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec_cols = al16(epi.sb) && al16(epi.bias);
   // Four consecutive outputs go out as one store when rows keep them aligned.
-  const int out_elt = OUT == 1 ? 2 : 4;
   const bool vec_out = (reinterpret_cast<uintptr_t>(C) % (4 * out_elt)) == 0 && ldc % 4 == 0;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kPPThreads), kSmem, stream, A, lda, B,
                      ldb, epi, static_cast<int>(M), static_cast<int>(N), static_cast<int>(Kb), C, ldc, tiles_m,
