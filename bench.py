@@ -78,7 +78,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0    # 8 TB/s HBM3E
 COLD_BYTES = 512 << 20
 SMALL_M = 16             # up to this many rows a linear runs on the weight-streaming kernel
-PACKIN_GATED_ROWS = 3    # up to this many decode rows the gated launch packs its own input
+PACKIN_GATED_ROWS = 4    # with --packin, up to this many decode rows the gated launch packs its own input
 METRIC = "convrot_linear effective int8 TOPS + % MFMA peak; rotate+quant GB/s % HBM"
 # the sources each kernel is compiled from; a traffic summary is valid only for these exact bytes
 KERNEL_SOURCE = {
@@ -219,10 +219,12 @@ class StepSet:
     def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False,
                  tiled=False, packin=False):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
-        # decode with at most PACKIN_GATED_ROWS rows and int8 weights: the
-        # gated launch packs its own bf16 input rows (the down projection,
-        # whose 16-wave workgroups would each pack a 6912-wide row, keeps the
-        # separate pack, which measured faster there)
+        # --packin, decode with at most PACKIN_GATED_ROWS rows and int8
+        # weights: the gated launch packs its own bf16 input rows (the down
+        # projection, whose 16-wave workgroups would each pack a 6912-wide
+        # row, keeps the separate pack).  Off by default: with TILE16
+        # weights the separate pack measured level at one row and faster
+        # from two rows on.
         self.packin = (packin and fused and wl.cfg == 5 and wl.X.shape[0] <= PACKIN_GATED_ROWS
                        and wl.xdtype == "bf16" and wl.extra.get("wbits") != 4
                        and all(l.W.shape[1] % wl.G == 0 for l in wl.linears))
@@ -654,9 +656,9 @@ def main():
     ap.add_argument("--row-weights", action="store_true",
                     help="decode (M <= 16): keep the packed weights in the row layout instead of the TILE16 layout "
                          "the weight-streaming kernel reads fastest")
-    ap.add_argument("--no-packin", action="store_true",
-                    help="decode with at most 3 rows: pack the gated launch's input in a launch of its own instead "
-                         "of inside the gated launch")
+    ap.add_argument("--packin", action="store_true",
+                    help="decode with at most 4 rows: pack the gated launch's input inside the gated launch instead "
+                         "of in a launch of its own")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy and MFMA-only ceilings")
     args = ap.parse_args()
@@ -682,7 +684,7 @@ def main():
     merge = not args.separate_linears
     pf = args.producer_fusion
     tl = not args.row_weights
-    pin = not args.no_packin
+    pin = args.packin
     sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl, packin=pin)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
         sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf,

@@ -749,6 +749,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   // for the staging to pay (a round is two units); int4 rows also need
   // K % 32 == 0 so that no 16-byte chunk straddles K.
   constexpr bool kStageable = I8;
+  const bool stage_tiled = !(tiled && !W4);
   const bool stage_ok = !W4 || kbytes % 32 == 0;
   const int64_t nunits = (kbytes + kUnit - 1) / kUnit;
   const int64_t tiles = (N + 15) / 16;
@@ -781,7 +782,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const int per = static_cast<int>((units + waves - 1) / waves);
     const SplitArgs sp{reinterpret_cast<i32x4*>(ws), static_cast<int>(splits), static_cast<int>(units)};
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splits));
-    if (kStageable && stage_ok && per >= kStageMinUnits)
+    if (kStageable && stage_ok && stage_tiled && per >= kStageMinUnits)
       launch_waves<I8, OUT, ACT, GATED, true, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
                                                                  ldc, sp, tiled, stream);
     else
@@ -798,7 +799,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   // Two tiles per workgroup share every activation fragment once there are
   // at least four tiles per CU (plain launches only; with fewer, the
   // workgroups of two tiles spread unevenly over the CUs).
-  const bool stage = kStageable && stage_ok && per >= kStageMinUnits;
+  const bool stage = kStageable && stage_ok && stage_tiled && per >= kStageMinUnits;
   const SplitArgs none{nullptr, 1, 0};
   if (!GATED && tiles >= 4 * cus) {
     const dim3 grid(static_cast<unsigned>((tiles + 1) / 2));
