@@ -47,7 +47,10 @@
 //
 // Walk.  The grid is one workgroup per CU; each takes every gridDim.x-th
 // tile of an XCD-ordered tile list, and requests the next tile's scales
-// and first slices before its current tile's epilogue.
+// and first slices before its current tile's epilogue.  With int8
+// operands every other round runs K last slice first, so that it starts on
+// the slices of the row group's A panels that the round before left in the
+// XCD's L2.
 //
 // Producer fusion (ROWMAX, 256-wide tiles): the epilogue also computes, for
 // the next layer's pack, the largest magnitude of every G-group (G <= 256)
@@ -132,14 +135,22 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     const uint8_t* a;
     const uint8_t* b;
     uint32_t off_a[kDmaA], off_b[kDmaB];
+    int kstep;  // bytes from one slice to the next: kBK, or -kBK when the tile runs K backwards
   };
   auto tile_at = [&](int id, Tile& T) {
     int tm, tn;
     tile_coords(id, tiles_m, tiles_n, tm, tn);
+    // int8: every other round of the walk runs K backwards, so that it
+    // starts on the slices the previous round (same row group on this XCD)
+    // left in L2.  Exact integer sums do not depend on the order; float
+    // sums keep one order so that their bits match the other kernels'.
+    const bool rev = I8 && ((id / gridDim.x) & 1);
+    const int k0 = rev ? (nk - 1) * kBK : 0;
+    T.kstep = rev ? -kBK : kBK;
     T.m_blk = tm * kBM;
     T.n_blk = tn * kBN;
-    T.a = A + static_cast<int64_t>(T.m_blk) * lda;
-    T.b = B + static_cast<int64_t>(T.n_blk) * ldb;
+    T.a = A + static_cast<int64_t>(T.m_blk) * lda + k0;
+    T.b = B + static_cast<int64_t>(T.n_blk) * ldb + k0;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) {
       const int row = 8 * (wid + 8 * i) + (lane >> 3);
@@ -152,12 +163,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void gemm_pp_kernel(
     }
   };
   auto dma_a = [&](const Tile& T, int slice, int buf) {
-    const uint8_t* g = T.a + slice * kBK;
+    const uint8_t* g = T.a + slice * T.kstep;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) dma16(g + T.off_a[i], smem + buf * kATileBytes + (wid_u + 8 * i) * 1024);
   };
   auto dma_b = [&](const Tile& T, int slice, int buf) {
-    const uint8_t* g = T.b + slice * kBK;
+    const uint8_t* g = T.b + slice * T.kstep;
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
       dma16(g + T.off_b[i], smem + kBBase + buf * kBTileBytes + (wid_u + 8 * i) * 1024);
