@@ -80,6 +80,30 @@ def test_epilogue_from_oracle_codes(cuda, M, N, K, with_bias):
     assert np.array_equal(ybf, O.bf16_round(y32))
 
 
+def test_persistent_walk_rounds(cuda):
+    """More tiles than workgroups: each workgroup of the persistent walk runs
+    several tiles, and int8 tiles of alternate rounds take K last slice
+    first.  fp32 and bf16 outputs against the oracle's epilogue of the exact
+    integer product, as for one round."""
+    M, N, K, G = 2048, 18432, 1024, 256
+    g = np.random.default_rng(11)
+    qx, qw = random_codes((M, K), 5), random_codes((N, K), 6)
+    sx = g.uniform(1e-3, 0.1, M).astype(np.float32)
+    sw = g.uniform(1e-5, 1e-3, N).astype(np.float32)
+    b = (g.standard_normal(N) * 0.01).astype(np.float32)
+    y64 = O.epilogue64(O.int_gemm(qx, qw), sx, sw, b)
+    a, w = _packed_from_codes(qx, sx, G, cuda), _packed_from_codes(qw, sw, G, cuda)
+    bd = to_dev(b, torch.float32)
+    y32 = to_np(cr.linear(a, w, bd, out_dtype=torch.float32))
+    assert R.rel_fro(y32, y64.astype(np.float32)) <= 1e-6
+    # every element, against its row's RMS: a tile that skipped or repeated a
+    # slice would be off by a sizeable fraction of it
+    worst = np.max(np.abs(y32 - y64) / np.sqrt(np.mean(y64 ** 2, axis=1, keepdims=True)))
+    assert float(worst) <= 1e-5, float(worst)
+    ybf = to_np(cr.linear(a, w, bd, out_dtype=torch.bfloat16))
+    assert np.array_equal(ybf, O.bf16_round(y32))
+
+
 def test_unit_layer_end_to_end(cuda):
     """Unit layer (fp32 X [64, 1024] with 0.5% outliers x50, W [1024, 1024],
     G=256): GPU pack of X and W, GPU linear, against the oracle."""
