@@ -24,8 +24,10 @@
 //  * Where a wave streams at least five K units, each weight row's 128-byte
 //    line goes global -> LDS whole (global_load_lds_dwordx4, 8 rows per
 //    transfer, chunks XOR-swizzled by row) and the MFMA fragments are read
-//    from LDS, so a line is touched once instead of twice (int8 weights, and
-//    int4 weights with K % 32 == 0).
+//    from LDS, so a line is touched once instead of twice (int8 weights in
+//    the row layout, int4 weights with K % 32 == 0, and the 16-wave
+//    workgroups below).  int8 TILE16 weights skip it: a wave's register
+//    load of one unit already reads 1 KiB of consecutive memory.
 //  * The partial accumulators of the waves are summed through LDS (exact in
 //    int8 mode) and wave 0 applies the epilogue, writing 4 consecutive
 //    outputs per lane.
