@@ -217,7 +217,7 @@ class StepSet:
     """Device state of one buffer set and the ordered launches of one step."""
 
     def __init__(self, wl, dev, torch, cr, template=None, fused=True, merge=True, producer_fusion=False,
-                 tiled=False, packin=False):
+                 tiled=False, packin=False, xtiled=False):
         self.torch, self.cr, self.wl, self.fused = torch, cr, wl, fused
         # --packin, decode with at most PACKIN_GATED_ROWS rows and int8
         # weights: the gated launch packs its own bf16 input rows (the down
@@ -231,6 +231,8 @@ class StepSet:
         self.producer_fusion = producer_fusion and fused and wl.cfg == 3
         # weights in the TILE16 layout, which only the M <= 16 path reads
         self.tiled = tiled and wl.X.shape[0] <= 16
+        # packed activations in the TILE16 layout (M <= 16, int8 weights)
+        self.xtiled = xtiled and wl.X.shape[0] <= 16 and wl.extra.get("wbits") != 4
         # linears that share the packed activation run as one launch over the
         # concatenated weight (configs whose linears all read the same input)
         self.merge = merge and wl.cfg == 2 and all(l.W.shape[1] % wl.G == 0 for l in wl.linears)
@@ -293,6 +295,7 @@ class StepSet:
             self.b = template.b
             self.X2 = template.X2.clone() if template.X2 is not None else None
         self.bufs = []
+        self.packed_acts = []
         self.ops = self._plan(dev)
 
     def _quant(self, w):
@@ -311,9 +314,12 @@ class StepSet:
     # -- buffers -----------------------------------------------------------
     def _packed(self, rows, K, dev):
         t = self.torch
-        p = self.cr.Packed(t.empty((rows, K), dtype=t.int8, device=dev), t.empty(rows, dtype=t.float32, device=dev),
-                           self.wl.G, self.wl.kind, self.signs.get(K))
+        tile = self.xtiled and K % 64 == 0
+        q = t.empty((16 if tile else rows, K), dtype=t.int8, device=dev)[:rows]
+        p = self.cr.Packed(q, t.empty(rows, dtype=t.float32, device=dev), self.wl.G, self.wl.kind, self.signs.get(K),
+                           self.cr.TILE16 if tile else self.cr.ROWS)
         self.bufs.append(p.q)
+        self.packed_acts.append(p)
         return p
 
     def _out(self, name, rows, dev):
@@ -656,6 +662,9 @@ def main():
     ap.add_argument("--row-weights", action="store_true",
                     help="decode (M <= 16): keep the packed weights in the row layout instead of the TILE16 layout "
                          "the weight-streaming kernel reads fastest")
+    ap.add_argument("--row-activations", action="store_true",
+                    help="decode (M <= 16): pack the activations in the row layout instead of the TILE16 layout "
+                         "(one 16-row tile) that the weight-streaming kernel reads in whole cache lines")
     ap.add_argument("--packin", action="store_true",
                     help="decode with at most 4 rows: pack the gated launch's input inside the gated launch instead "
                          "of in a launch of its own")
@@ -685,10 +694,12 @@ def main():
     pf = args.producer_fusion
     tl = not args.row_weights
     pin = args.packin
-    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl, packin=pin)]
+    xtl = not args.row_activations
+    sets = [StepSet(wl, dev, torch, cr, fused=fused, merge=merge, producer_fusion=pf, tiled=tl, packin=pin,
+                    xtiled=xtl)]
     while sum(s.nbytes() for s in sets) < COLD_BYTES:
         sets.append(StepSet(wl, dev, torch, cr, template=sets[0], fused=fused, merge=merge, producer_fusion=pf,
-                            tiled=tl, packin=pin))
+                            tiled=tl, packin=pin, xtiled=xtl))
     ops = sets[0].ops
     log(f"[bench] {len(sets)} buffer sets, {sum(s.nbytes() for s in sets) / 2**20:.0f} MiB rotated per cycle; "
         f"launches: {[o.name for o in ops]}")
@@ -832,6 +843,8 @@ def main():
                    "activation_pack": "in the gated launch" if sets[0].packin else "own launch",
                    "weight_layout": "tile16" if any(getattr(v, "layout", "rows") == "tile16"
                                                     for v in sets[0].W.values()) else "rows",
+                   "activation_layout": "tile16" if any(getattr(o, "layout", "rows") == "tile16"
+                                                        for o in sets[0].packed_acts) else "rows",
                    "shared_pack_linears": "one launch" if sets[0].merge else "one launch each",
                    "out": wl.out_dtype, "routed": [o.name for o in ops if o.kind == "bf16"],
                    "weights": "int4" if wl.extra.get("wbits") == 4 else "int8",

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 9
+#define CONVROT_ABI_VERSION 10
 
 typedef enum {
   CONVROT_OK = 0,
@@ -148,11 +148,10 @@ typedef struct {
   const int8_t* signs;  /* [K] +-1, randomized kind only */
 } convrot_rot;
 
-/* Where a packed weight's codes lie in memory (the `layout` field of
+/* Where a packed operand's codes lie in memory (the `layout` field of
  * convrot_packed and convrot_packed_w4).
  *   ROWS    row-major [rows, ld], as described with each struct (the
- *           checkpoint layout; every entry point reads it).  Packed
- *           activations are always ROWS.
+ *           checkpoint layout; every entry point reads it).
  *   TILE16  rows grouped in tiles of 16 consecutive rows and, within a
  *           tile, K cut into units of 64 bytes (64 int8 codes or 128 int4
  *           codes); with ld equal to the bytes of one row (K, or K / 2 for
@@ -165,7 +164,17 @@ typedef struct {
  *           CONVROT_ERR_INVALID_ARG.  It needs rows % 16 == 0, ld == the row
  *           bytes, and K % 64 == 0 (int4: K % 128 == 0).
  *           convrot_tile_weight and convrot_tile_weight_w4 convert a ROWS
- *           weight; the pack entry points write ROWS only. */
+ *           weight.
+ *           A packed activation may take it as well (the same formula;
+ *           ld == K, K % 64 == 0, any row count, the buffer holding whole
+ *           tiles of 16 rows, i.e. 16 K bytes for M <= 16): the
+ *           activation fragments of the weight-streaming kernel are then
+ *           1 KiB of consecutive memory per unit instead of 16 row pieces
+ *           (decode step at M = 4-16 about 4-5% faster).  convrot_pack_act
+ *           writes it when its output descriptor asks for it; convrot_linear,
+ *           _act, _gated and _noalloc read it for M <= 16 with int8 weights
+ *           of either layout; every other entry point takes ROWS
+ *           activations (CONVROT_ERR_INVALID_ARG otherwise). */
 typedef enum {
   CONVROT_LAYOUT_ROWS = 0,
   CONVROT_LAYOUT_TILE16 = 1
@@ -176,7 +185,7 @@ typedef enum {
  *   q      [rows, ld] int8, row-major, ld >= K, ld % 16 == 0 (or the TILE16
  *          layout above)
  *   scale  [rows] fp32
- *   layout convrot_layout (CONVROT_LAYOUT_ROWS for activations)
+ *   layout convrot_layout
  * The same struct describes a packed activation (rows = M) and a packed
  * weight (rows = N; the canonical checkpoint layout, one int8 row per output
  * feature, "INT8 Convrot Safetensors", "Checkpoint format"). */

@@ -532,9 +532,18 @@ def test_tiled_weight_serves_small_m_only(lib):
     assert act_status(lib, act=packed(rows=32), w=tiled) == _lib.ERR_INVALID_ARG
     assert w4_status(lib, w=packed_w4(layout=T16), ws=0x80000, ws_bytes=1 << 20) == _lib.ERR_INVALID_ARG
     assert b"M <= 16" in lib.convrot_last_error()
-    # an activation is never tiled
-    assert linear_status(lib, act=packed(rows=16, layout=T16), w=packed(rows=64, q=0x40000)) == _lib.ERR_INVALID_ARG
-    assert b"activation" in lib.convrot_last_error()
+    # a tiled activation serves M <= 16 with int8 weights, dense rows and whole 64-byte units
+    w = packed(rows=64, q=0x40000, scale=0x50000)
+    assert linear_status(lib, act=packed(rows=17, layout=T16), w=w) == _lib.ERR_INVALID_ARG
+    assert b"TILE16 activation serves M <= 16" in lib.convrot_last_error()
+    assert linear_status(lib, act=packed(rows=16, ld=512, layout=T16), w=w) == _lib.ERR_INVALID_ARG
+    assert b"ld == K" in lib.convrot_last_error()
+    assert linear_status(lib, act=packed(rows=4, K=96, G=16, layout=T16),
+                         w=packed(rows=64, K=96, G=16, q=0x40000, scale=0x50000)) == _lib.ERR_INVALID_ARG
+    assert linear_status(lib, act=packed(rows=4, layout=3), w=w) == _lib.ERR_INVALID_ARG
+    assert b"unknown layout" in lib.convrot_last_error()
+    assert w4_status(lib, act=packed(rows=4, layout=T16), ws=0x80000, ws_bytes=1 << 20) == _lib.ERR_INVALID_ARG
+    assert b"ROWS" in lib.convrot_last_error()
 
 
 def test_gated_pairs_share_a_layout(lib):
@@ -550,7 +559,13 @@ def test_gated_pairs_share_a_layout(lib):
 
 
 def test_packing_and_unpacking_stay_in_rows(lib):
-    assert pack_status(lib, out=packed(rows=16, layout=T16)) == _lib.ERR_INVALID_ARG
+    # a packed activation may be tiled (dense rows, K % 64 == 0); a packed weight is written in rows
+    assert pack_status(lib, out=packed(rows=16, ld=512, layout=T16)) == _lib.ERR_INVALID_ARG
+    assert b"ld == K" in lib.convrot_last_error()
+    assert pack_status(lib, out=packed(rows=4, K=96, G=16, layout=T16)) == _lib.ERR_INVALID_ARG
+    assert lib.convrot_pack_weight(A16C, _lib.BF16, 256, ctypes.byref(packed(rows=16, layout=T16)),
+                                   None) == _lib.ERR_INVALID_ARG
+    assert b"ROWS" in lib.convrot_last_error()
     out = packed_w4(layout=T16)
     assert lib.convrot_pack_weight_w4(A16C, _lib.BF16, 256, ctypes.byref(out), None) == _lib.ERR_INVALID_ARG
     assert lib.convrot_unpack_w4(ctypes.byref(out), A16C, 256, None) == _lib.ERR_INVALID_ARG

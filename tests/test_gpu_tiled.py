@@ -154,6 +154,65 @@ def test_tiled_weight_on_the_no_allocation_entry_point(cuda):
                           O.int_gemm(qx, qw))
 
 
+XSHAPES = [(1, 1152, 6912, 64, torch.bfloat16), (3, 17008, 2048, 256, torch.float32),
+           (5, 6912, 1152, 64, torch.bfloat16), (8, 640, 64, 64, torch.bfloat16),
+           (12, 9008, 5248, 16, torch.bfloat16), (16, 3200, 8192, 256, torch.float32),
+           (16, 1152, 6912, 64, torch.bfloat16)]
+
+
+@pytest.mark.parametrize("M,N,K,G,dt", XSHAPES)
+def test_tiled_activation_gives_the_same_bits(cuda, M, N, K, G, dt):
+    """pack_act(layout=TILE16) writes the TILE16 permutation of the ROWS
+    codes (one 16-row tile), and every int8-weight small-M call reading it
+    returns the bits it returns for the ROWS activation."""
+    seed = 19 * N + K + M
+    g = np.random.default_rng(seed)
+    x = torch.from_numpy(g.standard_normal((M, K)).astype(np.float32)).to(cuda).to(dt)
+    a = cr.pack_act(x, G)
+    at = cr.pack_act(x, G, layout=cr.TILE16)
+    assert at.layout == cr.TILE16 and tuple(at.q.shape) == (M, K)
+    assert torch.equal(at.scale, a.scale)
+    full = to_np(at.q.as_strided((16, K), (K, 1)))
+    pad = np.zeros((16 - M, K), dtype=np.int8)
+    exp = tile16(np.vstack([to_np(a.q), pad]))
+    mask = tile16(np.vstack([np.ones((M, K), dtype=np.int8), pad])).astype(bool)
+    assert np.array_equal(full[mask], exp[mask])
+
+    qg, qu = random_codes((N, K), seed + 1), random_codes((N, K), seed + 2)
+    wg = cr.Packed(to_dev(qg, torch.int8), to_dev(_scales(N, seed + 1), torch.float32), G)
+    wu = cr.Packed(to_dev(qu, torch.int8), to_dev(_scales(N, seed + 2), torch.float32), G)
+    b = to_dev((g.standard_normal(N) * 0.5).astype(np.float32), torch.float32)
+    ws = cr.linear_workspace("plain", M, N, K, cuda)
+    wsg = cr.linear_workspace("gated", M, N, K, cuda)
+    assert np.array_equal(to_np(cr.linear(at, wg, out_dtype=torch.int32)), O.int_gemm(to_np(a.q), qg))
+    tiled = N % 16 == 0
+    for w, u in ((wg, wu), (cr.tile_weight(wg), cr.tile_weight(wu))) if tiled else ((wg, wu),):
+        for w_s in (None, ws):
+            for odt in (torch.int32, torch.float32, torch.bfloat16):
+                assert _same(cr.linear(at, w, b, out_dtype=odt, workspace=w_s),
+                             cr.linear(a, w, b, out_dtype=odt, workspace=w_s))
+            assert _same(cr.linear_act(at, w, b, cr.GELU_ERF, workspace=w_s),
+                         cr.linear_act(a, w, b, cr.GELU_ERF, workspace=w_s))
+        for w_s in (None, wsg):
+            assert _same(cr.linear_gated(at, w, u, b, None, cr.GELU_TANH, out_dtype=torch.float32, workspace=w_s),
+                         cr.linear_gated(a, w, u, b, None, cr.GELU_TANH, out_dtype=torch.float32, workspace=w_s))
+        for odt in (torch.int32, torch.bfloat16):
+            assert _same(cr.linear_noalloc(at, w, torch.empty((M, N), dtype=odt, device=cuda), b),
+                         cr.linear_noalloc(a, w, torch.empty((M, N), dtype=odt, device=cuda), b))
+
+
+def test_tiled_activation_is_refused_where_it_is_not_read(cuda):
+    x = torch.randn(17, 256, device=cuda)
+    with pytest.raises(ValueError, match="M <= 16"):
+        cr.pack_act(x, 64, layout=cr.TILE16)
+    with pytest.raises(ValueError, match="K % 64"):
+        cr.pack_act(x[:4, :96], 16, layout=cr.TILE16)
+    at = cr.pack_act(x[:4], 64, layout=cr.TILE16)
+    w4 = cr.pack_weight_w4(torch.randn(64, 256, device=cuda), 64)
+    with pytest.raises(RuntimeError, match="ROWS"):
+        cr.linear_w4(at, w4)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("M", [1, 16])
 def test_decode_ffn_tiled_full(cuda, M):

@@ -12,7 +12,7 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libconvrot.so")
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # convrot_status

@@ -45,7 +45,7 @@ class Packed:
     group: int
     kind: str = REGULAR
     signs: torch.Tensor | None = None
-    layout: str = ROWS       # ROWS, or TILE16 for a weight read only at M <= 16 (tile_weight)
+    layout: str = ROWS       # ROWS, or TILE16 for operands read only at M <= 16 (tile_weight, pack_act)
 
     @property
     def rows(self) -> int:
@@ -177,24 +177,32 @@ def _check_signs(signs, K, kind):
         raise ValueError("signs are only used by the randomized rotation")
 
 
-def _pack(fn, x: torch.Tensor, group: int, kind: str, signs, out: Packed | None) -> Packed:
+def _pack(fn, x: torch.Tensor, group: int, kind: str, signs, out: Packed | None, layout: str = ROWS) -> Packed:
     _need_cuda(x, "input")
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("input must be float32 or bfloat16")
     rows, K = x.shape
     _check_signs(signs, K, kind)
     if out is None:
-        out = Packed(torch.empty((rows, K), dtype=torch.int8, device=x.device),
-                     torch.empty((rows,), dtype=torch.float32, device=x.device), group, kind, signs)
+        _layout(layout)
+        if layout == TILE16 and (rows > 16 or K % 64):
+            raise ValueError("a TILE16 activation needs M <= 16 and K % 64 == 0")
+        # a TILE16 activation is one 16-row tile (16 * K bytes) whatever M is
+        q = torch.empty((16 if layout == TILE16 else rows, K), dtype=torch.int8, device=x.device)[:rows]
+        out = Packed(q, torch.empty((rows,), dtype=torch.float32, device=x.device), group, kind, signs, layout)
     desc = out.descriptor()
     _lib.check(fn(x.data_ptr(), _DT[x.dtype], _ld(x), ctypes.byref(desc), _stream(x.device)))
     return out
 
 
 def pack_act(x: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,
-             out: Packed | None = None) -> Packed:
-    """Rotate + quantise activation rows (convrot_pack_act)."""
-    return _pack(_lib.load().convrot_pack_act, x, group, kind, signs, out)
+             out: Packed | None = None, layout: str = ROWS) -> Packed:
+    """Rotate + quantise activation rows (convrot_pack_act).  ``layout=TILE16``
+    (M <= 16, K % 64 == 0) writes the codes as one 16-row tile whose 64-byte
+    K units are each 1 KiB of consecutive memory, the layout the small-M
+    kernel reads in whole cache lines; only the int8-weight linear, act and
+    gated calls accept such an activation.  ``out`` keeps its own layout."""
+    return _pack(_lib.load().convrot_pack_act, x, group, kind, signs, out, layout)
 
 
 def pack_weight(w: torch.Tensor, group: int = 256, kind: str = REGULAR, signs: torch.Tensor | None = None,

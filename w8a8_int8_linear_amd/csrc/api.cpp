@@ -120,7 +120,22 @@ convrot_status check_layout(const char* name, int32_t layout, int64_t rows, int6
   return CONVROT_OK;
 }
 
-convrot_status check_packed(const char* name, const convrot_packed* p, int* log2G) {
+// An activation may take the TILE16 layout too, with dense rows and whole
+// 64-byte units; its buffer holds whole tiles of 16 rows (the rows past the
+// last are padding).  Only the weight-streaming path reads it (M <= 16, int8
+// weights).
+convrot_status check_act_layout(const char* name, const convrot_packed* p) {
+  if (p->layout == CONVROT_LAYOUT_ROWS) return CONVROT_OK;
+  if (p->layout != CONVROT_LAYOUT_TILE16)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: unknown layout %d", name, static_cast<int>(p->layout));
+  if (p->ld != p->K || p->K % 64 != 0)
+    return fail(CONVROT_ERR_INVALID_ARG,
+                "%s: a TILE16 activation needs ld == K (got ld %lld, K %lld) and K %% 64 == 0", name,
+                static_cast<long long>(p->ld), static_cast<long long>(p->K));
+  return CONVROT_OK;
+}
+
+convrot_status check_packed(const char* name, const convrot_packed* p, int* log2G, bool activation) {
   if (p == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s descriptor is NULL", name);
   convrot_status st = check_k(p->K, kMaxK);
   if (st != CONVROT_OK) return st;
@@ -131,11 +146,15 @@ convrot_status check_packed(const char* name, const convrot_packed* p, int* log2
   if (p->rows > 0 && p->scale == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s scale is NULL", name);
   if ((reinterpret_cast<uintptr_t>(p->scale) & 3u) != 0)
     return fail(CONVROT_ERR_ALIGN, "%s scale must be 4-byte aligned", name);
+  if (activation) return check_act_layout(name, p);
   return check_layout(name, p->layout, p->rows, p->ld, p->K, 64, p->K);
 }
 
-// Only weights may be tiled, and only the weight-streaming path (M <= 16)
-// reads the tiled layout.
+convrot_status check_packed(const char* name, const convrot_packed* p, int* log2G) {
+  return check_packed(name, p, log2G, false);
+}
+
+// Only the weight-streaming path (M <= 16) reads the tiled layout.
 convrot_status check_rows_layout(const char* name, int32_t layout) {
   if (layout != CONVROT_LAYOUT_ROWS)
     return fail(CONVROT_ERR_INVALID_ARG, "%s must be in the ROWS layout", name);
@@ -151,15 +170,17 @@ convrot_status check_weight_layout_for_m(const char* fn, int32_t layout, int64_t
 }
 
 convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int64_t ldx,
-                         const convrot_packed* out, void* stream) {
+                         const convrot_packed* out, void* stream, bool activation) {
   int log2G = 0;
   if (out == nullptr) return fail(CONVROT_ERR_INVALID_ARG, "%s: output descriptor is NULL", what);
   convrot_status st = check_k(out->K, kMaxPackK);
   if (st != CONVROT_OK) return st;
-  st = check_packed("packed output", out, &log2G);
+  st = check_packed("packed output", out, &log2G, activation);
   if (st != CONVROT_OK) return st;
-  st = check_rows_layout("packed output", out->layout);
-  if (st != CONVROT_OK) return st;
+  if (!activation) {
+    st = check_rows_layout("packed output", out->layout);
+    if (st != CONVROT_OK) return st;
+  }
   if (xdt != CONVROT_F32 && xdt != CONVROT_BF16)
     return fail(CONVROT_ERR_DTYPE, "%s: input must be CONVROT_F32 or CONVROT_BF16", what);
   st = check_matrix("input", X, out->rows, out->K, ldx, elt_size(xdt));
@@ -168,7 +189,7 @@ convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int
   const hipError_t e = convrot::launch_pack_rows(
       X, static_cast<convrot::Elt>(xdt), out->rows, out->K, ldx, log2G,
       static_cast<convrot::RotKind>(out->rot.kind), out->rot.signs, out->q, out->ld, out->scale, nullptr, 0,
-      static_cast<hipStream_t>(stream));
+      static_cast<hipStream_t>(stream), out->layout == CONVROT_LAYOUT_TILE16);
   return from_hip(e, what);
 }
 
@@ -177,12 +198,13 @@ convrot_status pack_impl(const char* what, const void* X, convrot_dtype xdt, int
 convrot_status check_linear(const char* fn, const convrot_packed* act, const convrot_packed* w, const float* bias,
                             const void* Y, convrot_dtype ydt, int64_t ldy, bool i32_ok) {
   int lga = 0, lgw = 0;
-  convrot_status st = check_packed("activation", act, &lga);
+  convrot_status st = check_packed("activation", act, &lga, true);
   if (st != CONVROT_OK) return st;
   st = check_packed("weight", w, &lgw);
   if (st != CONVROT_OK) return st;
-  st = check_rows_layout("activation", act->layout);
-  if (st != CONVROT_OK) return st;
+  if (act->layout == CONVROT_LAYOUT_TILE16 && act->rows > convrot::kGemvMaxRows)
+    return fail(CONVROT_ERR_INVALID_ARG, "%s: a TILE16 activation serves M <= %d only (M = %lld)", fn,
+                convrot::kGemvMaxRows, static_cast<long long>(act->rows));
   st = check_weight_layout_for_m(fn, w->layout, act->rows);
   if (st != CONVROT_OK) return st;
   if (act->K != w->K)
@@ -335,12 +357,12 @@ extern "C" {
 
 convrot_status convrot_pack_act(const void* X, convrot_dtype xdt, int64_t ldx, const convrot_packed* out,
                                 void* stream) {
-  return pack_impl("convrot_pack_act", X, xdt, ldx, out, stream);
+  return pack_impl("convrot_pack_act", X, xdt, ldx, out, stream, true);
 }
 
 convrot_status convrot_pack_weight(const void* W, convrot_dtype wdt, int64_t ldw, const convrot_packed* out,
                                    void* stream) {
-  return pack_impl("convrot_pack_weight", W, wdt, ldw, out, stream);
+  return pack_impl("convrot_pack_weight", W, wdt, ldw, out, stream, false);
 }
 
 convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w, const float* bias, void* Y,
@@ -357,7 +379,8 @@ convrot_status convrot_linear(const convrot_packed* act, const convrot_packed* w
     st = check_split_workspace(workspace, workspace_bytes, small_m_workspace(CONVROT_LINEAR_PLAIN, M, N, K));
     if (st != CONVROT_OK) return st;
     e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy,
-                                workspace, s, w->layout == CONVROT_LAYOUT_TILE16);
+                                workspace, s, w->layout == CONVROT_LAYOUT_TILE16,
+                                act->layout == CONVROT_LAYOUT_TILE16);
   } else {
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
@@ -421,7 +444,7 @@ convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_p
       if (st != CONVROT_OK) return st;
     }
     e = convrot::launch_gemv_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, ws,
-                                s, w->layout == CONVROT_LAYOUT_TILE16);
+                                s, w->layout == CONVROT_LAYOUT_TILE16, act->layout == CONVROT_LAYOUT_TILE16);
   } else {
     e = convrot::launch_gemm_i8(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, M, N, K, Y, out, ldy, s);
   }
@@ -466,7 +489,8 @@ convrot_status convrot_linear_act(const convrot_packed* act, const convrot_packe
   const hipError_t e =
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
-                                        out, ldy, workspace, s, w->layout == CONVROT_LAYOUT_TILE16)
+                                        out, ldy, workspace, s, w->layout == CONVROT_LAYOUT_TILE16,
+                                        act->layout == CONVROT_LAYOUT_TILE16)
           : convrot::launch_gemm_i8_act(act->q, act->ld, w->q, w->ld, act->scale, w->scale, bias, a, M, N, K, Y,
                                         out, ldy, s);
   return from_hip(e, "convrot_linear_act");
@@ -479,6 +503,8 @@ convrot_status convrot_linear_act_rowmax(const convrot_packed* act, const convro
   convrot_status st = check_act(fn);
   if (st != CONVROT_OK) return st;
   st = check_linear(what, act, w, bias, Y, ydt, ldy, false);
+  if (st != CONVROT_OK) return st;
+  st = check_rows_layout("activation", act->layout);
   if (st != CONVROT_OK) return st;
   const int lg = log2_exact(group_next);
   if (lg < 2 || lg > 8 || (lg & 1))
@@ -555,7 +581,8 @@ convrot_status convrot_linear_gated(const convrot_packed* act, const convrot_pac
       M <= convrot::kGemvMaxRows
           ? convrot::launch_gemv_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy,
-                                          workspace, s, w_gate->layout == CONVROT_LAYOUT_TILE16)
+                                          workspace, s, w_gate->layout == CONVROT_LAYOUT_TILE16,
+                                          act->layout == CONVROT_LAYOUT_TILE16)
           : convrot::launch_gemm_i8_gated(act->q, act->ld, w_gate->q, w_gate->ld, w_gate->scale, b_gate, w_up->q,
                                           w_up->ld, w_up->scale, b_up, act->scale, a, M, N, K, Y, out, ldy, s);
   return from_hip(e, "convrot_linear_gated");
@@ -695,6 +722,7 @@ convrot_status convrot_linear_w4(const convrot_packed* act, const convrot_packed
   if (st != CONVROT_OK) return st;
   const convrot_packed wv = as_int8_view(*w);
   st = check_linear(what, act, &wv, bias, Y, ydt, ldy, fn == CONVROT_ACT_NONE);
+  if (st == CONVROT_OK) st = check_rows_layout("activation", act->layout);
   if (st != CONVROT_OK) return st;
   const int64_t M = act->rows, N = w->rows, K = act->K;
   if (M == 0 || N == 0) return ok();
@@ -735,6 +763,7 @@ convrot_status convrot_linear_w4_gated(const convrot_packed* act, const convrot_
   if (st != CONVROT_OK) return st;
   const convrot_packed gv = as_int8_view(*w_gate), uv = as_int8_view(*w_up);
   st = check_linear(what, act, &gv, b_gate, Y, ydt, ldy, false);
+  if (st == CONVROT_OK) st = check_rows_layout("activation", act->layout);
   if (st != CONVROT_OK) return st;
   st = check_linear(what, act, &uv, b_up, Y, ydt, ldy, false);
   if (st != CONVROT_OK) return st;

@@ -299,7 +299,8 @@ template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPL
           int TILES = 1, bool DMA = false, bool XP = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled, XPackArgs xp) {
+    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled, bool xtiled,
+    XPackArgs xp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   static_assert(!W4 || I8, "int4 weights pair with int8 activations");
   static_assert(TILES == 1 || (!GATED && !SPLIT), "several tiles per workgroup only on the plain unsplit path");
@@ -348,7 +349,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   if constexpr (XP) {
     xlds = (lds_bytes_t)(xs + min(row, M - 1) * (kbytes + 16) + ch * 16);
   } else {
-    xrow = A + static_cast<int64_t>(min(row, M - 1)) * lda + ch * (W4 ? 32 : 16);
+    // xtiled (int8 weights only): the activation rows in the TILE16 layout,
+    // byte b of row r at (b / 64) KiB + r 64 + b % 64, so that a fragment
+    // load of one unit reads 1 KiB of consecutive memory.
+    xrow = A + (xtiled ? min(row, M - 1) * 64 : static_cast<int64_t>(min(row, M - 1)) * lda) + ch * (W4 ? 32 : 16);
   }
   auto xp_prologue = [&]() {
     if constexpr (XP) {
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     if constexpr (XP)
       return *(lds_i32x4_t)(xlds + byte);
     else
-      return *reinterpret_cast<const i32x4*>(xrow + byte);
+      return *reinterpret_cast<const i32x4*>(xrow + (xtiled ? ((byte >> 6) << 10) + (byte & 63) : byte));
   };
 
   const int nunits = (kbytes + kUnit - 1) / kUnit;
@@ -670,15 +674,15 @@ inline int gemv_num_cus() { return device_cus(); }
 template <bool I8, int OUT, int ACT, bool GATED, bool SPLIT, bool W4, int TILES = 1, bool DMA = false>
 void launch_waves(int waves, dim3 grid, const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
                   const EpiArgs& epi, int m, int n, int kb, int per, void* C, int64_t ldc, const SplitArgs& sp,
-                  bool tiled, hipStream_t stream) {
+                  bool tiled, bool xtiled, hipStream_t stream) {
   switch (waves) {
     case 4:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 4, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(256), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, XPackArgs{});
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, xtiled, XPackArgs{});
       break;
     default:
       hipLaunchKernelGGL((gemv_kernel<I8, OUT, 8, ACT, GATED, SPLIT, W4, TILES, DMA>), grid, dim3(512), 0, stream, a,
-                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, XPackArgs{});
+                         lda, b, ldb, epi, m, n, kb, per, C, ldc, sp, tiled, xtiled, XPackArgs{});
       break;
   }
 }
@@ -744,7 +748,8 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t kbytes, int sets, bool w4, bo
 template <bool I8, int OUT, int ACT = 0, bool GATED = false, bool W4 = false>
 hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, const EpiArgs& epi, int64_t M,
                       int64_t N, int64_t kbytes, void* C, int64_t ldc, void* ws, hipStream_t stream,
-                      bool tiled = false) {
+                      bool tiled = false, bool xtiled_in = false) {
+  const bool xtiled = xtiled_in && I8 && !W4;  // int8 activations with int8 weights only
   constexpr int kSets = GATED ? 2 : 1;
   constexpr int kUnit = W4 ? 128 : kStepBytes;
   // Weights go through LDS in whole lines when a wave streams enough units
@@ -769,11 +774,11 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
       if (per >= kStageMinUnits)
         hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, true>), grid,
                            dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled,
-                           XPackArgs{});
+                           xtiled, XPackArgs{});
       else
         hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, false>), grid,
                            dim3(64 * kWideWaves), 0, stream, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none, tiled,
-                           XPackArgs{});
+                           xtiled, XPackArgs{});
       return hipGetLastError();
     }
   }
@@ -786,10 +791,10 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splits));
     if (kStageable && stage_ok && stage_tiled && per >= kStageMinUnits)
       launch_waves<I8, OUT, ACT, GATED, true, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                 ldc, sp, tiled, stream);
+                                                                 ldc, sp, tiled, xtiled, stream);
     else
       launch_waves<I8, OUT, ACT, GATED, true, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, sp,
-                                                  tiled, stream);
+                                                  tiled, xtiled, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_combine_kernel<I8, OUT, ACT, GATED>), dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
@@ -807,19 +812,19 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
     const dim3 grid(static_cast<unsigned>((tiles + 1) / 2));
     if (stage)
       launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n,
-                                                                              kb, per, C, ldc, none, tiled, stream);
+                                                                              kb, per, C, ldc, none, tiled, xtiled, stream);
     else
       launch_waves<I8, OUT, ACT, GATED, false, W4, GATED ? 1 : 2>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                  ldc, none, tiled, stream);
+                                                                  ldc, none, tiled, xtiled, stream);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(tiles));
   if (stage)
     launch_waves<I8, OUT, ACT, GATED, false, W4, 1, kStageable>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C,
-                                                                ldc, none, tiled, stream);
+                                                                ldc, none, tiled, xtiled, stream);
   else
     launch_waves<I8, OUT, ACT, GATED, false, W4>(waves, grid, a, lda, b, ldb, epi, m, n, kb, per, C, ldc, none,
-                                                 tiled, stream);
+                                                 tiled, xtiled, stream);
   return hipGetLastError();
 }
 
@@ -856,10 +861,10 @@ hipError_t launch_out_packin(const XPackArgs& xp, const void* B, int64_t ldb, co
   const int m = static_cast<int>(M), n = static_cast<int>(N), kb = static_cast<int>(K);
   if (stage)
     hipLaunchKernelGGL(kdma, dim3(static_cast<unsigned>(tiles)), dim3(64 * kWaves), dyn, stream, nullptr, 0, b, ldb,
-                       epi, m, n, kb, per, C, ldc, none, tiled, xp);
+                       epi, m, n, kb, per, C, ldc, none, tiled, false, xp);
   else
     hipLaunchKernelGGL(kreg, dim3(static_cast<unsigned>(tiles)), dim3(64 * kWaves), dyn, stream, nullptr, 0, b, ldb,
-                       epi, m, n, kb, per, C, ldc, none, tiled, xp);
+                       epi, m, n, kb, per, C, ldc, none, tiled, false, xp);
   return hipGetLastError();
 }
 
@@ -911,41 +916,41 @@ int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, bool bf16, bool w4
 
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                           const float* sb, const float* bias, int64_t M, int64_t N, int64_t K, void* C, Elt out,
-                          int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
+                          int64_t ldc, void* ws, hipStream_t stream, bool tiled, bool xtiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   switch (out) {
-    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
-    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
-    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+    case Elt::F32: return launch_out<true, 0>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
+    case Elt::BF16: return launch_out<true, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
+    default: return launch_out<true, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
   }
 }
 
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const float* sa,
                               const float* sb, const float* bias, Act act, int64_t M, int64_t N, int64_t K, void* C,
-                              Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
+                              Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled, bool xtiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sb, bias, nullptr, 0, nullptr, nullptr};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
-               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
-  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled)
-             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled);
+    return f32 ? launch_out<true, 0, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled)
+               : launch_out<true, 1, 1>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
+  return f32 ? launch_out<true, 0, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled)
+             : launch_out<true, 1, 2>(A, lda, B, ldb, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
 }
 
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg, const float* sbg,
                                 const float* biasg, const int8_t* Bu, int64_t ldbu, const float* sbu,
                                 const float* biasu, const float* sa, Act act, int64_t M, int64_t N, int64_t K,
-                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled) {
+                                void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled, bool xtiled) {
   if (M == 0 || N == 0) return hipSuccess;
   const EpiArgs epi{sa, sbg, biasg, reinterpret_cast<const uint8_t*>(Bu), ldbu, sbu, biasu};
   const bool f32 = out == Elt::F32;
   if (act == Act::GeluErf)
-    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
-               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
-  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled)
-             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled);
+    return f32 ? launch_out<true, 0, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled)
+               : launch_out<true, 1, 1, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
+  return f32 ? launch_out<true, 0, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled)
+             : launch_out<true, 1, 2, true>(A, lda, Bg, ldbg, epi, M, N, K, C, ldc, ws, stream, tiled, xtiled);
 }
 
 hipError_t launch_gemv_w4(const int8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, const float* sa,

@@ -14,11 +14,13 @@ enum class Act : int { None = 0, GeluErf = 1, GeluTanh = 2 };
 
 // Fused group rotation + whole-row absmax + int8 quantisation of `rows` rows
 // of X.  When `q` is null the kernel writes the fp32 rotated rows to `xrot`
-// instead (checking mode).  Shapes were validated by the caller.
+// instead (checking mode).  t16: the codes in the TILE16 layout (ldq == K,
+// K % 64 == 0, q holding whole tiles of 16 rows).  Shapes were validated by
+// the caller.
 hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx,
                             int log2G, RotKind kind, const int8_t* signs,
                             int8_t* q, int64_t ldq, float* scale,
-                            float* xrot, int64_t ldr, hipStream_t stream);
+                            float* xrot, int64_t ldr, hipStream_t stream, bool t16 = false);
 
 // The same kernel in int4 weight mode: codes clamped to [-7, 7], scale =
 // row max / 7, written as nibble pairs (K / 2 bytes per row of q).
@@ -93,7 +95,8 @@ int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, bool bf16, bool w4
 hipError_t launch_gemv_i8(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                           const float* sa, const float* sb, const float* bias,
                           int64_t M, int64_t N, int64_t K,
-                          void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false);
+                          void* C, Elt out, int64_t ldc, void* ws, hipStream_t stream, bool tiled = false,
+                          bool xtiled = false);
 
 // Small-M linears that pack their own activation rows: bf16 X [M, ldx
 // elements], M <= kPackinMaxRows, K <= packin_max_k(gated), rotated with
@@ -117,16 +120,19 @@ hipError_t launch_gemv_bf16(const void* A, int64_t lda, const void* B, int64_t l
 hipError_t launch_gemv_i8_act(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                               const float* sa, const float* sb, const float* bias, Act act,
                               int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                              void* ws, hipStream_t stream, bool tiled = false);
+                              void* ws, hipStream_t stream, bool tiled = false, bool xtiled = false);
 hipError_t launch_gemv_i8_gated(const int8_t* A, int64_t lda, const int8_t* Bg, int64_t ldbg,
                                 const float* sbg, const float* biasg, const int8_t* Bu, int64_t ldbu,
                                 const float* sbu, const float* biasu, const float* sa, Act act,
                                 int64_t M, int64_t N, int64_t K, void* C, Elt out, int64_t ldc,
-                                void* ws, hipStream_t stream, bool tiled = false);
+                                void* ws, hipStream_t stream, bool tiled = false, bool xtiled = false);
 
 // The weight of a small-M launch in the TILE16 layout (`tiled`): tiles of
 // 16 rows, each 64-byte K unit of a tile 1 KiB of consecutive memory; ldb is
-// then the bytes of one row.  Needs N % 16 == 0 and whole units.
+// then the bytes of one row.  Needs N % 16 == 0 and whole units.  The int8
+// launches above also read the activation A in that layout (`xtiled`: M <=
+// 16 rows in one tile, lda == K, K % 64 == 0), whose fragment loads then
+// cover whole lines.
 //
 // TILE16 copy of rows of row_bytes bytes (row_bytes % 64 == 0, rows % 16 ==
 // 0): dst receives rows * row_bytes bytes, s_out a copy of s_in [rows].

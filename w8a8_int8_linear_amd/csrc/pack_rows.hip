@@ -63,7 +63,7 @@ using namespace pack;
 template <typename InT, int LOG2G, bool RAND, int QMODE, int CPT, bool PRE = false>
 __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     const InT* __restrict__ X, int64_t ldx, int K, const int8_t* __restrict__ signs,
-    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+    int8_t* __restrict__ q, int64_t ldq, bool t16, float* __restrict__ scale,
     float* __restrict__ xrot, int64_t ldr, const float* __restrict__ pmax, int64_t ldp) {
   static_assert(!PRE || (QMODE == 1 && !RAND), "given group maxima: int8 codes of the regular kind");
   constexpr int G = 1 << LOG2G;
@@ -189,10 +189,14 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
     if (tid == 0) scale[row] = row_scale(amax_u, norm, kQMax);
 
     if constexpr (QMODE == 1) {
-      const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + static_cast<int64_t>(row) * ldq, K);
+      // t16 (TILE16 codes, ldq == K, K % 64 == 0): byte b of the row lies at
+      // (b / 64) KiB + (row % 16) 64 + b % 64 from its 16-row tile.
+      const int64_t base = t16 ? (row >> 4) * 16 * ldq + (row & 15) * 64 : static_cast<int64_t>(row) * ldq;
+      const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + base, t16 ? (K >> 6) << 10 : K);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        __builtin_amdgcn_raw_buffer_store_b128(quant_chunk(v[c], inv), qr, off[c], 0, kNonTemporal);
+        const int o = t16 ? ((off[c] >> 6) << 10) | (off[c] & 63) : off[c];
+        __builtin_amdgcn_raw_buffer_store_b128(quant_chunk(v[c], inv), qr, o, 0, kNonTemporal);
       }
     } else {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kMaxThreads) void pack_rows_kernel(
 
 template <typename InT, int LOG2G, bool RAND, int QMODE, bool PRE = false>
 hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, const int8_t* signs,
-                        int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
+                        int8_t* q, int64_t ldq, bool t16, float* scale, float* xrot, int64_t ldr,
                         hipStream_t stream, const float* pmax = nullptr, int64_t ldp = 0) {
   const int64_t nvt = K / kChunk;  // chunks in a row
   // Chunks per thread: more of them spread the per-wavefront fixed work (the
@@ -226,15 +230,15 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
   switch (cpt) {
     case 1:
       hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 1, PRE>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
+                         static_cast<int>(K), signs, q, ldq, t16, scale, xrot, ldr, pmax, ldp);
       break;
     case 2:
       hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 2, PRE>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
+                         static_cast<int>(K), signs, q, ldq, t16, scale, xrot, ldr, pmax, ldp);
       break;
     case 4:
       hipLaunchKernelGGL((pack_rows_kernel<InT, LOG2G, RAND, QMODE, 4, PRE>), grid, block, 0, stream, x, ldx,
-                         static_cast<int>(K), signs, q, ldq, scale, xrot, ldr, pmax, ldp);
+                         static_cast<int>(K), signs, q, ldq, t16, scale, xrot, ldr, pmax, ldp);
       break;
     default:
       return hipErrorInvalidValue;  // K above 64 * 1024 is rejected by the caller
@@ -244,11 +248,11 @@ hipError_t dispatch_cpt(const void* X, int64_t rows, int64_t K, int64_t ldx, con
 
 template <typename InT, bool RAND, int QMODE>
 hipError_t dispatch_group(int log2G, const void* X, int64_t rows, int64_t K, int64_t ldx,
-                          const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot,
+                          const int8_t* signs, int8_t* q, int64_t ldq, bool t16, float* scale, float* xrot,
                           int64_t ldr, hipStream_t stream) {
-#define CONVROT_PACK_CASE(LG)                                                                   \
-  case LG:                                                                                      \
-    return dispatch_cpt<InT, LG, RAND, QMODE>(X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, \
+#define CONVROT_PACK_CASE(LG)                                                                        \
+  case LG:                                                                                           \
+    return dispatch_cpt<InT, LG, RAND, QMODE>(X, rows, K, ldx, signs, q, ldq, t16, scale, xrot, ldr, \
                                               stream);
   if constexpr (RAND) {
     switch (log2G) {
@@ -276,20 +280,21 @@ hipError_t dispatch_group(int log2G, const void* X, int64_t rows, int64_t K, int
 
 template <typename InT, int QMODE>
 hipError_t dispatch_kind(int log2G, RotKind kind, const void* X, int64_t rows, int64_t K, int64_t ldx,
-                         const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
-                         hipStream_t stream) {
+                         const int8_t* signs, int8_t* q, int64_t ldq, bool t16, float* scale, float* xrot,
+                         int64_t ldr, hipStream_t stream) {
   if (kind == RotKind::Randomized)
-    return dispatch_group<InT, true, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
-  return dispatch_group<InT, false, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+    return dispatch_group<InT, true, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, t16, scale, xrot, ldr, stream);
+  return dispatch_group<InT, false, QMODE>(log2G, X, rows, K, ldx, signs, q, ldq, t16, scale, xrot, ldr, stream);
 }
 
 template <int QMODE>
 hipError_t dispatch_input(Elt xdt, int log2G, RotKind kind, const void* X, int64_t rows, int64_t K, int64_t ldx,
-                          const int8_t* signs, int8_t* q, int64_t ldq, float* scale, float* xrot, int64_t ldr,
-                          hipStream_t stream) {
+                          const int8_t* signs, int8_t* q, int64_t ldq, bool t16, float* scale, float* xrot,
+                          int64_t ldr, hipStream_t stream) {
   if (xdt == Elt::BF16)
-    return dispatch_kind<uint16_t, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
-  return dispatch_kind<float, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, xrot, ldr, stream);
+    return dispatch_kind<uint16_t, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, t16, scale, xrot, ldr,
+                                          stream);
+  return dispatch_kind<float, QMODE>(log2G, kind, X, rows, K, ldx, signs, q, ldq, t16, scale, xrot, ldr, stream);
 }
 
 template <typename InT>
@@ -297,8 +302,8 @@ hipError_t dispatch_prescaled(int log2G, const void* X, int64_t rows, int64_t K,
                               float* scale, const float* pmax, int64_t ldp, hipStream_t stream) {
 #define CONVROT_PRE_CASE(LG)                                                                                 \
   case LG:                                                                                                   \
-    return dispatch_cpt<InT, LG, false, 1, true>(X, rows, K, ldx, nullptr, q, ldq, scale, nullptr, 0, stream, \
-                                                 pmax, ldp);
+    return dispatch_cpt<InT, LG, false, 1, true>(X, rows, K, ldx, nullptr, q, ldq, false, scale, nullptr, 0, \
+                                                 stream, pmax, ldp);
   switch (log2G) {
     CONVROT_PRE_CASE(2)
     CONVROT_PRE_CASE(4)
@@ -322,19 +327,19 @@ hipError_t launch_pack_rows_prescaled(const void* X, Elt xdt, int64_t rows, int6
 
 hipError_t launch_pack_rows(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
                             RotKind kind, const int8_t* signs, int8_t* q, int64_t ldq, float* scale,
-                            float* xrot, int64_t ldr, hipStream_t stream) {
+                            float* xrot, int64_t ldr, hipStream_t stream, bool t16) {
   if (rows == 0) return hipSuccess;
   if (q != nullptr)
-    return dispatch_input<1>(xdt, log2G, kind, X, rows, K, ldx, signs, q, ldq, scale, nullptr, 0, stream);
-  return dispatch_input<0>(xdt, log2G, kind, X, rows, K, ldx, signs, nullptr, 0, scale, xrot, ldr, stream);
+    return dispatch_input<1>(xdt, log2G, kind, X, rows, K, ldx, signs, q, ldq, t16, scale, nullptr, 0, stream);
+  return dispatch_input<0>(xdt, log2G, kind, X, rows, K, ldx, signs, nullptr, 0, false, scale, xrot, ldr, stream);
 }
 
 hipError_t launch_pack_rows_w4(const void* X, Elt xdt, int64_t rows, int64_t K, int64_t ldx, int log2G,
                                RotKind kind, const int8_t* signs, uint8_t* q, int64_t ldq, float* scale,
                                hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  return dispatch_input<2>(xdt, log2G, kind, X, rows, K, ldx, signs, reinterpret_cast<int8_t*>(q), ldq, scale,
-                           nullptr, 0, stream);
+  return dispatch_input<2>(xdt, log2G, kind, X, rows, K, ldx, signs, reinterpret_cast<int8_t*>(q), ldq, false,
+                           scale, nullptr, 0, stream);
 }
 
 }  // namespace convrot
