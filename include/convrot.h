@@ -170,7 +170,7 @@ typedef struct {
  *           tiles of 16 rows, i.e. 16 K bytes for M <= 16): the
  *           activation fragments of the weight-streaming kernel are then
  *           1 KiB of consecutive memory per unit instead of 16 row pieces
- *           (decode step at M = 4-16 about 4-5% faster).  convrot_pack_act
+ *           (measured: decode step 3.5-5% faster at M = 4-16, level at M = 1).  convrot_pack_act
  *           writes it when its output descriptor asks for it; convrot_linear,
  *           _act, _gated and _noalloc read it for M <= 16 with int8 weights
  *           of either layout; every other entry point takes ROWS
