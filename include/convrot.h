@@ -287,8 +287,10 @@ convrot_status convrot_linear_noalloc(const convrot_packed* act, const convrot_p
  *   M <= 16  the split-K partial sums (0 when the shape does not split K;
  *            always 0 for the int4 kinds, whose split measured slower, and
  *            for plain int8 calls with M <= 12, which run one wide
- *            workgroup per tile instead); optional, NULL selects the
- *            unsplit kernel
+ *            workgroup per tile instead; with a TILE16 activation plain
+ *            int8 calls up to M = 16 take the wide workgroups too and leave
+ *            the workspace unused); optional, NULL selects the unsplit
+ *            kernel
  *   M > 16   0, except CONVROT_LINEAR_W4 (N * K, required) and
  *            CONVROT_LINEAR_W4_GATED (2 * N * K, required)
  * The size depends on the device's CU count.  M, N >= 0 and K a positive

@@ -702,23 +702,29 @@ inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 
 // (1152 x 6912, TILE16 weights), against the split with its combining
 // launch: the step 8.7% faster at M = 1, 8% at M = 2, 6% at M = 4, 5% at
 // M = 8, 4.5% at M = 12, but 6.6% slower at M = 16, where the sixteen
-// activation rows double what each of the few CUs reads.
+// activation rows double what each of the few CUs reads.  With the
+// activation in the TILE16 layout its fragments are whole lines, and up to
+// 16 rows take the wide workgroups (M = 16 step 17.8-17.9 us against
+// 18.9-19.1 split, same box).
 constexpr int kWideWaves = 16;
 // A wave stages its weights through LDS when it streams at least this many
 // K units (a round is two units).
 constexpr int kStageMinUnits = 5;
 constexpr int64_t kWideMaxRows = 12;
-bool wide_tiles(int64_t M, int64_t N, int64_t nunits, bool i8, bool w4, int sets) {
-  return i8 && !w4 && sets == 1 && M <= kWideMaxRows && (N + 15) / 16 < gemv_num_cus() &&
-         nunits >= 2 * kWideWaves;
+constexpr int64_t kWideMaxRowsTiledX = 16;
+bool wide_tiles(int64_t M, int64_t N, int64_t nunits, bool i8, bool w4, int sets, bool xtiled = false) {
+  return i8 && !w4 && sets == 1 && M <= (xtiled ? kWideMaxRowsTiledX : kWideMaxRows) &&
+         (N + 15) / 16 < gemv_num_cus() && nunits >= 2 * kWideWaves;
 }
 
 // How a small-M launch splits K across workgroups: `splits` K ranges of
 // `units` K units per 16-feature tile (splits == 1: no split) and the bytes
 // of partial sums that needs (kSets x 64 lanes x 16 bytes per tile and
 // range).  K is split only when there are fewer tiles than CUs and the
-// launch does not take one wide workgroup per tile: aim at two workgroups
-// per CU and keep at least 8 MFMA steps per range.
+// launch does not take one wide workgroup per tile (the size assumes ROWS
+// activations; a TILE16 activation may take the wide workgroups instead and
+// leave the workspace unused): aim at two workgroups per CU and keep at
+// least 8 MFMA steps per range.
 struct SplitPlan {
   int64_t splits;
   int64_t units;
@@ -767,7 +773,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
 
   // The caller's workspace (validated to hold plan.bytes) enables the split.
   if constexpr (I8 && !W4 && !GATED) {
-    if (wide_tiles(M, N, nunits, I8, W4, kSets)) {
+    if (wide_tiles(M, N, nunits, I8, W4, kSets, xtiled)) {
       const int per = static_cast<int>((nunits + kWideWaves - 1) / kWideWaves);
       const dim3 grid(static_cast<unsigned>(tiles));
       const SplitArgs none{nullptr, 1, 0};
