@@ -31,6 +31,8 @@ Workloads (``--workload``):
                  block rotation (G = 128).  G = 1024 divides neither width,
                  so every linear routes to bf16.  Suffix "_w4": the same layer
                  with int4 weights (W4A8; codes in [-7, 7], nibble pairs).
+                 Weights and packed activations take the TILE16 layout
+                 (``--row-weights`` / ``--row-activations`` keep rows).
   unit_layer     X fp32 [64, 1024], W [1024, 1024], fp32 output.
 
 Inputs live in HBM before timing starts.  To keep the 256 MB Infinity Cache
