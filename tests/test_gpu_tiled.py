@@ -157,7 +157,7 @@ def test_tiled_weight_on_the_no_allocation_entry_point(cuda):
 XSHAPES = [(1, 1152, 6912, 64, torch.bfloat16), (3, 17008, 2048, 256, torch.float32),
            (5, 6912, 1152, 64, torch.bfloat16), (8, 640, 64, 64, torch.bfloat16),
            (12, 9008, 5248, 16, torch.bfloat16), (16, 3200, 8192, 256, torch.float32),
-           (16, 1152, 6912, 64, torch.bfloat16)]
+           (16, 1152, 6912, 64, torch.bfloat16), (5, 1000, 4096, 64, torch.bfloat16)]
 
 
 @pytest.mark.parametrize("M,N,K,G,dt", XSHAPES)

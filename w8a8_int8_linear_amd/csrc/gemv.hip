@@ -299,7 +299,7 @@ template <bool I8, int OUT, int WAVES, int ACT = 0, bool GATED = false, bool SPL
           int TILES = 1, bool DMA = false, bool XP = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, EpiArgs epi, int M,
-    int N, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled, bool xtiled,
+    int N_all, int kbytes, int per, void* __restrict__ C, int64_t ldc, SplitArgs sp, bool tiled, bool xtiled,
     XPackArgs xp) {
   static_assert(!GATED || I8, "the gated pair is an int8 feature");
   static_assert(!W4 || I8, "int4 weights pair with int8 activations");
@@ -316,7 +316,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int n0 = blockIdx.x * 16 * TILES;
+  // The wide workgroups (16 waves, not packing) each take 8 output features:
+  // rows 8-15 of the MFMA's weight operand repeat row 7 and their columns
+  // are not written, which doubles the workgroups streaming a narrow
+  // weight.  N below is this workgroup's end of the output features.
+  constexpr bool kHalf = WAVES == 16 && !XP;
+  const int n0 = kHalf ? blockIdx.x * 8 : blockIdx.x * 16 * TILES;
+  const int N = kHalf ? min(N_all, n0 + 8) : N_all;
   const int row = lane & 15;
   const int ch = lane >> 4;
 
@@ -325,7 +331,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   // of a row lies unit_stride bytes after the previous one, and row r of a
   // tile row_pitch bytes after its first row: 64 and ldb in the row layout,
   // 1024 and 64 in the TILE16 layout (whose tiles start where the row
-  // layout's 16-row blocks do, ldb being the bytes of one row).
+  // layout's 16-row blocks do, ldb being the bytes of one row; a workgroup
+  // of 8 features may start in the middle of a tile).
   const int unit_stride = tiled ? 1024 : 64;
   const int64_t pitch1 = tiled ? 64 : ldb;
   const int64_t pitch2 = tiled ? 64 : epi.ldb2;
@@ -334,7 +341,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   for (int i = 0; i < TILES; ++i) {
     const int64_t nt = n0 + 16 * i;
     const int64_t r = min(nt + row, static_cast<int64_t>(N) - 1) - nt;
-    wrow[0][i] = B + nt * ldb + r * pitch1 + ch * 16;
+    const int64_t tb = tiled ? (nt & ~int64_t{15}) : nt;
+    const int64_t rr = tiled ? (nt & 15) + r : r;
+    wrow[0][i] = B + tb * ldb + rr * pitch1 + ch * 16;
     if constexpr (GATED) wrow[kSets - 1][i] = epi.B2 + nt * epi.ldb2 + r * pitch2 + ch * 16;
   }
   // XP: the workgroup packs the M activation rows into LDS (codes at a
@@ -489,7 +498,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
         for (int h = 0; h < 2; ++h) {
           const int64_t nt = n0 + 16 * i;
           const int64_t r = min(nt + 8 * h + drow, static_cast<int64_t>(N) - 1) - nt;
-          dbase[t][i][h] = (t == 0 ? B + nt * ldb + r * pitch1 : epi.B2 + nt * epi.ldb2 + r * pitch2);
+          const int64_t tb = tiled ? (nt & ~int64_t{15}) : nt;
+          const int64_t rr = tiled ? (nt & 15) + r : r;
+          dbase[t][i][h] = (t == 0 ? B + tb * ldb + rr * pitch1 : epi.B2 + nt * epi.ldb2 + r * pitch2);
         }
     auto issue_w = [&](int u0, int buf) {
       const int wb = u0 * 64;  // weight byte of the round's line
@@ -705,7 +716,9 @@ inline int waves_for(int64_t units) { return (units + 3) / 4 <= kMaxUnits ? 4 : 
 // activation rows double what each of the few CUs reads.  With the
 // activation in the TILE16 layout its fragments are whole lines, and up to
 // 16 rows take the wide workgroups (M = 16 step 17.8-17.9 us against
-// 18.9-19.1 split, same box).
+// 18.9-19.1 split, same box).  Each wide workgroup covers 8 features
+// (twice the workgroups of 16-feature tiles): down projection at M = 16
+// 6.8 against 7.35 us, M = 8 5.85 against 6.45, M = 1 5.2 against 5.1.
 constexpr int kWideWaves = 16;
 // A wave stages its weights through LDS when it streams at least this many
 // K units (a round is two units).
@@ -775,7 +788,7 @@ hipError_t launch_out(const void* A, int64_t lda, const void* B, int64_t ldb, co
   if constexpr (I8 && !W4 && !GATED) {
     if (wide_tiles(M, N, nunits, I8, W4, kSets, xtiled)) {
       const int per = static_cast<int>((nunits + kWideWaves - 1) / kWideWaves);
-      const dim3 grid(static_cast<unsigned>(tiles));
+      const dim3 grid(static_cast<unsigned>((N + 7) / 8));
       const SplitArgs none{nullptr, 1, 0};
       if (per >= kStageMinUnits)
         hipLaunchKernelGGL((gemv_kernel<I8, OUT, kWideWaves, ACT, false, false, false, 1, true>), grid,
